@@ -1,0 +1,20 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _oracle_built():
+    """The CPU oracle is test infrastructure: build it here if nothing is built."""
+    from oracle import build_oracle
+    if not os.path.exists(build_oracle.LIB):
+        build_oracle.build()
