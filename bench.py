@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode hot path on one MI355X.
+
+One step = one decode step of one attention layer for the whole batch:
+pa_copy_blocks (copy-on-write pairs of the step; none in this workload),
+pa_write_kv of every sequence's new token, then pa_decode over every
+sequence's paged KV cache.  Inputs are seeded, synthetic and resident in HBM
+before timing starts.  R replicas (disjoint block sets of one pool, their
+own queries and new tokens) are cycled so that consecutive steps read
+different KV bytes, as successive layers would, and the 256 MB last-level
+cache cannot serve them.
+
+Prints one JSON line.  value = KV bytes read per step / seconds per step
+(GB/s); seq_steps_per_s = sequences / seconds per step.  roofline covers
+pa_decode, timed with HIP events on the stream it runs on.  cpu_baseline is
+the fp64 CPU oracle timed on this host's cores over a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="llama13b_f16",
+                    choices=["llama13b_f16", "mixed_gqa_bf16", "long_bf16"])
+    ap.add_argument("--replicas", type=int, default=0, help="0 = as many as the pool allows (max 16)")
+    ap.add_argument("--partition-size", type=int, default=-1, help="-1 = the workload's own")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget; 0 = skip")
+    ap.add_argument("--profile-steps", action="store_true", help="no cpu baseline (for profilers)")
+    return ap.parse_args()
+
+
+def build_case(name, replicas):
+    from paged_kv_cache_328_amd import workloads as wl
+    if name == "llama13b_f16":
+        probe = wl.llama13b_f16(fill=False)
+        need = int(sum(-(-int(c) // probe.BS) for c in probe.context_lens))
+        R = replicas or min(16, probe.NB // need)
+        return wl.llama13b_f16(fill=False, replicas=R)
+    if name == "mixed_gqa_bf16":
+        return wl.mixed_gqa_bf16(fill=False, replicas=replicas or 4)
+    return wl.long_bf16(fill=False, replicas=replicas or 2)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the kernels shard by sequence / KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from paged_kv_cache_328_amd import pagedattn as pa
+    from paged_kv_cache_328_amd import workloads as wl
+
+    pa.lib()  # fail loudly if the library is not built
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    case = build_case(args.config, args.replicas)
+    R, S, dtype = case.replicas, case.S, case.dtype
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    P = case.partition_size if args.partition_size < 0 else args.partition_size
+
+    # ---- inputs, resident in HBM
+    ks, vs = wl.pool_shapes(case.NB, case.Hkv, case.D, case.BS, dtype)
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.base_seed(case.name))
+    kd = torch.randn(ks, dtype=tdt, device=dev, generator=g)
+    vd = torch.randn(vs, dtype=tdt, device=dev, generator=g)
+
+    def dev_storage(a):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    tables = [torch.from_numpy(np.ascontiguousarray(case.block_tables[r])).to(dev) for r in range(R)]
+    lens = torch.from_numpy(case.context_lens).to(dev)
+    qs = [dev_storage(case.q[r]) for r in range(R)]
+    knew = [dev_storage(case.new_k[r]) for r in range(R)]
+    vnew = [dev_storage(case.new_v[r]) for r in range(R)]
+    slots = [torch.from_numpy(np.ascontiguousarray(case.slot_mapping[r])).to(dev) for r in range(R)]
+    no_pairs = torch.zeros((0, 2), dtype=torch.int32, device=dev)
+    out = torch.empty_like(qs[0])
+    max_ctx = case.max_context
+    a0 = pa.make_decode_args(out, qs[0], kd, vd, tables[0], lens, case.scale, max_ctx, P)
+    P_eff = pa.pa_decode_partition_size(a0)
+    ws_bytes = pa.pa_decode_workspace_bytes(a0)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        r = i % R
+        pa.pa_copy_blocks(kd, vd, no_pairs, stream=stream)
+        pa.pa_write_kv(knew[r], vnew[r], kd, vd, slots[r], stream=stream)
+        pa.pa_decode(out, qs[r], kd, vd, tables[r], lens, case.scale, max_ctx, partition_size=P,
+                     workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        r = i % R
+        pa.pa_copy_blocks(kd, vd, no_pairs, stream=stream)
+        pa.pa_write_kv(knew[r], vnew[r], kd, vd, slots[r], stream=stream)
+        ev[i][0].record(stream)
+        pa.pa_decode(out, qs[r], kd, vd, tables[r], lens, case.scale, max_ctx, partition_size=P,
+                     workspace=ws, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec_per_step = (t1 - t0) / args.steps
+    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # ---- algorithmic bytes of one pa_decode launch
+    esz = wl.ELEM_BYTES[dtype]
+    kv_bytes = case.kv_bytes()
+    n_blocks = int(sum(-(-int(c) // case.BS) for c in case.context_lens))
+    decode_bytes = kv_bytes + n_blocks * 4 + S * 4 + 2 * S * case.Hq * case.D * esz
+    achieved = decode_bytes / (decode_ms * 1e-3) / 1e9
+
+    # ---- host bookkeeping (allocator) for one step, reported separately
+    A = pa.Allocator(case.NB, case.BS)
+    for s in range(S):
+        A.pa_seq_add(s)
+        for _ in range(int(case.context_lens[s]) - 1):
+            A.pa_seq_append_slot(s)
+    th = time.perf_counter()
+    n_rep = 200
+    for _ in range(n_rep):
+        A.pa_seq_append_slots(list(range(S)))
+    host_us = (time.perf_counter() - th) / n_rep * 1e6
+    A.close()
+
+    result = {
+        "metric": "paged decode attention: achieved KV GB/s (% HBM peak) and seq-steps/s",
+        "value": round(kv_bytes / sec_per_step / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "pct_hbm_peak": round(100 * kv_bytes / sec_per_step / 1e9 / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(S / sec_per_step, 1),
+        "config": {"workload": case.name, "num_seqs": S, "q_heads": case.Hq, "kv_heads": case.Hkv,
+                   "head_dim": case.D, "block_size": case.BS, "num_blocks": case.NB,
+                   "context_tokens": int(case.context_lens.sum()),
+                   "max_context": max_ctx, "partition_size": P_eff, "replicas": R,
+                   "kv_bytes_per_step": kv_bytes,
+                   "step": "pa_copy_blocks(0 pairs) + pa_write_kv + pa_decode"},
+        "roofline": {"kernel": "pa_decode", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_ms": round(decode_ms, 5),
+                     "algorithmic_bytes_per_launch": decode_bytes},
+        "host_bookkeeping_us": round(host_us, 2),
+    }
+    if args.cpu_seconds > 0 and not args.profile_steps:
+        result["cpu_baseline"] = cpu_baseline(case, kd, vd, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(case, kd, vd, budget_s):
+    """The fp64 CPU oracle on a bounded sample: the first sequences of replica
+    0 (all heads), repeated until ~budget_s of CPU work."""
+    import torch
+    from oracle import oracle
+    from paged_kv_cache_328_amd import workloads as wl
+    dtype = case.dtype
+    cores = len(os.sched_getaffinity(0))
+    n = min(case.S, 4)
+    t = case.block_tables[0][:n]
+    lens = np.ascontiguousarray(case.context_lens[:n])
+    used = np.unique(np.concatenate([t[s, :-(-int(lens[s]) // case.BS)] for s in range(n)]))
+    remap = {int(b): i for i, b in enumerate(used)}
+    tables = np.zeros((n, t.shape[1]), np.int32)
+    for s in range(n):
+        for j in range(-(-int(lens[s]) // case.BS)):
+            tables[s, j] = remap[int(t[s, j])]
+    idx = torch.from_numpy(used.astype(np.int64)).to(kd.device)
+
+    def host(x):
+        x = x.index_select(0, idx).cpu().contiguous()
+        return x.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else x.numpy()
+
+    kc, vc = host(kd), host(vd)
+    q = np.ascontiguousarray(case.q[0][:n])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(q, kc, vc, tables, lens, case.scale, dtype, num_threads=cores)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    kv = 2 * int(lens.sum()) * case.Hkv * case.D * wl.ELEM_BYTES[dtype]
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "seq_steps_per_s": round(n / dt, 3),
+            "sample": f"pa_decode of sequences 0..{n - 1} of replica 0 ({int(lens.sum())} context "
+                      f"tokens, all {case.Hq} query heads), {reps} repetitions in {reps * dt:.1f} s, "
+                      f"{cores} OpenMP threads"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn: paged decode attention on MI355X
+ * (gfx950) plus the host-side block manager that feeds it.
+ *
+ * The method (PagedAttention): a sequence's KV cache lives in fixed-size
+ * physical blocks of block_size tokens that sit anywhere in one device pool;
+ * a per-sequence block table maps logical block i to its physical block id
+ * (wiblog "PagedAttention" page, section on mapping a contiguous sequence
+ * onto scattered blocks).  Decode attention reads the blocks in place through
+ * the table, without first concatenating them (same page, section on why a
+ * dedicated attention kernel is needed).  The attention formula itself is the
+ * ordinary one (same page, opening section).
+ *
+ * Pool layout (the one printed on the intelliparadigm "vLLM Paged Attention
+ * technique" page, section 2.2), row-major, x = 16 bytes / element size:
+ *     k_cache [num_blocks, num_kv_heads, head_dim / x, block_size, x]
+ *     v_cache [num_blocks, num_kv_heads, head_dim,     block_size]
+ * One (block, KV head) tile is one contiguous run of head_dim * block_size
+ * elements in each pool.
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument of a device op is device memory owned by the
+ *     caller; the library allocates no device memory and frees none.
+ *   - Device ops are enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return without synchronising it.  PA_ERR_HIP means the
+ *     launch itself failed; errors inside a kernel surface on the caller's
+ *     next synchronisation.
+ *   - Host-side arguments (sizes, dtype, alignment, workspace size) are
+ *     validated and rejected with PA_ERR_INVALID / PA_ERR_UNSUPPORTED /
+ *     PA_ERR_WORKSPACE before anything is launched.  Device contents (block
+ *     ids, context lengths, slots) are preconditions; a violation gives
+ *     unspecified results for the affected sequence or token, but the kernels
+ *     clamp every index so that no access leaves the arrays described here.
+ *   - No function throws or aborts; nothing is thread-safe unless stated.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_API __attribute__((visibility("default")))
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,      /* bad argument: null pointer, non-positive size, misalignment, ... */
+  PA_ERR_UNSUPPORTED = 2,  /* valid but not compiled in: head_dim, block_size, dtype, group size */
+  PA_ERR_NO_BLOCKS = 3,    /* block manager: free pool exhausted (state unchanged) */
+  PA_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
+  PA_ERR_WORKSPACE = 5,    /* pa_decode: workspace missing or smaller than required */
+  PA_ERR_UNKNOWN_SEQ = 6,  /* block manager: sequence id not present */
+  PA_ERR_EXISTS = 7        /* block manager: sequence id already present */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Static, never-NULL text for a status code. */
+PA_API const char* pa_status_string(pa_status s);
+
+/* ------------------------------------------------------------------------
+ * pa_decode -- one decode step of attention for every sequence.
+ *
+ * For sequence s with context length c = context_lens[s] and query head h
+ * (KV head g = floor(h / G), G = num_q_heads / num_kv_heads, consecutive
+ * grouping):
+ *     x_t = scale * <q[s,h,:], K_t>,  t = 0..c-1 in logical order, where
+ *           K_t / V_t are row (t mod block_size) of physical block
+ *           block_tables[s][t / block_size], KV head g;
+ *     out[s,h,:] = sum_t exp(x_t - max x) V_t / sum_t exp(x_t - max x).
+ * c counts every cached token including the one written this step; c == 0
+ * writes zeros.  Arithmetic: fp32 accumulation; 16-bit inputs feed the
+ * matrix cores with the softmax weights rounded to the input type; out is
+ * rounded once to the element type.
+ *
+ * Long contexts are split into partitions of `partition_size` tokens (the
+ * PARTITION_SIZE split of the intelliparadigm page, sections 3.1-3.2); each
+ * partition yields (running max, sum, unnormalised output) and a second pass
+ * merges them with the log-sum-exp rule.  partition_size == 0 lets the
+ * library choose; otherwise it must be a positive multiple of 32 tokens and
+ * of block_size.
+ *
+ * Layouts: q, out [num_seqs, num_q_heads, head_dim] of `dtype`;
+ * block_tables [num_seqs, max_blocks_per_seq] int32; context_lens
+ * [num_seqs] int32 with 0 <= c <= max_context_len <= max_blocks_per_seq *
+ * block_size.  Entries of a table row past ceil(c / block_size) are never
+ * read.  All pointers 16-byte aligned.
+ * Supported: dtype f16 / bf16 / f32, head_dim 64 or 128, block_size 16 or
+ * 32, any G = num_q_heads / num_kv_heads >= 1.
+ * The workspace (caller-allocated device memory, any contents) holds the
+ * split-K partials; its size comes from pa_decode_workspace_bytes.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_decode_args {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;  /* host-known upper bound of context_lens */
+  float scale;              /* usually 1 / sqrt(head_dim) */
+  int32_t dtype;            /* pa_dtype of q, out, k_cache and v_cache */
+  int32_t partition_size;   /* 0 = library choice */
+  void* workspace;
+  size_t workspace_bytes;
+} pa_decode_args;
+
+/* Bytes of workspace pa_decode needs for these sizes (pointers are not read).
+ * 0 when the step needs none, or when the arguments are invalid. */
+PA_API size_t pa_decode_workspace_bytes(const pa_decode_args* args);
+
+/* The partition size pa_decode will use for these arguments, or -1 when
+ * they are invalid. */
+PA_API int32_t pa_decode_partition_size(const pa_decode_args* args);
+
+PA_API pa_status pa_decode(const pa_decode_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_write_kv -- cache write of the step's new tokens (the "append KV" box
+ * of the wiblog page's flowchart).  For each token t with slot =
+ * slot_mapping[t] >= 0: K and V rows of every KV head go to in-block
+ * position slot % block_size of physical block slot / block_size, bit for
+ * bit.  Negative slots are padding and are skipped; slots >= num_blocks *
+ * block_size are skipped too.  k_new, v_new: [num_tokens, num_kv_heads,
+ * head_dim] of dtype; slot_mapping: [num_tokens] int64.  Two tokens with the
+ * same slot race.
+ * ------------------------------------------------------------------------ */
+PA_API pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             const int64_t* slot_mapping, int32_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_copy_blocks -- copy-on-write block copies (bmjup explainer, section 2
+ * "copy-on-write"; wiblog COW paragraph).  block_mapping is [num_pairs][2]
+ * int32 = {src, dst}: every element of physical block dst (all KV heads,
+ * K and V) becomes a bit copy of block src.  A dst must not appear twice nor
+ * as any pair's src (the pairs pa_seq_append_slot reports satisfy this).
+ * Pairs with an id outside [0, num_blocks) are skipped.
+ * ------------------------------------------------------------------------ */
+PA_API pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
+                                int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t num_blocks, int32_t dtype,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_gather_kv -- test hook: copies each sequence's K and V through its block
+ * table into contiguous k_out, v_out [num_seqs, max_context_len,
+ * num_kv_heads, head_dim] of dtype, bit for bit, in logical token order.
+ * Rows t >= context_lens[s] are left untouched.  This is the "concatenate
+ * the blocks, then run ordinary attention" route that the wiblog page warns
+ * costs extra copies; it exists only to check addressing.
+ * ------------------------------------------------------------------------ */
+PA_API pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              void* k_out, void* v_out, int32_t num_seqs, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block manager (the allocator, free pool, refcounts and block tables
+ * of the pages: bmjup section 3 "dynamic allocation", wiblog flowchart and
+ * COW paragraphs, kongchang refcount paragraph).  Opaque, owned by the
+ * caller, not thread-safe.  Rules:
+ *   - append: when len % block_size == 0 a new block is taken from the free
+ *     pool; otherwise the token goes to the next slot of the last block.  If
+ *     that last block is partly filled AND shared (refcount > 1), the caller
+ *     gets a fresh block instead: the old block's refcount drops by one and
+ *     (old, fresh) is reported so that the caller copies it with
+ *     pa_copy_blocks before writing.  slot = block * block_size + len %
+ *     block_size.
+ *   - fork: the child references every block of the parent (refcount + 1).
+ *   - free: every block's refcount drops by one; blocks reaching 0 return to
+ *     the free pool at once (in logical order).
+ *   - free pool: a stack, initially init_free_order with element 0 on top
+ *     (NULL = 0, 1, 2, ...); freed blocks are pushed on top.
+ *   - PA_ERR_NO_BLOCKS leaves the state unchanged.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_allocator pa_allocator;
+
+/* init_free_order: NULL or a permutation of 0..num_blocks-1 (copied). */
+PA_API pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
+                                 const int32_t* init_free_order, pa_allocator** out);
+PA_API void pa_alloc_destroy(pa_allocator* a);
+PA_API int32_t pa_alloc_num_free(const pa_allocator* a);       /* -1 if a is NULL */
+PA_API int32_t pa_alloc_num_seqs(const pa_allocator* a);       /* -1 if a is NULL */
+PA_API int32_t pa_block_refcount(const pa_allocator* a, int32_t block); /* -1 if out of range */
+
+PA_API pa_status pa_seq_add(pa_allocator* a, int64_t seq);
+PA_API pa_status pa_seq_fork(pa_allocator* a, int64_t parent, int64_t child);
+/* One token; *cow_src = *cow_dst = -1 when nothing must be copied. */
+PA_API pa_status pa_seq_append_slot(pa_allocator* a, int64_t seq, int64_t* slot,
+                                    int32_t* cow_src, int32_t* cow_dst);
+/* One token for each of n distinct sequences (a decode step).  slots[n]
+ * receives the slots; cow_pairs (room for n pairs, [n][2] int32) receives the
+ * copy pairs in sequence order and *num_cow their count.  Either every
+ * append happens or none (PA_ERR_NO_BLOCKS, PA_ERR_UNKNOWN_SEQ, or
+ * PA_ERR_INVALID for a repeated sequence id). */
+PA_API pa_status pa_seq_append_slots(pa_allocator* a, const int64_t* seqs, int32_t n,
+                                     int64_t* slots, int32_t* cow_pairs, int32_t* num_cow);
+PA_API pa_status pa_seq_free(pa_allocator* a, int64_t seq);
+PA_API int32_t pa_seq_len(const pa_allocator* a, int64_t seq);          /* -1 if unknown */
+PA_API int32_t pa_seq_num_blocks(const pa_allocator* a, int64_t seq);   /* -1 if unknown */
+/* Copies the block table into out[0..cap); *n = its full length. */
+PA_API pa_status pa_seq_block_table(const pa_allocator* a, int64_t seq, int32_t* out,
+                                    int32_t cap, int32_t* n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

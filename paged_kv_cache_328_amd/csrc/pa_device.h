@@ -1,0 +1,65 @@
+// Device-side helpers shared by the libpagedattn kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pagedattn.h"
+
+namespace pa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// 16-bit element types: storage is the raw 16-bit pattern.
+struct F16 {
+  using vec8 = f16x8;
+  static __device__ __forceinline__ float to_f32(uint16_t u) {
+    return (float)__builtin_bit_cast(_Float16, u);
+  }
+  static __device__ __forceinline__ uint16_t from_f32(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+  }
+  static __device__ __forceinline__ f32x4 mma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct BF16 {
+  using vec8 = bf16x8;
+  static __device__ __forceinline__ float to_f32(uint16_t u) {
+    return __uint_as_float((uint32_t)u << 16);
+  }
+  static __device__ __forceinline__ uint16_t from_f32(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);  // round to nearest even
+  }
+  static __device__ __forceinline__ f32x4 mma(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void store16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) {
+  return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
+}
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// Wave-uniform value as a scalar (the compiler keeps it in an SGPR).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace pa

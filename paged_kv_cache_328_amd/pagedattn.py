@@ -1,0 +1,300 @@
+"""Thin ctypes binding of libpagedattn.so (argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does no
+arithmetic of its own: it checks shapes/dtypes, turns torch tensors into
+device pointers and the current HIP stream into a handle, and raises
+PaError on a non-zero status.  The library must be built
+(python -m paged_kv_cache_328_amd.build); nothing falls back to another
+implementation when it is missing.
+
+Tensor layouts (all contiguous, on the GPU for the device ops):
+  q, out        [S, Hq, D]                  float32 / float16 / bfloat16
+  k_cache       [NB, Hkv, D/x, BS, x]       x = 16 bytes / element size
+  v_cache       [NB, Hkv, D, BS]
+  block_tables  [S, max_blocks] int32;  context_lens [S] int32
+  k_new, v_new  [T, Hkv, D];            slot_mapping [T] int64
+  block_mapping [P, 2] int32 (src, dst)
+"""
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pagedattn.h")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS = 0, 1, 2, 3
+PA_ERR_HIP, PA_ERR_WORKSPACE, PA_ERR_UNKNOWN_SEQ, PA_ERR_EXISTS = 4, 5, 6, 7
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+DTYPE_NAMES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_lib = None
+
+
+class PaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = lib().pa_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+class pa_decode_args(ctypes.Structure):
+    _fields_ = [
+        ("out", _P), ("q", _P), ("k_cache", _P), ("v_cache", _P),
+        ("block_tables", _P), ("context_lens", _P),
+        ("num_seqs", _I32), ("num_q_heads", _I32), ("num_kv_heads", _I32), ("head_dim", _I32),
+        ("block_size", _I32), ("num_blocks", _I32), ("max_blocks_per_seq", _I32),
+        ("max_context_len", _I32), ("scale", ctypes.c_float), ("dtype", _I32),
+        ("partition_size", _I32), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def lib():
+    """Load libpagedattn.so and declare its signatures (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run python -m paged_kv_cache_328_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    A = ctypes.POINTER(pa_decode_args)
+    sig = {
+        "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "pa_decode_workspace_bytes": (ctypes.c_size_t, [A]),
+        "pa_decode_partition_size": (_I32, [A]),
+        "pa_decode": (ctypes.c_int, [A, _P]),
+        "pa_write_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+        "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+        "pa_gather_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                        _I32, _I32, _I32, _P]),
+        "pa_alloc_create": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_P)]),
+        "pa_alloc_destroy": (None, [_P]),
+        "pa_alloc_num_free": (_I32, [_P]),
+        "pa_alloc_num_seqs": (_I32, [_P]),
+        "pa_block_refcount": (_I32, [_P, _I32]),
+        "pa_seq_add": (ctypes.c_int, [_P, _I64]),
+        "pa_seq_fork": (ctypes.c_int, [_P, _I64, _I64]),
+        "pa_seq_append_slot": (ctypes.c_int, [_P, _I64, ctypes.POINTER(_I64),
+                                              ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+        "pa_seq_append_slots": (ctypes.c_int, [_P, _P, _I32, _P, _P, ctypes.POINTER(_I32)]),
+        "pa_seq_free": (ctypes.c_int, [_P, _I64]),
+        "pa_seq_len": (_I32, [_P, _I64]),
+        "pa_seq_num_blocks": (_I32, [_P, _I64]),
+        "pa_seq_block_table": (ctypes.c_int, [_P, _I64, _P, _I32, ctypes.POINTER(_I32)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def header_symbols():
+    """Names of every entry point declared in include/pagedattn.h."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"PA_API\s+[\w\s\*]+?\b(pa_\w+)\s*\(", text)))
+
+
+def _check(status, where):
+    if status != PA_OK:
+        raise PaError(status, where)
+
+
+# ---------------------------------------------------------------------------- tensors
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    codes = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpagedattn must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def cache_geometry(k_cache, v_cache):
+    """(NB, Hkv, D, BS) of the two pools; checks they agree with the layout."""
+    if k_cache.dim() != 5 or v_cache.dim() != 4 or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache must be [NB, Hkv, D/x, BS, x] and v_cache [NB, Hkv, D, BS]")
+    NB, Hkv, Dx, BS, x = k_cache.shape
+    if x * k_cache.element_size() != 16:
+        raise ValueError(f"k_cache last dim {x} is not 16 bytes of {k_cache.dtype}")
+    D = Dx * x
+    if tuple(v_cache.shape) != (NB, Hkv, D, BS):
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} != {(NB, Hkv, D, BS)}")
+    return NB, Hkv, D, BS
+
+
+def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                     max_context_len, partition_size=0, workspace=None):
+    """Fill a pa_decode_args from tensors (no call into the library)."""
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
+    S, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("q / out must be [S, Hq, D] of the cache's dtype")
+    torch = _torch()
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    a = pa_decode_args()
+    a.out, a.q, a.k_cache, a.v_cache = _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache)
+    a.block_tables, a.context_lens = _ptr(block_tables), _ptr(context_lens)
+    a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim, a.block_size = S, Hq, Hkv, D, BS
+    a.num_blocks, a.max_blocks_per_seq = NB, block_tables.shape[1]
+    a.max_context_len = int(max_context_len)
+    a.scale = float(scale)
+    a.dtype = _dtype_code(q)
+    a.partition_size = int(partition_size)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def pa_decode_workspace_bytes(args):
+    return int(lib().pa_decode_workspace_bytes(ctypes.byref(args)))
+
+
+def pa_decode_partition_size(args):
+    return int(lib().pa_decode_partition_size(ctypes.byref(args)))
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+              partition_size=0, workspace=None, stream=None):
+    """Paged decode attention into `out`.  When the step needs split-K
+    partials and no workspace is given, a byte tensor is allocated with torch
+    on q's device."""
+    a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                         max_context_len, partition_size, workspace)
+    need = pa_decode_workspace_bytes(a)
+    if need and workspace is None:
+        workspace = _torch().empty(need, dtype=_torch().uint8, device=q.device)
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = need
+    _check(lib().pa_decode(ctypes.byref(a), _stream(stream)), "pa_decode")
+    return out
+
+
+def pa_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
+    T = slot_mapping.shape[0]
+    if tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D):
+        raise ValueError("k_new / v_new must be [T, Hkv, D]")
+    if slot_mapping.dtype != _torch().int64 or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise TypeError("slot_mapping must be int64 and k_new / v_new of the cache's dtype")
+    _check(lib().pa_write_kv(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                             _ptr(slot_mapping), T, Hkv, D, BS, NB, _dtype_code(k_cache),
+                             _stream(stream)), "pa_write_kv")
+
+
+def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None):
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
+    if block_mapping.dtype != _torch().int32 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [P, 2] int32")
+    _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
+                                block_mapping.shape[0], Hkv, D, BS, NB, _dtype_code(k_cache),
+                                _stream(stream)), "pa_copy_blocks")
+
+
+def pa_gather_kv(k_cache, v_cache, block_tables, context_lens, k_out, v_out, stream=None):
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
+    S, max_ctx = k_out.shape[0], k_out.shape[1]
+    if tuple(k_out.shape) != (S, max_ctx, Hkv, D) or tuple(v_out.shape) != tuple(k_out.shape):
+        raise ValueError("k_out / v_out must be [S, max_ctx, Hkv, D]")
+    _check(lib().pa_gather_kv(_ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                              _ptr(k_out), _ptr(v_out), S, Hkv, D, BS, NB, block_tables.shape[1],
+                              max_ctx, _dtype_code(k_cache), _stream(stream)), "pa_gather_kv")
+
+
+# ---------------------------------------------------------------------------- block manager
+
+class Allocator:
+    """Owner of one pa_allocator (host block manager)."""
+
+    def __init__(self, num_blocks, block_size, init_free_order=None):
+        self._h = None
+        order = None
+        if init_free_order is not None:
+            order = (_I32 * num_blocks)(*[int(b) for b in init_free_order])
+        h = _P()
+        _check(lib().pa_alloc_create(num_blocks, block_size, order, ctypes.byref(h)), "pa_alloc_create")
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self):
+        if self._h is not None and _lib is not None:
+            _lib.pa_alloc_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def pa_alloc_num_free(self):
+        return lib().pa_alloc_num_free(self._h)
+
+    def pa_alloc_num_seqs(self):
+        return lib().pa_alloc_num_seqs(self._h)
+
+    def pa_block_refcount(self, block):
+        return lib().pa_block_refcount(self._h, block)
+
+    def pa_seq_add(self, seq):
+        _check(lib().pa_seq_add(self._h, seq), "pa_seq_add")
+
+    def pa_seq_fork(self, parent, child):
+        _check(lib().pa_seq_fork(self._h, parent, child), "pa_seq_fork")
+
+    def pa_seq_append_slot(self, seq):
+        slot, src, dst = _I64(), _I32(), _I32()
+        _check(lib().pa_seq_append_slot(self._h, seq, ctypes.byref(slot), ctypes.byref(src),
+                                        ctypes.byref(dst)), "pa_seq_append_slot")
+        return slot.value, src.value, dst.value
+
+    def pa_seq_append_slots(self, seqs):
+        """-> (slots list, [(src, dst), ...])"""
+        n = len(seqs)
+        s_arr = (_I64 * max(n, 1))(*seqs)
+        slots = (_I64 * max(n, 1))()
+        pairs = (_I32 * max(2 * n, 2))()
+        ncow = _I32()
+        _check(lib().pa_seq_append_slots(self._h, s_arr, n, slots, pairs, ctypes.byref(ncow)),
+               "pa_seq_append_slots")
+        return list(slots[:n]), [(pairs[2 * i], pairs[2 * i + 1]) for i in range(ncow.value)]
+
+    def pa_seq_free(self, seq):
+        _check(lib().pa_seq_free(self._h, seq), "pa_seq_free")
+
+    def pa_seq_len(self, seq):
+        return lib().pa_seq_len(self._h, seq)
+
+    def pa_seq_num_blocks(self, seq):
+        return lib().pa_seq_num_blocks(self._h, seq)
+
+    def pa_seq_block_table(self, seq):
+        n = _I32()
+        _check(lib().pa_seq_block_table(self._h, seq, None, 0, ctypes.byref(n)), "pa_seq_block_table")
+        buf = (_I32 * max(n.value, 1))()
+        _check(lib().pa_seq_block_table(self._h, seq, buf, n.value, ctypes.byref(n)), "pa_seq_block_table")
+        return list(buf[:n.value])

@@ -1,0 +1,271 @@
+"""GPU parity of libpagedattn against the fp64 CPU oracle (needs an MI355X).
+
+Same seeded inputs go to both sides.  Gathers, cache writes and block
+copies must match bit for bit; the attention output must match within
+1e-5 (fp32 KV) or 2e-2 (f16 / bf16 KV, fp32 accumulation).  Every pool holds
+NaN in blocks no table references and in the unused tail slots of each
+sequence's last block, so a read past a context shows up as NaN.
+Every call goes through the C ABI via the ctypes binding.
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle
+from oracle.allocator_model import BlockManagerModel
+from paged_kv_cache_328_amd import pagedattn as pa
+from paged_kv_cache_328_amd import workloads as wl
+import tests._gpu as _g
+from tests._gpu import (TOL, announce, check_attention, ints_to_dev, poison_tails, same_bits,
+                        to_dev, to_host, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    import torch
+    if _g.DEVICE == "cuda":
+        torch.cuda.synchronize()
+
+
+def run_decode_case(case, label, r=0, partition_size=None, write=True, gather_seqs="all",
+                    compare_pools=False):
+    """Cache write of the step's new tokens (if any), gather check, decode check."""
+    import torch
+    dtype = case.dtype
+    tables = np.ascontiguousarray(case.block_tables[r])
+    lens = case.context_lens
+    kc, vc = case.k_cache, case.v_cache
+    poison_tails(oracle, kc, vc, tables, lens, dtype)
+    announce(f"{label}: upload pools NB={case.NB} S={case.S} Hq={case.Hq} Hkv={case.Hkv} "
+             f"D={case.D} BS={case.BS} {dtype} max_ctx={case.max_context}")
+    kd, vd = to_dev(kc, dtype), to_dev(vc, dtype)
+    td, ld = ints_to_dev(tables), ints_to_dev(lens)
+    if write and case.slot_mapping is not None:
+        announce(f"{label}: pa_write_kv T={case.S}")
+        pa.pa_write_kv(to_dev(case.new_k[r], dtype), to_dev(case.new_v[r], dtype), kd, vd,
+                       ints_to_dev(case.slot_mapping[r]))
+        oracle.write_kv(np.ascontiguousarray(case.new_k[r]), np.ascontiguousarray(case.new_v[r]),
+                        kc, vc, np.ascontiguousarray(case.slot_mapping[r]), dtype)
+        _sync()
+    if compare_pools:
+        assert same_bits(to_host(kd, dtype), kc) and same_bits(to_host(vd, dtype), vc)
+    if gather_seqs is not None:
+        sel = np.arange(case.S) if gather_seqs == "all" else np.asarray(gather_seqs)
+        gt, gl = np.ascontiguousarray(tables[sel]), np.ascontiguousarray(lens[sel])
+        mc = int(gl.max()) if gl.size else 0
+        if mc:
+            announce(f"{label}: pa_gather_kv seqs={sel.tolist()} max_ctx={mc}")
+            ko = torch.zeros((sel.size, mc, case.Hkv, case.D), dtype=torch_dtype(dtype), device=_g.DEVICE)
+            vo = torch.zeros_like(ko)
+            pa.pa_gather_kv(kd, vd, ints_to_dev(gt), ints_to_dev(gl), ko, vo)
+            _sync()
+            kr, vr = oracle.gather_raw(kc, vc, gt, gl, mc, dtype)
+            assert same_bits(to_host(ko, dtype), kr), f"{label}: K gather differs"
+            assert same_bits(to_host(vo, dtype), vr), f"{label}: V gather differs"
+    q = np.ascontiguousarray(case.q[r])
+    qd = to_dev(q, dtype)
+    out = torch.empty_like(qd)
+    P = case.partition_size if partition_size is None else partition_size
+    announce(f"{label}: pa_decode P={P}")
+    pa.pa_decode(out, qd, kd, vd, td, ld, case.scale, case.max_context, partition_size=P)
+    _sync()
+    want = oracle.decode(q, kc, vc, tables, lens, case.scale, dtype, num_threads=16)
+    return check_attention(to_host(out, dtype), want, dtype, label), to_host(out, dtype)
+
+
+# ---------------------------------------------------------------------------- the five workloads
+
+def test_tiny_f32():
+    case = wl.tiny_f32()
+    run_decode_case(case, "tiny_f32", compare_pools=True)
+
+
+def test_llama13b_f16_full_size():
+    case = wl.llama13b_f16()
+    run_decode_case(case, "llama13b_f16")
+
+
+def test_mixed_gqa_bf16_full_size():
+    case = wl.mixed_gqa_bf16()
+    run_decode_case(case, "mixed_gqa_bf16")
+
+
+def test_long_bf16_full_size_p512():
+    case = wl.long_bf16()
+    assert case.partition_size == 512
+    run_decode_case(case, "long_bf16", gather_seqs=[0])
+
+
+def test_cow_shared_prefix_step():
+    """32 sequences share a 2048-token prefix; each has a private suffix and a
+    forked sibling that shares all its blocks.  One step appends a token to
+    each of the 32: the shared partly-filled tails are copied, the new token
+    is written into the copy, then all 32 decode."""
+    import torch
+    plan = wl.cow_plan()
+    BS, NB, n, dtype = plan["BS"], plan["NB"], plan["n"], plan["dtype"]
+    A = pa.Allocator(NB, BS, plan["init_free_order"])
+    M = BlockManagerModel(NB, BS, plan["init_free_order"])
+    A.pa_seq_add(0)
+    M.add(0)
+    for _ in range(plan["prefix"]):
+        assert A.pa_seq_append_slot(0) == M.append_slot(0)
+    for i in range(1, n):
+        A.pa_seq_fork(0, i)
+        M.fork(0, i)
+    for i in range(n):
+        for _ in range(plan["suffix"][i]):
+            assert A.pa_seq_append_slot(i) == M.append_slot(i)
+    for i in range(n):  # parallel-sampling fork: sibling kept alive, not decoded
+        A.pa_seq_fork(i, 1000 + i)
+        M.fork(i, 1000 + i)
+    prefix_block = M.block_table(0)[0]
+    assert A.pa_block_refcount(prefix_block) == M.refcount(prefix_block) == 2 * n
+
+    kc, vc = plan["k_cache"], plan["v_cache"]
+    referenced = np.zeros(NB, bool)
+    for s in list(range(n)) + [1000 + i for i in range(n)]:
+        referenced[M.block_table(s)] = True
+    kc[~referenced] = wl.nan_bits(dtype)
+    vc[~referenced] = wl.nan_bits(dtype)
+    pre_len = [M.seq_len(i) for i in range(n)]
+    pre_tables = [M.block_table(i) for i in range(n)]
+    maxb = max(len(t) for t in pre_tables) + 1
+    pre_t = np.full((n, maxb), 0, np.int32)
+    for i, t in enumerate(pre_tables):
+        pre_t[i, :len(t)] = t
+    poison_tails(oracle, kc, vc, pre_t, np.asarray(pre_len), dtype)
+    sib_before = {i: M.block_table(1000 + i) for i in range(n)}
+    k_before, v_before = kc.copy(), vc.copy()
+
+    slots, pairs = A.pa_seq_append_slots(list(range(n)))
+    want = [M.append_slot(i) for i in range(n)]
+    assert slots == [w[0] for w in want]
+    assert pairs == [(w[1], w[2]) for w in want if w[1] >= 0]
+    n_partial = sum(1 for L in pre_len if L % BS)
+    assert len(pairs) == n_partial and n_partial > 0
+
+    announce(f"cow: upload NB={NB} pairs={len(pairs)}")
+    kd, vd = to_dev(kc, dtype), to_dev(vc, dtype)
+    announce("cow: pa_copy_blocks")
+    pa.pa_copy_blocks(kd, vd, ints_to_dev(np.asarray(pairs, np.int32).reshape(-1, 2)))
+    oracle.copy_blocks(kc, vc, np.asarray(pairs, np.int32), dtype)
+    announce("cow: pa_write_kv")
+    pa.pa_write_kv(to_dev(plan["new_k"], dtype), to_dev(plan["new_v"], dtype), kd, vd,
+                   ints_to_dev(np.asarray(slots, np.int64)))
+    oracle.write_kv(plan["new_k"], plan["new_v"], kc, vc, np.asarray(slots, np.int64), dtype)
+    _sync()
+    assert same_bits(to_host(kd, dtype), kc), "K pool after copy+write differs from the oracle"
+    assert same_bits(to_host(vd, dtype), vc), "V pool after copy+write differs from the oracle"
+
+    # siblings: tables and every block they reference are bit-unchanged
+    for i in range(n):
+        assert A.pa_seq_block_table(1000 + i) == sib_before[i]
+        for b in sib_before[i]:
+            assert same_bits(kc[b], k_before[b]) and same_bits(vc[b], v_before[b])
+    # each copy = its source, except the new token's row
+    for (src, dst), slot in zip(pairs, [s for s, w in zip(slots, want) if w[1] >= 0]):
+        o = slot % BS
+        kr, vr = oracle.gather_raw(kc, vc, np.array([[src], [dst]], np.int32),
+                                   np.array([BS, BS], np.int32), BS, dtype)
+        keep = np.arange(BS) != o
+        assert same_bits(kr[0][keep], kr[1][keep]) and same_bits(vr[0][keep], vr[1][keep])
+
+    lens = np.asarray([M.seq_len(i) for i in range(n)], np.int32)
+    tables = np.zeros((n, maxb), np.int32)
+    for i in range(n):
+        t = A.pa_seq_block_table(i)
+        assert t == M.block_table(i)
+        tables[i, :len(t)] = t
+    qd = to_dev(plan["q"], dtype)
+    out = torch.empty_like(qd)
+    announce(f"cow: pa_decode S={n} max_ctx={int(lens.max())}")
+    pa.pa_decode(out, qd, kd, vd, ints_to_dev(tables), ints_to_dev(lens), plan["scale"], int(lens.max()))
+    _sync()
+    want_out = oracle.decode(plan["q"], kc, vc, tables, lens, plan["scale"], dtype, num_threads=16)
+    check_attention(to_host(out, dtype), want_out, dtype, "cow_bf16")
+
+
+# ---------------------------------------------------------------------------- edge cases
+
+EDGE_LENS = [0, 1, 15, 16, 17, 33, 100, 257]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("BS", [16, 32])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (12, 4), (16, 2), (40, 2)])
+def test_edge_shapes_16bit(dtype, D, BS, Hq, Hkv):
+    case = wl.random_case(500 + D + BS + Hq, len(EDGE_LENS), Hq, Hkv, D, BS, dtype, EDGE_LENS,
+                          partition_size=64)
+    run_decode_case(case, f"edge {dtype} D{D} BS{BS} {Hq}/{Hkv} P64", gather_seqs="all")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("BS", [16, 32])
+@pytest.mark.parametrize("Hq,Hkv,P", [(2, 2, 0), (8, 2, 32), (3, 1, 64)])
+def test_edge_shapes_f32(D, BS, Hq, Hkv, P):
+    case = wl.random_case(700 + D + BS + Hq, len(EDGE_LENS), Hq, Hkv, D, BS, "f32", EDGE_LENS,
+                          partition_size=P)
+    run_decode_case(case, f"edge f32 D{D} BS{BS} {Hq}/{Hkv} P{P}", compare_pools=True)
+
+
+@pytest.mark.parametrize("P", [0, 32, 64, 128, 512, 2048])
+def test_partition_sizes_all_match(P):
+    lens = [1, 31, 32, 33, 511, 512, 513, 1500, 3000]
+    case = wl.random_case(900, len(lens), 32, 8, 128, 16, "bf16", lens, partition_size=P)
+    run_decode_case(case, f"partition P={P}", gather_seqs=None)
+
+
+def test_block_relabelling_and_determinism_bit_identical():
+    import torch
+    lens = [5, 40, 129, 700, 1601]
+    case = wl.random_case(901, len(lens), 16, 4, 128, 16, "bf16", lens, NB=400, partition_size=256)
+    dtype = "bf16"
+    t0 = case.block_tables[0]
+    poison_tails(oracle, case.k_cache, case.v_cache, t0, case.context_lens, dtype)
+    rng = np.random.default_rng(5)
+    pi = rng.permutation(case.NB)
+    k2, v2 = np.empty_like(case.k_cache), np.empty_like(case.v_cache)
+    k2[pi], v2[pi] = case.k_cache, case.v_cache
+    t2 = pi[t0].astype(np.int32)
+    qd = to_dev(case.q[0], dtype)
+    outs = []
+    for kc, vc, tb in [(case.k_cache, case.v_cache, t0), (k2, v2, t2), (case.k_cache, case.v_cache, t0)]:
+        announce("relabel/determinism: pa_decode")
+        out = torch.empty_like(qd)
+        pa.pa_decode(out, qd, to_dev(kc, dtype), to_dev(vc, dtype), ints_to_dev(tb),
+                     ints_to_dev(case.context_lens), case.scale, case.max_context, partition_size=256)
+        _sync()
+        outs.append(to_host(out, dtype))
+    assert same_bits(outs[0], outs[1]), "output changed under physical block relabelling"
+    assert same_bits(outs[0], outs[2]), "two identical runs differ"
+
+
+def test_large_logits_stay_finite():
+    lens = [64, 300, 1000]
+    case = wl.random_case(902, len(lens), 8, 2, 128, 16, "bf16", lens, partition_size=128)
+    qf = wl.storage_to_f32(case.q, "bf16") * 16.0  # logits of order 100
+    case.q = wl.round_to_storage(qf, "bf16")
+    run_decode_case(case, "large logits", gather_seqs=None)
+
+
+def test_write_skips_padding_and_copy_is_bit_exact():
+    dtype, NB, Hkv, D, BS = "bf16", 12, 2, 128, 16
+    rng = np.random.default_rng(17)
+    ks, vs = wl.pool_shapes(NB, Hkv, D, BS, dtype)
+    kc = wl.round_to_storage(rng.standard_normal(ks, dtype=np.float32), dtype)
+    vc = wl.round_to_storage(rng.standard_normal(vs, dtype=np.float32), dtype)
+    kd, vd = to_dev(kc, dtype), to_dev(vc, dtype)
+    slots = np.array([3, -1, 11 * BS + 15, 7 * BS, -5, NB * BS + 3], np.int64)  # padding + out of pool
+    kn = wl.round_to_storage(rng.standard_normal((6, Hkv, D), dtype=np.float32), dtype)
+    vn = wl.round_to_storage(rng.standard_normal((6, Hkv, D), dtype=np.float32), dtype)
+    announce("write/copy small: pa_write_kv")
+    pa.pa_write_kv(to_dev(kn, dtype), to_dev(vn, dtype), kd, vd, ints_to_dev(slots))
+    oracle.write_kv(kn[:5], vn[:5], kc, vc, slots[:5], dtype)  # the oracle rejects the last slot
+    pairs = np.array([[2, 9], [7, 4], [11, 0]], np.int32)
+    announce("write/copy small: pa_copy_blocks")
+    pa.pa_copy_blocks(kd, vd, ints_to_dev(pairs))
+    oracle.copy_blocks(kc, vc, pairs, dtype)
+    _sync()
+    assert same_bits(to_host(kd, dtype), kc) and same_bits(to_host(vd, dtype), vc)
