@@ -15,24 +15,31 @@
 //   K [NB, Hkv, D/8, BS, 8]: for a fixed 8-channel chunk, the BS tokens of a
 //     block are consecutive 16-byte vectors;
 //   V [NB, Hkv, D, BS]:      for a fixed channel, the BS tokens are consecutive.
-// These are exactly the operand layouts of the gfx950 matrix instruction
-// v_mfma_f32_16x16x32_{f16,bf16}, where each lane feeds 8 consecutive
-// reduction-dimension elements of one row:
-//   QK:  S[token][head]  = K[token][d]   x Q^T[d][head]   (reduction over d:
-//        a lane loads one token's 8-channel chunk = one 16-byte vector of K)
-//   PV:  O^T[d][head]   += V^T[d][token] x P^T[token][head] (reduction over
-//        tokens: a lane loads 8 consecutive tokens of one channel = one
-//        16-byte vector of V)
-// The S accumulator leaves lane l holding 8 logits of head l%16, which is
-// exactly the P^T operand lane l must feed to the PV product, so the softmax
-// weights never move between lanes; the running max / sum per head is
-// lane-local too, because O^T keeps head l%16 in lane l.
+// Both products run on the gfx950 matrix instruction
+// v_mfma_f32_16x16x32_{f16,bf16} (lane l feeds row/column l%16 and 8
+// consecutive reduction-dimension elements 8*(l/16)..+7; the 16x16 result
+// leaves rows 4*(l/16)..+3 of column l%16 in lane l):
+//   QK:  S[token][head] = K[token][d] x Q^T[d][head], reduction over d.  Row i
+//        of the 16-token tile is token i, so for one 8-channel chunk the 16
+//        lanes of a row group read 16 consecutive 16-byte vectors: 256
+//        contiguous bytes, whole cache lines.
+//   PV:  O^T[d][head] += V^T[d][k] x P^T[k][head], reduction over the 32
+//        tokens of a chunk.  The reduction index k is ordered so that lane l
+//        already holds the weights it must feed: k = 8*(l/16) + j is token
+//        4*(l/16) + j of tile 0 for j < 4 and token 16 + 4*(l/16) + j - 4 of
+//        tile 1 otherwise.  The V^T operand follows the same order: two
+//        8-byte reads of 4 consecutive tokens of one channel.
+// So the softmax weights never move between lanes, and the running max / sum
+// of head l%16 stays lane-local apart from one reduction over the 4 row
+// groups of the wave.
 //
-// Work decomposition: one wave (64 lanes) per (partition, KV head, group of
-// up to 16 query heads sharing that KV head, sequence).  The group of G
-// query heads that read one KV head is the N = 16 dimension of both products,
-// so K/V bytes are read once per KV head whatever G is.  A wave walks its
-// partition in chunks of 32 tokens (two 16-token MFMA tiles).
+// Work decomposition: one workgroup of NW waves per (KV head, group of up to
+// 16 query heads sharing that KV head, partition, sequence).  The group's
+// query heads are the N = 16 dimension of both products, so K/V bytes are read
+// once per KV head whatever the group size G is.  The partition is cut into
+// chunks of 32 tokens dealt round-robin to the waves (the intelliparadigm
+// page's warp-to-block assignment, section 4.2); each wave keeps its own
+// running (max, sum, output) and the waves are merged through LDS at the end.
 #include <math.h>
 
 #include "pa_device.h"
@@ -44,13 +51,35 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 32;          // tokens per step of the 16-bit kernel
 constexpr int kMaxF32Part = 1024;   // largest partition of the fp32 kernel
+constexpr int kMergeThreads = 256;
+
+// K/V are streamed: every byte is read once per step, so the loads are
+// non-temporal (they do not displace reusable lines in the caches); this is
+// worth several percent of HBM bandwidth on these scattered 4-8 KiB tiles.
+__device__ __forceinline__ u32x4 stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 stream8(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
 
 // ----------------------------------------------------------------------------
 // 16-bit pass 1 (matrix cores).
-// grid: x = partition, y = KV head * groups + group, z = sequence; block = 64.
+// grid: x = KV head * n_groups + group, y = partition, z = sequence;
+// block = 64 * NW threads; dynamic LDS = merge_lds_bytes(NW, G, D).
+// Partitions beyond a sequence's context exit at once.  Neighbouring
+// workgroups are the KV heads of one (sequence, partition): they read the
+// adjacent head tiles of the same physical blocks.
 // ----------------------------------------------------------------------------
-template <typename Ty, int D, int BS>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(
+// Raw K / V operand registers of one 32-token chunk.
+template <int KK, int MM>
+struct Raw {
+  u32x4 k[2][KK];
+  u32x4 v[MM];
+};
+
+template <typename Ty, int D, int BS, int NW, bool PF>
+__global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, int Hq, int Hkv, int G, int n_groups, int NB,
@@ -62,29 +91,33 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   constexpr int KK = D / 32;     // QK products along head_dim (32 channels each)
   constexpr int MM = D / 16;     // PV products along head_dim (16 channels each)
   constexpr int TILE = D * BS;   // elements of one (block, KV head) tile
+  constexpr int DP = D + 4;      // padded LDS row of the merge buffer
+  extern __shared__ float lds[];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
   const int i = lane & 15;       // row (A operand) / column (B operand, output)
   const int g4 = lane >> 4;      // which 8-element slice of the reduction dim
-  const int p = blockIdx.x;
-  const int hk = blockIdx.y / n_groups;
-  const int grp = blockIdx.y - hk * n_groups;
+  const int hk = blockIdx.x / n_groups;
+  const int grp = blockIdx.x - hk * n_groups;
+  const int p = blockIdx.y;
   const int s = blockIdx.z;
 
   const int c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
   const int n_p = (c + P - 1) / P;
-  if (p >= max(n_p, 1)) return;
+  if (p < 0 || p >= max(n_p, 1)) return;
   const int t_begin = p * P;
   const int t_end = min(c, t_begin + P);
+  const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
 
-  const int hl = grp * 16 + i;   // query head within the KV head's group
-  const bool head_ok = hl < G;
-  const int qh = hk * G + (head_ok ? hl : 0);
+  const int Gv = min(16, G - grp * 16);  // query heads of this group
+  const bool head_ok = i < Gv;
+  const int qh0 = hk * G + grp * 16;     // first query head of the group
 
   // Q^T operand of the QK product: lane feeds head i, channels 8*(4*kk+g4)..+8.
   V8 qop[KK];
   {
-    const uint16_t* qrow = q + ((int64_t)s * Hq + qh) * D;
+    const uint16_t* qrow = q + ((int64_t)s * Hq + qh0 + (head_ok ? i : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 raw = head_ok ? load16(qrow + 8 * (4 * kk + g4)) : u32x4{0u, 0u, 0u, 0u};
@@ -95,52 +128,53 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
   f32x4 acc[MM];
 #pragma unroll
   for (int mm = 0; mm < MM; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max of the base-2 logits (per head i)
+  float m_run = -INFINITY;  // running max of the base-2 logits (head i)
   float l_run = 0.f;        // this lane's share of the running sum
 
   const int32_t* trow = tables + (int64_t)s * max_blocks;
   const int64_t blk_stride = (int64_t)Hkv * TILE;
   const int64_t head_off = (int64_t)hk * TILE;
-  // Token (within the 32-token chunk) fed by A-operand row i of tile 0; tile 1
-  // adds 4.  With this order the S accumulator of lane l holds tokens
-  // 8*g4 .. 8*g4+7, the same 8 tokens lane l feeds to the PV product.
-  const int tok_row = 8 * (i >> 2) + (i & 3);
 
-  for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
-    const int bA = uniform(clampi(trow[t0 / BS], 0, NB - 1));
-    int bB = bA;
+  // Physical blocks of chunk `ch` (tile 0 / tile 1); tile 1 of a 16-token
+  // block size reads the next table entry unless it lies past the context.
+  auto block_ids = [&](int ch, int& bA, int& bB) {
+    const int t0 = t_begin + ch * kChunk;
+    bA = uniform(clampi(trow[t0 / BS], 0, NB - 1));
+    bB = bA;
     if (BS == 16 && t0 + 16 < c) bB = uniform(clampi(trow[t0 / BS + 1], 0, NB - 1));
+  };
+  // Issue every K and V load of one chunk (2 x KK 16-byte K vectors, 2 x MM
+  // 8-byte V pieces per lane).
+  auto issue = [&](int bA, int bB, Raw<KK, MM>& r) {
     const uint16_t* kA = kc + bA * blk_stride + head_off;
     const uint16_t* kB = kc + bB * blk_stride + head_off;
     const uint16_t* vA = vc + bA * blk_stride + head_off;
     const uint16_t* vB = vc + bB * blk_stride + head_off;
-
-    // K operands: row i of tile `tl` is token tok_row + 4*tl, chunk 4*kk+g4.
-    u32x4 kraw[2][KK];
+    const int o1 = BS == 16 ? i : 16 + i;  // in-block row of tile-1 token i
 #pragma unroll
-    for (int tl = 0; tl < 2; ++tl) {
-      const int tok = tok_row + 4 * tl;
-      const uint16_t* kb = (BS == 16 && tok >= 16) ? kB : kA;
-      const int o = BS == 16 ? (tok & 15) : tok;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kraw[tl][kk] = load16(kb + ((4 * kk + g4) * BS + o) * 8);
+    for (int kk = 0; kk < KK; ++kk) {
+      r.k[0][kk] = stream16(kA + ((4 * kk + g4) * BS + i) * 8);
+      r.k[1][kk] = stream16(kB + ((4 * kk + g4) * BS + o1) * 8);
     }
-    // V operands: channel 16*mm + i, tokens 8*g4 .. 8*g4+7.
-    u32x4 vraw[MM];
-    {
-      const uint16_t* vb = (BS == 16 && g4 >= 2) ? vB : vA;
-      const int o0 = BS == 16 ? 8 * (g4 & 1) : 8 * g4;
+    // V^T operand: channel 16*mm + i, tokens 4*g4..+3 of tile 0, then of tile 1.
+    const int v1 = BS == 16 ? 4 * g4 : 16 + 4 * g4;
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm) vraw[mm] = load16(vb + (16 * mm + i) * BS + o0);
+    for (int mm = 0; mm < MM; ++mm) {
+      const u32x2 a = stream8(vA + (16 * mm + i) * BS + 4 * g4);
+      const u32x2 b = stream8(vB + (16 * mm + i) * BS + v1);
+      r.v[mm] = u32x4{a[0], a[1], b[0], b[1]};
     }
-
+  };
+  // Both products and the online-softmax update for the chunk at token t0.
+  auto consume = [&](int t0, Raw<KK, MM>& r) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      s0 = Ty::mma(__builtin_bit_cast(V8, kraw[0][kk]), qop[kk], s0);
-      s1 = Ty::mma(__builtin_bit_cast(V8, kraw[1][kk]), qop[kk], s1);
+      s0 = Ty::mma(__builtin_bit_cast(V8, r.k[0][kk]), qop[kk], s0);
+      s1 = Ty::mma(__builtin_bit_cast(V8, r.k[1][kk]), qop[kk], s1);
     }
-    // x[e]: base-2 logit of token t0 + 8*g4 + e for head i.
+    // x[e]: base-2 logit for head i of token t0 + 4*g4 + e (e < 4) or
+    // t0 + 16 + 4*g4 + e - 4 (e >= 4): reduction index 8*g4 + e of the PV product.
     float x[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -148,18 +182,18 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
       x[4 + j] = s1[j] * scale_log2;
     }
     if (t0 + kChunk > c) {  // last chunk: drop tokens past the context by select
-      const int first = t0 + 8 * g4;
       uint32_t keep[4];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (first + e >= c) x[e] = -INFINITY;
+        if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= c) x[e] = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        keep[w] = (first + 2 * w < c ? 0x0000FFFFu : 0u) | (first + 2 * w + 1 < c ? 0xFFFF0000u : 0u);
+      for (int wd = 0; wd < 4; ++wd)
+        keep[wd] = (x[2 * wd] != -INFINITY ? 0x0000FFFFu : 0u) |
+                   (x[2 * wd + 1] != -INFINITY ? 0xFFFF0000u : 0u);
 #pragma unroll
       for (int mm = 0; mm < MM; ++mm)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) vraw[mm][w] &= keep[w];
+        for (int wd = 0; wd < 4; ++wd) r.v[mm][wd] &= keep[wd];
     }
 
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
@@ -167,50 +201,112 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2_fast(m_run - m_new);  // 0 on the first chunk
+    const float alpha = exp2_fast(m_run - m_new);  // 0 on the wave's first chunk
     m_run = m_new;
 
     uint32_t pw[4];
     float psum = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint16_t lo = Ty::from_f32(exp2_fast(x[2 * w] - m_new));
-      const uint16_t hi = Ty::from_f32(exp2_fast(x[2 * w + 1] - m_new));
+    for (int wd = 0; wd < 4; ++wd) {
+      const uint16_t lo = Ty::from_f32(exp2_fast(x[2 * wd] - m_new));
+      const uint16_t hi = Ty::from_f32(exp2_fast(x[2 * wd + 1] - m_new));
       psum += Ty::to_f32(lo) + Ty::to_f32(hi);  // the sum uses the weights the PV product sees
-      pw[w] = (uint32_t)lo | ((uint32_t)hi << 16);
+      pw[wd] = (uint32_t)lo | ((uint32_t)hi << 16);
     }
     l_run = l_run * alpha + psum;
     const V8 pop = __builtin_bit_cast(V8, u32x4{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
     for (int mm = 0; mm < MM; ++mm) {
       acc[mm] *= alpha;
-      acc[mm] = Ty::mma(__builtin_bit_cast(V8, vraw[mm]), pop, acc[mm]);
+      acc[mm] = Ty::mma(__builtin_bit_cast(V8, r.v[mm]), pop, acc[mm]);
+    }
+  };
+
+  // Chunk loop.  All loads of a chunk are issued before any of them is used
+  // (the scheduling barrier keeps the compiler from interleaving the
+  // products with the loads), and the table entries of the wave's next chunk
+  // are fetched while the current chunk's data is in flight.  With PF the
+  // next chunk's K/V loads are issued too before the current chunk is used.
+  int nA = 0, nB = 0;
+  int ch = w;
+  if (ch < n_chunks) block_ids(ch, nA, nB);
+  if constexpr (!PF) {
+    for (; ch < n_chunks; ch += NW) {
+      Raw<KK, MM> r;
+      issue(nA, nB, r);
+      if (ch + NW < n_chunks) block_ids(ch + NW, nA, nB);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(t_begin + ch * kChunk, r);
+    }
+  } else {
+    Raw<KK, MM> cur, nxt;
+    if (ch < n_chunks) {
+      issue(nA, nB, cur);
+      if (ch + NW < n_chunks) block_ids(ch + NW, nA, nB);
+    }
+    for (; ch < n_chunks; ch += NW) {
+      if (ch + NW < n_chunks) {
+        issue(nA, nB, nxt);
+        if (ch + 2 * NW < n_chunks) block_ids(ch + 2 * NW, nA, nB);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      consume(t_begin + ch * kChunk, cur);
+      cur = nxt;
     }
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (!head_ok) return;
 
-  // Lane holds O^T[d = 16*mm + 4*g4 + j][head i], j = 0..3.
-  if (n_p <= 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = out + ((int64_t)s * Hq + qh) * D;
+  // Merge the NW waves: M = max_w m_w per head, then every wave rescales its
+  // sum and output by 2^(m_w - M) into LDS and the workgroup adds them up in
+  // wave order.  A wave that saw no token has m_w = -inf and weight 0.
+  float* m_sh = lds;                  // [NW][16]
+  float* l_sh = lds + NW * 16;        // [NW][16]
+  float* a_sh = lds + 2 * NW * 16;    // [NW][Gv][DP]
+  if (g4 == 0) m_sh[w * 16 + i] = m_run;
+  __syncthreads();
+  float M = -INFINITY;
 #pragma unroll
-    for (int mm = 0; mm < MM; ++mm) {
-      const f32x4 a = acc[mm] * inv;
-      const u32x2 packed = {(uint32_t)Ty::from_f32(a[0]) | ((uint32_t)Ty::from_f32(a[1]) << 16),
-                            (uint32_t)Ty::from_f32(a[2]) | ((uint32_t)Ty::from_f32(a[3]) << 16)};
-      *reinterpret_cast<u32x2*>(orow + 16 * mm + 4 * g4) = packed;
+  for (int v = 0; v < NW; ++v) M = fmaxf(M, m_sh[v * 16 + i]);
+  const float f = m_run > -INFINITY ? exp2_fast(m_run - M) : 0.f;
+  if (head_ok) {
+    if (g4 == 0) l_sh[w * 16 + i] = l_tot * f;
+    // lane holds O^T[d = 16*mm + 4*g4 + j][head i], j = 0..3
+    float* arow = a_sh + (w * Gv + i) * DP + 4 * g4;
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) *reinterpret_cast<f32x4*>(arow + 16 * mm) = acc[mm] * f;
+  }
+  __syncthreads();
+
+  const bool split = n_p > 1;
+  for (int e = threadIdx.x; e < Gv * (D / 4); e += 64 * NW) {
+    const int hh = e / (D / 4);
+    const int d = 4 * (e - hh * (D / 4));
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      sum += *reinterpret_cast<const f32x4*>(a_sh + (v * Gv + hh) * DP + d);
+      L += l_sh[v * 16 + hh];
     }
-  } else {
-    const int64_t idx = ((int64_t)s * Hq + qh) * max_parts + p;
-    float* a = ws_acc + idx * D;
+    const int64_t row = (int64_t)s * Hq + qh0 + hh;
+    if (!split) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      const f32x4 r = sum * inv;
+      const u32x2 packed = {(uint32_t)Ty::from_f32(r[0]) | ((uint32_t)Ty::from_f32(r[1]) << 16),
+                            (uint32_t)Ty::from_f32(r[2]) | ((uint32_t)Ty::from_f32(r[3]) << 16)};
+      *reinterpret_cast<u32x2*>(out + row * D + d) = packed;
+    } else {
+      const int64_t idx = row * max_parts + p;
+      *reinterpret_cast<f32x4*>(ws_acc + idx * D + d) = sum;
+      if (d == 0) {
+        float Mh = -INFINITY;
 #pragma unroll
-    for (int mm = 0; mm < MM; ++mm) *reinterpret_cast<f32x4*>(a + 16 * mm + 4 * g4) = acc[mm];
-    if (g4 == 0) {
-      ws_ml[2 * idx] = m_run;
-      ws_ml[2 * idx + 1] = l_tot;
+        for (int v = 0; v < NW; ++v) Mh = fmaxf(Mh, m_sh[v * 16 + hh]);
+        ws_ml[2 * idx] = Mh;
+        ws_ml[2 * idx + 1] = L;
+      }
     }
   }
 }
@@ -295,39 +391,82 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
 
 // ----------------------------------------------------------------------------
 // Pass 2: merge the partitions of every (sequence, query head) that has more
-// than one.  grid: x = query head, y = sequence; block = D threads.
+// than one.  grid: x = query head, y = sequence; block = 256 threads.  All
+// partitions are read in parallel: thread (r, c4) takes channels 4*c4..+3 of
+// partitions r, r + ROWS, ...; the ROWS partial sums are added in LDS in a
+// fixed order, so the result depends only on the logical partition contents.
 // ----------------------------------------------------------------------------
-template <typename OutT>
-__global__ __launch_bounds__(256) void merge_kernel(
-    OutT* __restrict__ out, const int32_t* __restrict__ lens, const float* __restrict__ ws_acc,
-    const float* __restrict__ ws_ml, int Hq, int D, int max_ctx, int max_blocks, int BS, int P,
-    int max_parts) {
-  const int h = blockIdx.x, s = blockIdx.y, d = threadIdx.x;
+template <typename Store, int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+    typename Store::T* __restrict__ out, const int32_t* __restrict__ lens,
+    const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, int Hq, int max_ctx,
+    int max_blocks, int BS, int P, int max_parts) {
+  constexpr int C4 = D / 4;                   // threads per partition row
+  constexpr int ROWS = kMergeThreads / C4;    // partitions read at once
+  constexpr int NWV = kMergeThreads / kWave;
+  __shared__ float red[NWV];
+  __shared__ f32x4 part[ROWS][C4];
+  const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
   const int n_p = (c + P - 1) / P;
-  if (n_p <= 1 || d >= D) return;
+  if (n_p <= 1) return;
   const int64_t base = ((int64_t)s * Hq + h) * max_parts;
-  float M = -INFINITY;
-  for (int p = 0; p < n_p; ++p) M = fmaxf(M, ws_ml[2 * (base + p)]);
-  float L = 0.f, o = 0.f;
-  for (int p = 0; p < n_p; ++p) {
-    const float w = exp2_fast(ws_ml[2 * (base + p)] - M);
-    L = fmaf(w, ws_ml[2 * (base + p) + 1], L);
-    o = fmaf(w, ws_acc[(base + p) * D + d], o);
+
+  float mx = -INFINITY;
+  for (int p = tid; p < n_p; p += kMergeThreads) mx = fmaxf(mx, ws_ml[2 * (base + p)]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) red[wv] = mx;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int v = 1; v < NWV; ++v) M = fmaxf(M, red[v]);
+  __syncthreads();
+
+  float ls = 0.f;
+  for (int p = tid; p < n_p; p += kMergeThreads)
+    ls += exp2_fast(ws_ml[2 * (base + p)] - M) * ws_ml[2 * (base + p) + 1];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
+  if (lane == 0) red[wv] = ls;
+  __syncthreads();
+  float L = 0.f;
+#pragma unroll
+  for (int v = 0; v < NWV; ++v) L += red[v];
+
+  const int r = tid / C4, c4 = tid - r * C4;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int p = r; p < n_p; p += ROWS) {
+    const float wgt = exp2_fast(ws_ml[2 * (base + p)] - M);
+    o += wgt * *reinterpret_cast<const f32x4*>(ws_acc + (base + p) * D + 4 * c4);
   }
-  const float r = o / L;
-  if constexpr (sizeof(OutT) == 4) {
-    out[((int64_t)s * Hq + h) * D + d] = r;
-  } else {
-    out[((int64_t)s * Hq + h) * D + d] = OutT::from_f32(r);
+  part[r][c4] = o;
+  __syncthreads();
+  if (r == 0) {
+    f32x4 sum = part[0][c4];
+#pragma unroll
+    for (int rr = 1; rr < ROWS; ++rr) sum += part[rr][c4];
+    Store::put(out + ((int64_t)s * Hq + h) * D + 4 * c4, sum * (1.f / L));
   }
 }
 
-// Output adaptor for 16-bit merges (stores the rounded bit pattern).
+struct StoreF32 {
+  using T = float;
+  static __device__ __forceinline__ void put(float* dst, f32x4 v) {
+    *reinterpret_cast<f32x4*>(dst) = v;
+  }
+};
+
 template <typename Ty>
-struct Out16 {
-  uint16_t bits;
-  static __device__ __forceinline__ Out16 from_f32(float f) { return Out16{Ty::from_f32(f)}; }
+struct Store16 {
+  using T = uint16_t;
+  static __device__ __forceinline__ void put(uint16_t* dst, f32x4 v) {
+    *reinterpret_cast<u32x2*>(dst) =
+        u32x2{(uint32_t)Ty::from_f32(v[0]) | ((uint32_t)Ty::from_f32(v[1]) << 16),
+              (uint32_t)Ty::from_f32(v[2]) | ((uint32_t)Ty::from_f32(v[3]) << 16)};
+  }
 };
 
 // ----------------------------------------------------------------------------
@@ -337,6 +476,8 @@ struct Plan {
   int P = 0;          // partition size in tokens
   int max_parts = 0;  // partitions of the longest context
   int groups = 1;     // query-head groups of 16 per KV head (16-bit kernel)
+  int waves = 4;      // waves per workgroup (16-bit kernel)
+  bool prefetch = true;   // double-buffered chunk loads (16-bit kernel)
   size_t ws_bytes = 0;
 };
 
@@ -360,43 +501,86 @@ pa_status validate(const pa_decode_args* a) {
   return PA_OK;
 }
 
-// Partition size when the caller leaves it to the library: the smallest of
-// 512/256/128 tokens that still yields enough waves to cover the chip
-// (256 CUs x 16 waves), judged from the longest context.
-int choose_partition(const pa_decode_args* a, int waves_per_part) {
+// Partition size when the caller leaves it to the library (16-bit kernel).
+// Measured on MI355X (non-temporal loads, 4 waves per workgroup): a
+// workgroup streams best when it walks a long run of tokens, but splits must
+// leave enough workgroups to keep every CU's loads in flight, and with mixed
+// lengths long runs leave a tail of late-starting long workgroups.  So:
+//   - contexts up to 2048 tokens are not split when the (sequence, KV head,
+//     head group) workgroups alone fill the chip (>= 512 of them);
+//   - otherwise P = max_context / 16 rounded up to a power of two within
+//     [256, 2048] tokens, halved (down to one 32-token chunk) while fewer
+//     than 1024 workgroups would exist even if every context were maximal.
+int choose_partition(const pa_decode_args* a, int wg_per_part) {
   if (a->dtype == PA_F32) return 512;
-  const int64_t base = (int64_t)a->num_seqs * waves_per_part;
-  const int64_t target = 256 * 16;
-  for (int P : {512, 256, 128}) {
-    const int64_t parts = (a->max_context_len + P - 1) / P;
-    if (base * parts >= target) return P;
-  }
-  return 128;
+  const int64_t base = (int64_t)a->num_seqs * wg_per_part;
+  const int64_t max_ctx = a->max_context_len;
+  if (max_ctx <= 2048 && base >= 512) return 2048;
+  int P = 256;
+  while (P < 2048 && (int64_t)P * 16 < max_ctx) P *= 2;
+  while (P > kChunk && base * ((max_ctx + P - 1) / P) < 1024) P /= 2;
+  return P;
 }
 
 Plan make_plan(const pa_decode_args* a) {
   Plan pl;
   const int G = a->num_q_heads / a->num_kv_heads;
   pl.groups = a->dtype == PA_F32 ? 1 : (G + 15) / 16;
-  const int waves_per_part = a->dtype == PA_F32 ? a->num_q_heads : a->num_kv_heads * pl.groups;
-  pl.P = a->partition_size > 0 ? a->partition_size : choose_partition(a, waves_per_part);
+  const int wg_per_part = a->dtype == PA_F32 ? a->num_q_heads : a->num_kv_heads * pl.groups;
+  pl.P = a->partition_size > 0 ? a->partition_size : choose_partition(a, wg_per_part);
   pl.max_parts = (a->max_context_len + pl.P - 1) / pl.P;
   if (pl.max_parts > 1)
     pl.ws_bytes = (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * (a->head_dim + 2) * 4;
   return pl;
 }
 
-template <typename Ty, int D, int BS>
+size_t merge_lds_bytes(int NW, int G, int D) {
+  return (size_t)(2 * NW * 16 + NW * min(G, 16) * (D + 4)) * sizeof(float);
+}
+
+template <typename Ty, int D, int BS, int NW, bool PF>
 void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* ws_ml,
                  hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
-  dim3 grid((unsigned)max(pl.max_parts, 1), (unsigned)(a->num_kv_heads * pl.groups),
+  dim3 grid((unsigned)(a->num_kv_heads * pl.groups), (unsigned)max(pl.max_parts, 1),
             (unsigned)a->num_seqs);
-  decode_mfma_kernel<Ty, D, BS><<<grid, 64, 0, st>>>(
+  decode_mfma_kernel<Ty, D, BS, NW, PF><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
       (uint16_t*)a->out, (const uint16_t*)a->q, (const uint16_t*)a->k_cache,
       (const uint16_t*)a->v_cache, a->block_tables, a->context_lens, a->num_q_heads,
       a->num_kv_heads, G, pl.groups, a->num_blocks, a->max_blocks_per_seq, a->max_context_len,
-      a->scale * kLog2e, pl.P, pl.max_parts, ws_acc, ws_ml);
+      a->scale * kLog2e, pl.P, max(pl.max_parts, 1), ws_acc, ws_ml);
+}
+
+template <typename Ty, int D, int BS>
+void launch_mfma_waves(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
+                       hipStream_t st) {
+  if (pl.prefetch) {
+    switch (pl.waves) {
+      case 1: launch_mfma<Ty, D, BS, 1, true>(a, pl, wa, wm, st); break;
+      case 2: launch_mfma<Ty, D, BS, 2, true>(a, pl, wa, wm, st); break;
+      case 8: launch_mfma<Ty, D, BS, 8, true>(a, pl, wa, wm, st); break;
+      default: launch_mfma<Ty, D, BS, 4, true>(a, pl, wa, wm, st);
+    }
+  } else {
+    switch (pl.waves) {
+      case 1: launch_mfma<Ty, D, BS, 1, false>(a, pl, wa, wm, st); break;
+      case 2: launch_mfma<Ty, D, BS, 2, false>(a, pl, wa, wm, st); break;
+      case 8: launch_mfma<Ty, D, BS, 8, false>(a, pl, wa, wm, st); break;
+      default: launch_mfma<Ty, D, BS, 4, false>(a, pl, wa, wm, st);
+    }
+  }
+}
+
+template <typename Ty>
+void launch_mfma_dims(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
+                      hipStream_t st) {
+  if (a->head_dim == 128) {
+    if (a->block_size == 16) launch_mfma_waves<Ty, 128, 16>(a, pl, wa, wm, st);
+    else launch_mfma_waves<Ty, 128, 32>(a, pl, wa, wm, st);
+  } else {
+    if (a->block_size == 16) launch_mfma_waves<Ty, 64, 16>(a, pl, wa, wm, st);
+    else launch_mfma_waves<Ty, 64, 32>(a, pl, wa, wm, st);
+  }
 }
 
 template <int D, int BS>
@@ -411,16 +595,53 @@ void launch_f32(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* w
       ws_ml);
 }
 
-template <typename Ty>
-void launch_mfma_dims(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
-                      hipStream_t st) {
-  if (a->head_dim == 128) {
-    if (a->block_size == 16) launch_mfma<Ty, 128, 16>(a, pl, wa, wm, st);
-    else launch_mfma<Ty, 128, 32>(a, pl, wa, wm, st);
-  } else {
-    if (a->block_size == 16) launch_mfma<Ty, 64, 16>(a, pl, wa, wm, st);
-    else launch_mfma<Ty, 64, 32>(a, pl, wa, wm, st);
+template <typename Store, int D>
+void launch_merge(const pa_decode_args* a, const Plan& pl, const float* wa, const float* wm,
+                  hipStream_t st) {
+  dim3 grid((unsigned)a->num_q_heads, (unsigned)a->num_seqs);
+  merge_kernel<Store, D><<<grid, kMergeThreads, 0, st>>>(
+      (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
+      a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts);
+}
+
+template <typename Store>
+void launch_merge_dims(const pa_decode_args* a, const Plan& pl, const float* wa,
+                       const float* wm, hipStream_t st) {
+  if (a->head_dim == 128) launch_merge<Store, 128>(a, pl, wa, wm, st);
+  else launch_merge<Store, 64>(a, pl, wa, wm, st);
+}
+
+// Launches pass 1 and, when some context spans several partitions, pass 2.
+pa_status run_plan(const pa_decode_args* a, const Plan& pl, hipStream_t hs) {
+  float* ws_acc = nullptr;
+  float* ws_ml = nullptr;
+  if (pl.ws_bytes) {
+    ws_acc = (float*)a->workspace;
+    ws_ml = ws_acc + (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * a->head_dim;
   }
+  switch (a->dtype) {
+    case PA_F16: launch_mfma_dims<F16>(a, pl, ws_acc, ws_ml, hs); break;
+    case PA_BF16: launch_mfma_dims<BF16>(a, pl, ws_acc, ws_ml, hs); break;
+    default:
+      if (a->head_dim == 128) {
+        if (a->block_size == 16) launch_f32<128, 16>(a, pl, ws_acc, ws_ml, hs);
+        else launch_f32<128, 32>(a, pl, ws_acc, ws_ml, hs);
+      } else {
+        if (a->block_size == 16) launch_f32<64, 16>(a, pl, ws_acc, ws_ml, hs);
+        else launch_f32<64, 32>(a, pl, ws_acc, ws_ml, hs);
+      }
+  }
+  pa_status st = launch_status();
+  if (st != PA_OK) return st;
+  if (pl.max_parts > 1) {
+    switch (a->dtype) {
+      case PA_F16: launch_merge_dims<Store16<F16>>(a, pl, ws_acc, ws_ml, hs); break;
+      case PA_BF16: launch_merge_dims<Store16<BF16>>(a, pl, ws_acc, ws_ml, hs); break;
+      default: launch_merge_dims<StoreF32>(a, pl, ws_acc, ws_ml, hs);
+    }
+    st = launch_status();
+  }
+  return st;
 }
 
 }  // namespace
@@ -448,52 +669,12 @@ PA_API pa_status pa_decode(const pa_decode_args* a, void* stream) {
       !aligned16(a->v_cache) || !a->block_tables || !a->context_lens)
     return PA_ERR_INVALID;
   const Plan pl = make_plan(a);
-  if (a->num_seqs > 65535 || (int64_t)a->num_kv_heads * pl.groups > 65535 ||
-      a->num_q_heads > 65535)
+  if (a->num_seqs > 65535 || pl.max_parts > 65535 || a->num_q_heads > 65535)
     return PA_ERR_UNSUPPORTED;
-  float* ws_acc = nullptr;
-  float* ws_ml = nullptr;
-  if (pl.ws_bytes) {
-    if (!a->workspace || a->workspace_bytes < pl.ws_bytes || !aligned16(a->workspace))
-      return PA_ERR_WORKSPACE;
-    ws_acc = (float*)a->workspace;
-    ws_ml = ws_acc + (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * a->head_dim;
-  }
-  hipStream_t hs = (hipStream_t)stream;
-  switch (a->dtype) {
-    case PA_F16: launch_mfma_dims<F16>(a, pl, ws_acc, ws_ml, hs); break;
-    case PA_BF16: launch_mfma_dims<BF16>(a, pl, ws_acc, ws_ml, hs); break;
-    default:
-      if (a->head_dim == 128) {
-        if (a->block_size == 16) launch_f32<128, 16>(a, pl, ws_acc, ws_ml, hs);
-        else launch_f32<128, 32>(a, pl, ws_acc, ws_ml, hs);
-      } else {
-        if (a->block_size == 16) launch_f32<64, 16>(a, pl, ws_acc, ws_ml, hs);
-        else launch_f32<64, 32>(a, pl, ws_acc, ws_ml, hs);
-      }
-  }
-  if ((st = launch_status()) != PA_OK) return st;
-  if (pl.max_parts > 1) {
-    dim3 grid((unsigned)a->num_q_heads, (unsigned)a->num_seqs);
-    switch (a->dtype) {
-      case PA_F16:
-        merge_kernel<Out16<F16>><<<grid, a->head_dim, 0, hs>>>(
-            (Out16<F16>*)a->out, a->context_lens, ws_acc, ws_ml, a->num_q_heads, a->head_dim,
-            a->max_context_len, a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts);
-        break;
-      case PA_BF16:
-        merge_kernel<Out16<BF16>><<<grid, a->head_dim, 0, hs>>>(
-            (Out16<BF16>*)a->out, a->context_lens, ws_acc, ws_ml, a->num_q_heads, a->head_dim,
-            a->max_context_len, a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts);
-        break;
-      default:
-        merge_kernel<float><<<grid, a->head_dim, 0, hs>>>(
-            (float*)a->out, a->context_lens, ws_acc, ws_ml, a->num_q_heads, a->head_dim,
-            a->max_context_len, a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts);
-    }
-    if ((st = launch_status()) != PA_OK) return st;
-  }
-  return PA_OK;
+  if (pl.ws_bytes &&
+      (!a->workspace || a->workspace_bytes < pl.ws_bytes || !aligned16(a->workspace)))
+    return PA_ERR_WORKSPACE;
+  return run_plan(a, pl, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -197,6 +197,57 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
     return out
 
 
+class PreparedCall:
+    """One library call with its arguments marshalled once (for tight loops
+    such as a benchmark): calling it only passes the prepared arguments to
+    the C entry point and checks the status.  The tensors it was built from
+    must stay alive and unchanged in shape while it is used."""
+
+    def __init__(self, name, fn, args, keep):
+        self._name, self._fn, self._args, self._keep = name, fn, args, keep
+
+    def __call__(self):
+        _check(self._fn(*self._args), self._name)
+
+
+def prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                   partition_size=0, workspace=None, stream=None):
+    """pa_decode with its argument struct filled once; the workspace (when
+    the step needs one) is allocated here."""
+    a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                         max_context_len, partition_size, workspace)
+    need = pa_decode_workspace_bytes(a)
+    if need and workspace is None:
+        workspace = _torch().empty(need, dtype=_torch().uint8, device=q.device)
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = need
+    return PreparedCall("pa_decode", lib().pa_decode, (ctypes.byref(a), _stream(stream)),
+                        (a, workspace, out, q, k_cache, v_cache, block_tables, context_lens))
+
+
+def prepare_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
+    T = slot_mapping.shape[0]
+    if tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D):
+        raise ValueError("k_new / v_new must be [T, Hkv, D]")
+    if slot_mapping.dtype != _torch().int64 or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise TypeError("slot_mapping must be int64 and k_new / v_new of the cache's dtype")
+    args = (_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, Hkv, D,
+            BS, NB, _dtype_code(k_cache), _stream(stream))
+    return PreparedCall("pa_write_kv", lib().pa_write_kv, args,
+                        (k_new, v_new, k_cache, v_cache, slot_mapping))
+
+
+def prepare_copy_blocks(k_cache, v_cache, block_mapping, stream=None):
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
+    if block_mapping.dtype != _torch().int32 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [P, 2] int32")
+    args = (_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), block_mapping.shape[0], Hkv, D, BS,
+            NB, _dtype_code(k_cache), _stream(stream))
+    return PreparedCall("pa_copy_blocks", lib().pa_copy_blocks, args,
+                        (k_cache, v_cache, block_mapping))
+
+
 def pa_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
     NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
     T = slot_mapping.shape[0]
