@@ -2,9 +2,10 @@
 """Benchmark of the paged decode hot path on one MI355X.
 
 One step = one decode step of one attention layer for the whole batch:
-pa_copy_blocks (copy-on-write pairs of the step; none in this workload),
-pa_write_kv of every sequence's new token, then pa_decode over every
-sequence's paged KV cache.  Inputs are seeded, synthetic and resident in HBM
+pa_copy_blocks (copy-on-write pairs of the step; none in these workloads),
+then pa_decode over every sequence's paged KV cache, which also stores each
+sequence's new token into its slot (fused append; --separate-write runs
+pa_write_kv first instead).  Inputs are seeded, synthetic and resident in HBM
 before timing starts.  R replicas (disjoint block sets of one pool, their
 own queries and new tokens) are cycled so that consecutive steps read
 different KV bytes, as successive layers would, and the 256 MB last-level
@@ -40,6 +41,9 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=-1, help="-1 = the workload's own")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget; 0 = skip")
     ap.add_argument("--profile-steps", action="store_true", help="no cpu baseline (for profilers)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="write the new tokens with pa_write_kv, then pa_decode (default: "
+                         "pa_decode appends them itself)")
     ap.add_argument("--calib-bytes", type=int, default=0,
                     help="first run one plain device-to-device copy of this many bytes (a "
                          "known-size reference for hardware byte counters)")
@@ -100,9 +104,14 @@ def main():
     stream = torch.cuda.current_stream()
     # arguments are marshalled once per replica; the timed loop only enqueues
     outs = [torch.empty_like(qs[0]) for _ in range(R)]
+    fused = not args.separate_write
     decode = [pa.prepare_decode(outs[r], qs[r], kd, vd, tables[r], lens, case.scale, max_ctx,
-                                partition_size=P, stream=stream) for r in range(R)]
+                                partition_size=P, stream=stream,
+                                k_new=knew[r] if fused else None, v_new=vnew[r] if fused else None)
+              for r in range(R)]
     write = [pa.prepare_write_kv(knew[r], vnew[r], kd, vd, slots[r], stream=stream) for r in range(R)]
+    if fused:
+        write = [lambda: None] * R
     copy = pa.prepare_copy_blocks(kd, vd, no_pairs, stream=stream)
     a0 = pa.make_decode_args(outs[0], qs[0], kd, vd, tables[0], lens, case.scale, max_ctx, P)
     P_eff = pa.pa_decode_partition_size(a0)
@@ -125,27 +134,40 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # Timed region: K steps enqueued back to back, bracketed by one pair of HIP
+    # events on the launch stream (no event between launches: an event record
+    # between two kernels adds several microseconds of its own).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(args.steps):
-        r = i % R
-        copy()
-        write[r]()
-        ev[i][0].record(stream)
-        decode[r]()
-        ev[i][1].record(stream)
+        step(i)
+    e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec_per_step = (t1 - t0) / args.steps
-    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
+    # The decode launch alone: in the fused step it is the step's only launch;
+    # with --separate-write it is timed in a second loop of decode launches.
+    if fused:
+        decode_ms = gpu_ms_per_step
+    else:
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            decode[i % R]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        decode_ms = e0.elapsed_time(e1) / args.steps
 
     # ---- algorithmic bytes of one pa_decode launch
     esz = wl.ELEM_BYTES[dtype]
     kv_bytes = case.kv_bytes()
     n_blocks = int(sum(-(-int(c) // case.BS) for c in case.context_lens))
     decode_bytes = kv_bytes + n_blocks * 4 + S * 4 + 2 * S * case.Hq * case.D * esz
+    if fused:  # the appended token is also written to its slot
+        decode_bytes += 2 * S * case.Hkv * case.D * esz
     achieved = decode_bytes / (decode_ms * 1e-3) / 1e9
 
     # ---- host bookkeeping (allocator) for one step, reported separately
@@ -169,6 +191,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(sec_per_step * 1e3, 5),
+        "gpu_ms_per_step": round(gpu_ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -181,8 +204,10 @@ def main():
                    "context_tokens": int(case.context_lens.sum()),
                    "max_context": max_ctx, "partition_size": P_eff, "replicas": R,
                    "kv_bytes_per_step": kv_bytes,
-                   "step": "pa_copy_blocks(0 pairs) + pa_write_kv + pa_decode"},
-        "roofline": {"kernel": "decode_mfma_kernel" + (" + merge_kernel (split-K)" if split else ""),
+                   "step": ("pa_copy_blocks(0 pairs) + pa_decode(fused append of the new token)"
+                            if fused else "pa_copy_blocks(0 pairs) + pa_write_kv + pa_decode")},
+        "roofline": {"kernel": "decode_mfma_kernel" + (" (fused append)" if fused else "")
+                     + (" + merge_kernel (split-K)" if split else ""),
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "avg_launch_ms": round(decode_ms, 5),

@@ -113,6 +113,19 @@ typedef struct pa_decode_args {
   int32_t partition_size;   /* 0 = library choice */
   void* workspace;
   size_t workspace_bytes;
+  /* Optional fused cache write of the step's new token (NULL, NULL = none).
+   * k_new, v_new: [num_seqs, num_kv_heads, head_dim] of dtype, 16-byte
+   * aligned, both set or both NULL.  When set, sequence s's token at logical
+   * position context_lens[s] - 1 is taken from k_new[s] / v_new[s] rather than
+   * from the cache, and is also stored, bit for bit, into that position's slot
+   * (physical block block_tables[s][(c - 1) / block_size], row (c - 1) %
+   * block_size).  The pool afterwards equals that of pa_write_kv with those
+   * slots; the output equals pa_decode after that write up to the rounding
+   * order of the one new token's contribution.  Sequences with c == 0 append
+   * nothing.  The slot of position c - 1 must not be shared with another
+   * sequence (copy-on-write it first with pa_copy_blocks). */
+  const void* k_new;
+  const void* v_new;
 } pa_decode_args;
 
 /* Bytes of workspace pa_decode needs for these sizes (pointers are not read).

@@ -53,6 +53,10 @@ constexpr int kChunk = 32;          // tokens per step of the 16-bit kernel
 constexpr int kMaxF32Part = 1024;   // largest partition of the fp32 kernel
 constexpr int kMergeThreads = 256;
 
+__device__ __forceinline__ u32x2 load8(const void* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
 // K/V are streamed: every byte is read once per step, so the loads are
 // non-temporal (they do not displace reusable lines in the caches); this is
 // worth several percent of HBM bandwidth on these scattered 4-8 KiB tiles.
@@ -82,7 +86,8 @@ template <typename Ty, int D, int BS, int NW, bool PF>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables,
-    const int32_t* __restrict__ lens, int Hq, int Hkv, int G, int n_groups, int NB,
+    const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, int Hq, int Hkv, int G, int n_groups, int NB,
     int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
     float* __restrict__ ws_acc, float* __restrict__ ws_ml) {
   static_assert(BS == 16 || BS == 32, "block size 16 or 32");
@@ -107,8 +112,14 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   const int n_p = (c + P - 1) / P;
   if (p < 0 || p >= max(n_p, 1)) return;
   const int t_begin = p * P;
-  const int t_end = min(c, t_begin + P);
-  const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
+  // With a fused append the token at c - 1 comes from k_new / v_new, not from
+  // the cache: the chunk loop reads [t_begin, cc) and the new token is added
+  // afterwards by the workgroup whose partition holds it.
+  const bool append = k_new != nullptr;
+  const int cc = append ? max(c - 1, 0) : c;
+  const bool has_new = append && c > 0 && c - 1 >= t_begin && c - 1 < t_begin + P;
+  const int t_end = min(cc, t_begin + P);
+  const int n_chunks = max(0, t_end - t_begin + kChunk - 1) / kChunk;
 
   const int Gv = min(16, G - grp * 16);  // query heads of this group
   const bool head_ok = i < Gv;
@@ -123,6 +134,17 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       u32x4 raw = head_ok ? load16(qrow + 8 * (4 * kk + g4)) : u32x4{0u, 0u, 0u, 0u};
       qop[kk] = __builtin_bit_cast(V8, raw);
     }
+  }
+
+  // Fused append: wave 0 of the workgroup whose partition holds token c - 1
+  // fetches the new K row and V row up front, 8 bytes per lane (lanes
+  // [0, D/4) hold K elements 4*lane..+3, lanes [D/4, D/2) hold V elements
+  // 4*(lane - D/4)..+3), so the data is in registers when the token is added.
+  const bool new_here = has_new && w == 0;
+  u32x2 nv = {0u, 0u};
+  if (new_here && lane < D / 2) {
+    const int64_t row = ((int64_t)s * Hkv + hk) * D;
+    nv = lane < D / 4 ? load8(k_new + row + 4 * lane) : load8(v_new + row + 4 * (lane - D / 4));
   }
 
   f32x4 acc[MM];
@@ -141,7 +163,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     const int t0 = t_begin + ch * kChunk;
     bA = uniform(clampi(trow[t0 / BS], 0, NB - 1));
     bB = bA;
-    if (BS == 16 && t0 + 16 < c) bB = uniform(clampi(trow[t0 / BS + 1], 0, NB - 1));
+    if (BS == 16 && t0 + 16 < cc) bB = uniform(clampi(trow[t0 / BS + 1], 0, NB - 1));
   };
   // Issue every K and V load of one chunk (2 x KK 16-byte K vectors, 2 x MM
   // 8-byte V pieces per lane).
@@ -181,11 +203,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       x[j] = s0[j] * scale_log2;
       x[4 + j] = s1[j] * scale_log2;
     }
-    if (t0 + kChunk > c) {  // last chunk: drop tokens past the context by select
+    if (t0 + kChunk > cc) {  // last chunk: drop tokens past the cached range by select
       uint32_t keep[4];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= c) x[e] = -INFINITY;
+        if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= cc) x[e] = -INFINITY;
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd)
         keep[wd] = (x[2 * wd] != -INFINITY ? 0x0000FFFFu : 0u) |
@@ -255,6 +277,69 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     }
   }
 
+  // Fused append: that wave adds token c - 1 to its running state on the
+  // vector ALU (one logit per head: each lane of a head takes 32 channels and
+  // the 4 row groups are added), rounding the weight to the element type as
+  // the matrix-core path does.  The group-0 workgroup also stores the token
+  // into the cache slot of position c - 1, bit for bit.
+  if (new_here) {
+    // operands gathered from the lanes holding them: K chunk 4*kk+g4 (16 B)
+    // sits in lanes 2*chunk, 2*chunk+1; V channels 16*mm+4*g4..+3 (8 B) in
+    // lane D/4 + 4*mm + g4.
+    u32x4 kx[KK];
+    u32x2 vx[MM];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int src = 2 * (4 * kk + g4);
+      kx[kk] = u32x4{(uint32_t)__shfl((int)nv[0], src), (uint32_t)__shfl((int)nv[1], src),
+                     (uint32_t)__shfl((int)nv[0], src + 1), (uint32_t)__shfl((int)nv[1], src + 1)};
+    }
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) {
+      const int src = D / 4 + 4 * mm + g4;
+      vx[mm] = u32x2{(uint32_t)__shfl((int)nv[0], src), (uint32_t)__shfl((int)nv[1], src)};
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4 qw = __builtin_bit_cast(u32x4, qop[kk]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        dot = fmaf(Ty::to_f32((uint16_t)(qw[e / 2] >> (16 * (e & 1)))),
+                   Ty::to_f32((uint16_t)(kx[kk][e / 2] >> (16 * (e & 1)))), dot);
+    }
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    const float xn = dot * scale_log2;
+    const float m_new = fmaxf(m_run, xn);
+    const float alpha = exp2_fast(m_run - m_new);  // 0 when the wave saw no cached token
+    const float pn = Ty::to_f32(Ty::from_f32(exp2_fast(xn - m_new)));
+    m_run = m_new;
+    l_run = l_run * alpha + (g4 == 0 ? pn : 0.f);
+    // lane holds O^T[d = 16*mm + 4*g4 + j][head i]; vx[mm] holds v_new[16*mm + 4*g4 + j]
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[mm][j] = fmaf(pn, Ty::to_f32((uint16_t)(vx[mm][j / 2] >> (16 * (j & 1)))),
+                          acc[mm][j] * alpha);
+    if (grp == 0 && lane < D / 2) {
+      const int tn = c - 1;
+      const int64_t b = clampi(trow[tn / BS], 0, NB - 1);
+      const int o = tn % BS;
+      if (lane < D / 4) {  // K elements 4*lane..+3: half of chunk lane/2's 16-byte row piece
+        uint16_t* kd = const_cast<uint16_t*>(kc) + b * blk_stride + head_off;
+        *reinterpret_cast<u32x2*>(kd + ((lane / 2) * BS + o) * 8 + 4 * (lane & 1)) = nv;
+      } else {             // V channels 4*(lane - D/4)..+3 of row o
+        uint16_t* vd = const_cast<uint16_t*>(vc) + b * blk_stride + head_off;
+        const int d0 = 4 * (lane - D / 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vd[(d0 + j) * BS + o] = (uint16_t)(nv[j / 2] >> (16 * (j & 1)));
+      }
+    }
+  }
+
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
 
@@ -320,7 +405,8 @@ template <int D, int BS>
 __global__ __launch_bounds__(64) void decode_f32_kernel(
     float* __restrict__ out, const float* __restrict__ q, const float* __restrict__ kc,
     const float* __restrict__ vc, const int32_t* __restrict__ tables,
-    const int32_t* __restrict__ lens, int Hq, int Hkv, int G, int NB, int max_blocks,
+    const int32_t* __restrict__ lens, const float* __restrict__ k_new,
+    const float* __restrict__ v_new, int Hq, int Hkv, int G, int NB, int max_blocks,
     int max_ctx, float scale_log2, int P, int max_parts, float* __restrict__ ws_acc,
     float* __restrict__ ws_ml) {
   __shared__ float xs[kMaxF32Part];
@@ -335,6 +421,10 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
   const int n = max(0, min(c, t_begin + P) - t_begin);
   const int32_t* trow = tables + (int64_t)s * max_blocks;
   const int64_t tile = (int64_t)D * BS;
+  // fused append: token c - 1 is read from k_new / v_new ([S, Hkv, D])
+  const int t_new = k_new != nullptr ? c - 1 : -1;
+  const float* kn = k_new != nullptr ? k_new + ((int64_t)s * Hkv + hk) * D : nullptr;
+  const float* vn = v_new != nullptr ? v_new + ((int64_t)s * Hkv + hk) * D : nullptr;
 
   for (int d = lane; d < D; d += kWave) qs[d] = q[((int64_t)s * Hq + h) * D + d];
   __syncthreads();
@@ -343,11 +433,13 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
   for (int t = lane; t < n; t += kWave) {
     const int tok = t_begin + t;
     const int64_t b = clampi(trow[tok / BS], 0, NB - 1);
-    const float* kb = kc + (b * Hkv + hk) * tile + (tok % BS) * 4;
+    const bool fresh = tok == t_new;
+    const float* kb = fresh ? kn : kc + (b * Hkv + hk) * tile + (tok % BS) * 4;
+    const int kstride = fresh ? 4 : BS * 4;
     float dot = 0.f;
 #pragma unroll 4
     for (int cc = 0; cc < D / 4; ++cc) {
-      const f32x4 k4 = *reinterpret_cast<const f32x4*>(kb + cc * BS * 4);
+      const f32x4 k4 = *reinterpret_cast<const f32x4*>(kb + cc * kstride);
       dot = fmaf(qs[4 * cc], k4[0], dot);
       dot = fmaf(qs[4 * cc + 1], k4[1], dot);
       dot = fmaf(qs[4 * cc + 2], k4[2], dot);
@@ -374,7 +466,15 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
     for (int t = 0; t < n; ++t) {
       const int tok = t_begin + t;
       const int64_t b = clampi(trow[tok / BS], 0, NB - 1);
-      a = fmaf(xs[t], vc[((b * Hkv + hk) * D + d) * BS + tok % BS], a);
+      const float v = tok == t_new ? vn[d] : vc[((b * Hkv + hk) * D + d) * BS + tok % BS];
+      a = fmaf(xs[t], v, a);
+    }
+    // the cache write of the step: one workgroup per (sequence, KV head)
+    if (t_new >= t_begin && t_new < t_begin + P && h == hk * G) {
+      const int64_t b = clampi(trow[t_new / BS], 0, NB - 1);
+      const int o = t_new % BS;
+      const_cast<float*>(kc)[((b * Hkv + hk) * (D / 4) + d / 4) * BS * 4 + o * 4 + d % 4] = kn[d];
+      const_cast<float*>(vc)[((b * Hkv + hk) * D + d) * BS + o] = vn[d];
     }
     if (n_p <= 1) {
       out[((int64_t)s * Hq + h) * D + d] = lloc > 0.f ? a / lloc : 0.f;
@@ -546,9 +646,10 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
             (unsigned)a->num_seqs);
   decode_mfma_kernel<Ty, D, BS, NW, PF><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
       (uint16_t*)a->out, (const uint16_t*)a->q, (const uint16_t*)a->k_cache,
-      (const uint16_t*)a->v_cache, a->block_tables, a->context_lens, a->num_q_heads,
-      a->num_kv_heads, G, pl.groups, a->num_blocks, a->max_blocks_per_seq, a->max_context_len,
-      a->scale * kLog2e, pl.P, max(pl.max_parts, 1), ws_acc, ws_ml);
+      (const uint16_t*)a->v_cache, a->block_tables, a->context_lens, (const uint16_t*)a->k_new,
+      (const uint16_t*)a->v_new, a->num_q_heads, a->num_kv_heads, G, pl.groups, a->num_blocks,
+      a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, pl.P, max(pl.max_parts, 1),
+      ws_acc, ws_ml);
 }
 
 template <typename Ty, int D, int BS>
@@ -590,7 +691,8 @@ void launch_f32(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* w
   dim3 grid((unsigned)max(pl.max_parts, 1), (unsigned)a->num_q_heads, (unsigned)a->num_seqs);
   decode_f32_kernel<D, BS><<<grid, 64, 0, st>>>(
       (float*)a->out, (const float*)a->q, (const float*)a->k_cache, (const float*)a->v_cache,
-      a->block_tables, a->context_lens, a->num_q_heads, a->num_kv_heads, G, a->num_blocks,
+      a->block_tables, a->context_lens, (const float*)a->k_new, (const float*)a->v_new,
+      a->num_q_heads, a->num_kv_heads, G, a->num_blocks,
       a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, pl.P, pl.max_parts, ws_acc,
       ws_ml);
 }
@@ -671,6 +773,8 @@ PA_API pa_status pa_decode(const pa_decode_args* a, void* stream) {
   const Plan pl = make_plan(a);
   if (a->num_seqs > 65535 || pl.max_parts > 65535 || a->num_q_heads > 65535)
     return PA_ERR_UNSUPPORTED;
+  if ((a->k_new == nullptr) != (a->v_new == nullptr)) return PA_ERR_INVALID;
+  if (a->k_new && (!aligned16(a->k_new) || !aligned16(a->v_new))) return PA_ERR_INVALID;
   if (pl.ws_bytes &&
       (!a->workspace || a->workspace_bytes < pl.ws_bytes || !aligned16(a->workspace)))
     return PA_ERR_WORKSPACE;

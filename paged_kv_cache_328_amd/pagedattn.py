@@ -49,6 +49,7 @@ class pa_decode_args(ctypes.Structure):
         ("block_size", _I32), ("num_blocks", _I32), ("max_blocks_per_seq", _I32),
         ("max_context_len", _I32), ("scale", ctypes.c_float), ("dtype", _I32),
         ("partition_size", _I32), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+        ("k_new", _P), ("v_new", _P),
     ]
 
 
@@ -147,8 +148,10 @@ def cache_geometry(k_cache, v_cache):
 
 
 def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                     max_context_len, partition_size=0, workspace=None):
-    """Fill a pa_decode_args from tensors (no call into the library)."""
+                     max_context_len, partition_size=0, workspace=None, k_new=None, v_new=None):
+    """Fill a pa_decode_args from tensors (no call into the library).
+    k_new / v_new ([S, Hkv, D], optional): the step's new token of every
+    sequence, appended at position context_lens[s] - 1 by pa_decode itself."""
     NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
     S, Hq, Dq = q.shape
     if Dq != D or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or q.dtype != k_cache.dtype:
@@ -170,6 +173,14 @@ def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale
     if workspace is not None:
         a.workspace = _ptr(workspace)
         a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        if tuple(k_new.shape) != (S, Hkv, D) or tuple(v_new.shape) != (S, Hkv, D):
+            raise ValueError("k_new / v_new must be [S, Hkv, D]")
+        if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+            raise TypeError("k_new / v_new must have the cache's dtype")
+        a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
     return a
 
 
@@ -182,12 +193,13 @@ def pa_decode_partition_size(args):
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-              partition_size=0, workspace=None, stream=None):
-    """Paged decode attention into `out`.  When the step needs split-K
-    partials and no workspace is given, a byte tensor is allocated with torch
-    on q's device."""
+              partition_size=0, workspace=None, stream=None, k_new=None, v_new=None):
+    """Paged decode attention into `out` (with k_new / v_new: fused append of
+    the step's token at position context_lens[s] - 1).  When the step needs
+    split-K partials and no workspace is given, a byte tensor is allocated with
+    torch on q's device."""
     a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                         max_context_len, partition_size, workspace)
+                         max_context_len, partition_size, workspace, k_new, v_new)
     need = pa_decode_workspace_bytes(a)
     if need and workspace is None:
         workspace = _torch().empty(need, dtype=_torch().uint8, device=q.device)
@@ -211,18 +223,19 @@ class PreparedCall:
 
 
 def prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-                   partition_size=0, workspace=None, stream=None):
+                   partition_size=0, workspace=None, stream=None, k_new=None, v_new=None):
     """pa_decode with its argument struct filled once; the workspace (when
     the step needs one) is allocated here."""
     a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                         max_context_len, partition_size, workspace)
+                         max_context_len, partition_size, workspace, k_new, v_new)
     need = pa_decode_workspace_bytes(a)
     if need and workspace is None:
         workspace = _torch().empty(need, dtype=_torch().uint8, device=q.device)
         a.workspace = _ptr(workspace)
         a.workspace_bytes = need
     return PreparedCall("pa_decode", lib().pa_decode, (ctypes.byref(a), _stream(stream)),
-                        (a, workspace, out, q, k_cache, v_cache, block_tables, context_lens))
+                        (a, workspace, out, q, k_cache, v_cache, block_tables, context_lens,
+                         k_new, v_new))
 
 
 def prepare_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):

@@ -68,6 +68,19 @@ def test_decode_rejects_null_pointers_and_missing_workspace(L):
     assert L.pa_decode(None, None) == pa.PA_ERR_INVALID
 
 
+def test_fused_append_needs_both_tensors(L):
+    import ctypes
+    buf = (ctypes.c_uint8 * 64)()
+    addr = (ctypes.addressof(buf) + 15) // 16 * 16
+    a = _args()
+    a.out = a.q = a.k_cache = a.v_cache = addr
+    a.block_tables = a.context_lens = addr
+    a.k_new = addr          # v_new missing
+    assert L.pa_decode(a, None) == pa.PA_ERR_INVALID
+    a.v_new = addr + 8      # misaligned
+    assert L.pa_decode(a, None) == pa.PA_ERR_INVALID
+
+
 def test_cache_ops_reject_bad_arguments(L):
     assert L.pa_write_kv(None, None, None, None, None, 1, 2, 128, 16, 10, 9, None) == pa.PA_ERR_INVALID
     assert L.pa_write_kv(None, None, None, None, None, 1, 2, 100, 16, 10, pa.PA_BF16, None) == pa.PA_ERR_UNSUPPORTED

@@ -186,6 +186,80 @@ def test_cow_shared_prefix_step():
     check_attention(to_host(out, dtype), want_out, dtype, "cow_bf16")
 
 
+# ---------------------------------------------------------------------------- fused append
+
+def run_fused_case(case, label, partition_size=None, r=0):
+    """pa_decode with k_new / v_new: the step's token of every sequence is
+    stored at position c - 1 and attended to in the same launch.  The device
+    pool's slot c - 1 is poisoned with NaN first, so a read of the stale slot
+    would show.  Checks: the touched blocks equal the oracle's cache write bit
+    for bit, and the output matches the oracle's decode after that write."""
+    import torch
+    dtype = case.dtype
+    tables = np.ascontiguousarray(case.block_tables[r])
+    lens = case.context_lens
+    kc, vc = case.k_cache, case.v_cache
+    poison_tails(oracle, kc, vc, tables, lens, dtype)
+    slots = np.ascontiguousarray(case.slot_mapping[r])
+    live = slots >= 0
+    nan = np.full((int(live.sum()), case.Hkv, case.D), wl.nan_bits(dtype), wl.NP_STORAGE[dtype])
+    oracle.write_kv(nan, nan.copy(), kc, vc, slots[live], dtype)  # poison slot c - 1
+    announce(f"{label}: upload pools NB={case.NB} S={case.S} Hq={case.Hq} Hkv={case.Hkv} "
+             f"D={case.D} BS={case.BS} {dtype} max_ctx={case.max_context}")
+    kd, vd = to_dev(kc, dtype), to_dev(vc, dtype)
+    k_new, v_new = np.ascontiguousarray(case.new_k[r]), np.ascontiguousarray(case.new_v[r])
+    oracle.write_kv(k_new, v_new, kc, vc, slots, dtype)
+    q = np.ascontiguousarray(case.q[r])
+    qd = to_dev(q, dtype)
+    out = torch.empty_like(qd)
+    P = case.partition_size if partition_size is None else partition_size
+    announce(f"{label}: pa_decode fused append P={P}")
+    pa.pa_decode(out, qd, kd, vd, ints_to_dev(tables), ints_to_dev(lens), case.scale,
+                 case.max_context, partition_size=P, k_new=to_dev(k_new, dtype),
+                 v_new=to_dev(v_new, dtype))
+    _sync()
+    touched = np.unique(slots[live] // case.BS)
+    idx = torch.from_numpy(touched.astype(np.int64)).to(_g.DEVICE)
+    assert same_bits(to_host(kd.index_select(0, idx), dtype), kc[touched]), f"{label}: K blocks"
+    assert same_bits(to_host(vd.index_select(0, idx), dtype), vc[touched]), f"{label}: V blocks"
+    want = oracle.decode(q, kc, vc, tables, lens, case.scale, dtype, num_threads=16)
+    return check_attention(to_host(out, dtype), want, dtype, label + " fused"), to_host(out, dtype)
+
+
+def test_fused_append_tiny_f32_equals_write_then_decode():
+    """fp32: the fused launch runs the same arithmetic in the same order as
+    pa_write_kv followed by pa_decode, so the outputs are bit-identical."""
+    _, fused = run_fused_case(wl.tiny_f32(), "tiny_f32")
+    _, separate = run_decode_case(wl.tiny_f32(), "tiny_f32 separate", gather_seqs=None)
+    assert same_bits(fused, separate)
+
+
+def test_fused_append_llama13b_f16_full_size():
+    run_fused_case(wl.llama13b_f16(), "llama13b_f16")
+
+
+def test_fused_append_mixed_gqa_bf16_full_size():
+    run_fused_case(wl.mixed_gqa_bf16(), "mixed_gqa_bf16")
+
+
+def test_fused_append_long_bf16_full_size_p512():
+    run_fused_case(wl.long_bf16(), "long_bf16")
+
+
+FUSED_LENS = [0, 1, 2, 16, 17, 32, 33, 64, 65, 100, 129, 257]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("D,BS", [(64, 16), (128, 16), (128, 32)])
+@pytest.mark.parametrize("Hq,Hkv,P", [(4, 4, 0), (12, 4, 32), (40, 2, 64), (8, 8, 128)])
+def test_fused_append_edge_shapes(dtype, D, BS, Hq, Hkv, P):
+    if P and P % BS:
+        pytest.skip("partition size must be a multiple of the block size")
+    case = wl.random_case(1300 + D + BS + Hq + P, len(FUSED_LENS), Hq, Hkv, D, BS, dtype, FUSED_LENS,
+                          partition_size=P)
+    run_fused_case(case, f"fused {dtype} D{D} BS{BS} {Hq}/{Hkv} P{P}")
+
+
 # ---------------------------------------------------------------------------- edge cases
 
 EDGE_LENS = [0, 1, 15, 16, 17, 33, 100, 257]
