@@ -210,13 +210,32 @@ def main():
                      + (" + merge_kernel (split-K)" if split else ""),
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_ms": round(decode_ms, 5),
+                     "traffic": measured_traffic(case.name, P_eff, fused),
+                     "avg_launch_ms": round(decode_ms, 5),
                      "algorithmic_bytes_per_launch": decode_bytes},
         "host_bookkeeping_us": round(host_us, 2),
     }
     if args.cpu_seconds > 0 and not args.profile_steps:
         result["cpu_baseline"] = cpu_baseline(case, kd, vd, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(workload, partition_size, fused):
+    """HBM bytes per pa_decode launch from the committed rocprofv3 byte
+    counters (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE, each scaled by
+    what the counter reads for a plain copy of known size), or None when no
+    record matches this launch or the kernel sources changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload)
+    if not rec or rec.get("partition_size") != partition_size or rec.get("fused_append") != fused:
+        return None
+    h = hashlib.sha256()
+    for f in ["paged_kv_cache_328_amd/csrc/pa_decode.hip", "paged_kv_cache_328_amd/csrc/pa_device.h"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return rec["bytes_per_launch"] if h.hexdigest() == rec["kernel_sources_sha256"] else None
 
 
 def cpu_baseline(case, kd, vd, budget_s):

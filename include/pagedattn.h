@@ -91,7 +91,9 @@ PA_API const char* pa_status_string(pa_status s);
  * Supported: dtype f16 / bf16 / f32, head_dim 64 or 128, block_size 16 or
  * 32, any G = num_q_heads / num_kv_heads >= 1.
  * The workspace (caller-allocated device memory, any contents) holds the
- * split-K partials; its size comes from pa_decode_workspace_bytes.
+ * split-K partials; its size comes from pa_decode_workspace_bytes (0 when no
+ * context spans more than one partition).  Two calls in flight at once must
+ * not share a workspace.
  * ------------------------------------------------------------------------ */
 typedef struct pa_decode_args {
   void* out;

@@ -51,10 +51,27 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 32;          // tokens per step of the 16-bit kernel
 constexpr int kMaxF32Part = 1024;   // largest partition of the fp32 kernel
-constexpr int kMergeThreads = 256;
 
 __device__ __forceinline__ u32x2 load8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
+}
+
+// Running state of a log-sum-exp merge: max m, sum l, unnormalised output o
+// (4 channels).  Adding partition (m', l', o') with M = max(m, m'):
+// l <- l 2^(m-M) + l' 2^(m'-M), o likewise, m <- M.
+struct Lse {
+  float m, l;
+  f32x4 o;
+};
+
+// Adds a partition (m, l, o) to a running state (online log-sum-exp).
+__device__ __forceinline__ void lse_add(Lse& st, float m, float l, f32x4 o) {
+  const float mn = fmaxf(st.m, m);
+  const float a = exp2_fast(st.m - mn);  // 0 while the state is empty
+  const float b = exp2_fast(m - mn);
+  st.l = st.l * a + l * b;
+  st.o = st.o * a + o * b;
+  st.m = mn;
 }
 
 // K/V are streamed: every byte is read once per step, so the loads are
@@ -491,64 +508,69 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
 
 // ----------------------------------------------------------------------------
 // Pass 2: merge the partitions of every (sequence, query head) that has more
-// than one.  grid: x = query head, y = sequence; block = 256 threads.  All
-// partitions are read in parallel: thread (r, c4) takes channels 4*c4..+3 of
-// partitions r, r + ROWS, ...; the ROWS partial sums are added in LDS in a
-// fixed order, so the result depends only on the logical partition contents.
+// than one.  grid: x = query head, y = sequence; block = NT threads (128
+// when every context fits in 16 partitions, else 512).
+// Thread (r, c4) walks partitions r, r + ROWS, ... keeping its own running
+// (max, sum, output for channels 4*c4..+3) with the log-sum-exp rule, so one
+// pass reads every partial once and all loads of a batch are independent; the
+// first batch is fetched together with the context length.  The ROWS states
+// are then combined in LDS in row order, so the result depends only on the
+// partition contents, never on where the blocks sit.
 // ----------------------------------------------------------------------------
-template <typename Store, int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+template <typename Store, int D, int NT>
+__global__ __launch_bounds__(NT) void merge_kernel(
     typename Store::T* __restrict__ out, const int32_t* __restrict__ lens,
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, int Hq, int max_ctx,
     int max_blocks, int BS, int P, int max_parts) {
   constexpr int C4 = D / 4;                   // threads per partition row
-  constexpr int ROWS = kMergeThreads / C4;    // partitions read at once
-  constexpr int NWV = kMergeThreads / kWave;
-  __shared__ float red[NWV];
-  __shared__ f32x4 part[ROWS][C4];
+  constexpr int ROWS = NT / C4;               // partitions read at once
+  constexpr int U = 8;                        // partitions per thread per batch
+  __shared__ float sm[ROWS][C4], sl[ROWS][C4];
+  __shared__ f32x4 so[ROWS][C4];
   const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
+  const int r = tid / C4, c4 = tid - r * C4;
+  const int64_t base = ((int64_t)s * Hq + h) * max_parts;
+
+  Lse st = {-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+  float bm[U], bl[U];
+  f32x4 bo[U];
+  // first batch: issued before the context length is known (indices stay
+  // below max_parts, so every read is inside the workspace)
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int pp = min(r + k * ROWS, max_parts - 1);
+    bm[k] = ws_ml[2 * (base + pp)];
+    bl[k] = ws_ml[2 * (base + pp) + 1];
+    bo[k] = *reinterpret_cast<const f32x4*>(ws_acc + (base + pp) * D + 4 * c4);
+  }
   const int c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
   const int n_p = (c + P - 1) / P;
   if (n_p <= 1) return;
-  const int64_t base = ((int64_t)s * Hq + h) * max_parts;
-
-  float mx = -INFINITY;
-  for (int p = tid; p < n_p; p += kMergeThreads) mx = fmaxf(mx, ws_ml[2 * (base + p)]);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) red[wv] = mx;
-  __syncthreads();
-  float M = red[0];
+  for (int k = 0; k < U; ++k)
+    if (r + k * ROWS < n_p) lse_add(st, bm[k], bl[k], bo[k]);
+  for (int p0 = r + U * ROWS; p0 < n_p; p0 += U * ROWS) {
 #pragma unroll
-  for (int v = 1; v < NWV; ++v) M = fmaxf(M, red[v]);
-  __syncthreads();
-
-  float ls = 0.f;
-  for (int p = tid; p < n_p; p += kMergeThreads)
-    ls += exp2_fast(ws_ml[2 * (base + p)] - M) * ws_ml[2 * (base + p) + 1];
+    for (int k = 0; k < U; ++k) {
+      const int pp = min(p0 + k * ROWS, n_p - 1);
+      bm[k] = ws_ml[2 * (base + pp)];
+      bl[k] = ws_ml[2 * (base + pp) + 1];
+      bo[k] = *reinterpret_cast<const f32x4*>(ws_acc + (base + pp) * D + 4 * c4);
+    }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
-  if (lane == 0) red[wv] = ls;
-  __syncthreads();
-  float L = 0.f;
-#pragma unroll
-  for (int v = 0; v < NWV; ++v) L += red[v];
-
-  const int r = tid / C4, c4 = tid - r * C4;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int p = r; p < n_p; p += ROWS) {
-    const float wgt = exp2_fast(ws_ml[2 * (base + p)] - M);
-    o += wgt * *reinterpret_cast<const f32x4*>(ws_acc + (base + p) * D + 4 * c4);
+    for (int k = 0; k < U; ++k)
+      if (p0 + k * ROWS < n_p) lse_add(st, bm[k], bl[k], bo[k]);
   }
-  part[r][c4] = o;
+  sm[r][c4] = st.m;
+  sl[r][c4] = st.l;
+  so[r][c4] = st.o;
   __syncthreads();
   if (r == 0) {
-    f32x4 sum = part[0][c4];
+    Lse tot = {sm[0][c4], sl[0][c4], so[0][c4]};
 #pragma unroll
-    for (int rr = 1; rr < ROWS; ++rr) sum += part[rr][c4];
-    Store::put(out + ((int64_t)s * Hq + h) * D + 4 * c4, sum * (1.f / L));
+    for (int rr = 1; rr < ROWS; ++rr)
+      if (rr < n_p) lse_add(tot, sm[rr][c4], sl[rr][c4], so[rr][c4]);
+    Store::put(out + ((int64_t)s * Hq + h) * D + 4 * c4, tot.o * (1.f / tot.l));
   }
 }
 
@@ -701,9 +723,14 @@ template <typename Store, int D>
 void launch_merge(const pa_decode_args* a, const Plan& pl, const float* wa, const float* wm,
                   hipStream_t st) {
   dim3 grid((unsigned)a->num_q_heads, (unsigned)a->num_seqs);
-  merge_kernel<Store, D><<<grid, kMergeThreads, 0, st>>>(
-      (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
-      a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts);
+  if (pl.max_parts <= 16)
+    merge_kernel<Store, D, 128><<<grid, 128, 0, st>>>(
+        (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
+        a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts);
+  else
+    merge_kernel<Store, D, 512><<<grid, 512, 0, st>>>(
+        (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
+        a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts);
 }
 
 template <typename Store>

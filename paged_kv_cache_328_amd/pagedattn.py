@@ -202,7 +202,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
                          max_context_len, partition_size, workspace, k_new, v_new)
     need = pa_decode_workspace_bytes(a)
     if need and workspace is None:
-        workspace = _torch().empty(need, dtype=_torch().uint8, device=q.device)
+        workspace = _torch().zeros(need, dtype=_torch().uint8, device=q.device)
         a.workspace = _ptr(workspace)
         a.workspace_bytes = need
     _check(lib().pa_decode(ctypes.byref(a), _stream(stream)), "pa_decode")
@@ -230,7 +230,7 @@ def prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, 
                          max_context_len, partition_size, workspace, k_new, v_new)
     need = pa_decode_workspace_bytes(a)
     if need and workspace is None:
-        workspace = _torch().empty(need, dtype=_torch().uint8, device=q.device)
+        workspace = _torch().zeros(need, dtype=_torch().uint8, device=q.device)
         a.workspace = _ptr(workspace)
         a.workspace_bytes = need
     return PreparedCall("pa_decode", lib().pa_decode, (ctypes.byref(a), _stream(stream)),

@@ -63,6 +63,8 @@ def test_decode_rejects_null_pointers_and_missing_workspace(L):
     assert L.pa_decode_partition_size(a) == 32
     # 160 tokens / 32 -> 5 partitions: S * Hq * parts * (D + 2) floats
     assert L.pa_decode_workspace_bytes(a) == 4 * 8 * 5 * 130 * 4
+    a32 = _args(partition_size=32, dtype=pa.PA_F32)
+    assert L.pa_decode_workspace_bytes(a32) == 4 * 8 * 5 * 130 * 4
     a1 = _args(partition_size=160 // 32 * 32 * 2)  # one partition: no workspace
     assert L.pa_decode_workspace_bytes(a1) == 0
     assert L.pa_decode(None, None) == pa.PA_ERR_INVALID

@@ -316,6 +316,78 @@ def test_block_relabelling_and_determinism_bit_identical():
     assert same_bits(outs[0], outs[2]), "two identical runs differ"
 
 
+def test_one_workspace_serves_repeated_and_smaller_calls():
+    """Split contexts: one workspace (filled with garbage first) serves
+    repeated calls and a smaller batch; the outputs match the oracle and
+    repeat bit for bit."""
+    import torch
+    lens = [1, 300, 700, 1500, 2000, 129]
+    P = 128
+    case = wl.random_case(903, len(lens), 16, 4, 128, 16, "bf16", lens, partition_size=P)
+    dtype = "bf16"
+    t0 = np.ascontiguousarray(case.block_tables[0])
+    poison_tails(oracle, case.k_cache, case.v_cache, t0, case.context_lens, dtype)
+    kd, vd = to_dev(case.k_cache, dtype), to_dev(case.v_cache, dtype)
+    qd = to_dev(case.q[0], dtype)
+    a = pa.make_decode_args(torch.empty_like(qd), qd, kd, vd, ints_to_dev(t0),
+                            ints_to_dev(case.context_lens), case.scale, case.max_context, P)
+    need = pa.pa_decode_workspace_bytes(a)
+    assert need > 0
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=_g.DEVICE)
+    want = oracle.decode(np.ascontiguousarray(case.q[0]), case.k_cache, case.v_cache, t0,
+                         case.context_lens, case.scale, dtype, num_threads=16)
+    outs = []
+    for rep in range(3):
+        announce(f"workspace reuse: call {rep}")
+        out = torch.empty_like(qd)
+        pa.pa_decode(out, qd, kd, vd, ints_to_dev(t0), ints_to_dev(case.context_lens), case.scale,
+                     case.max_context, partition_size=P, workspace=ws)
+        _sync()
+        outs.append(to_host(out, dtype))
+        check_attention(outs[-1], want, dtype, f"workspace reuse call {rep}")
+    assert same_bits(outs[0], outs[1]) and same_bits(outs[0], outs[2])
+    sub = slice(3, 6)
+    out2 = torch.empty((3, case.Hq, case.D), dtype=torch_dtype(dtype), device=_g.DEVICE)
+    announce("workspace reuse: smaller batch")
+    pa.pa_decode(out2, to_dev(case.q[0][sub], dtype), kd, vd, ints_to_dev(t0[sub]),
+                 ints_to_dev(case.context_lens[sub]), case.scale, int(case.context_lens[sub].max()),
+                 partition_size=P, workspace=ws)
+    _sync()
+    check_attention(to_host(out2, dtype), want[sub], dtype, "workspace reuse, smaller batch")
+
+
+def test_split_merge_repeats_bit_for_bit():
+    """64 sequences of 600-4000 tokens at P = 256: nearly every (sequence, KV
+    head) is split into up to 16 partitions and merged by the second pass.
+    Ten launches must all match the oracle and agree bit for bit."""
+    import torch
+    rng = np.random.default_rng(77)
+    lens = rng.integers(600, 4000, size=64).tolist()
+    P = 256
+    case = wl.random_case(904, len(lens), 32, 8, 128, 16, "bf16", lens, partition_size=P)
+    dtype = "bf16"
+    t0 = np.ascontiguousarray(case.block_tables[0])
+    kd, vd = to_dev(case.k_cache, dtype), to_dev(case.v_cache, dtype)
+    qd = to_dev(case.q[0], dtype)
+    td, ld = ints_to_dev(t0), ints_to_dev(case.context_lens)
+    want = oracle.decode(np.ascontiguousarray(case.q[0]), case.k_cache, case.v_cache, t0,
+                         case.context_lens, case.scale, dtype, num_threads=16)
+    a = pa.make_decode_args(torch.empty_like(qd), qd, kd, vd, td, ld, case.scale, case.max_context, P)
+    ws = torch.empty(pa.pa_decode_workspace_bytes(a), dtype=torch.uint8, device=_g.DEVICE)
+    first = None
+    for rep in range(10):
+        announce(f"split merge repeat {rep}")
+        out = torch.empty_like(qd)
+        pa.pa_decode(out, qd, kd, vd, td, ld, case.scale, case.max_context, partition_size=P,
+                     workspace=ws)
+        _sync()
+        got = to_host(out, dtype)
+        if first is None:
+            first = got
+            check_attention(got, want, dtype, "split merge repeats")
+        assert same_bits(got, first), f"launch {rep} differs from launch 0"
+
+
 def test_large_logits_stay_finite():
     lens = [64, 300, 1000]
     case = wl.random_case(902, len(lens), 8, 2, 128, 16, "bf16", lens, partition_size=128)
