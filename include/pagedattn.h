@@ -2,17 +2,24 @@
  * pagedattn.h -- C ABI of libpagedattn: paged decode attention on MI355X
  * (gfx950) plus the host-side block manager that feeds it.
  *
+ * Sources (web pages on PagedAttention; cited below by site and section):
+ *   bmjup.com        "PagedAttention：大模型推理性能优化的核心技术解析"
+ *   wiblog.cn        "AI 推理系列（十六）：PagedAttention——为什么 vLLM 能把 GPU
+ *                    显存“像操作系统一样”管理？"
+ *   kongchang.com    "PagedAttention原理详解：GPU显存优化与模型路由技术"
+ *   intelliparadigm.com "vLLM的Paged Attention技术：高效注意力机制解析"
+ *
  * The method (PagedAttention): a sequence's KV cache lives in fixed-size
  * physical blocks of block_size tokens that sit anywhere in one device pool;
  * a per-sequence block table maps logical block i to its physical block id
- * (wiblog "PagedAttention" page, section on mapping a contiguous sequence
- * onto scattered blocks).  Decode attention reads the blocks in place through
- * the table, without first concatenating them (same page, section on why a
- * dedicated attention kernel is needed).  The attention formula itself is the
- * ordinary one (same page, opening section).
+ * (wiblog.cn, section "PagedAttention 如何把连续序列映射到离散显存块").
+ * Decode attention reads the blocks in place through the table, without
+ * first concatenating them (wiblog.cn, section "非连续 KV 为什么需要专门的
+ * Attention Kernel").  The attention formula itself is the ordinary one
+ * (wiblog.cn, opening section: paging is not a new attention formula).
  *
- * Pool layout (the one printed on the intelliparadigm "vLLM Paged Attention
- * technique" page, section 2.2), row-major, x = 16 bytes / element size:
+ * Pool layout (intelliparadigm.com, section "2.2 内存布局优化"), row-major,
+ * x = 16 bytes / element size:
  *     k_cache [num_blocks, num_kv_heads, head_dim / x, block_size, x]
  *     v_cache [num_blocks, num_kv_heads, head_dim,     block_size]
  * One (block, KV head) tile is one contiguous run of head_dim * block_size
@@ -77,7 +84,8 @@ PA_API const char* pa_status_string(pa_status s);
  * rounded once to the element type.
  *
  * Long contexts are split into partitions of `partition_size` tokens (the
- * PARTITION_SIZE split of the intelliparadigm page, sections 3.1-3.2); each
+ * PARTITION_SIZE split of intelliparadigm.com, sections "3.1 核函数签名解析"
+ * and "3.2 执行层次结构"); each
  * partition yields (running max, sum, unnormalised output) and a second pass
  * merges them with the log-sum-exp rule.  partition_size == 0 lets the
  * library choose; otherwise it must be a positive multiple of 32 tokens and
@@ -141,8 +149,9 @@ PA_API int32_t pa_decode_partition_size(const pa_decode_args* args);
 PA_API pa_status pa_decode(const pa_decode_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
- * pa_write_kv -- cache write of the step's new tokens (the "append KV" box
- * of the wiblog page's flowchart).  For each token t with slot =
+ * pa_write_kv -- cache write of the step's new tokens (the "追加 KV" (append
+ * KV) box of the flowchart in wiblog.cn, section "PagedAttention 如何把连续序列
+ * 映射到离散显存块").  For each token t with slot =
  * slot_mapping[t] >= 0: K and V rows of every KV head go to in-block
  * position slot % block_size of physical block slot / block_size, bit for
  * bit.  Negative slots are padding and are skipped; slots >= num_blocks *
@@ -156,10 +165,11 @@ PA_API pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache
                              int32_t num_blocks, int32_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
- * pa_copy_blocks -- copy-on-write block copies (bmjup explainer, section 2
- * "copy-on-write"; wiblog COW paragraph).  block_mapping is [num_pairs][2]
- * int32 = {src, dst}: every element of physical block dst (all KV heads,
- * K and V) becomes a bit copy of block src.  A dst must not appear twice nor
+ * pa_copy_blocks -- copy-on-write block copies (bmjup.com, section
+ * "PagedAttention 的核心工作机制与创新", item 2 "写入时拷贝（Copy-on-Write）";
+ * wiblog.cn, section "Copy-on-Write、并行采样与 Prefix Caching 不是同一件
+ * 事").  block_mapping is [num_pairs][2] int32 = {src, dst}: every element of
+ * physical block dst (all KV heads, K and V) becomes a bit copy of block src.  A dst must not appear twice nor
  * as any pair's src (the pairs pa_seq_append_slot reports satisfy this).
  * Pairs with an id outside [0, num_blocks) are skipped.
  * ------------------------------------------------------------------------ */
@@ -173,8 +183,9 @@ PA_API pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* blo
  * table into contiguous k_out, v_out [num_seqs, max_context_len,
  * num_kv_heads, head_dim] of dtype, bit for bit, in logical token order.
  * Rows t >= context_lens[s] are left untouched.  This is the "concatenate
- * the blocks, then run ordinary attention" route that the wiblog page warns
- * costs extra copies; it exists only to check addressing.
+ * the blocks, then run ordinary attention" route that wiblog.cn (section
+ * "非连续 KV 为什么需要专门的 Attention Kernel") warns costs extra copies; it
+ * exists only to check addressing.
  * ------------------------------------------------------------------------ */
 PA_API pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
                               const int32_t* block_tables, const int32_t* context_lens,
@@ -184,9 +195,11 @@ PA_API pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
                               void* stream);
 
 /* ------------------------------------------------------------------------
- * Host block manager (the allocator, free pool, refcounts and block tables
- * of the pages: bmjup section 3 "dynamic allocation", wiblog flowchart and
- * COW paragraphs, kongchang refcount paragraph).  Opaque, owned by the
+ * Host block manager (the allocator, free pool, refcounts and block tables:
+ * bmjup.com, section "PagedAttention 的核心工作机制与创新", item 3 "动态内存
+ * 分配"; the wiblog.cn flowchart and its copy-on-write section; kongchang.com,
+ * section "PagedAttention的三大核心优势", second advantage (shared prefix
+ * blocks with reference counts and copy-on-write)).  Opaque, owned by the
  * caller, not thread-safe.  Rules:
  *   - append: when len % block_size == 0 a new block is taken from the free
  *     pool; otherwise the token goes to the next slot of the last block.  If

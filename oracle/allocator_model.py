@@ -7,23 +7,26 @@ operation sequences; the two share no code.
 Behaviour, with the passage each rule follows:
   * A sequence's KV lives in fixed-size blocks of `block_size` tokens; a
     per-sequence block table lists its physical block ids in logical order
-    (wiblog "vLLM paged attention" page, section on mapping a contiguous
-    sequence onto scattered blocks).
-  * Appending one token (the page's flowchart): if the current last block is
-    full -- equivalently len % block_size == 0, which includes the empty
-    sequence -- a new physical block is taken from the free pool and
+    (wiblog.cn, "AI 推理系列（十六）：PagedAttention", section "PagedAttention
+    如何把连续序列映射到离散显存块").
+  * Appending one token (the same section's flowchart): if the current last
+    block is full -- equivalently len % block_size == 0, which includes the
+    empty sequence -- a new physical block is taken from the free pool and
     appended to the table; otherwise the token goes to the next slot of the
     last block.  The returned slot is block * block_size + len % block_size.
   * Blocks are taken on demand from a global free pool and returned to it as
     soon as a sequence finishes; the tables of running sequences are not
-    touched (bmjup explainer, "dynamic memory allocation"; wiblog section on
-    continuous batching).
+    touched (bmjup.com, "PagedAttention：大模型推理性能优化的核心技术解析",
+    section "PagedAttention 的核心工作机制与创新", item 3 "动态内存分配";
+    wiblog.cn, section "Continuous Batching 为什么依赖可快速回收的 KV Cache").
   * Sharing: a forked sequence references the same physical blocks and each
-    block keeps a reference count (kongchang page, second advantage: parallel
+    block keeps a reference count (kongchang.com, "PagedAttention原理详解",
+    section "PagedAttention的三大核心优势", second advantage: parallel
     sampling and beam search share prefix blocks with reference counts and
     copy-on-write).  A block is copied only when a sequence must write into a
-    block that another sequence also references (bmjup section 2; wiblog COW
-    paragraph).
+    block that another sequence also references (bmjup.com, same section,
+    item 2 "写入时拷贝（Copy-on-Write）"; wiblog.cn, section "Copy-on-Write、
+    并行采样与 Prefix Caching 不是同一件事").
 Readings where the pages are silent:
   * Copy-on-write is decided at append time: the writer whose last block is
     partly filled and has refcount > 1 takes a fresh block, the old block's

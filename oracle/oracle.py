@@ -7,8 +7,8 @@ Array conventions (numpy, C-contiguous):
   * element types: "f32" -> float32, "f16" -> float16, "bf16" -> uint16
     holding the bfloat16 bit patterns (numpy has no bfloat16);
   * k_cache [NB, Hkv, D/x, BS, x] and v_cache [NB, Hkv, D, BS], x = 16 bytes /
-    element size: the block layout printed on the "vLLM Paged Attention
-    technique" page, section 2.2;
+    element size: the block layout printed by intelliparadigm.com,
+    "vLLM的Paged Attention技术", section "2.2 内存布局优化";
   * q [S, Hq, D]; block_tables [S, max_blocks] int32; context_lens [S] int32;
     slot_mapping [T] int64; copy pairs [P, 2] int32 = (src, dst).
 """

@@ -10,22 +10,26 @@
  *
  *   - The paged KV cache: fixed-size physical blocks of BS tokens, reached
  *     through a per-sequence block table that maps logical block i to a
- *     physical block id ("vLLM paged attention / continuous batching" page,
- *     section on mapping a contiguous sequence onto scattered blocks, with its
- *     worked example logical 0,1,2 -> physical 17,4,29).
- *   - The physical layout of one block is the one printed on the
- *     "vLLM Paged Attention technique" page, section 2.2 (memory layout):
+ *     physical block id (wiblog.cn, "AI 推理系列（十六）：PagedAttention",
+ *     section "PagedAttention 如何把连续序列映射到离散显存块", with its worked
+ *     example logical 0,1,2 -> physical 17,4,29).
+ *   - The physical layout of one block is the one printed by
+ *     intelliparadigm.com, "vLLM的Paged Attention技术", section "2.2 内存布局
+ *     优化":
  *         k_cache [num_blocks, kv_heads, head_dim/x, block_size, x]
  *         v_cache [num_blocks, kv_heads, head_dim,   block_size]
- *     with x = 16 bytes / element size (the 16-byte vector of section 4.1).
+ *     with x = 16 bytes / element size (the 16-byte vector of its section
+ *     "4.1 向量化内存访问").
  *   - Decode attention: PagedAttention changes where K/V live, not the
- *     attention formula ("vLLM paged attention" page, opening section and the
- *     section on why a dedicated kernel is needed).  So the oracle is the
- *     textbook single-query softmax attention over the sequence's tokens in
- *     logical order, gathered through the block table, in fp64.
- *   - Cache write ("append KV" box of the same page's flowchart) and block
- *     copy (copy-on-write, "PagedAttention core mechanism" section 2 of the
- *     bmjup explainer; COW paragraph of the wiblog page) are plain copies.
+ *     attention formula (wiblog.cn, opening section, and section "非连续 KV
+ *     为什么需要专门的 Attention Kernel").  So the oracle is the textbook
+ *     single-query softmax attention over the sequence's tokens in logical
+ *     order, gathered through the block table, in fp64.
+ *   - Cache write (the "追加 KV" (append KV) box of the wiblog.cn flowchart)
+ *     and block copy (copy-on-write: bmjup.com, "PagedAttention：大模型推理
+ *     性能优化的核心技术解析", section "PagedAttention 的核心工作机制与创新",
+ *     item 2; wiblog.cn, section "Copy-on-Write、并行采样与 Prefix Caching 不是
+ *     同一件事") are plain copies.
  *
  * Readings of the pages that this file encodes (the pages are silent):
  *   - GQA: query head h reads KV head floor(h / G), G = Hq / Hkv.

@@ -1,12 +1,16 @@
 // Host-side block manager of libpagedattn (plain C++17, no device code).
 //
 // Free pool, per-block reference counts, per-sequence block tables, fork and
-// copy-on-write, following the pages: blocks are taken on demand and given
-// back as soon as a sequence ends (bmjup explainer, section 3 "dynamic
-// allocation"); one append walks the wiblog page's flowchart (a new physical
-// block exactly when the last one is full); forked sequences share blocks
-// with reference counts and copy a block only when they must write into a
-// shared one (kongchang page, second advantage; wiblog COW paragraph).
+// copy-on-write.  Blocks are taken on demand and given back as soon as a
+// sequence ends (bmjup.com, "PagedAttention：大模型推理性能优化的核心技术解析",
+// section "PagedAttention 的核心工作机制与创新", item 3 "动态内存分配"); one
+// append walks the flowchart of wiblog.cn, "AI 推理系列（十六）：PagedAttention",
+// section "PagedAttention 如何把连续序列映射到离散显存块" (a new physical block
+// exactly when the last one is full); forked sequences share blocks with
+// reference counts and copy a block only when they must write into a shared
+// one (kongchang.com, "PagedAttention原理详解", section "PagedAttention的三大
+// 核心优势", second advantage; wiblog.cn, section "Copy-on-Write、并行采样与
+// Prefix Caching 不是同一件事").
 // The exact rules are stated with the declarations in pagedattn.h.
 #include <new>
 #include <unordered_map>

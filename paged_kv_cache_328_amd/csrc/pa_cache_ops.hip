@@ -2,7 +2,8 @@
 // copy-on-write block copies and the gather test hook.  All three are plain
 // bit copies moved in 16-byte vectors; none does arithmetic on the values.
 //
-// Pool layout (intelliparadigm page, section 2.2), x = 16 B / element size:
+// Pool layout (intelliparadigm.com, "vLLM的Paged Attention技术", section
+// "2.2 内存布局优化"), x = 16 B / element size:
 //   k_cache [NB, Hkv, D/x, BS, x]   -> a token's x-element chunk cc of head h in
 //                                      block b starts at ((b*Hkv+h)*(D/x)+cc)*BS*x + o*x
 //   v_cache [NB, Hkv, D, BS]         -> element d of that token at ((b*Hkv+h)*D+d)*BS + o

@@ -3,15 +3,18 @@
 //
 // What is computed: for sequence s and query head h, the softmax attention of
 // q[s,h] over the sequence's cached keys/values, which sit in fixed-size
-// physical blocks reached through the block table (wiblog "PagedAttention"
-// page, sections on the block mapping and on the dedicated kernel; the
-// attention formula itself is the ordinary one).  Long contexts are split
-// into partitions (the PARTITION_SIZE split of the intelliparadigm page,
-// sections 3.1-3.2); each partition writes (max, sum, unnormalised output)
-// and pass 2 merges them exactly: M = max_p m_p, out = sum_p 2^(m_p-M) acc_p /
-// sum_p 2^(m_p-M) l_p (logits are kept in base 2: x * scale * log2(e)).
+// physical blocks reached through the block table (wiblog.cn, "AI 推理系列
+// （十六）：PagedAttention", sections "PagedAttention 如何把连续序列映射到离散显存块"
+// and "非连续 KV 为什么需要专门的 Attention Kernel"; the attention formula itself
+// is the ordinary one).  Long contexts are split into partitions (the
+// PARTITION_SIZE split of intelliparadigm.com, "vLLM的Paged Attention技术",
+// sections 3.1 and 3.2); each partition writes (max, sum, unnormalised
+// output) and pass 2 merges them exactly: M = max_p m_p, out = sum_p
+// 2^(m_p-M) acc_p / sum_p 2^(m_p-M) l_p (logits are kept in base 2:
+// x * scale * log2(e)).
 //
-// Pool layout (intelliparadigm page, section 2.2), 16-bit types, x = 8:
+// Pool layout (intelliparadigm.com, section "2.2 内存布局优化"), 16-bit types,
+// x = 8:
 //   K [NB, Hkv, D/8, BS, 8]: for a fixed 8-channel chunk, the BS tokens of a
 //     block are consecutive 16-byte vectors;
 //   V [NB, Hkv, D, BS]:      for a fixed channel, the BS tokens are consecutive.
@@ -37,8 +40,8 @@
 // 16 query heads sharing that KV head, partition, sequence).  The group's
 // query heads are the N = 16 dimension of both products, so K/V bytes are read
 // once per KV head whatever the group size G is.  The partition is cut into
-// chunks of 32 tokens dealt round-robin to the waves (the intelliparadigm
-// page's warp-to-block assignment, section 4.2); each wave keeps its own
+// chunks of 32 tokens dealt round-robin to the waves (the warp-to-block
+// assignment of intelliparadigm.com, section "4.2 动态负载均衡"); each wave keeps its own
 // running (max, sum, output) and the waves are merged through LDS at the end.
 #include <math.h>
 

@@ -68,7 +68,8 @@ def pool_shapes(NB, Hkv, D, BS, dtype):
 
 def kv_cache_bytes(layers, tokens, kv_heads, head_dim, elem_bytes):
     """KV cache size of `tokens` tokens: 2 (K and V) x layers x tokens x
-    kv_heads x head_dim x element size (kongchang page, KV cache formula)."""
+    kv_heads x head_dim x element size (kongchang.com, "PagedAttention原理详解",
+    section "显存消耗的三大来源")."""
     return 2 * layers * tokens * kv_heads * head_dim * elem_bytes
 
 

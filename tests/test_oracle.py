@@ -366,8 +366,9 @@ def test_rejects_bad_dimensions():
 
 def test_kv_size_formula_agrees_across_the_pages():
     """Two pages give the KV size two ways: per token 2 x layers x hidden x
-    element size (bmjup explainer) and 2 x L x n x heads x d_head x element size
-    (kongchang page).  With hidden = heads x d_head they agree."""
+    element size (bmjup.com, section "为什么传统注意力机制需要优化？") and
+    2 x L x n x heads x d_head x element size (kongchang.com, section
+    "显存消耗的三大来源").  With hidden = heads x d_head they agree."""
     layers, heads, dh, elem = 40, 40, 128, 2  # LLaMA-13B shape, fp16
     per_token = 2 * layers * (heads * dh) * elem
     assert per_token == 819_200
