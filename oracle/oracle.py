@@ -52,6 +52,22 @@ def lib():
         L.oracle_write_kv.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I]
         L.oracle_copy_blocks.restype = _I
         L.oracle_copy_blocks.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I]
+        for name in ("oracle_i8_k_offset", "oracle_i8_v_offset"):
+            getattr(L, name).restype = _I64
+            getattr(L, name).argtypes = [_I64, _I, _I, _I, _I, _I, _I]
+        L.oracle_i8_scale_offset.restype = _I64
+        L.oracle_i8_scale_offset.argtypes = [_I64, _I, _I, _I, _I, _I]
+        L.oracle_i8_tile_bytes.restype = _I64
+        L.oracle_i8_tile_bytes.argtypes = [_I, _I]
+        L.oracle_quantize_row.restype = None
+        L.oracle_quantize_row.argtypes = [_P, _I, _P, _P]
+        L.oracle_write_kv_i8.restype = _I
+        L.oracle_write_kv_i8.argtypes = [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I]
+        L.oracle_copy_blocks_i8.restype = _I
+        L.oracle_copy_blocks_i8.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I]
+        L.oracle_decode_i8.restype = _I
+        L.oracle_decode_i8.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                       ctypes.c_float, _I, _P]
         _lib = L
     return _lib
 
@@ -164,3 +180,80 @@ def copy_blocks(k_cache, v_cache, pairs, dtype):
                                   Hkv, D, BS, NB, DTYPE_CODE[dtype])
     if rc != 0:
         raise ValueError("oracle_copy_blocks rejected its arguments")
+
+
+# ---------------------------------------------------------------------------- INT8 KV cache
+# Pools are uint8 arrays [NB, Hkv, tile_bytes] with tile_bytes = D*BS + 4*BS:
+# codes ([D/16][BS][16] for K, [D][BS] for V) followed by BS fp32 scales (see
+# the INT8 section of pa_oracle.c for the readings).
+
+def i8_tile_bytes(D, BS):
+    return int(lib().oracle_i8_tile_bytes(D, BS))
+
+
+def i8_geometry(k_pool, v_pool, D, BS):
+    """(NB, Hkv) of two INT8 pools; checks their shapes."""
+    if k_pool.ndim != 3 or k_pool.shape != v_pool.shape or k_pool.shape[2] != i8_tile_bytes(D, BS):
+        raise ValueError("INT8 pools must both be [NB, Hkv, D*BS + 4*BS] uint8")
+    _check(k_pool, np.uint8, "k_pool")
+    _check(v_pool, np.uint8, "v_pool")
+    return k_pool.shape[0], k_pool.shape[1]
+
+
+def i8_offsets(b, h, o, d, Hkv, D, BS):
+    """Byte offsets (K code, V code, scale) of element (b, h, o, d)."""
+    L = lib()
+    return (L.oracle_i8_k_offset(b, h, o, d, Hkv, D, BS), L.oracle_i8_v_offset(b, h, o, d, Hkv, D, BS),
+            L.oracle_i8_scale_offset(b, h, o, Hkv, D, BS))
+
+
+def quantize_row(x):
+    """fp32 row -> (int8 codes, fp32 scale)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.empty(x.shape[0], np.int8)
+    sc = np.empty(1, np.float32)
+    lib().oracle_quantize_row(_ptr(x), x.shape[0], _ptr(codes), _ptr(sc))
+    return codes, sc[0]
+
+
+def write_kv_i8(k_new, v_new, src_dtype, k_pool, v_pool, slot_mapping, D, BS):
+    """Quantising cache write of k_new / v_new [T, Hkv, D] (src_dtype storage)."""
+    NB, Hkv = i8_geometry(k_pool, v_pool, D, BS)
+    _check(k_new, NP_STORAGE[src_dtype], "k_new")
+    _check(v_new, NP_STORAGE[src_dtype], "v_new")
+    _check(slot_mapping, np.int64, "slot_mapping")
+    T = slot_mapping.shape[0]
+    if k_new.shape != (T, Hkv, D) or v_new.shape != (T, Hkv, D):
+        raise ValueError("k_new / v_new must be [T, Hkv, D]")
+    rc = lib().oracle_write_kv_i8(_ptr(k_new), _ptr(v_new), DTYPE_CODE[src_dtype], _ptr(k_pool),
+                                  _ptr(v_pool), _ptr(slot_mapping), T, Hkv, D, BS, NB)
+    if rc != 0:
+        raise ValueError("oracle_write_kv_i8 rejected its arguments")
+
+
+def copy_blocks_i8(k_pool, v_pool, pairs, D, BS):
+    NB, Hkv = i8_geometry(k_pool, v_pool, D, BS)
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    rc = lib().oracle_copy_blocks_i8(_ptr(k_pool), _ptr(v_pool), _ptr(pairs), pairs.shape[0], Hkv, D,
+                                     BS, NB)
+    if rc != 0:
+        raise ValueError("oracle_copy_blocks_i8 rejected its arguments")
+
+
+def decode_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, scale, D, BS, num_threads=1):
+    """Paged decode attention over INT8 pools, fp64 output [S, Hq, D]."""
+    NB, Hkv = i8_geometry(k_pool, v_pool, D, BS)
+    _check(q, NP_STORAGE[q_dtype], "q")
+    _check(block_tables, np.int32, "block_tables")
+    _check(context_lens, np.int32, "context_lens")
+    S, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError("q head_dim does not match")
+    out = np.empty((S, Hq, D), np.float64)
+    rc = lib().oracle_decode_i8(_ptr(q), DTYPE_CODE[q_dtype], _ptr(k_pool), _ptr(v_pool),
+                                _ptr(block_tables), _ptr(context_lens), S, Hq, Hkv, D, BS,
+                                block_tables.shape[1], ctypes.c_float(scale), int(num_threads),
+                                _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_decode_i8 rejected its arguments")
+    return out

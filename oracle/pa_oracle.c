@@ -276,3 +276,192 @@ int oracle_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int n
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * INT8 KV cache.
+ *
+ * KV-cache quantisation stores fewer bits per cached element, at the price
+ * of a quantisation error and a conversion (wiblog.cn, section "非连续 KV 为什么
+ * 需要专门的 Attention Kernel", mechanism table, row "KV Cache
+ * Quantization"); INT8 halves the KV memory and is orthogonal to paging:
+ * quantisation shrinks what each block holds, paging decides where blocks
+ * live (kongchang.com, section "量化技术：与PagedAttention正交的显存优化路径").
+ *
+ * Readings (the pages fix neither the scale granularity nor the layout):
+ *   - symmetric INT8 with one fp32 scale per (token, KV head), for K and V;
+ *   - a block keeps its scales in its own tile, after the codes, so block
+ *     copies and gathers stay whole-tile operations.  Per (block, KV head):
+ *       K tile: codes [D/16][BS][16] int8 (the printed K layout with
+ *               x = 16 bytes / 1 byte), then BS fp32 scales;
+ *       V tile: codes [D][BS] int8, then BS fp32 scales;
+ *     tile bytes = D*BS + 4*BS.  Pools are [NB][Hkv][tile bytes].
+ *   - quantising a row x[0..D) (the new token's K or V of one head, widened
+ *     exactly to fp32) takes its decisions in fp32: amax = max_d |x_d|,
+ *     s = amax / 127, code_d = rint(x_d / s) clamped to [-127, 127]; a zero
+ *     row gets s = 0 and zero codes.
+ *   - the value of a cached element is code * s, widened exactly to fp64.
+ * ------------------------------------------------------------------------ */
+
+int64_t oracle_i8_tile_bytes(int D, int BS) { return (int64_t)D * BS + 4 * (int64_t)BS; }
+
+/* Byte offsets in a K / V pool of code (b, h, o, d) and of scale (b, h, o). */
+int64_t oracle_i8_k_offset(int64_t b, int h, int o, int d, int Hkv, int D, int BS) {
+  return (b * Hkv + h) * oracle_i8_tile_bytes(D, BS) + ((int64_t)(d / 16) * BS + o) * 16 + d % 16;
+}
+int64_t oracle_i8_v_offset(int64_t b, int h, int o, int d, int Hkv, int D, int BS) {
+  return (b * Hkv + h) * oracle_i8_tile_bytes(D, BS) + (int64_t)d * BS + o;
+}
+int64_t oracle_i8_scale_offset(int64_t b, int h, int o, int Hkv, int D, int BS) {
+  return (b * Hkv + h) * oracle_i8_tile_bytes(D, BS) + (int64_t)D * BS + 4 * (int64_t)o;
+}
+
+static float load_f32(const void* base, int64_t idx, int dtype) {
+  return (float)load_elem(base, idx, dtype); /* exact: every source type fits in fp32 */
+}
+
+/* Quantises x[0..D) (fp32) into codes[0..D) and *scale, in fp32 as stated above. */
+void oracle_quantize_row(const float* x, int D, int8_t* codes, float* scale) {
+  float amax = 0.0f;
+  for (int d = 0; d < D; ++d) {
+    float a = fabsf(x[d]);
+    if (a > amax) amax = a;
+  }
+  float s = amax / 127.0f;
+  *scale = s;
+  for (int d = 0; d < D; ++d) {
+    if (s == 0.0f) {
+      codes[d] = 0;
+      continue;
+    }
+    float r = rintf(x[d] / s);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    codes[d] = (int8_t)r;
+  }
+}
+
+/* Quantising cache write: token t's K and V rows of every KV head (k_new,
+ * v_new [T, Hkv, D] of src_dtype) go to slot slot_mapping[t] as codes plus
+ * scale; negative slots are skipped; a slot past the pool is an error. */
+int oracle_write_kv_i8(const void* k_new, const void* v_new, int src_dtype, uint8_t* k_pool,
+                       uint8_t* v_pool, const int64_t* slot_mapping, int T, int Hkv, int D,
+                       int BS, int num_blocks) {
+  if (src_dtype < OR_F32 || src_dtype > OR_BF16 || T < 0 || Hkv <= 0 || D <= 0 || D % 16 ||
+      BS <= 0)
+    return -1;
+  for (int t = 0; t < T; ++t)
+    if (slot_mapping[t] >= (int64_t)num_blocks * BS) return -1;
+  float* row = (float*)malloc(sizeof(float) * (size_t)D);
+  int8_t* codes = (int8_t*)malloc((size_t)D);
+  if (!row || !codes) {
+    free(row);
+    free(codes);
+    return -1;
+  }
+  for (int t = 0; t < T; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    int64_t b = slot / BS;
+    int o = (int)(slot % BS);
+    for (int h = 0; h < Hkv; ++h) {
+      for (int kv = 0; kv < 2; ++kv) {
+        const void* src = kv == 0 ? k_new : v_new;
+        uint8_t* pool = kv == 0 ? k_pool : v_pool;
+        for (int d = 0; d < D; ++d) row[d] = load_f32(src, ((int64_t)t * Hkv + h) * D + d, src_dtype);
+        float s;
+        oracle_quantize_row(row, D, codes, &s);
+        for (int d = 0; d < D; ++d) {
+          int64_t off = kv == 0 ? oracle_i8_k_offset(b, h, o, d, Hkv, D, BS)
+                                : oracle_i8_v_offset(b, h, o, d, Hkv, D, BS);
+          pool[off] = (uint8_t)codes[d];
+        }
+        memcpy(pool + oracle_i8_scale_offset(b, h, o, Hkv, D, BS), &s, sizeof s);
+      }
+    }
+  }
+  free(row);
+  free(codes);
+  return 0;
+}
+
+/* Block copy of INT8 pools: whole tiles (codes and scales) of every KV head. */
+int oracle_copy_blocks_i8(uint8_t* k_pool, uint8_t* v_pool, const int32_t* pairs, int num_pairs,
+                          int Hkv, int D, int BS, int num_blocks) {
+  if (num_pairs < 0 || Hkv <= 0 || D <= 0 || D % 16 || BS <= 0) return -1;
+  for (int p = 0; p < num_pairs; ++p)
+    if (pairs[2 * p] < 0 || pairs[2 * p] >= num_blocks || pairs[2 * p + 1] < 0 ||
+        pairs[2 * p + 1] >= num_blocks)
+      return -1;
+  const int64_t slab = (int64_t)Hkv * oracle_i8_tile_bytes(D, BS);
+  for (int p = 0; p < num_pairs; ++p) {
+    int64_t src = pairs[2 * p], dst = pairs[2 * p + 1];
+    memmove(k_pool + dst * slab, k_pool + src * slab, (size_t)slab);
+    memmove(v_pool + dst * slab, v_pool + src * slab, (size_t)slab);
+  }
+  return 0;
+}
+
+static double i8_value(const uint8_t* pool, int64_t code_off, int64_t scale_off) {
+  float s;
+  memcpy(&s, pool + scale_off, sizeof s);
+  return (double)(int8_t)pool[code_off] * (double)s;
+}
+
+/* Decode attention over INT8 pools: the same textbook single-query softmax
+ * attention as oracle_decode, on the exact values code * scale (fp64).
+ * q is [S, Hq, D] of q_dtype; out is [S, Hq, D] fp64. */
+int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
+                     const int32_t* block_tables, const int32_t* context_lens, int S, int Hq,
+                     int Hkv, int D, int BS, int max_blocks, float scale, int num_threads,
+                     double* out) {
+  if (q_dtype < OR_F32 || q_dtype > OR_BF16 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
+      D <= 0 || D % 16 || BS <= 0)
+    return -1;
+  for (int s = 0; s < S; ++s)
+    if (context_lens[s] > max_blocks * BS) return -1;
+  const int G = Hq / Hkv;
+  const double sc = (double)scale;
+  const int64_t pairs = (int64_t)S * Hq;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads > 0 ? num_threads : 1)
+  for (int64_t sh = 0; sh < pairs; ++sh) {
+    const int s = (int)(sh / Hq), h = (int)(sh % Hq);
+    const int g = h / G;
+    const int c = context_lens[s];
+    double* o = out + sh * D;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (c <= 0) continue;
+    double* x = (double*)malloc(sizeof(double) * (size_t)c);
+    if (!x) {
+#pragma omp atomic write
+      bad = 1;
+      continue;
+    }
+    for (int t = 0; t < c; ++t) {
+      int64_t b = block_of(block_tables, max_blocks, s, t, BS);
+      int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d)
+        dot += load_elem(q, sh * D + d, q_dtype) *
+               i8_value(k_pool, oracle_i8_k_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+      x[t] = sc * dot;
+    }
+    double m = x[0];
+    for (int t = 1; t < c; ++t)
+      if (x[t] > m) m = x[t];
+    double z = 0.0;
+    for (int t = 0; t < c; ++t) {
+      x[t] = exp(x[t] - m);
+      z += x[t];
+    }
+    for (int t = 0; t < c; ++t) {
+      int64_t b = block_of(block_tables, max_blocks, s, t, BS);
+      int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
+      for (int d = 0; d < D; ++d)
+        o[d] += x[t] * i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+    }
+    for (int d = 0; d < D; ++d) o[d] /= z;
+    free(x);
+  }
+  return bad ? -1 : 0;
+}

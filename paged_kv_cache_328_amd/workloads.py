@@ -95,6 +95,7 @@ class DecodeCase:
     slot_mapping: np.ndarray = None   # [R, S] int64: slot of each new token
     referenced: np.ndarray = None     # [NB] bool: block referenced by some table
     trap_block: int = 0               # unreferenced block used to pad table rows
+    kv_dtype: str = None              # cache type: same as dtype, or "i8" (INT8 pools)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -110,8 +111,12 @@ class DecodeCase:
         return int(self.context_lens.max()) if self.S else 0
 
     def kv_bytes(self):
-        """K + V bytes over every context (one replica)."""
-        return 2 * int(self.context_lens.astype(np.int64).sum()) * self.Hkv * self.D * ELEM_BYTES[self.dtype]
+        """K + V bytes over every context (one replica); for INT8 pools the
+        codes plus each token's two fp32 scales."""
+        tokens = int(self.context_lens.astype(np.int64).sum()) * self.Hkv
+        if self.kv_dtype == "i8":
+            return 2 * tokens * (self.D + 4)
+        return 2 * tokens * self.D * ELEM_BYTES[self.dtype]
 
 
 def _blocks_needed(lens, BS):
@@ -138,8 +143,35 @@ def _fill_pool(rng_k, rng_v, NB, Hkv, D, BS, dtype, referenced, chunk_blocks=204
     return k, v
 
 
+def i8_tile_bytes(D, BS):
+    """Bytes of one (block, KV head) tile of an INT8 pool: D*BS codes, then
+    BS fp32 scales."""
+    return D * BS + 4 * BS
+
+
+def _fill_pool_i8(rng_k, rng_v, NB, Hkv, D, BS, referenced, chunk_blocks=2048):
+    """INT8 pools [NB, Hkv, tile] (uint8).  Referenced blocks get random codes
+    (a rounded normal of spread 40, clipped to [-127, 127]) and random scales
+    uniform in [0.01, 0.04]; other blocks get code 0x7F and NaN scales.  Only
+    random numbers are drawn here: no quantisation is performed."""
+    tile = i8_tile_bytes(D, BS)
+    out = []
+    for rng in (rng_k, rng_v):
+        pool = np.full((NB, Hkv, tile), 0x7F, np.uint8)
+        pool[:, :, D * BS:] = np.frombuffer(np.full(BS, np.nan, np.float32).tobytes(), np.uint8)
+        ids = np.flatnonzero(referenced)
+        for i in range(0, ids.size, chunk_blocks):
+            sel = ids[i:i + chunk_blocks]
+            codes = np.clip(np.rint(40.0 * rng.standard_normal((sel.size, Hkv, D * BS))), -127, 127)
+            scales = rng.uniform(0.01, 0.04, size=(sel.size, Hkv, BS)).astype(np.float32)
+            pool[sel, :, :D * BS] = codes.astype(np.int8).view(np.uint8)
+            pool[sel, :, D * BS:] = scales.view(np.uint8).reshape(sel.size, Hkv, 4 * BS)
+        out.append(pool)
+    return out[0], out[1]
+
+
 def _finish(name, dtype, S, Hq, Hkv, D, BS, NB, partition_size, lens, table_lists, rngs, fill,
-            with_new_token):
+            with_new_token, kv_dtype=None):
     """Common tail: tables, q, pools, new tokens."""
     R = len(table_lists)
     max_blocks = max(1, max(_blocks_needed(lens, BS)))
@@ -155,7 +187,10 @@ def _finish(name, dtype, S, Hq, Hkv, D, BS, NB, partition_size, lens, table_list
                       scale=float(np.float32(1.0 / math.sqrt(D))), partition_size=partition_size,
                       context_lens=np.asarray(lens, np.int32), block_tables=tables, q=q,
                       referenced=referenced, trap_block=trap)
-    if fill:
+    case.kv_dtype = kv_dtype or dtype
+    if fill and case.kv_dtype == "i8":
+        case.k_cache, case.v_cache = _fill_pool_i8(rngs["k"], rngs["v"], NB, Hkv, D, BS, referenced)
+    elif fill:
         case.k_cache, case.v_cache = _fill_pool(rngs["k"], rngs["v"], NB, Hkv, D, BS, dtype, referenced)
     if with_new_token:
         case.new_k = round_to_storage(rngs["new"].standard_normal((R, S, Hkv, D), dtype=np.float32), dtype)
@@ -197,17 +232,18 @@ def tiny_f32(seed=None, replicas=1, fill=True):
     return _finish(name, "f32", 4, 2, 2, 64, BS, NB, 0, lens, tables, rngs, fill, True)
 
 
-def llama13b_f16(seed=None, replicas=1, fill=True, num_blocks=20000):
+def llama13b_f16(seed=None, replicas=1, fill=True, num_blocks=20000, kv_dtype=None):
     name = "llama13b_f16"
     rngs = _rngs(base_seed(name) if seed is None else seed)
     lens = rngs["lens"].integers(1024, 1280, size=16, endpoint=True).tolist()
     BS = 16
     perm = rngs["perm"].permutation(num_blocks)
     tables = _permutation_tables(lens, BS, perm, replicas)
-    return _finish(name, "f16", 16, 40, 40, 128, BS, num_blocks, 0, lens, tables, rngs, fill, True)
+    return _finish(name, "f16", 16, 40, 40, 128, BS, num_blocks, 0, lens, tables, rngs, fill, True,
+                   kv_dtype)
 
 
-def long_bf16(seed=None, replicas=1, fill=True):
+def long_bf16(seed=None, replicas=1, fill=True, kv_dtype=None):
     name = "long_bf16"
     rngs = _rngs(base_seed(name) if seed is None else seed)
     lens = [16384, 32768, 65536, 131072]
@@ -215,14 +251,14 @@ def long_bf16(seed=None, replicas=1, fill=True):
     NB = 16384 * replicas
     perm = rngs["perm"].permutation(NB)
     tables = _permutation_tables(lens, BS, perm, replicas)
-    return _finish(name, "bf16", 4, 64, 8, 128, BS, NB, 512, lens, tables, rngs, fill, True)
+    return _finish(name, "bf16", 4, 64, 8, 128, BS, NB, 512, lens, tables, rngs, fill, True, kv_dtype)
 
 
 def _log_uniform_lens(rng, n, lo, hi):
     return np.clip(np.rint(np.exp(rng.uniform(math.log(lo), math.log(hi), size=n))), lo, hi).astype(int).tolist()
 
 
-def mixed_gqa_bf16(seed=None, replicas=1, fill=True):
+def mixed_gqa_bf16(seed=None, replicas=1, fill=True, kv_dtype=None):
     """Fragmented pool: the free pool starts as a seeded permutation used as a
     stack; dummy sequences take blocks until 60% of the pool is in use, a
     seeded half of them is released, then the real sequences take their
@@ -257,7 +293,8 @@ def mixed_gqa_bf16(seed=None, replicas=1, fill=True):
                     lists[s].append(stack.pop())
                     remaining[s] -= 1
         table_lists.append(lists)
-    return _finish(name, "bf16", S, 32, 8, 128, BS, NB, 0, lens, table_lists, rngs, fill, True)
+    return _finish(name, "bf16", S, 32, 8, 128, BS, NB, 0, lens, table_lists, rngs, fill, True,
+                   kv_dtype)
 
 
 def cow_plan(seed=None):
@@ -281,14 +318,16 @@ def cow_plan(seed=None):
                 init_free_order=init_free_order, k_cache=k, v_cache=v, q=q, new_k=new_k, new_v=new_v)
 
 
-def random_case(seed, S, Hq, Hkv, D, BS, dtype, lens, NB=None, partition_size=0, fill=True):
+def random_case(seed, S, Hq, Hkv, D, BS, dtype, lens, NB=None, partition_size=0, fill=True,
+                kv_dtype=None):
     """A free-form case (edge cases and sweeps): seeded permutation pool."""
     rngs = _rngs(seed)
     need = sum(_blocks_needed(lens, BS))
     NB = NB if NB is not None else max(need + 2, 4)
     perm = rngs["perm"].permutation(NB)
     tables = _permutation_tables(lens, BS, perm, 1)
-    return _finish("random", dtype, S, Hq, Hkv, D, BS, NB, partition_size, lens, tables, rngs, fill, True)
+    return _finish("random", dtype, S, Hq, Hkv, D, BS, NB, partition_size, lens, tables, rngs, fill, True,
+                   kv_dtype)
 
 
 BUILDERS = {
