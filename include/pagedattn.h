@@ -63,7 +63,17 @@ typedef enum pa_status {
   PA_ERR_EXISTS = 7        /* block manager: sequence id already present */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* Element types.  PA_I8 is a cache type only: INT8 KV-cache quantisation
+ * (kongchang.com, section "量化技术：与PagedAttention正交的显存优化路径": INT8
+ * halves the KV memory, orthogonal to paging).  An INT8 pool is
+ * [num_blocks, num_kv_heads, tile] bytes; each (block, KV head) tile holds
+ * head_dim * block_size codes (K: [head_dim/16][block_size][16], the printed K
+ * layout with x = 16; V: [head_dim][block_size]) followed by block_size fp32
+ * scales, one per token: tile = head_dim * block_size + 4 * block_size bytes.
+ * A cached value is code * scale.  Codes are made symmetric per (token, KV
+ * head) in fp32: scale = max|x| / 127, code = rint(x / scale) clamped to
+ * [-127, 127] (a zero row has scale 0). */
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_I8 = 3 } pa_dtype;
 
 /* Static, never-NULL text for a status code. */
 PA_API const char* pa_status_string(pa_status s);
@@ -97,7 +107,11 @@ PA_API const char* pa_status_string(pa_status s);
  * block_size.  Entries of a table row past ceil(c / block_size) are never
  * read.  All pointers 16-byte aligned.
  * Supported: dtype f16 / bf16 / f32, head_dim 64 or 128, block_size 16 or
- * 32, any G = num_q_heads / num_kv_heads >= 1.
+ * 32, any G = num_q_heads / num_kv_heads >= 1.  The caches hold dtype, or
+ * (kv_dtype PA_I8, f16 / bf16 only) INT8 codes whose values code * scale
+ * stand for K_t and V_t: each code is widened exactly to dtype for the
+ * matrix cores, K's scale multiplies the token's logit and V's scale the
+ * token's softmax weight before that weight is rounded to dtype.
  * The workspace (caller-allocated device memory, any contents) holds the
  * split-K partials; its size comes from pa_decode_workspace_bytes (0 when no
  * context spans more than one partition).  Two calls in flight at once must
@@ -119,7 +133,7 @@ typedef struct pa_decode_args {
   int32_t max_blocks_per_seq;
   int32_t max_context_len;  /* host-known upper bound of context_lens */
   float scale;              /* usually 1 / sqrt(head_dim) */
-  int32_t dtype;            /* pa_dtype of q, out, k_cache and v_cache */
+  int32_t dtype;            /* pa_dtype of q and out (PA_F32, PA_F16, PA_BF16) */
   int32_t partition_size;   /* 0 = library choice */
   void* workspace;
   size_t workspace_bytes;
@@ -136,6 +150,10 @@ typedef struct pa_decode_args {
    * sequence (copy-on-write it first with pa_copy_blocks). */
   const void* k_new;
   const void* v_new;
+  /* pa_dtype of k_cache / v_cache: equal to dtype, or PA_I8 (INT8 pools, see
+   * pa_dtype) with f16 / bf16 queries.  With PA_I8 a fused append quantises
+   * the new token as pa_write_kv_i8 does; k_new / v_new stay of dtype. */
+  int32_t kv_dtype;
 } pa_decode_args;
 
 /* Bytes of workspace pa_decode needs for these sizes (pointers are not read).
@@ -165,13 +183,34 @@ PA_API pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache
                              int32_t num_blocks, int32_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * pa_write_kv_i8 -- quantising cache write into INT8 pools (the append-KV
+ * step above combined with KV-cache quantisation: wiblog.cn, section "非连续
+ * KV 为什么需要专门的 Attention Kernel", mechanism table, row "KV Cache
+ * Quantization"; kongchang.com, section "量化技术：与PagedAttention正交的显存
+ * 优化路径").  For each token t with slot = slot_mapping[t] in [0,
+ * num_blocks * block_size): the K row and the V row of every KV head are
+ * quantised as pa_dtype states (one scale per row) and their codes and
+ * scale stored at in-block position slot % block_size of block slot /
+ * block_size; other slots are skipped.  k_new, v_new: [num_tokens,
+ * num_kv_heads, head_dim] of src_dtype (PA_F32, PA_F16 or PA_BF16); the
+ * pools are [num_blocks, num_kv_heads, head_dim * block_size + 4 *
+ * block_size] bytes.  head_dim must be a multiple of 16.  Two tokens with
+ * the same slot race.
+ * ------------------------------------------------------------------------ */
+PA_API pa_status pa_write_kv_i8(const void* k_new, const void* v_new, int32_t src_dtype,
+                                void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t num_blocks, void* stream);
+
+/* ------------------------------------------------------------------------
  * pa_copy_blocks -- copy-on-write block copies (bmjup.com, section
  * "PagedAttention 的核心工作机制与创新", item 2 "写入时拷贝（Copy-on-Write）";
  * wiblog.cn, section "Copy-on-Write、并行采样与 Prefix Caching 不是同一件
  * 事").  block_mapping is [num_pairs][2] int32 = {src, dst}: every element of
  * physical block dst (all KV heads, K and V) becomes a bit copy of block src.  A dst must not appear twice nor
  * as any pair's src (the pairs pa_seq_append_slot reports satisfy this).
- * Pairs with an id outside [0, num_blocks) are skipped.
+ * Pairs with an id outside [0, num_blocks) are skipped.  dtype PA_I8 copies
+ * whole INT8 tiles, codes and scales (block_size must be a multiple of 4).
  * ------------------------------------------------------------------------ */
 PA_API pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
                                 int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
@@ -185,7 +224,7 @@ PA_API pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* blo
  * Rows t >= context_lens[s] are left untouched.  This is the "concatenate
  * the blocks, then run ordinary attention" route that wiblog.cn (section
  * "非连续 KV 为什么需要专门的 Attention Kernel") warns costs extra copies; it
- * exists only to check addressing.
+ * exists only to check addressing.  PA_I8 pools are not supported.
  * ------------------------------------------------------------------------ */
 PA_API pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
                               const int32_t* block_tables, const int32_t* context_lens,

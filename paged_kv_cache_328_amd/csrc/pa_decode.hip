@@ -45,6 +45,8 @@
 // running (max, sum, output) and the waves are merged through LDS at the end.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -120,6 +122,34 @@ __device__ __forceinline__ u32x2 stream8(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
 
+__device__ __forceinline__ uint32_t stream4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ f32x4 stream_f4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+
+// INT8 codes -> 16-bit operand values.  |code| <= 127 has at most 7
+// significant bits, so the conversion to f16 or bf16 is exact.
+__device__ __forceinline__ int sbyte(uint32_t w, int k) { return (int)(int8_t)(w >> (8 * k)); }
+template <typename Ty>
+__device__ __forceinline__ uint32_t pack2(int a, int b) {
+  return (uint32_t)Ty::from_f32((float)a) | ((uint32_t)Ty::from_f32((float)b) << 16);
+}
+template <typename Ty>
+__device__ __forceinline__ u32x4 codes_to_operand(u32x2 c) {
+  return u32x4{pack2<Ty>(sbyte(c[0], 0), sbyte(c[0], 1)), pack2<Ty>(sbyte(c[0], 2), sbyte(c[0], 3)),
+               pack2<Ty>(sbyte(c[1], 0), sbyte(c[1], 1)), pack2<Ty>(sbyte(c[1], 2), sbyte(c[1], 3))};
+}
+
+// INT8 tile of one (block, KV head): D*BS codes (K: [D/16][BS][16], V:
+// [D][BS]), then BS fp32 scales, one per token.
+template <int D, int BS>
+struct I8Tile {
+  static constexpr int kBytes = D * BS + 4 * BS;
+  static constexpr int kScales = D * BS;  // byte offset of the scales
+};
+
 // ----------------------------------------------------------------------------
 // 16-bit pass 1 (matrix cores).
 // grid: x = KV head * n_groups + group, y = partition, z = sequence;
@@ -128,17 +158,24 @@ __device__ __forceinline__ u32x2 stream8(const void* p) {
 // workgroups are the KV heads of one (sequence, partition): they read the
 // adjacent head tiles of the same physical blocks.
 // ----------------------------------------------------------------------------
-// Raw K / V operand registers of one 32-token chunk.
-template <int KK, int MM>
+// Raw K / V operand registers of one 32-token chunk: 16-bit elements, or
+// (KV8) INT8 codes plus the scales of the lane's 8 tokens.
+template <int KK, int MM, bool KV8>
 struct Raw {
   u32x4 k[2][KK];
   u32x4 v[MM];
 };
+template <int KK, int MM>
+struct Raw<KK, MM, true> {
+  u32x2 k[2][KK];  // 8 codes (channels 8*(4*kk+g4)..+8) of tile-0 / tile-1 token i
+  u32x2 v[MM];     // 4 codes of tile 0, 4 of tile 1, channel 16*mm + i
+  f32x4 sk[2], sv[2];  // K / V scales of tokens 4*g4..+3 of tile 0 / tile 1
+};
 
-template <typename Ty, int D, int BS, int NW, bool PF>
+template <typename Ty, int D, int BS, int NW, bool KV8>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
-    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables,
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
+    const void* __restrict__ vcv, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, int Hq, int Hkv, int G, int n_groups, int NB,
     int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
@@ -148,7 +185,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   using V8 = typename Ty::vec8;
   constexpr int KK = D / 32;     // QK products along head_dim (32 channels each)
   constexpr int MM = D / 16;     // PV products along head_dim (16 channels each)
-  constexpr int TILE = D * BS;   // elements of one (block, KV head) tile
+  // one (block, KV head) tile: D*BS 16-bit elements, or an INT8 tile (bytes)
+  constexpr int TILE = KV8 ? I8Tile<D, BS>::kBytes : D * BS;
+  using Elem = typename std::conditional<KV8, uint8_t, uint16_t>::type;
+  const Elem* kc = reinterpret_cast<const Elem*>(kcv);
+  const Elem* vc = reinterpret_cast<const Elem*>(vcv);
   constexpr int DP = D + 4;      // padded LDS row of the merge buffer
   extern __shared__ float lds[];
 
@@ -230,33 +271,62 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   };
   // Issue every K and V load of one chunk (2 x KK 16-byte K vectors, 2 x MM
   // 8-byte V pieces per lane).
-  auto issue = [&](int bA, int bB, Raw<KK, MM>& r) {
-    const uint16_t* kA = kc + bA * blk_stride + head_off;
-    const uint16_t* kB = kc + bB * blk_stride + head_off;
-    const uint16_t* vA = vc + bA * blk_stride + head_off;
-    const uint16_t* vB = vc + bB * blk_stride + head_off;
+  auto issue = [&](int bA, int bB, Raw<KK, MM, KV8>& r) {
+    const Elem* kA = kc + bA * blk_stride + head_off;
+    const Elem* kB = kc + bB * blk_stride + head_off;
+    const Elem* vA = vc + bA * blk_stride + head_off;
+    const Elem* vB = vc + bB * blk_stride + head_off;
     const int o1 = BS == 16 ? i : 16 + i;  // in-block row of tile-1 token i
+    const int v1 = BS == 16 ? 4 * g4 : 16 + 4 * g4;  // tile-1 tokens of this row group
+    if constexpr (!KV8) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      r.k[0][kk] = stream16(kA + ((4 * kk + g4) * BS + i) * 8);
-      r.k[1][kk] = stream16(kB + ((4 * kk + g4) * BS + o1) * 8);
-    }
-    // V^T operand: channel 16*mm + i, tokens 4*g4..+3 of tile 0, then of tile 1.
-    const int v1 = BS == 16 ? 4 * g4 : 16 + 4 * g4;
+      for (int kk = 0; kk < KK; ++kk) {
+        r.k[0][kk] = stream16(kA + ((4 * kk + g4) * BS + i) * 8);
+        r.k[1][kk] = stream16(kB + ((4 * kk + g4) * BS + o1) * 8);
+      }
+      // V^T operand: channel 16*mm + i, tokens 4*g4..+3 of tile 0, then of tile 1.
 #pragma unroll
-    for (int mm = 0; mm < MM; ++mm) {
-      const u32x2 a = stream8(vA + (16 * mm + i) * BS + 4 * g4);
-      const u32x2 b = stream8(vB + (16 * mm + i) * BS + v1);
-      r.v[mm] = u32x4{a[0], a[1], b[0], b[1]};
+      for (int mm = 0; mm < MM; ++mm) {
+        const u32x2 a = stream8(vA + (16 * mm + i) * BS + 4 * g4);
+        const u32x2 b = stream8(vB + (16 * mm + i) * BS + v1);
+        r.v[mm] = u32x4{a[0], a[1], b[0], b[1]};
+      }
+    } else {
+      // K codes: channels 8m..8m+7 (m = 4*kk + g4) are half m&1 of the
+      // 16-byte x-vector m/2 of the token's row.
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int m = 4 * kk + g4;
+        r.k[0][kk] = stream8(kA + ((m >> 1) * BS + i) * 16 + 8 * (m & 1));
+        r.k[1][kk] = stream8(kB + ((m >> 1) * BS + o1) * 16 + 8 * (m & 1));
+      }
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm)
+        r.v[mm] = u32x2{stream4(vA + (16 * mm + i) * BS + 4 * g4),
+                        stream4(vB + (16 * mm + i) * BS + v1)};
+      constexpr int SC = I8Tile<D, BS>::kScales;
+      r.sk[0] = stream_f4(kA + SC + 4 * (4 * g4));
+      r.sk[1] = stream_f4(kB + SC + 4 * v1);
+      r.sv[0] = stream_f4(vA + SC + 4 * (4 * g4));
+      r.sv[1] = stream_f4(vB + SC + 4 * v1);
     }
   };
   // Both products and the online-softmax update for the chunk at token t0.
-  auto consume = [&](int t0, Raw<KK, MM>& r) {
+  auto consume = [&](int t0, Raw<KK, MM, KV8>& r) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      s0 = Ty::mma(__builtin_bit_cast(V8, r.k[0][kk]), qop[kk], s0);
-      s1 = Ty::mma(__builtin_bit_cast(V8, r.k[1][kk]), qop[kk], s1);
+      if constexpr (!KV8) {
+        s0 = Ty::mma(__builtin_bit_cast(V8, r.k[0][kk]), qop[kk], s0);
+        s1 = Ty::mma(__builtin_bit_cast(V8, r.k[1][kk]), qop[kk], s1);
+      } else {
+        s0 = Ty::mma(__builtin_bit_cast(V8, codes_to_operand<Ty>(r.k[0][kk])), qop[kk], s0);
+        s1 = Ty::mma(__builtin_bit_cast(V8, codes_to_operand<Ty>(r.k[1][kk])), qop[kk], s1);
+      }
+    }
+    if constexpr (KV8) {  // logits of INT8 keys: code dot q times the token's scale
+      s0 *= r.sk[0];
+      s1 *= r.sk[1];
     }
     // x[e]: base-2 logit for head i of token t0 + 4*g4 + e (e < 4) or
     // t0 + 16 + 4*g4 + e - 4 (e >= 4): reduction index 8*g4 + e of the PV product.
@@ -271,14 +341,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= cc) x[e] = -INFINITY;
+      if constexpr (!KV8) {  // zero the V bits of dropped tokens (they may hold NaN)
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd)
-        keep[wd] = (x[2 * wd] != -INFINITY ? 0x0000FFFFu : 0u) |
-                   (x[2 * wd + 1] != -INFINITY ? 0xFFFF0000u : 0u);
+        for (int wd = 0; wd < 4; ++wd)
+          keep[wd] = (x[2 * wd] != -INFINITY ? 0x0000FFFFu : 0u) |
+                     (x[2 * wd + 1] != -INFINITY ? 0xFFFF0000u : 0u);
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm)
+        for (int mm = 0; mm < MM; ++mm)
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) r.v[mm][wd] &= keep[wd];
+          for (int wd = 0; wd < 4; ++wd) r.v[mm][wd] &= keep[wd];
+      }
     }
 
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
@@ -291,53 +363,63 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
 
     uint32_t pw[4];
     float psum = 0.f;
+    if constexpr (!KV8) {
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      const uint16_t lo = Ty::from_f32(exp2_fast(x[2 * wd] - m_new));
-      const uint16_t hi = Ty::from_f32(exp2_fast(x[2 * wd + 1] - m_new));
-      psum += Ty::to_f32(lo) + Ty::to_f32(hi);  // the sum uses the weights the PV product sees
-      pw[wd] = (uint32_t)lo | ((uint32_t)hi << 16);
+      for (int wd = 0; wd < 4; ++wd) {
+        const uint16_t lo = Ty::from_f32(exp2_fast(x[2 * wd] - m_new));
+        const uint16_t hi = Ty::from_f32(exp2_fast(x[2 * wd + 1] - m_new));
+        psum += Ty::to_f32(lo) + Ty::to_f32(hi);  // the sum uses the weights the PV product sees
+        pw[wd] = (uint32_t)lo | ((uint32_t)hi << 16);
+      }
+    } else {
+      // INT8 values: the PV product sees weight * V scale per token (the
+      // scale varies along the reduction, so it rides on the weight); a
+      // dropped token gets an exact 0 whatever its scale holds.
+      float pe[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = exp2_fast(x[e] - m_new);
+        psum += pr;
+        const float sv = e < 4 ? r.sv[0][e] : r.sv[1][e - 4];
+        pe[e] = x[e] != -INFINITY ? pr * sv : 0.f;
+      }
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd)
+        pw[wd] = (uint32_t)Ty::from_f32(pe[2 * wd]) | ((uint32_t)Ty::from_f32(pe[2 * wd + 1]) << 16);
     }
     l_run = l_run * alpha + psum;
     const V8 pop = __builtin_bit_cast(V8, u32x4{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
     for (int mm = 0; mm < MM; ++mm) {
       acc[mm] *= alpha;
-      acc[mm] = Ty::mma(__builtin_bit_cast(V8, r.v[mm]), pop, acc[mm]);
+      if constexpr (!KV8)
+        acc[mm] = Ty::mma(__builtin_bit_cast(V8, r.v[mm]), pop, acc[mm]);
+      else
+        acc[mm] = Ty::mma(__builtin_bit_cast(V8, codes_to_operand<Ty>(r.v[mm])), pop, acc[mm]);
     }
   };
 
   // Chunk loop.  All loads of a chunk are issued before any of them is used
   // (the scheduling barrier keeps the compiler from interleaving the
-  // products with the loads), and the table entries of the wave's next chunk
-  // are fetched while the current chunk's data is in flight.  With PF the
-  // next chunk's K/V loads are issued too before the current chunk is used.
+  // products with the loads), and the loads of the wave's next chunk (and
+  // the table entries of the one after) are issued before the current chunk
+  // is used: two chunks in flight per wave.
   int nA = 0, nB = 0;
   int ch = w;
   if (ch < n_chunks) block_ids(ch, nA, nB);
-  if constexpr (!PF) {
-    for (; ch < n_chunks; ch += NW) {
-      Raw<KK, MM> r;
-      issue(nA, nB, r);
-      if (ch + NW < n_chunks) block_ids(ch + NW, nA, nB);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(t_begin + ch * kChunk, r);
+  Raw<KK, MM, KV8> cur, nxt;
+  if (ch < n_chunks) {
+    issue(nA, nB, cur);
+    if (ch + NW < n_chunks) block_ids(ch + NW, nA, nB);
+  }
+  for (; ch < n_chunks; ch += NW) {
+    if (ch + NW < n_chunks) {
+      issue(nA, nB, nxt);
+      if (ch + 2 * NW < n_chunks) block_ids(ch + 2 * NW, nA, nB);
     }
-  } else {
-    Raw<KK, MM> cur, nxt;
-    if (ch < n_chunks) {
-      issue(nA, nB, cur);
-      if (ch + NW < n_chunks) block_ids(ch + NW, nA, nB);
-    }
-    for (; ch < n_chunks; ch += NW) {
-      if (ch + NW < n_chunks) {
-        issue(nA, nB, nxt);
-        if (ch + 2 * NW < n_chunks) block_ids(ch + 2 * NW, nA, nB);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      consume(t_begin + ch * kChunk, cur);
-      cur = nxt;
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    consume(t_begin + ch * kChunk, cur);
+    cur = nxt;
   }
 
   // Fused append: that wave adds token c - 1 to its running state on the
@@ -346,59 +428,128 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   // the matrix-core path does.  The group-0 workgroup also stores the token
   // into the cache slot of position c - 1, bit for bit.
   if (new_here) {
-    // operands gathered from the lanes holding them: K chunk 4*kk+g4 (16 B)
-    // sits in lanes 2*chunk, 2*chunk+1; V channels 16*mm+4*g4..+3 (8 B) in
-    // lane D/4 + 4*mm + g4.
-    u32x4 kx[KK];
-    u32x2 vx[MM];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int src = 2 * (4 * kk + g4);
-      kx[kk] = u32x4{(uint32_t)__shfl((int)nv[0], src), (uint32_t)__shfl((int)nv[1], src),
-                     (uint32_t)__shfl((int)nv[0], src + 1), (uint32_t)__shfl((int)nv[1], src + 1)};
-    }
-#pragma unroll
-    for (int mm = 0; mm < MM; ++mm) {
-      const int src = D / 4 + 4 * mm + g4;
-      vx[mm] = u32x2{(uint32_t)__shfl((int)nv[0], src), (uint32_t)__shfl((int)nv[1], src)};
-    }
-    float dot = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 qw = __builtin_bit_cast(u32x4, qop[kk]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        dot = fmaf(Ty::to_f32((uint16_t)(qw[e / 2] >> (16 * (e & 1)))),
-                   Ty::to_f32((uint16_t)(kx[kk][e / 2] >> (16 * (e & 1)))), dot);
-    }
-    dot += __shfl_xor(dot, 16);
-    dot += __shfl_xor(dot, 32);
-    const float xn = dot * scale_log2;
-    const float m_new = fmaxf(m_run, xn);
-    const float alpha = exp2_fast(m_run - m_new);  // 0 when the wave saw no cached token
-    const float pn = Ty::to_f32(Ty::from_f32(exp2_fast(xn - m_new)));
-    m_run = m_new;
-    l_run = l_run * alpha + (g4 == 0 ? pn : 0.f);
-    // lane holds O^T[d = 16*mm + 4*g4 + j][head i]; vx[mm] holds v_new[16*mm + 4*g4 + j]
-#pragma unroll
-    for (int mm = 0; mm < MM; ++mm)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[mm][j] = fmaf(pn, Ty::to_f32((uint16_t)(vx[mm][j / 2] >> (16 * (j & 1)))),
-                          acc[mm][j] * alpha);
-    if (grp == 0 && lane < D / 2) {
-      const int tn = c - 1;
-      const int64_t b = clampi(trow[tn / BS], 0, NB - 1);
-      const int o = tn % BS;
-      if (lane < D / 4) {  // K elements 4*lane..+3: half of chunk lane/2's 16-byte row piece
-        uint16_t* kd = const_cast<uint16_t*>(kc) + b * blk_stride + head_off;
-        *reinterpret_cast<u32x2*>(kd + ((lane / 2) * BS + o) * 8 + 4 * (lane & 1)) = nv;
-      } else {             // V channels 4*(lane - D/4)..+3 of row o
-        uint16_t* vd = const_cast<uint16_t*>(vc) + b * blk_stride + head_off;
-        const int d0 = 4 * (lane - D / 4);
-#pragma unroll
+    if constexpr (!KV8) {
+      // operands gathered from the lanes holding them: K chunk 4*kk+g4 (16 B)
+      // sits in lanes 2*chunk, 2*chunk+1; V channels 16*mm+4*g4..+3 (8 B) in
+      // lane D/4 + 4*mm + g4.
+      u32x4 kx[KK];
+      u32x2 vx[MM];
+  #pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int src = 2 * (4 * kk + g4);
+        kx[kk] = u32x4{(uint32_t)__shfl((int)nv[0], src), (uint32_t)__shfl((int)nv[1], src),
+                       (uint32_t)__shfl((int)nv[0], src + 1), (uint32_t)__shfl((int)nv[1], src + 1)};
+      }
+  #pragma unroll
+      for (int mm = 0; mm < MM; ++mm) {
+        const int src = D / 4 + 4 * mm + g4;
+        vx[mm] = u32x2{(uint32_t)__shfl((int)nv[0], src), (uint32_t)__shfl((int)nv[1], src)};
+      }
+      float dot = 0.f;
+  #pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4 qw = __builtin_bit_cast(u32x4, qop[kk]);
+  #pragma unroll
+        for (int e = 0; e < 8; ++e)
+          dot = fmaf(Ty::to_f32((uint16_t)(qw[e / 2] >> (16 * (e & 1)))),
+                     Ty::to_f32((uint16_t)(kx[kk][e / 2] >> (16 * (e & 1)))), dot);
+      }
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      const float xn = dot * scale_log2;
+      const float m_new = fmaxf(m_run, xn);
+      const float alpha = exp2_fast(m_run - m_new);  // 0 when the wave saw no cached token
+      const float pn = Ty::to_f32(Ty::from_f32(exp2_fast(xn - m_new)));
+      m_run = m_new;
+      l_run = l_run * alpha + (g4 == 0 ? pn : 0.f);
+      // lane holds O^T[d = 16*mm + 4*g4 + j][head i]; vx[mm] holds v_new[16*mm + 4*g4 + j]
+  #pragma unroll
+      for (int mm = 0; mm < MM; ++mm)
+  #pragma unroll
         for (int j = 0; j < 4; ++j)
-          vd[(d0 + j) * BS + o] = (uint16_t)(nv[j / 2] >> (16 * (j & 1)));
+          acc[mm][j] = fmaf(pn, Ty::to_f32((uint16_t)(vx[mm][j / 2] >> (16 * (j & 1)))),
+                            acc[mm][j] * alpha);
+      if (grp == 0 && lane < D / 2) {
+        const int tn = c - 1;
+        const int64_t b = clampi(trow[tn / BS], 0, NB - 1);
+        const int o = tn % BS;
+        if (lane < D / 4) {  // K elements 4*lane..+3: half of chunk lane/2's 16-byte row piece
+          uint16_t* kd = const_cast<Elem*>(kc) + b * blk_stride + head_off;
+          *reinterpret_cast<u32x2*>(kd + ((lane / 2) * BS + o) * 8 + 4 * (lane & 1)) = nv;
+        } else {             // V channels 4*(lane - D/4)..+3 of row o
+          uint16_t* vd = const_cast<Elem*>(vc) + b * blk_stride + head_off;
+          const int d0 = 4 * (lane - D / 4);
+  #pragma unroll
+          for (int j = 0; j < 4; ++j)
+            vd[(d0 + j) * BS + o] = (uint16_t)(nv[j / 2] >> (16 * (j & 1)));
+        }
+      }
+    } else {
+      // INT8 caches: quantise the token's K and V rows in fp32 (scale =
+      // max|x| / 127, code = rint(x / scale) clamped to +-127), then add the
+      // token with the values code * scale, as a cache write followed by a
+      // read would.  Lanes [0, D/4) hold K elements 4*lane..+3, lanes
+      // [D/4, D/2) V elements; each half finds its row maximum.
+      float xv[4];
+      float am = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xv[j] = lane < D / 2 ? Ty::to_f32((uint16_t)(nv[j / 2] >> (16 * (j & 1)))) : 0.f;
+        am = fmaxf(am, fabsf(xv[j]));
+      }
+#pragma unroll
+      for (int off = D / 8; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+      const float qsc = am / 127.0f;
+      uint32_t cw = 0;  // this lane's 4 codes
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float r = qsc > 0.f ? fminf(fmaxf(rintf(xv[j] / qsc), -127.f), 127.f) : 0.f;
+        cw |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * j);
+      }
+      const float sk_new = __shfl(qsc, 0);
+      const float sv_new = __shfl(qsc, D / 4);
+      float dot = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {  // K codes of channels 8*(4*kk+g4)..+8
+        const int src = 2 * (4 * kk + g4);
+        const u32x2 kq = {(uint32_t)__shfl((int)cw, src), (uint32_t)__shfl((int)cw, src + 1)};
+        const u32x4 qw = __builtin_bit_cast(u32x4, qop[kk]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          dot = fmaf(Ty::to_f32((uint16_t)(qw[e / 2] >> (16 * (e & 1)))),
+                     (float)sbyte(kq[e / 4], e % 4), dot);
+      }
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      const float xn = dot * sk_new * scale_log2;
+      const float m_new = fmaxf(m_run, xn);
+      const float alpha = exp2_fast(m_run - m_new);
+      const float pn = exp2_fast(xn - m_new);
+      m_run = m_new;
+      l_run = l_run * alpha + (g4 == 0 ? pn : 0.f);
+      const float pv = pn * sv_new;
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm) {  // V codes of channels 16*mm + 4*g4..+3
+        const uint32_t vq = (uint32_t)__shfl((int)cw, D / 4 + 4 * mm + g4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mm][j] = fmaf(pv, (float)sbyte(vq, j), acc[mm][j] * alpha);
+      }
+      if (grp == 0 && lane < D / 2) {
+        const int tn = c - 1;
+        const int64_t b = clampi(trow[tn / BS], 0, NB - 1);
+        const int o = tn % BS;
+        constexpr int SC = I8Tile<D, BS>::kScales;
+        if (lane < D / 4) {  // K codes of channels 4*lane..+3: bytes 4*(lane%4).. of x-vector lane/4
+          uint8_t* kd = const_cast<Elem*>(kc) + b * blk_stride + head_off;
+          *reinterpret_cast<uint32_t*>(kd + ((lane / 4) * BS + o) * 16 + 4 * (lane & 3)) = cw;
+          if (lane == 0) *reinterpret_cast<float*>(kd + SC + 4 * o) = qsc;
+        } else {             // V codes of channels 4*(lane - D/4)..+3 of row o
+          uint8_t* vd = const_cast<Elem*>(vc) + b * blk_stride + head_off;
+          const int d0 = 4 * (lane - D / 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) vd[(d0 + j) * BS + o] = (uint8_t)(cw >> (8 * j));
+          if (lane == D / 4) *reinterpret_cast<float*>(vd + SC + 4 * o) = qsc;
+        }
       }
     }
   }
@@ -644,15 +795,16 @@ struct Plan {
   int P = 0;          // partition size in tokens
   int max_parts = 0;  // partitions of the longest context
   int groups = 1;     // query-head groups of 16 per KV head (16-bit kernel)
-  int waves = 4;      // waves per workgroup (16-bit kernel)
   bool flat = true;   // flat (sequence, partition) work list (16-bit kernel)
-  bool prefetch = true;   // double-buffered chunk loads (16-bit kernel)
   size_t ws_bytes = 0;
 };
 
 pa_status validate(const pa_decode_args* a) {
   if (!a) return PA_ERR_INVALID;
-  if (!elem_bytes(a->dtype)) return PA_ERR_INVALID;
+  if (!elem_bytes(a->dtype) || a->dtype == PA_I8) return PA_ERR_INVALID;
+  // the caches hold q's type, or INT8 codes with scales under 16-bit queries
+  if (a->kv_dtype != a->dtype && !(a->kv_dtype == PA_I8 && a->dtype != PA_F32))
+    return PA_ERR_INVALID;
   if (a->num_seqs < 0 || a->num_q_heads <= 0 || a->num_kv_heads <= 0 || a->head_dim <= 0 ||
       a->block_size <= 0 || a->num_blocks <= 0 || a->max_blocks_per_seq <= 0 ||
       a->max_context_len < 0)
@@ -715,7 +867,11 @@ size_t merge_lds_bytes(int NW, int G, int D) {
   return (size_t)(2 * NW * 16 + NW * min(G, 16) * (D + 4)) * sizeof(float);
 }
 
-template <typename Ty, int D, int BS, int NW, bool PF>
+// Waves per workgroup of the 16-bit kernel (measured best on MI355X among 1,
+// 2, 4 and 8 for the workloads of the tests and the benchmark).
+constexpr int kWaves = 4;
+
+template <typename Ty, int D, int BS, int NW, bool KV8>
 void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* ws_ml,
                  hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
@@ -724,43 +880,22 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
             flat ? (unsigned)((int64_t)a->num_seqs * max(pl.max_parts, 1))
                  : (unsigned)max(pl.max_parts, 1),
             flat ? 1u : (unsigned)a->num_seqs);
-  decode_mfma_kernel<Ty, D, BS, NW, PF><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
-      (uint16_t*)a->out, (const uint16_t*)a->q, (const uint16_t*)a->k_cache,
-      (const uint16_t*)a->v_cache, a->block_tables, a->context_lens, (const uint16_t*)a->k_new,
+  decode_mfma_kernel<Ty, D, BS, NW, KV8><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
+      (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables, a->context_lens, (const uint16_t*)a->k_new,
       (const uint16_t*)a->v_new, a->num_q_heads, a->num_kv_heads, G, pl.groups, a->num_blocks,
       a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, pl.P, max(pl.max_parts, 1),
       ws_acc, ws_ml, flat ? a->num_seqs : 0);
 }
 
-template <typename Ty, int D, int BS>
-void launch_mfma_waves(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
-                       hipStream_t st) {
-  if (pl.prefetch) {
-    switch (pl.waves) {
-      case 1: launch_mfma<Ty, D, BS, 1, true>(a, pl, wa, wm, st); break;
-      case 2: launch_mfma<Ty, D, BS, 2, true>(a, pl, wa, wm, st); break;
-      case 8: launch_mfma<Ty, D, BS, 8, true>(a, pl, wa, wm, st); break;
-      default: launch_mfma<Ty, D, BS, 4, true>(a, pl, wa, wm, st);
-    }
-  } else {
-    switch (pl.waves) {
-      case 1: launch_mfma<Ty, D, BS, 1, false>(a, pl, wa, wm, st); break;
-      case 2: launch_mfma<Ty, D, BS, 2, false>(a, pl, wa, wm, st); break;
-      case 8: launch_mfma<Ty, D, BS, 8, false>(a, pl, wa, wm, st); break;
-      default: launch_mfma<Ty, D, BS, 4, false>(a, pl, wa, wm, st);
-    }
-  }
-}
-
-template <typename Ty>
+template <typename Ty, bool KV8>
 void launch_mfma_dims(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
                       hipStream_t st) {
   if (a->head_dim == 128) {
-    if (a->block_size == 16) launch_mfma_waves<Ty, 128, 16>(a, pl, wa, wm, st);
-    else launch_mfma_waves<Ty, 128, 32>(a, pl, wa, wm, st);
+    if (a->block_size == 16) launch_mfma<Ty, 128, 16, kWaves, KV8>(a, pl, wa, wm, st);
+    else launch_mfma<Ty, 128, 32, kWaves, KV8>(a, pl, wa, wm, st);
   } else {
-    if (a->block_size == 16) launch_mfma_waves<Ty, 64, 16>(a, pl, wa, wm, st);
-    else launch_mfma_waves<Ty, 64, 32>(a, pl, wa, wm, st);
+    if (a->block_size == 16) launch_mfma<Ty, 64, 16, kWaves, KV8>(a, pl, wa, wm, st);
+    else launch_mfma<Ty, 64, 32, kWaves, KV8>(a, pl, wa, wm, st);
   }
 }
 
@@ -806,9 +941,16 @@ pa_status run_plan(const pa_decode_args* a, const Plan& pl, hipStream_t hs) {
     ws_acc = (float*)a->workspace;
     ws_ml = ws_acc + (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * a->head_dim;
   }
+  const bool kv8 = a->kv_dtype == PA_I8;
   switch (a->dtype) {
-    case PA_F16: launch_mfma_dims<F16>(a, pl, ws_acc, ws_ml, hs); break;
-    case PA_BF16: launch_mfma_dims<BF16>(a, pl, ws_acc, ws_ml, hs); break;
+    case PA_F16:
+      if (kv8) launch_mfma_dims<F16, true>(a, pl, ws_acc, ws_ml, hs);
+      else launch_mfma_dims<F16, false>(a, pl, ws_acc, ws_ml, hs);
+      break;
+    case PA_BF16:
+      if (kv8) launch_mfma_dims<BF16, true>(a, pl, ws_acc, ws_ml, hs);
+      else launch_mfma_dims<BF16, false>(a, pl, ws_acc, ws_ml, hs);
+      break;
     default:
       if (a->head_dim == 128) {
         if (a->block_size == 16) launch_f32<128, 16>(a, pl, ws_acc, ws_ml, hs);

@@ -14,6 +14,9 @@ Tensor layouts (all contiguous, on the GPU for the device ops):
   block_tables  [S, max_blocks] int32;  context_lens [S] int32
   k_new, v_new  [T, Hkv, D];            slot_mapping [T] int64
   block_mapping [P, 2] int32 (src, dst)
+INT8 pools (k_cache, v_cache of torch.uint8) are [NB, Hkv, D*BS + 4*BS]:
+each (block, KV head) tile holds the codes (K: [D/16][BS][16], V: [D][BS])
+followed by BS float32 scales; head_dim comes from q / k_new or is passed.
 """
 import ctypes
 import os
@@ -25,8 +28,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pagedattn.h")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS = 0, 1, 2, 3
 PA_ERR_HIP, PA_ERR_WORKSPACE, PA_ERR_UNKNOWN_SEQ, PA_ERR_EXISTS = 4, 5, 6, 7
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
-DTYPE_NAMES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
+PA_F32, PA_F16, PA_BF16, PA_I8 = 0, 1, 2, 3
+DTYPE_NAMES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "i8": PA_I8}
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -49,7 +52,7 @@ class pa_decode_args(ctypes.Structure):
         ("block_size", _I32), ("num_blocks", _I32), ("max_blocks_per_seq", _I32),
         ("max_context_len", _I32), ("scale", ctypes.c_float), ("dtype", _I32),
         ("partition_size", _I32), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
-        ("k_new", _P), ("v_new", _P),
+        ("k_new", _P), ("v_new", _P), ("kv_dtype", _I32),
     ]
 
 
@@ -68,6 +71,8 @@ def lib():
         "pa_decode_partition_size": (_I32, [A]),
         "pa_decode": (ctypes.c_int, [A, _P]),
         "pa_write_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+        "pa_write_kv_i8": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                          _P]),
         "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
         "pa_gather_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _I32, _P]),
@@ -134,8 +139,28 @@ def _stream(stream):
     return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
 
 
-def cache_geometry(k_cache, v_cache):
-    """(NB, Hkv, D, BS) of the two pools; checks they agree with the layout."""
+def is_i8(k_cache):
+    return k_cache.dtype == _torch().uint8
+
+
+def i8_tile_bytes(head_dim, block_size):
+    """Bytes of one (block, KV head) tile of an INT8 pool."""
+    return head_dim * block_size + 4 * block_size
+
+
+def cache_geometry(k_cache, v_cache, head_dim=None):
+    """(NB, Hkv, D, BS) of the two pools; checks they agree with the layout.
+    INT8 pools need head_dim."""
+    if is_i8(k_cache):
+        if head_dim is None:
+            raise ValueError("INT8 pools need head_dim")
+        if k_cache.dim() != 3 or tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype:
+            raise ValueError("INT8 pools must both be [NB, Hkv, D*BS + 4*BS] uint8")
+        NB, Hkv, tile = k_cache.shape
+        D = int(head_dim)
+        if D <= 0 or tile % (D + 4):
+            raise ValueError(f"INT8 tile of {tile} bytes does not fit head_dim {D}")
+        return NB, Hkv, D, tile // (D + 4)
     if k_cache.dim() != 5 or v_cache.dim() != 4 or k_cache.dtype != v_cache.dtype:
         raise ValueError("k_cache must be [NB, Hkv, D/x, BS, x] and v_cache [NB, Hkv, D, BS]")
     NB, Hkv, Dx, BS, x = k_cache.shape
@@ -152,9 +177,11 @@ def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale
     """Fill a pa_decode_args from tensors (no call into the library).
     k_new / v_new ([S, Hkv, D], optional): the step's new token of every
     sequence, appended at position context_lens[s] - 1 by pa_decode itself."""
-    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
     S, Hq, Dq = q.shape
-    if Dq != D or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, Dq)
+    i8 = is_i8(k_cache)
+    if (Dq != D or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or
+            (q.dtype != k_cache.dtype and not i8)):
         raise ValueError("q / out must be [S, Hq, D] of the cache's dtype")
     torch = _torch()
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
@@ -169,6 +196,7 @@ def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale
     a.max_context_len = int(max_context_len)
     a.scale = float(scale)
     a.dtype = _dtype_code(q)
+    a.kv_dtype = PA_I8 if i8 else _dtype_code(k_cache)
     a.partition_size = int(partition_size)
     if workspace is not None:
         a.workspace = _ptr(workspace)
@@ -178,8 +206,8 @@ def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale
     if k_new is not None:
         if tuple(k_new.shape) != (S, Hkv, D) or tuple(v_new.shape) != (S, Hkv, D):
             raise ValueError("k_new / v_new must be [S, Hkv, D]")
-        if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
-            raise TypeError("k_new / v_new must have the cache's dtype")
+        if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+            raise TypeError("k_new / v_new must have q's dtype")
         a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
     return a
 
@@ -238,7 +266,32 @@ def prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, 
                          k_new, v_new))
 
 
+def _write_i8_args(k_new, v_new, k_cache, v_cache, slot_mapping, stream):
+    T = slot_mapping.shape[0]
+    if k_new.dim() != 3:
+        raise ValueError("k_new / v_new must be [T, Hkv, D]")
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, k_new.shape[2])
+    if tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D) or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must be [T, Hkv, D] of one dtype")
+    if slot_mapping.dtype != _torch().int64:
+        raise TypeError("slot_mapping must be int64")
+    return (_ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(k_cache), _ptr(v_cache),
+            _ptr(slot_mapping), T, Hkv, D, BS, NB, _stream(stream))
+
+
+def pa_write_kv_i8(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
+    """Quantising cache write of k_new / v_new [T, Hkv, D] (float32 / float16
+    / bfloat16) into INT8 pools."""
+    _check(lib().pa_write_kv_i8(*_write_i8_args(k_new, v_new, k_cache, v_cache, slot_mapping, stream)),
+           "pa_write_kv_i8")
+
+
 def prepare_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
+    """pa_write_kv (pa_write_kv_i8 for INT8 pools) with its arguments marshalled once."""
+    if is_i8(k_cache):
+        args = _write_i8_args(k_new, v_new, k_cache, v_cache, slot_mapping, stream)
+        return PreparedCall("pa_write_kv_i8", lib().pa_write_kv_i8, args,
+                            (k_new, v_new, k_cache, v_cache, slot_mapping))
     NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
     T = slot_mapping.shape[0]
     if tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D):
@@ -251,12 +304,16 @@ def prepare_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
                         (k_new, v_new, k_cache, v_cache, slot_mapping))
 
 
-def prepare_copy_blocks(k_cache, v_cache, block_mapping, stream=None):
-    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
+def _pool_code(k_cache):
+    return PA_I8 if is_i8(k_cache) else _dtype_code(k_cache)
+
+
+def prepare_copy_blocks(k_cache, v_cache, block_mapping, stream=None, head_dim=None):
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, head_dim)
     if block_mapping.dtype != _torch().int32 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [P, 2] int32")
     args = (_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping), block_mapping.shape[0], Hkv, D, BS,
-            NB, _dtype_code(k_cache), _stream(stream))
+            NB, _pool_code(k_cache), _stream(stream))
     return PreparedCall("pa_copy_blocks", lib().pa_copy_blocks, args,
                         (k_cache, v_cache, block_mapping))
 
@@ -273,12 +330,13 @@ def pa_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
                              _stream(stream)), "pa_write_kv")
 
 
-def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None):
-    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
+def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None, head_dim=None):
+    """Copy-on-write block copies (INT8 pools: whole tiles; pass head_dim)."""
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, head_dim)
     if block_mapping.dtype != _torch().int32 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [P, 2] int32")
     _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_mapping),
-                                block_mapping.shape[0], Hkv, D, BS, NB, _dtype_code(k_cache),
+                                block_mapping.shape[0], Hkv, D, BS, NB, _pool_code(k_cache),
                                 _stream(stream)), "pa_copy_blocks")
 
 

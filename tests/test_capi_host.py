@@ -34,6 +34,8 @@ def _args(**over):
     a.scale, a.dtype, a.partition_size = 0.088, pa.PA_BF16, 0
     for k, v in over.items():
         setattr(a, k, v)
+    if "kv_dtype" not in over:
+        a.kv_dtype = a.dtype
     return a
 
 
@@ -48,6 +50,10 @@ def _args(**over):
     ({"num_blocks": 0}, pa.PA_ERR_INVALID),
     ({"scale": float("nan")}, pa.PA_ERR_INVALID),
     ({"dtype": pa.PA_F32, "partition_size": 2048}, pa.PA_ERR_UNSUPPORTED),
+    ({"kv_dtype": pa.PA_F16}, pa.PA_ERR_INVALID),       # bf16 queries over f16 pools
+    ({"dtype": pa.PA_I8}, pa.PA_ERR_INVALID),           # INT8 is a cache type only
+    ({"dtype": pa.PA_F32, "kv_dtype": pa.PA_I8}, pa.PA_ERR_INVALID),
+    ({"kv_dtype": pa.PA_I8, "head_dim": 96}, pa.PA_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects_bad_arguments_before_launch(L, over, status):
     a = _args(**over)
@@ -91,6 +97,25 @@ def test_cache_ops_reject_bad_arguments(L):
     assert L.pa_copy_blocks(None, None, None, 0, 2, 128, 16, 10, pa.PA_BF16, None) == pa.PA_OK
     assert L.pa_gather_kv(None, None, None, None, None, None, 1, 2, 128, 16, 10, 4, 64,
                           pa.PA_BF16, None) == pa.PA_ERR_INVALID
+    # INT8 pools
+    assert L.pa_write_kv_i8(None, None, 9, None, None, None, 1, 2, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert L.pa_write_kv_i8(None, None, pa.PA_I8, None, None, None, 1, 2, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert L.pa_write_kv_i8(None, None, pa.PA_BF16, None, None, None, 1, 2, 72, 16, 10, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_write_kv_i8(None, None, pa.PA_BF16, None, None, None, 0, 2, 128, 16, 10, None) == pa.PA_OK
+    assert L.pa_write_kv_i8(None, None, pa.PA_F16, None, None, None, 1, 2, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert L.pa_write_kv(None, None, None, None, None, 1, 2, 128, 16, 10, pa.PA_I8, None) == pa.PA_ERR_INVALID
+    assert L.pa_copy_blocks(None, None, None, 1, 2, 128, 6, 10, pa.PA_I8, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_copy_blocks(None, None, None, 1, 2, 72, 16, 10, pa.PA_I8, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_copy_blocks(None, None, None, 0, 2, 128, 16, 10, pa.PA_I8, None) == pa.PA_OK
+    assert L.pa_gather_kv(None, None, None, None, None, None, 1, 2, 128, 16, 10, 4, 64,
+                          pa.PA_I8, None) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_int8_workspace_matches_16_bit(L):
+    a16 = _args(partition_size=32)
+    a8 = _args(partition_size=32, kv_dtype=pa.PA_I8)
+    assert L.pa_decode_workspace_bytes(a8) == L.pa_decode_workspace_bytes(a16) > 0
+    assert L.pa_decode_partition_size(_args(kv_dtype=pa.PA_I8)) == L.pa_decode_partition_size(_args())
 
 
 # ---------------------------------------------------------------------------- block manager
