@@ -22,7 +22,11 @@ ARCH = "gfx950"
 SOURCES = ["pa_decode.hip", "pa_cache_ops.hip", "pa_allocator.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{CSRC}"]
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed-fp32 instructions off; matrix-core accumulators kept in ordinary VGPRs
+# (the decode loop rescales them on the vector ALU, and keeping them in AGPRs
+# made the compiler copy all of them to VGPRs and back on every iteration).
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def _hipcc():

@@ -56,6 +56,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 32;          // tokens per step of the 16-bit kernel
 constexpr int kMaxF32Part = 1024;   // largest partition of the fp32 kernel
+constexpr float kSlack = 8.f;       // base-2 headroom of the 16-bit kernel's running max
 
 __device__ __forceinline__ u32x2 load8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
@@ -129,17 +130,12 @@ __device__ __forceinline__ f32x4 stream_f4(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
 }
 
-// INT8 codes -> 16-bit operand values.  |code| <= 127 has at most 7
-// significant bits, so the conversion to f16 or bf16 is exact.
+// INT8 codes -> 16-bit operand values (8 codes, exact: Ty::codes4).
 __device__ __forceinline__ int sbyte(uint32_t w, int k) { return (int)(int8_t)(w >> (8 * k)); }
 template <typename Ty>
-__device__ __forceinline__ uint32_t pack2(int a, int b) {
-  return (uint32_t)Ty::from_f32((float)a) | ((uint32_t)Ty::from_f32((float)b) << 16);
-}
-template <typename Ty>
 __device__ __forceinline__ u32x4 codes_to_operand(u32x2 c) {
-  return u32x4{pack2<Ty>(sbyte(c[0], 0), sbyte(c[0], 1)), pack2<Ty>(sbyte(c[0], 2), sbyte(c[0], 3)),
-               pack2<Ty>(sbyte(c[1], 0), sbyte(c[1], 1)), pack2<Ty>(sbyte(c[1], 2), sbyte(c[1], 3))};
+  const u32x2 a = Ty::codes4(c[0]), b = Ty::codes4(c[1]);
+  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 // INT8 tile of one (block, KV head): D*BS codes (K: [D/16][BS][16], V:
@@ -160,15 +156,19 @@ struct I8Tile {
 // ----------------------------------------------------------------------------
 // Raw K / V operand registers of one 32-token chunk: 16-bit elements, or
 // (KV8) INT8 codes plus the scales of the lane's 8 tokens.
+// Tokens of a chunk are numbered 0..31; tile 0 is tokens 0..15, tile 1 tokens
+// 16..31.  K operands hold token i of each tile; V operands hold tokens
+// 8*g4..8*g4+7 of one channel.
 template <int KK, int MM, bool KV8>
 struct Raw {
-  u32x4 k[2][KK];
-  u32x4 v[MM];
+  u32x4 k[2][KK];  // channels 8*(4*kk+g4)..+8 of tile-0 / tile-1 token i
+  u32x4 v[MM];     // channel 16*mm + i, tokens 8*g4..+8
 };
 template <int KK, int MM>
 struct Raw<KK, MM, true> {
-  u32x2 k[2][KK];  // 8 codes (channels 8*(4*kk+g4)..+8) of tile-0 / tile-1 token i
-  u32x2 v[MM];     // 4 codes of tile 0, 4 of tile 1, channel 16*mm + i
+  u32x2 k[2][KK];  // 8 codes of tile-0 / tile-1 token i, channels 8*m..+8 with
+                   // m = 8*(kk/2) + 2*g4 + kk%2 (half kk%2 of one 16-byte x-vector)
+  u32x2 v[MM];     // 8 codes: channel 16*mm + i, tokens 8*g4..+8
   f32x4 sk[2], sv[2];  // K / V scales of tokens 4*g4..+3 of tile 0 / tile 1
 };
 
@@ -229,13 +229,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   const bool head_ok = i < Gv;
   const int qh0 = hk * G + grp * 16;     // first query head of the group
 
-  // Q^T operand of the QK product: lane feeds head i, channels 8*(4*kk+g4)..+8.
+  // Q^T operand of the QK product: lane feeds head i, channels 8*m..+8 of the
+  // K operand it meets (m = 4*kk + g4; INT8: 8*(kk/2) + 2*g4 + kk%2, so that
+  // one 16-byte load of codes feeds two products).
+  auto qchunk = [&](int kk) { return KV8 ? 8 * (kk >> 1) + 2 * g4 + (kk & 1) : 4 * kk + g4; };
   V8 qop[KK];
   {
     const uint16_t* qrow = q + ((int64_t)s * Hq + qh0 + (head_ok ? i : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      u32x4 raw = head_ok ? load16(qrow + 8 * (4 * kk + g4)) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 raw = head_ok ? load16(qrow + 8 * qchunk(kk)) : u32x4{0u, 0u, 0u, 0u};
       qop[kk] = __builtin_bit_cast(V8, raw);
     }
   }
@@ -258,16 +261,23 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   float l_run = 0.f;        // this lane's share of the running sum
 
   const int32_t* trow = tables + (int64_t)s * max_blocks;
+  // The chunk loop reads the table through the constant address space: with a
+  // wave-uniform address that is a scalar load, counted apart from the vector
+  // loads, so waiting for the next chunk's block ids does not also wait for
+  // the K/V loads already in flight (a vector load would: those complete in
+  // order).  The table is never written while the kernel runs.
+  const __attribute__((address_space(4))) int32_t* trow_s =
+      (const __attribute__((address_space(4))) int32_t*)(tables + (int64_t)uniform(s) * max_blocks);
   const int64_t blk_stride = (int64_t)Hkv * TILE;
   const int64_t head_off = (int64_t)hk * TILE;
 
   // Physical blocks of chunk `ch` (tile 0 / tile 1); tile 1 of a 16-token
   // block size reads the next table entry unless it lies past the context.
   auto block_ids = [&](int ch, int& bA, int& bB) {
-    const int t0 = t_begin + ch * kChunk;
-    bA = uniform(clampi(trow[t0 / BS], 0, NB - 1));
+    const int t0 = uniform(t_begin + ch * kChunk);
+    bA = clampi(trow_s[t0 / BS], 0, NB - 1);
     bB = bA;
-    if (BS == 16 && t0 + 16 < cc) bB = uniform(clampi(trow[t0 / BS + 1], 0, NB - 1));
+    if (BS == 16 && t0 + 16 < cc) bB = clampi(trow_s[t0 / BS + 1], 0, NB - 1);
   };
   // Issue every K and V load of one chunk (2 x KK 16-byte K vectors, 2 x MM
   // 8-byte V pieces per lane).
@@ -277,33 +287,33 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     const Elem* vA = vc + bA * blk_stride + head_off;
     const Elem* vB = vc + bB * blk_stride + head_off;
     const int o1 = BS == 16 ? i : 16 + i;  // in-block row of tile-1 token i
-    const int v1 = BS == 16 ? 4 * g4 : 16 + 4 * g4;  // tile-1 tokens of this row group
+    const int v1 = BS == 16 ? 4 * g4 : 16 + 4 * g4;  // tile-1 tokens 4*g4.. of this row group
+    // V^T operand rows: channel 16*mm + i, the 8 tokens 8*g4..+8 of the chunk
+    // (tile g4/2), which sit next to each other in the [D][BS] V tile.
+    const Elem* vT = g4 >= 2 ? vB : vA;
+    const int ov = BS == 16 ? 8 * (g4 & 1) : 8 * g4;
     if constexpr (!KV8) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         r.k[0][kk] = stream16(kA + ((4 * kk + g4) * BS + i) * 8);
         r.k[1][kk] = stream16(kB + ((4 * kk + g4) * BS + o1) * 8);
       }
-      // V^T operand: channel 16*mm + i, tokens 4*g4..+3 of tile 0, then of tile 1.
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm) {
-        const u32x2 a = stream8(vA + (16 * mm + i) * BS + 4 * g4);
-        const u32x2 b = stream8(vB + (16 * mm + i) * BS + v1);
-        r.v[mm] = u32x4{a[0], a[1], b[0], b[1]};
-      }
+      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream16(vT + (16 * mm + i) * BS + ov);
     } else {
-      // K codes: channels 8m..8m+7 (m = 4*kk + g4) are half m&1 of the
-      // 16-byte x-vector m/2 of the token's row.
+      // K codes: one 16-byte x-vector 4*k2 + g4 (channels 16*(4*k2+g4)..+16)
+      // of the token's row feeds products 2*k2 and 2*k2 + 1.
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int m = 4 * kk + g4;
-        r.k[0][kk] = stream8(kA + ((m >> 1) * BS + i) * 16 + 8 * (m & 1));
-        r.k[1][kk] = stream8(kB + ((m >> 1) * BS + o1) * 16 + 8 * (m & 1));
+      for (int k2 = 0; k2 < KK / 2; ++k2) {
+        const u32x4 a = stream16(kA + ((4 * k2 + g4) * BS + i) * 16);
+        const u32x4 b = stream16(kB + ((4 * k2 + g4) * BS + o1) * 16);
+        r.k[0][2 * k2] = u32x2{a[0], a[1]};
+        r.k[0][2 * k2 + 1] = u32x2{a[2], a[3]};
+        r.k[1][2 * k2] = u32x2{b[0], b[1]};
+        r.k[1][2 * k2 + 1] = u32x2{b[2], b[3]};
       }
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm)
-        r.v[mm] = u32x2{stream4(vA + (16 * mm + i) * BS + 4 * g4),
-                        stream4(vB + (16 * mm + i) * BS + v1)};
+      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream8(vT + (16 * mm + i) * BS + ov);
       constexpr int SC = I8Tile<D, BS>::kScales;
       r.sk[0] = stream_f4(kA + SC + 4 * (4 * g4));
       r.sk[1] = stream_f4(kB + SC + 4 * v1);
@@ -337,19 +347,23 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       x[4 + j] = s1[j] * scale_log2;
     }
     if (t0 + kChunk > cc) {  // last chunk: drop tokens past the cached range by select
-      uint32_t keep[4];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= cc) x[e] = -INFINITY;
       if constexpr (!KV8) {  // zero the V bits of dropped tokens (they may hold NaN)
+        uint32_t keep[4];  // V word wd holds tokens t0 + 8*g4 + 2*wd, +1
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd)
-          keep[wd] = (x[2 * wd] != -INFINITY ? 0x0000FFFFu : 0u) |
-                     (x[2 * wd + 1] != -INFINITY ? 0xFFFF0000u : 0u);
+          keep[wd] = (t0 + 8 * g4 + 2 * wd < cc ? 0x0000FFFFu : 0u) |
+                     (t0 + 8 * g4 + 2 * wd + 1 < cc ? 0xFFFF0000u : 0u);
 #pragma unroll
         for (int mm = 0; mm < MM; ++mm)
 #pragma unroll
           for (int wd = 0; wd < 4; ++wd) r.v[mm][wd] &= keep[wd];
+      } else {  // and their V scales (codes are finite; a scale may be NaN)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (x[e] == -INFINITY) r.sv[e >> 2][e & 3] = 0.f;
       }
     }
 
@@ -357,41 +371,52 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
                      fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2_fast(m_run - m_new);  // 0 on the wave's first chunk
-    m_run = m_new;
+    // The reference m_run moves only when some head's chunk maximum passes it
+    // by more than kSlack: the weights then stay below 2^kSlack, and on most
+    // chunks the rescaling of the sums and accumulators is skipped.  The
+    // branch is wave-uniform.
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2_fast(m_run - m_new);  // 0 on the wave's first chunk
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm) acc[mm] *= alpha;
+    }
 
     uint32_t pw[4];
     float psum = 0.f;
     if constexpr (!KV8) {
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
-        const uint16_t lo = Ty::from_f32(exp2_fast(x[2 * wd] - m_new));
-        const uint16_t hi = Ty::from_f32(exp2_fast(x[2 * wd + 1] - m_new));
-        psum += Ty::to_f32(lo) + Ty::to_f32(hi);  // the sum uses the weights the PV product sees
-        pw[wd] = (uint32_t)lo | ((uint32_t)hi << 16);
+        pw[wd] = Ty::pack2(exp2_fast(x[2 * wd] - m_run), exp2_fast(x[2 * wd + 1] - m_run));
+        psum += Ty::lo_f32(pw[wd]) + Ty::hi_f32(pw[wd]);  // the weights the PV product sees
       }
     } else {
       // INT8 values: the PV product sees weight * V scale per token (the
-      // scale varies along the reduction, so it rides on the weight); a
-      // dropped token gets an exact 0 whatever its scale holds.
+      // scale varies along the reduction, so it rides on the weight).
       float pe[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pr = exp2_fast(x[e] - m_new);
+        const float pr = exp2_fast(x[e] - m_run);
         psum += pr;
-        const float sv = e < 4 ? r.sv[0][e] : r.sv[1][e - 4];
-        pe[e] = x[e] != -INFINITY ? pr * sv : 0.f;
+        pe[e] = pr * r.sv[e >> 2][e & 3];
       }
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd)
-        pw[wd] = (uint32_t)Ty::from_f32(pe[2 * wd]) | ((uint32_t)Ty::from_f32(pe[2 * wd + 1]) << 16);
+      for (int wd = 0; wd < 4; ++wd) pw[wd] = Ty::pack2(pe[2 * wd], pe[2 * wd + 1]);
     }
-    l_run = l_run * alpha + psum;
-    const V8 pop = __builtin_bit_cast(V8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    l_run += psum;
+    // Row g4 holds the weights of tokens 4*g4..+3 (pw[0], pw[1]) and
+    // 16 + 4*g4..+3 (pw[2], pw[3]); the PV product wants tokens 8*g4..+8 in
+    // row g4.  Swapping rows between the two word pairs (upper half with lower
+    // half, then odd rows with even rows) regroups them.
+    const auto a32 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+    const auto b32 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+    const auto a16 = __builtin_amdgcn_permlane16_swap(a32[0], a32[1], false, false);
+    const auto b16 = __builtin_amdgcn_permlane16_swap(b32[0], b32[1], false, false);
+    const V8 pop = __builtin_bit_cast(V8, u32x4{a16[0], b16[0], a16[1], b16[1]});
 #pragma unroll
     for (int mm = 0; mm < MM; ++mm) {
-      acc[mm] *= alpha;
       if constexpr (!KV8)
         acc[mm] = Ty::mma(__builtin_bit_cast(V8, r.v[mm]), pop, acc[mm]);
       else
@@ -510,8 +535,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       const float sv_new = __shfl(qsc, D / 4);
       float dot = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {  // K codes of channels 8*(4*kk+g4)..+8
-        const int src = 2 * (4 * kk + g4);
+      for (int kk = 0; kk < KK; ++kk) {  // K codes of the channels qop[kk] holds
+        const int src = 2 * qchunk(kk);
         const u32x2 kq = {(uint32_t)__shfl((int)cw, src), (uint32_t)__shfl((int)cw, src + 1)};
         const u32x4 qw = __builtin_bit_cast(u32x4, qop[kk]);
 #pragma unroll

@@ -13,6 +13,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -24,6 +27,23 @@ struct F16 {
   }
   static __device__ __forceinline__ uint16_t from_f32(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);  // round to nearest even
+  }
+  // two values rounded to nearest even, packed (low half = a)
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+  }
+  static __device__ __forceinline__ float lo_f32(uint32_t w) { return to_f32((uint16_t)w); }
+  static __device__ __forceinline__ float hi_f32(uint32_t w) { return to_f32((uint16_t)(w >> 16)); }
+  // four signed bytes -> four f16 (two packed words), exactly: with the sign
+  // bit flipped a byte is c + 128 in [1, 255]; as the mantissa under 0x64 it
+  // reads 1024 + c + 128, and subtracting 1152 leaves c (all values exact).
+  static __device__ __forceinline__ u32x2 codes4(uint32_t c) {
+    const uint32_t u = c ^ 0x80808080u;
+    const f16x2 bias = {(_Float16)-1152.f, (_Float16)-1152.f};
+    const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+    const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) + bias),
+                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) + bias)};
   }
   static __device__ __forceinline__ f32x4 mma(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -37,6 +57,16 @@ struct BF16 {
   }
   static __device__ __forceinline__ uint16_t from_f32(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);  // round to nearest even
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  }
+  static __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+  // four signed bytes -> four bf16, exactly (|c| <= 128 needs 8 significant bits)
+  static __device__ __forceinline__ u32x2 codes4(uint32_t c) {
+    return u32x2{pack2((float)(int8_t)c, (float)(int8_t)(c >> 8)),
+                 pack2((float)(int8_t)(c >> 16), (float)(int8_t)(c >> 24))};
   }
   static __device__ __forceinline__ f32x4 mma(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
