@@ -261,26 +261,36 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   float l_run = 0.f;        // this lane's share of the running sum
 
   const int32_t* trow = tables + (int64_t)s * max_blocks;
-  // The chunk loop reads the table through the constant address space: with a
-  // wave-uniform address that is a scalar load, counted apart from the vector
-  // loads, so waiting for the next chunk's block ids does not also wait for
-  // the K/V loads already in flight (a vector load would: those complete in
-  // order).  The table is never written while the kernel runs.
-  const __attribute__((address_space(4))) int32_t* trow_s =
-      (const __attribute__((address_space(4))) int32_t*)(tables + (int64_t)uniform(s) * max_blocks);
   const int64_t blk_stride = (int64_t)Hkv * TILE;
   const int64_t head_off = (int64_t)hk * TILE;
 
-  // Physical blocks of chunk `ch` (tile 0 / tile 1); tile 1 of a 16-token
-  // block size reads the next table entry unless it lies past the context.
-  auto block_ids = [&](int ch, int& bA, int& bB) {
-    const int t0 = uniform(t_begin + ch * kChunk);
-    bA = clampi(trow_s[t0 / BS], 0, NB - 1);
-    bB = bA;
-    if (BS == 16 && t0 + 16 < cc) bB = clampi(trow_s[t0 / BS + 1], 0, NB - 1);
+  // Block ids of this wave's chunks (w, w + NW, ...), held in registers: lane
+  // j has the id of block j % BPC of the wave's chunk number j / BPC of the
+  // current batch of CPB chunks.  One vector load fetches a batch before the
+  // first K/V load is issued, so no chunk waits on a table read (a chunk
+  // whose block ids came from a load in the loop would also wait for every
+  // K/V load issued before that read).  Entries past the cached range are
+  // not read (id 0 stands in; those tokens are dropped).
+  constexpr int BPC = kChunk / BS;   // blocks per chunk
+  constexpr int CPB = 64 / BPC;      // chunks per batch
+  int tbl = 0;
+  auto load_batch = [&](int k0) {
+    const int ch = w + NW * (k0 + lane / BPC);
+    const int t = t_begin + ch * kChunk + (lane % BPC) * BS;
+    tbl = ch < n_chunks && t < cc ? clampi(trow[t / BS], 0, NB - 1) : 0;
   };
-  // Issue every K and V load of one chunk (2 x KK 16-byte K vectors, 2 x MM
-  // 8-byte V pieces per lane).
+  if (w < n_chunks) load_batch(0);
+  // Physical blocks of chunk `ch` (tile 0 / tile 1; one block for BS = 32).
+  auto block_ids = [&](int ch, int& bA, int& bB) {
+    const int k = uniform((ch - w) / NW);
+    if (k > 0 && k % CPB == 0) load_batch(k);
+    const int e = (k % CPB) * BPC;
+    bA = __builtin_amdgcn_readlane(tbl, e);
+    bB = BPC > 1 ? __builtin_amdgcn_readlane(tbl, e + 1) : bA;
+  };
+  // Issue every K and V load of one chunk (per lane: 2 x KK 16-byte K vectors
+  // and MM 16-byte V rows, or for INT8 codes 2 x KK/2 16-byte K vectors, MM
+  // 8-byte V rows and four 16-byte groups of scales).
   auto issue = [&](int bA, int bB, Raw<KK, MM, KV8>& r) {
     const Elem* kA = kc + bA * blk_stride + head_off;
     const Elem* kB = kc + bB * blk_stride + head_off;

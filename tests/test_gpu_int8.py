@@ -185,6 +185,15 @@ def test_i8_partition_sizes(P):
     run_i8_decode(case, f"i8 partition P={P}", fused=True)
 
 
+@pytest.mark.parametrize("BS,P", [(16, 8192), (32, 16384)])
+def test_i8_long_partitions(BS, P):
+    """Partitions long enough that each wave reloads its block ids."""
+    lens = [4095, 8193, 20000, 33000]
+    case = wl.random_case(2450 + BS, len(lens), 8, 2, 128, BS, "f16", lens, partition_size=P,
+                          kv_dtype="i8")
+    run_i8_decode(case, f"i8 long partition BS={BS} P={P}", fused=True)
+
+
 def test_i8_matches_16_bit_path_on_exactly_representable_values():
     """Where code * scale is exact in the query type (scales powers of two),
     the INT8 decode sees the same values as a 16-bit decode over the

@@ -291,6 +291,19 @@ def test_partition_sizes_all_match(P):
     run_decode_case(case, f"partition P={P}", gather_seqs=None)
 
 
+@pytest.mark.parametrize("BS,P", [(16, 8192), (32, 16384), (16, 4096)])
+def test_long_partitions_reload_block_ids(BS, P):
+    """A wave keeps the block ids of at most 64 blocks in registers and
+    fetches the next batch when it runs out: partitions of more than 4096
+    (BS 16) or 8192 (BS 32) tokens cross batches; 4096 at BS 16 ends exactly
+    at a batch boundary."""
+    lens = [4095, 4096, 4097, 8191, 8192, 8193, 20000, 33000]
+    case = wl.random_case(950 + BS, len(lens), 8, 2, 128, BS, "bf16", lens, partition_size=P)
+    run_decode_case(case, f"long partition BS={BS} P={P}", gather_seqs=None)
+    case = wl.random_case(960 + BS, len(lens), 8, 2, 128, BS, "bf16", lens, partition_size=P)
+    run_fused_case(case, f"long partition BS={BS} P={P}")
+
+
 def test_block_relabelling_and_determinism_bit_identical():
     import torch
     lens = [5, 40, 129, 700, 1601]
