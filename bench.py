@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="llama13b_f16",
-                    choices=["llama13b_f16", "mixed_gqa_bf16", "long_bf16"])
+                    choices=["llama13b_f16", "mixed_gqa_bf16", "long_bf16", "prefill_llama13b_f16"])
     ap.add_argument("--replicas", type=int, default=0, help="0 = as many as the pool allows (max 16)")
     ap.add_argument("--partition-size", type=int, default=-1, help="-1 = the workload's own")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget; 0 = skip")
@@ -47,22 +47,26 @@ def parse():
     ap.add_argument("--kv", default="same", choices=["same", "i8"],
                     help="KV-cache type: the workload's own element type, or INT8 codes with "
                          "per-token scales (queries keep the workload's type)")
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64],
+                    help="tokens per cache block (the workloads are defined at 16; the pool keeps "
+                         "its bytes)")
     ap.add_argument("--calib-bytes", type=int, default=0,
                     help="first run one plain device-to-device copy of this many bytes (a "
                          "known-size reference for hardware byte counters)")
     return ap.parse_args()
 
 
-def build_case(name, replicas, kv_dtype=None):
+def build_case(name, replicas, kv_dtype=None, block_size=16):
     from paged_kv_cache_328_amd import workloads as wl
+    kw = dict(fill=False, kv_dtype=kv_dtype, block_size=block_size)
     if name == "llama13b_f16":
-        probe = wl.llama13b_f16(fill=False)
+        probe = wl.llama13b_f16(**kw)
         need = int(sum(-(-int(c) // probe.BS) for c in probe.context_lens))
         R = replicas or min(16, probe.NB // need)
-        return wl.llama13b_f16(fill=False, replicas=R, kv_dtype=kv_dtype)
+        return wl.llama13b_f16(replicas=R, **kw)
     if name == "mixed_gqa_bf16":
-        return wl.mixed_gqa_bf16(fill=False, replicas=replicas or 4, kv_dtype=kv_dtype)
-    return wl.long_bf16(fill=False, replicas=replicas or 2, kv_dtype=kv_dtype)
+        return wl.mixed_gqa_bf16(replicas=replicas or 4, **kw)
+    return wl.long_bf16(replicas=replicas or 2, **kw)
 
 
 def main():
@@ -79,8 +83,10 @@ def main():
     pa.lib()  # fail loudly if the library is not built
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.config.startswith("prefill"):
+        return bench_prefill(args, dev)
     i8 = args.kv == "i8"
-    case = build_case(args.config, args.replicas, "i8" if i8 else None)
+    case = build_case(args.config, args.replicas, "i8" if i8 else None, args.block_size)
     R, S, dtype = case.replicas, case.S, case.dtype
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
     P = case.partition_size if args.partition_size < 0 else args.partition_size
@@ -215,7 +221,8 @@ def main():
         "data": "synthetic",
         "pct_hbm_peak": round(100 * kv_bytes / sec_per_step / 1e9 / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(S / sec_per_step, 1),
-        "config": {"workload": case.name + (" (INT8 KV)" if i8 else ""), "kv_dtype": case.kv_dtype,
+        "config": {"workload": case.name + (" (INT8 KV)" if i8 else "")
+                   + (f" (block size {case.BS})" if case.BS != 16 else ""), "kv_dtype": case.kv_dtype,
                    "num_seqs": S, "q_heads": case.Hq, "kv_heads": case.Hkv,
                    "head_dim": case.D, "block_size": case.BS, "num_blocks": case.NB,
                    "context_tokens": int(case.context_lens.sum()),
@@ -228,7 +235,8 @@ def main():
                      + (" + merge_kernel (split-K)" if split else ""),
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(case.name + (":i8" if i8 else ""), P_eff, fused),
+                     "traffic": measured_traffic(case.name + (":i8" if i8 else "")
+                                                 + (f":bs{case.BS}" if case.BS != 16 else ""), P_eff, fused),
                      "avg_launch_ms": round(decode_ms, 5),
                      "algorithmic_bytes_per_launch": decode_bytes},
         "host_bookkeeping_us": round(host_us, 2),
@@ -236,6 +244,121 @@ def main():
     if args.cpu_seconds > 0 and not args.profile_steps:
         result["cpu_baseline"] = cpu_baseline(case, kd, vd, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16 / bf16 matrix cores
+
+
+def bench_prefill(args, dev):
+    """One step = one pa_prefill call: every sequence's chunk attends causally
+    over its paged context.  value = algorithmic TFLOP/s (QK and PV, 4 * D
+    flops per (row, head, key)); the roofline is the dense f16 MFMA peak."""
+    import torch
+    from paged_kv_cache_328_amd import pagedattn as pa
+    from paged_kv_cache_328_amd import workloads as wl
+    i8 = args.kv == "i8"
+    case = wl.prefill_llama13b_f16(fill=False, kv_dtype="i8" if i8 else None,
+                                   block_size=args.block_size)
+    dtype = case.dtype
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.base_seed(case.name))
+    if i8:
+        tile, cb = wl.i8_tile_bytes(case.D, case.BS), case.D * case.BS
+        pools = []
+        for _ in range(2):
+            p = torch.randint(-127, 128, (case.NB, case.Hkv, tile), dtype=torch.int8, device=dev,
+                              generator=g).view(torch.uint8)
+            sc = torch.rand((case.NB, case.Hkv, case.BS), device=dev, generator=g) * 0.03 + 0.01
+            p[:, :, cb:] = sc.view(torch.uint8)
+            pools.append(p)
+        kd, vd = pools
+    else:
+        ks, vs = wl.pool_shapes(case.NB, case.Hkv, case.D, case.BS, dtype)
+        kd = torch.randn(ks, dtype=tdt, device=dev, generator=g)
+        vd = torch.randn(vs, dtype=tdt, device=dev, generator=g)
+    qd = torch.from_numpy(np.ascontiguousarray(case.q)).to(dev)
+    out = torch.empty_like(qd)
+    tables = torch.from_numpy(np.ascontiguousarray(case.block_tables)).to(dev)
+    lens = torch.from_numpy(case.context_lens).to(dev)
+    qs = torch.from_numpy(case.query_start).to(dev)
+    stream = torch.cuda.current_stream()
+    call = pa.prepare_prefill(out, qd, kd, vd, tables, lens, qs, case.scale, case.max_query_len,
+                              case.max_context, stream=stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = case.flops()
+    rows = int(case.query_start[-1])
+    result = {
+        "metric": "paged prefill attention: achieved TFLOP/s (% of dense MFMA peak) and prompt tokens/s",
+        "value": round(flops / sec / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5), "gpu_ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic",
+        "tokens_per_s": round(rows / sec, 1),
+        "config": {"workload": case.name + (" (INT8 KV)" if i8 else "")
+                   + (f" (block size {case.BS})" if case.BS != 16 else ""), "kv_dtype": case.kv_dtype,
+                   "num_seqs": case.S, "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": case.D,
+                   "block_size": case.BS, "chunk_rows": rows,
+                   "context_tokens": int(case.context_lens.sum()),
+                   "flops_per_step": flops, "step": "pa_prefill"},
+        "roofline": {"kernel": "decode_mfma_kernel (prefill mode)", "bound": "mfma",
+                     "achieved": round(flops / (ms * 1e-3) / 1e12, 2), "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(ms, 5), "algorithmic_flops_per_launch": flops},
+    }
+    if args.cpu_seconds > 0 and not args.profile_steps:
+        result["cpu_baseline"] = cpu_baseline_prefill(case, kd, vd, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_prefill(case, kd, vd, budget_s):
+    """The fp64 CPU oracle on a bounded sample: the first 64 rows of sequence 0
+    (all heads), repeated until ~budget_s of CPU work."""
+    import torch
+    from oracle import oracle
+    cores = len(os.sched_getaffinity(0))
+    n = int(min(64, case.query_start[1]))
+    c = int(case.context_lens[0]) - int(case.query_start[1]) + n  # rows keep their positions
+    nblk = -(-c // case.BS)
+    used = case.block_tables[0, :nblk].astype(np.int64)
+    idx = torch.from_numpy(used).to(kd.device)
+    tables = np.arange(nblk, dtype=np.int32).reshape(1, nblk)
+    lens = np.array([c], np.int32)
+    qs = np.array([0, n], np.int32)
+    q = np.ascontiguousarray(case.q[:n])
+    kc = kd.index_select(0, idx).cpu().contiguous()
+    vc = vd.index_select(0, idx).cpu().contiguous()
+    i8 = case.kv_dtype == "i8"
+    kc, vc = kc.numpy(), vc.numpy()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        if i8:
+            oracle.prefill_i8(q, case.dtype, kc, vc, tables, lens, qs, case.scale, case.D, case.BS,
+                              num_threads=cores)
+        else:
+            oracle.prefill(q, kc, vc, tables, lens, qs, case.scale, case.dtype, num_threads=cores)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    flops = 4 * case.D * case.Hq * sum(range(c - n + 1, c + 1))
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"pa_prefill of the first {n} chunk rows of sequence 0 (positions {c - n}..{c - 1}, "
+                      f"all {case.Hq} query heads), {reps} repetitions in {reps * dt:.1f} s, "
+                      f"{cores} OpenMP threads"}
 
 
 def measured_traffic(workload, partition_size, fused):

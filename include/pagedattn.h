@@ -106,8 +106,8 @@ PA_API const char* pa_status_string(pa_status s);
  * [num_seqs] int32 with 0 <= c <= max_context_len <= max_blocks_per_seq *
  * block_size.  Entries of a table row past ceil(c / block_size) are never
  * read.  All pointers 16-byte aligned.
- * Supported: dtype f16 / bf16 / f32, head_dim 64 or 128, block_size 16 or
- * 32, any G = num_q_heads / num_kv_heads >= 1.  The caches hold dtype, or
+ * Supported: dtype f16 / bf16 / f32, head_dim 64 or 128, block_size 8, 16,
+ * 32 or 64, any G = num_q_heads / num_kv_heads >= 1.  The caches hold dtype, or
  * (kv_dtype PA_I8, f16 / bf16 only) INT8 codes whose values code * scale
  * stand for K_t and V_t: each code is widened exactly to dtype for the
  * matrix cores, K's scale multiplies the token's logit and V's scale the
@@ -165,6 +165,54 @@ PA_API size_t pa_decode_workspace_bytes(const pa_decode_args* args);
 PA_API int32_t pa_decode_partition_size(const pa_decode_args* args);
 
 PA_API pa_status pa_decode(const pa_decode_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_prefill -- paged (chunked) prefill: attention for the prompt tokens of
+ * each sequence, read through its block table (the prefill / chunked
+ * prefill of wiblog.cn, section "如何判断服务瓶颈是否真的来自
+ * PagedAttention", where long prompts make prefill the bulk of the time to
+ * first token).  Sequence s holds c = context_lens[s] cached tokens; the
+ * last n_s = query_start[s+1] - query_start[s] of them are the chunk being
+ * prefilled, their K/V already written (pa_write_kv / pa_write_kv_i8).
+ * Query row r of the chunk (r in [query_start[s], query_start[s+1])) sits at
+ * logical position p = c - n_s + (r - query_start[s]) and attends to
+ * positions 0..p (causal):
+ *     out[r,h,:] = sum_{t<=p} exp(x_t - max x) V_t / sum_{t<=p} exp(x_t - max x),
+ *     x_t = scale * <q[r,h,:], K_t>, KV head floor(h / G),
+ * with the arithmetic of pa_decode.  A chunk equal to the whole context is a
+ * plain prompt prefill; a chunk of one row is one decode query.
+ * Layouts: q, out [num_tokens, num_q_heads, head_dim] of dtype (f16 / bf16;
+ * PA_F32 returns PA_ERR_UNSUPPORTED), rows of sequence s contiguous;
+ * query_start [num_seqs + 1] int32 with query_start[0] = 0,
+ * non-decreasing, query_start[num_seqs] = num_tokens and 0 <= n_s <=
+ * min(c, max_query_len); the caches, tables and lengths as for pa_decode
+ * (kv_dtype PA_I8 for INT8 pools).  No workspace.  Device contents are
+ * preconditions; out-of-range lengths are clamped, never read past.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_prefill_args {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  int32_t num_seqs;
+  int32_t num_tokens;          /* rows of q and out */
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t max_query_len;       /* host-known upper bound of the chunk lengths */
+  int32_t max_context_len;     /* host-known upper bound of context_lens */
+  float scale;
+  int32_t dtype;               /* pa_dtype of q and out */
+  int32_t kv_dtype;            /* dtype, or PA_I8 */
+} pa_prefill_args;
+
+PA_API pa_status pa_prefill(const pa_prefill_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
  * pa_write_kv -- cache write of the step's new tokens (the "追加 KV" (append

@@ -48,6 +48,12 @@ def lib():
         L.oracle_decode.restype = _I
         L.oracle_decode.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                     ctypes.c_float, _I, _I, _P]
+        L.oracle_prefill.restype = _I
+        L.oracle_prefill.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                     ctypes.c_float, _I, _I, _P]
+        L.oracle_prefill_i8.restype = _I
+        L.oracle_prefill_i8.argtypes = [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                        ctypes.c_float, _I, _P]
         L.oracle_write_kv.restype = _I
         L.oracle_write_kv.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I]
         L.oracle_copy_blocks.restype = _I
@@ -157,6 +163,29 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype, num_th
     return out
 
 
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, dtype,
+            num_threads=1):
+    """Paged (chunked) prefill: causal attention of each query row over its
+    sequence's positions 0..p, fp64 output [T, Hq, D]."""
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, dtype)
+    _check(q, NP_STORAGE[dtype], "q")
+    _check(block_tables, np.int32, "block_tables")
+    _check(context_lens, np.int32, "context_lens")
+    _check(query_start, np.int32, "query_start")
+    S = context_lens.shape[0]
+    T, Hq, Dq = q.shape
+    if Dq != D or query_start.shape != (S + 1,) or int(query_start[-1]) != T:
+        raise ValueError("q must be [T, Hq, D] with T = query_start[S]")
+    out = np.empty((T, Hq, D), np.float64)
+    rc = lib().oracle_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                              _ptr(context_lens), _ptr(query_start), S, Hq, Hkv, D, BS,
+                              block_tables.shape[1], ctypes.c_float(scale), DTYPE_CODE[dtype],
+                              int(num_threads), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_prefill rejected its arguments")
+    return out
+
+
 def write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, dtype):
     """In-place cache write of k_new / v_new [T, Hkv, D] at slot_mapping [T]."""
     NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, dtype)
@@ -256,4 +285,26 @@ def decode_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, scale, D, 
                                 _ptr(out))
     if rc != 0:
         raise ValueError("oracle_decode_i8 rejected its arguments")
+    return out
+
+
+def prefill_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, query_start, scale, D, BS,
+               num_threads=1):
+    """Paged (chunked) prefill over INT8 pools, fp64 output [T, Hq, D]."""
+    NB, Hkv = i8_geometry(k_pool, v_pool, D, BS)
+    _check(q, NP_STORAGE[q_dtype], "q")
+    _check(block_tables, np.int32, "block_tables")
+    _check(context_lens, np.int32, "context_lens")
+    _check(query_start, np.int32, "query_start")
+    S = context_lens.shape[0]
+    T, Hq, Dq = q.shape
+    if Dq != D or query_start.shape != (S + 1,) or int(query_start[-1]) != T:
+        raise ValueError("q must be [T, Hq, D] with T = query_start[S]")
+    out = np.empty((T, Hq, D), np.float64)
+    rc = lib().oracle_prefill_i8(_ptr(q), DTYPE_CODE[q_dtype], _ptr(k_pool), _ptr(v_pool),
+                                 _ptr(block_tables), _ptr(context_lens), _ptr(query_start), S, Hq,
+                                 Hkv, D, BS, block_tables.shape[1], ctypes.c_float(scale),
+                                 int(num_threads), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_prefill_i8 rejected its arguments")
     return out

@@ -232,6 +232,82 @@ int oracle_decode(const void* q, const void* k_cache, const void* v_cache,
 /* Cache write: for every token t with slot_mapping[t] >= 0, the slot is
  * block slot / BS, in-block position slot % BS; K and V of every KV head
  * are copied bit for bit from k_new / v_new [T, Hkv, D]. */
+/* ------------------------------------------------------------------------
+ * Paged prefill (chunked prefill).  Prefill computes attention for the
+ * prompt tokens before decoding starts, and chunked prefill feeds a long
+ * prompt in pieces; long prompts make it the bulk of the time to first token
+ * (wiblog.cn, section "如何判断服务瓶颈是否真的来自 PagedAttention").  The
+ * pages give no formula beyond ordinary causal attention; the reading taken:
+ * sequence s holds context_lens[s] cached tokens whose last n_s =
+ * query_start[s+1] - query_start[s] are the chunk being prefilled (their K/V
+ * already written through the slot mapping).  Query row r of the chunk sits
+ * at logical position p = context_lens[s] - n_s + (r - query_start[s]) and
+ * attends to positions 0..p of its own sequence through the block table:
+ * out = sum_{t<=p} softmax_t(scale * <q, K_t>) V_t.  q and out are
+ * [T, Hq, D], T = query_start[S].
+ * ------------------------------------------------------------------------ */
+int oracle_prefill(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   const int32_t* query_start, int S, int Hq, int Hkv, int D, int BS,
+                   int max_blocks, float scale, int dtype, int num_threads, double* out) {
+  if (!dims_ok(Hkv, D, BS, dtype) || S < 0 || Hq <= 0 || Hq % Hkv != 0) return -1;
+  if (query_start[0] != 0) return -1;
+  for (int s = 0; s < S; ++s) {
+    const int n = query_start[s + 1] - query_start[s];
+    if (n < 0 || n > context_lens[s] || context_lens[s] > max_blocks * BS) return -1;
+  }
+  const int T = query_start[S];
+  int* seq_of = (int*)malloc(sizeof(int) * (size_t)(T > 0 ? T : 1));
+  if (!seq_of) return -1;
+  for (int s = 0; s < S; ++s)
+    for (int r = query_start[s]; r < query_start[s + 1]; ++r) seq_of[r] = s;
+  const int G = Hq / Hkv;
+  const double sc = (double)scale;
+  const int64_t pairs = (int64_t)T * Hq;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(num_threads > 0 ? num_threads : 1)
+  for (int64_t rh = 0; rh < pairs; ++rh) {
+    const int r = (int)(rh / Hq), h = (int)(rh % Hq);
+    const int s = seq_of[r];
+    const int g = h / G;
+    const int n = query_start[s + 1] - query_start[s];
+    const int c = context_lens[s] - n + (r - query_start[s]) + 1; /* positions 0..p */
+    double* o = out + rh * D;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    double* x = (double*)malloc(sizeof(double) * (size_t)c);
+    if (!x) {
+#pragma omp atomic write
+      bad = 1;
+      continue;
+    }
+    for (int t = 0; t < c; ++t) {
+      int64_t b = block_of(block_tables, max_blocks, s, t, BS);
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d)
+        dot += load_elem(q, rh * D + d, dtype) *
+               load_elem(k_cache, oracle_k_index(b, g, t % BS, d, Hkv, D, BS, dtype), dtype);
+      x[t] = sc * dot;
+    }
+    double m = x[0];
+    for (int t = 1; t < c; ++t)
+      if (x[t] > m) m = x[t];
+    double z = 0.0;
+    for (int t = 0; t < c; ++t) {
+      x[t] = exp(x[t] - m);
+      z += x[t];
+    }
+    for (int t = 0; t < c; ++t) {
+      int64_t b = block_of(block_tables, max_blocks, s, t, BS);
+      for (int d = 0; d < D; ++d)
+        o[d] += x[t] * load_elem(v_cache, oracle_v_index(b, g, t % BS, d, Hkv, D, BS), dtype);
+    }
+    for (int d = 0; d < D; ++d) o[d] /= z;
+    free(x);
+  }
+  free(seq_of);
+  return bad ? -1 : 0;
+}
+
 int oracle_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                     const int64_t* slot_mapping, int T, int Hkv, int D, int BS, int num_blocks,
                     int dtype) {
@@ -463,5 +539,72 @@ int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const ui
     for (int d = 0; d < D; ++d) o[d] /= z;
     free(x);
   }
+  return bad ? -1 : 0;
+}
+
+/* Paged prefill over INT8 pools: oracle_prefill's causal rows on the exact
+ * values code * scale (fp64).  q is [T, Hq, D] of q_dtype. */
+int oracle_prefill_i8(const void* q, int q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* query_start, int S, int Hq, int Hkv, int D, int BS,
+                      int max_blocks, float scale, int num_threads, double* out) {
+  if (q_dtype < OR_F32 || q_dtype > OR_BF16 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
+      D <= 0 || D % 16 || BS <= 0 || query_start[0] != 0)
+    return -1;
+  for (int s = 0; s < S; ++s) {
+    const int n = query_start[s + 1] - query_start[s];
+    if (n < 0 || n > context_lens[s] || context_lens[s] > max_blocks * BS) return -1;
+  }
+  const int T = query_start[S];
+  int* seq_of = (int*)malloc(sizeof(int) * (size_t)(T > 0 ? T : 1));
+  if (!seq_of) return -1;
+  for (int s = 0; s < S; ++s)
+    for (int r = query_start[s]; r < query_start[s + 1]; ++r) seq_of[r] = s;
+  const int G = Hq / Hkv;
+  const double sc = (double)scale;
+  const int64_t pairs = (int64_t)T * Hq;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 4) num_threads(num_threads > 0 ? num_threads : 1)
+  for (int64_t rh = 0; rh < pairs; ++rh) {
+    const int r = (int)(rh / Hq), h = (int)(rh % Hq);
+    const int s = seq_of[r];
+    const int g = h / G;
+    const int n = query_start[s + 1] - query_start[s];
+    const int c = context_lens[s] - n + (r - query_start[s]) + 1;
+    double* o = out + rh * D;
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    double* x = (double*)malloc(sizeof(double) * (size_t)c);
+    if (!x) {
+#pragma omp atomic write
+      bad = 1;
+      continue;
+    }
+    for (int t = 0; t < c; ++t) {
+      int64_t b = block_of(block_tables, max_blocks, s, t, BS);
+      int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d)
+        dot += load_elem(q, rh * D + d, q_dtype) *
+               i8_value(k_pool, oracle_i8_k_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+      x[t] = sc * dot;
+    }
+    double m = x[0];
+    for (int t = 1; t < c; ++t)
+      if (x[t] > m) m = x[t];
+    double z = 0.0;
+    for (int t = 0; t < c; ++t) {
+      x[t] = exp(x[t] - m);
+      z += x[t];
+    }
+    for (int t = 0; t < c; ++t) {
+      int64_t b = block_of(block_tables, max_blocks, s, t, BS);
+      int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
+      for (int d = 0; d < D; ++d)
+        o[d] += x[t] * i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+    }
+    for (int d = 0; d < D; ++d) o[d] /= z;
+    free(x);
+  }
+  free(seq_of);
   return bad ? -1 : 0;
 }

@@ -172,15 +172,16 @@ struct Raw<KK, MM, true> {
   f32x4 sk[2], sv[2];  // K / V scales of tokens 4*g4..+3 of tile 0 / tile 1
 };
 
-template <typename Ty, int D, int BS, int NW, bool KV8>
+template <typename Ty, int D, int BS, int NW, bool KV8, bool PRE>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
     const void* __restrict__ vcv, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, int Hq, int Hkv, int G, int n_groups, int NB,
     int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
-    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs) {
-  static_assert(BS == 16 || BS == 32, "block size 16 or 32");
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs,
+    const int32_t* __restrict__ qstart, int max_q, int num_rows) {
+  static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
   static_assert(D % 32 == 0, "head_dim multiple of 32");
   using V8 = typename Ty::vec8;
   constexpr int KK = D / 32;     // QK products along head_dim (32 channels each)
@@ -197,10 +198,22 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   const int w = uniform(threadIdx.x >> 6);
   const int i = lane & 15;       // row (A operand) / column (B operand, output)
   const int g4 = lane >> 4;      // which 8-element slice of the reduction dim
-  const int hk = blockIdx.x / n_groups;
-  const int grp = blockIdx.x - hk * n_groups;
-  int p, s, c;
-  if (num_seqs > 0) {
+  int hk, grp = 0, p = 0, s, c;
+  int q0 = 0, nq = 0, tile = 0;  // prefill: first row and rows of the chunk, slot tile
+  if constexpr (PRE) {
+    // Prefill: x = tile of 16 (query row, head) slots, y = KV head, z =
+    // sequence.  Slot u = 16 * tile + i is row q0 + u / G, query head
+    // hk * G + u % G, at position c - nq + u / G.
+    tile = blockIdx.x;
+    hk = blockIdx.y;
+    s = blockIdx.z;
+    c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
+    q0 = clampi(qstart[s], 0, num_rows);
+    nq = clampi(qstart[s + 1] - q0, 0, min(min(max_q, c), num_rows - q0));
+    if (tile * 16 >= nq * G) return;
+  } else if (num_seqs > 0) {
+    hk = blockIdx.x / n_groups;
+    grp = blockIdx.x - hk * n_groups;
     // Flat work list: y enumerates the (sequence, partition) units that exist,
     // sequence by sequence; each wave finds its unit from a prefix sum of the
     // sequences' partition counts, so grid slots past the real work sit at
@@ -209,25 +222,44 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
                    c))
       return;
   } else {
+    hk = blockIdx.x / n_groups;
+    grp = blockIdx.x - hk * n_groups;
     p = blockIdx.y;
     s = blockIdx.z;
     c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
   }
-  const int n_p = (c + P - 1) / P;
-  if (p < 0 || p >= max(n_p, 1)) return;
+  const int n_p = PRE ? 1 : (c + P - 1) / P;
+  if (!PRE && (p < 0 || p >= max(n_p, 1))) return;
   const int t_begin = p * P;
   // With a fused append the token at c - 1 comes from k_new / v_new, not from
   // the cache: the chunk loop reads [t_begin, cc) and the new token is added
-  // afterwards by the workgroup whose partition holds it.
-  const bool append = k_new != nullptr;
-  const int cc = append ? max(c - 1, 0) : c;
+  // afterwards by the workgroup whose partition holds it.  In prefill, slot
+  // column i sees keys [0, lim) (its position + 1); the chunk loop reads up to
+  // the tile's largest limit and masks per column from its smallest on.
+  const bool append = !PRE && k_new != nullptr;
+  const int slots = PRE ? nq * G - tile * 16 : 0;  // valid slots of a prefill tile
+  const int cc = PRE ? c - nq + (tile * 16 + min(slots, 16) - 1) / G + 1
+                     : (append ? max(c - 1, 0) : c);
+  const int lim_min = PRE ? c - nq + (tile * 16) / G + 1 : cc;
   const bool has_new = append && c > 0 && c - 1 >= t_begin && c - 1 < t_begin + P;
-  const int t_end = min(cc, t_begin + P);
+  const int t_end = PRE ? cc : min(cc, t_begin + P);
   const int n_chunks = max(0, t_end - t_begin + kChunk - 1) / kChunk;
 
-  const int Gv = min(16, G - grp * 16);  // query heads of this group
+  // Columns: decode, query heads qh0 + i of the group; prefill, slots.
+  const int Gv = PRE ? min(slots, 16) : min(16, G - grp * 16);  // valid columns
   const bool head_ok = i < Gv;
-  const int qh0 = hk * G + grp * 16;     // first query head of the group
+  const int qh0 = hk * G + grp * 16;     // first query head of the group (decode)
+  const int u_i = tile * 16 + i;         // prefill slot of column i
+  const int lim = PRE ? (head_ok ? c - nq + u_i / G + 1 : cc) : cc;  // keys [0, lim) for column i
+  // q / out row (times Hq, plus head) of column `col`
+  auto out_row = [&](int col) -> int64_t {
+    if constexpr (PRE) {
+      const int u = tile * 16 + col;
+      return (int64_t)(q0 + u / G) * Hq + hk * G + u % G;
+    } else {
+      return (int64_t)s * Hq + qh0 + col;
+    }
+  };
 
   // Q^T operand of the QK product: lane feeds head i, channels 8*m..+8 of the
   // K operand it meets (m = 4*kk + g4; INT8: 8*(kk/2) + 2*g4 + kk%2, so that
@@ -235,7 +267,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   auto qchunk = [&](int kk) { return KV8 ? 8 * (kk >> 1) + 2 * g4 + (kk & 1) : 4 * kk + g4; };
   V8 qop[KK];
   {
-    const uint16_t* qrow = q + ((int64_t)s * Hq + qh0 + (head_ok ? i : 0)) * D;
+    const uint16_t* qrow = q + out_row(head_ok ? i : 0) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 raw = head_ok ? load16(qrow + 8 * qchunk(kk)) : u32x4{0u, 0u, 0u, 0u};
@@ -271,8 +303,8 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   // whose block ids came from a load in the loop would also wait for every
   // K/V load issued before that read).  Entries past the cached range are
   // not read (id 0 stands in; those tokens are dropped).
-  constexpr int BPC = kChunk / BS;   // blocks per chunk
-  constexpr int CPB = 64 / BPC;      // chunks per batch
+  constexpr int BPC = BS >= kChunk ? 1 : kChunk / BS;  // blocks per chunk
+  constexpr int CPB = 64 / BPC;                         // chunks per batch
   int tbl = 0;
   auto load_batch = [&](int k0) {
     const int ch = w + NW * (k0 + lane / BPC);
@@ -280,55 +312,63 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     tbl = ch < n_chunks && t < cc ? clampi(trow[t / BS], 0, NB - 1) : 0;
   };
   if (w < n_chunks) load_batch(0);
-  // Physical blocks of chunk `ch` (tile 0 / tile 1; one block for BS = 32).
-  auto block_ids = [&](int ch, int& bA, int& bB) {
+  // Physical blocks of chunk `ch`, in token order (one block when BS >= 32).
+  auto block_ids = [&](int ch, int (&b)[BPC]) {
     const int k = uniform((ch - w) / NW);
     if (k > 0 && k % CPB == 0) load_batch(k);
     const int e = (k % CPB) * BPC;
-    bA = __builtin_amdgcn_readlane(tbl, e);
-    bB = BPC > 1 ? __builtin_amdgcn_readlane(tbl, e + 1) : bA;
+#pragma unroll
+    for (int j = 0; j < BPC; ++j) b[j] = __builtin_amdgcn_readlane(tbl, e + j);
   };
-  // Issue every K and V load of one chunk (per lane: 2 x KK 16-byte K vectors
-  // and MM 16-byte V rows, or for INT8 codes 2 x KK/2 16-byte K vectors, MM
-  // 8-byte V rows and four 16-byte groups of scales).
-  auto issue = [&](int bA, int bB, Raw<KK, MM, KV8>& r) {
-    const Elem* kA = kc + bA * blk_stride + head_off;
-    const Elem* kB = kc + bB * blk_stride + head_off;
-    const Elem* vA = vc + bA * blk_stride + head_off;
-    const Elem* vB = vc + bB * blk_stride + head_off;
-    const int o1 = BS == 16 ? i : 16 + i;  // in-block row of tile-1 token i
-    const int v1 = BS == 16 ? 4 * g4 : 16 + 4 * g4;  // tile-1 tokens 4*g4.. of this row group
-    // V^T operand rows: channel 16*mm + i, the 8 tokens 8*g4..+8 of the chunk
-    // (tile g4/2), which sit next to each other in the [D][BS] V tile.
-    const Elem* vT = g4 >= 2 ? vB : vA;
-    const int ov = BS == 16 ? 8 * (g4 & 1) : 8 * g4;
+  // Issue every K and V load of the chunk at token t0 (per lane: 2 x KK
+  // 16-byte K vectors and MM 16-byte V rows, or for INT8 codes 2 x KK/2
+  // 16-byte K vectors, MM 8-byte V rows and four 16-byte groups of scales).
+  // Token tau of the chunk (0..31) sits in block tau / BS of the chunk at row
+  // tau % BS; a block of 64 tokens holds the whole chunk from row t0 % 64.
+  auto issue = [&](const int (&b)[BPC], int t0, Raw<KK, MM, KV8>& r) {
+    const int r0 = BS > kChunk ? t0 % BS : 0;
+    auto at = [&](int tau, int64_t& off, int& row) {  // tile offset and row of token tau
+      int id = b[0];
+#pragma unroll
+      for (int j = 1; j < BPC; ++j)
+        if (tau / BS == j) id = b[j];
+      off = (int64_t)id * blk_stride + head_off;
+      row = BS >= kChunk ? r0 + tau : tau % BS;
+    };
+    int64_t ok0, ok1, ov, os0, os1;
+    int rk0, rk1, rv, rs0, rs1;
+    at(i, ok0, rk0);               // K operand of tile 0: token i
+    at(16 + i, ok1, rk1);          // tile 1: token 16 + i
+    at(8 * g4, ov, rv);            // V^T operand: tokens 8*g4..+8 (one block row)
+    at(4 * g4, os0, rs0);          // scales of tokens 4*g4..+3 of tile 0
+    at(16 + 4 * g4, os1, rs1);     // and of tile 1
     if constexpr (!KV8) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        r.k[0][kk] = stream16(kA + ((4 * kk + g4) * BS + i) * 8);
-        r.k[1][kk] = stream16(kB + ((4 * kk + g4) * BS + o1) * 8);
+        r.k[0][kk] = stream16(kc + ok0 + ((4 * kk + g4) * BS + rk0) * 8);
+        r.k[1][kk] = stream16(kc + ok1 + ((4 * kk + g4) * BS + rk1) * 8);
       }
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream16(vT + (16 * mm + i) * BS + ov);
+      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream16(vc + ov + (16 * mm + i) * BS + rv);
     } else {
       // K codes: one 16-byte x-vector 4*k2 + g4 (channels 16*(4*k2+g4)..+16)
       // of the token's row feeds products 2*k2 and 2*k2 + 1.
 #pragma unroll
       for (int k2 = 0; k2 < KK / 2; ++k2) {
-        const u32x4 a = stream16(kA + ((4 * k2 + g4) * BS + i) * 16);
-        const u32x4 b = stream16(kB + ((4 * k2 + g4) * BS + o1) * 16);
+        const u32x4 a = stream16(kc + ok0 + ((4 * k2 + g4) * BS + rk0) * 16);
+        const u32x4 c = stream16(kc + ok1 + ((4 * k2 + g4) * BS + rk1) * 16);
         r.k[0][2 * k2] = u32x2{a[0], a[1]};
         r.k[0][2 * k2 + 1] = u32x2{a[2], a[3]};
-        r.k[1][2 * k2] = u32x2{b[0], b[1]};
-        r.k[1][2 * k2 + 1] = u32x2{b[2], b[3]};
+        r.k[1][2 * k2] = u32x2{c[0], c[1]};
+        r.k[1][2 * k2 + 1] = u32x2{c[2], c[3]};
       }
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream8(vT + (16 * mm + i) * BS + ov);
+      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream8(vc + ov + (16 * mm + i) * BS + rv);
       constexpr int SC = I8Tile<D, BS>::kScales;
-      r.sk[0] = stream_f4(kA + SC + 4 * (4 * g4));
-      r.sk[1] = stream_f4(kB + SC + 4 * v1);
-      r.sv[0] = stream_f4(vA + SC + 4 * (4 * g4));
-      r.sv[1] = stream_f4(vB + SC + 4 * v1);
+      r.sk[0] = stream_f4(kc + os0 + SC + 4 * rs0);
+      r.sk[1] = stream_f4(kc + os1 + SC + 4 * rs1);
+      r.sv[0] = stream_f4(vc + os0 + SC + 4 * rs0);
+      r.sv[1] = stream_f4(vc + os1 + SC + 4 * rs1);
     }
   };
   // Both products and the online-softmax update for the chunk at token t0.
@@ -356,10 +396,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       x[j] = s0[j] * scale_log2;
       x[4 + j] = s1[j] * scale_log2;
     }
-    if (t0 + kChunk > cc) {  // last chunk: drop tokens past the cached range by select
+    if (t0 + kChunk > lim_min) {  // drop tokens past the column's range by select
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= cc) x[e] = -INFINITY;
+        if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= lim) x[e] = -INFINITY;
       if constexpr (!KV8) {  // zero the V bits of dropped tokens (they may hold NaN)
         uint32_t keep[4];  // V word wd holds tokens t0 + 8*g4 + 2*wd, +1
 #pragma unroll
@@ -387,33 +427,41 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     // branch is wave-uniform.
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2_fast(m_run - m_new);  // 0 on the wave's first chunk
+      // 0 on the column's first kept key; 1 while the column has none yet
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int mm = 0; mm < MM; ++mm) acc[mm] *= alpha;
     }
 
+    // A column whose keys were all dropped so far keeps m_run = -inf; its
+    // weights must come out 0, not 2^(-inf + inf).
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     uint32_t pw[4];
     float psum = 0.f;
     if constexpr (!KV8) {
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
-        pw[wd] = Ty::pack2(exp2_fast(x[2 * wd] - m_run), exp2_fast(x[2 * wd + 1] - m_run));
+        pw[wd] = Ty::pack2(exp2_fast(x[2 * wd] - m_use), exp2_fast(x[2 * wd + 1] - m_use));
         psum += Ty::lo_f32(pw[wd]) + Ty::hi_f32(pw[wd]);  // the weights the PV product sees
       }
     } else {
       // INT8 values: the PV product sees weight * V scale per token (the
-      // scale varies along the reduction, so it rides on the weight).
-      float pe[8];
+      // scale varies along the reduction, so it rides on the weight).  The
+      // sum takes the weights the product sees, rounded(p * s) / s, so that
+      // the output stays a convex combination of the cached values (a token
+      // with scale 0 has values 0 and counts with its weight p).
+      float pr[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pr = exp2_fast(x[e] - m_run);
-        psum += pr;
-        pe[e] = pr * r.sv[e >> 2][e & 3];
+      for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(x[e] - m_use);
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const float s0 = r.sv[wd >> 1][(2 * wd) & 3], s1 = r.sv[wd >> 1][(2 * wd + 1) & 3];
+        pw[wd] = Ty::pack2(pr[2 * wd] * s0, pr[2 * wd + 1] * s1);
+        psum += s0 != 0.f ? Ty::lo_f32(pw[wd]) * __builtin_amdgcn_rcpf(s0) : pr[2 * wd];
+        psum += s1 != 0.f ? Ty::hi_f32(pw[wd]) * __builtin_amdgcn_rcpf(s1) : pr[2 * wd + 1];
       }
-#pragma unroll
-      for (int wd = 0; wd < 4; ++wd) pw[wd] = Ty::pack2(pe[2 * wd], pe[2 * wd + 1]);
     }
     l_run += psum;
     // Row g4 holds the weights of tokens 4*g4..+3 (pw[0], pw[1]) and
@@ -439,18 +487,18 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   // products with the loads), and the loads of the wave's next chunk (and
   // the table entries of the one after) are issued before the current chunk
   // is used: two chunks in flight per wave.
-  int nA = 0, nB = 0;
+  int nb[BPC] = {};
   int ch = w;
-  if (ch < n_chunks) block_ids(ch, nA, nB);
+  if (ch < n_chunks) block_ids(ch, nb);
   Raw<KK, MM, KV8> cur, nxt;
   if (ch < n_chunks) {
-    issue(nA, nB, cur);
-    if (ch + NW < n_chunks) block_ids(ch + NW, nA, nB);
+    issue(nb, t_begin + ch * kChunk, cur);
+    if (ch + NW < n_chunks) block_ids(ch + NW, nb);
   }
   for (; ch < n_chunks; ch += NW) {
     if (ch + NW < n_chunks) {
-      issue(nA, nB, nxt);
-      if (ch + 2 * NW < n_chunks) block_ids(ch + 2 * NW, nA, nB);
+      issue(nb, t_begin + (ch + NW) * kChunk, nxt);
+      if (ch + 2 * NW < n_chunks) block_ids(ch + 2 * NW, nb);
     }
     __builtin_amdgcn_sched_barrier(0);
     consume(t_begin + ch * kChunk, cur);
@@ -624,7 +672,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       sum += *reinterpret_cast<const f32x4*>(a_sh + (v * Gv + hh) * DP + d);
       L += l_sh[v * 16 + hh];
     }
-    const int64_t row = (int64_t)s * Hq + qh0 + hh;
+    const int64_t row = out_row(hh);
     if (!split) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
       const f32x4 r = sum * inv;
@@ -852,7 +900,8 @@ pa_status validate(const pa_decode_args* a) {
     return PA_ERR_INVALID;
   if (!isfinite(a->scale)) return PA_ERR_INVALID;
   if (a->head_dim != 64 && a->head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (a->block_size != 16 && a->block_size != 32) return PA_ERR_UNSUPPORTED;
+  if (a->block_size != 8 && a->block_size != 16 && a->block_size != 32 && a->block_size != 64)
+    return PA_ERR_UNSUPPORTED;
   if (a->dtype == PA_F32 && a->partition_size > kMaxF32Part) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
@@ -875,7 +924,7 @@ int choose_partition(const pa_decode_args* a, int wg_per_part) {
   int P = 256;
   while (P < 2048 && (int64_t)P * 16 < max_ctx) P *= 2;
   while (P > kChunk && base * ((max_ctx + P - 1) / P) < 1024) P /= 2;
-  return P;
+  return max(P, a->block_size);  // a power of two >= 32: a multiple of the block size
 }
 
 Plan make_plan(const pa_decode_args* a) {
@@ -915,23 +964,60 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
             flat ? (unsigned)((int64_t)a->num_seqs * max(pl.max_parts, 1))
                  : (unsigned)max(pl.max_parts, 1),
             flat ? 1u : (unsigned)a->num_seqs);
-  decode_mfma_kernel<Ty, D, BS, NW, KV8><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
-      (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables, a->context_lens, (const uint16_t*)a->k_new,
-      (const uint16_t*)a->v_new, a->num_q_heads, a->num_kv_heads, G, pl.groups, a->num_blocks,
-      a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, pl.P, max(pl.max_parts, 1),
-      ws_acc, ws_ml, flat ? a->num_seqs : 0);
+  decode_mfma_kernel<Ty, D, BS, NW, KV8, false><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
+      (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
+      a->context_lens, (const uint16_t*)a->k_new, (const uint16_t*)a->v_new, a->num_q_heads,
+      a->num_kv_heads, G, pl.groups, a->num_blocks, a->max_blocks_per_seq, a->max_context_len,
+      a->scale * kLog2e, pl.P, max(pl.max_parts, 1), ws_acc, ws_ml, flat ? a->num_seqs : 0,
+      nullptr, 0, 0);
+}
+
+// Prefill: grid x = tiles of 16 (row, head) slots of the longest chunk, y =
+// KV head, z = sequence; no split-K (each tile's key range is its own).
+template <typename Ty, int D, int BS, int NW, bool KV8>
+void launch_prefill(const pa_prefill_args* a, hipStream_t st) {
+  const int G = a->num_q_heads / a->num_kv_heads;
+  const int64_t tiles = ((int64_t)a->max_query_len * G + 15) / 16;
+  dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
+  decode_mfma_kernel<Ty, D, BS, NW, KV8, true><<<grid, 64 * NW, merge_lds_bytes(NW, 16, D), st>>>(
+      (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
+      a->context_lens, nullptr, nullptr, a->num_q_heads, a->num_kv_heads, G, 1, a->num_blocks,
+      a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, kChunk, 1, nullptr, nullptr, 0,
+      a->query_start, a->max_query_len, a->num_tokens);
+}
+
+template <typename Ty, bool KV8, int D>
+void launch_prefill_bs(const pa_prefill_args* a, hipStream_t st) {
+  switch (a->block_size) {
+    case 8: launch_prefill<Ty, D, 8, kWaves, KV8>(a, st); break;
+    case 16: launch_prefill<Ty, D, 16, kWaves, KV8>(a, st); break;
+    case 32: launch_prefill<Ty, D, 32, kWaves, KV8>(a, st); break;
+    default: launch_prefill<Ty, D, 64, kWaves, KV8>(a, st); break;
+  }
+}
+
+template <typename Ty, bool KV8>
+void launch_prefill_dims(const pa_prefill_args* a, hipStream_t st) {
+  if (a->head_dim == 128) launch_prefill_bs<Ty, KV8, 128>(a, st);
+  else launch_prefill_bs<Ty, KV8, 64>(a, st);
+}
+
+template <typename Ty, bool KV8, int D>
+void launch_mfma_bs(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
+                    hipStream_t st) {
+  switch (a->block_size) {
+    case 8: launch_mfma<Ty, D, 8, kWaves, KV8>(a, pl, wa, wm, st); break;
+    case 16: launch_mfma<Ty, D, 16, kWaves, KV8>(a, pl, wa, wm, st); break;
+    case 32: launch_mfma<Ty, D, 32, kWaves, KV8>(a, pl, wa, wm, st); break;
+    default: launch_mfma<Ty, D, 64, kWaves, KV8>(a, pl, wa, wm, st); break;
+  }
 }
 
 template <typename Ty, bool KV8>
 void launch_mfma_dims(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
                       hipStream_t st) {
-  if (a->head_dim == 128) {
-    if (a->block_size == 16) launch_mfma<Ty, 128, 16, kWaves, KV8>(a, pl, wa, wm, st);
-    else launch_mfma<Ty, 128, 32, kWaves, KV8>(a, pl, wa, wm, st);
-  } else {
-    if (a->block_size == 16) launch_mfma<Ty, 64, 16, kWaves, KV8>(a, pl, wa, wm, st);
-    else launch_mfma<Ty, 64, 32, kWaves, KV8>(a, pl, wa, wm, st);
-  }
+  if (a->head_dim == 128) launch_mfma_bs<Ty, KV8, 128>(a, pl, wa, wm, st);
+  else launch_mfma_bs<Ty, KV8, 64>(a, pl, wa, wm, st);
 }
 
 template <int D, int BS>
@@ -945,6 +1031,16 @@ void launch_f32(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* w
       a->num_q_heads, a->num_kv_heads, G, a->num_blocks,
       a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, pl.P, pl.max_parts, ws_acc,
       ws_ml);
+}
+
+template <int D>
+void launch_f32_bs(const pa_decode_args* a, const Plan& pl, float* wa, float* wm, hipStream_t st) {
+  switch (a->block_size) {
+    case 8: launch_f32<D, 8>(a, pl, wa, wm, st); break;
+    case 16: launch_f32<D, 16>(a, pl, wa, wm, st); break;
+    case 32: launch_f32<D, 32>(a, pl, wa, wm, st); break;
+    default: launch_f32<D, 64>(a, pl, wa, wm, st); break;
+  }
 }
 
 template <typename Store, int D>
@@ -987,13 +1083,8 @@ pa_status run_plan(const pa_decode_args* a, const Plan& pl, hipStream_t hs) {
       else launch_mfma_dims<BF16, false>(a, pl, ws_acc, ws_ml, hs);
       break;
     default:
-      if (a->head_dim == 128) {
-        if (a->block_size == 16) launch_f32<128, 16>(a, pl, ws_acc, ws_ml, hs);
-        else launch_f32<128, 32>(a, pl, ws_acc, ws_ml, hs);
-      } else {
-        if (a->block_size == 16) launch_f32<64, 16>(a, pl, ws_acc, ws_ml, hs);
-        else launch_f32<64, 32>(a, pl, ws_acc, ws_ml, hs);
-      }
+      if (a->head_dim == 128) launch_f32_bs<128>(a, pl, ws_acc, ws_ml, hs);
+      else launch_f32_bs<64>(a, pl, ws_acc, ws_ml, hs);
   }
   pa_status st = launch_status();
   if (st != PA_OK) return st;
@@ -1023,6 +1114,43 @@ PA_API size_t pa_decode_workspace_bytes(const pa_decode_args* args) {
 PA_API int32_t pa_decode_partition_size(const pa_decode_args* args) {
   if (validate(args) != PA_OK) return -1;
   return make_plan(args).P;
+}
+
+PA_API pa_status pa_prefill(const pa_prefill_args* a, void* stream) {
+  if (!a) return PA_ERR_INVALID;
+  if (a->dtype != PA_F16 && a->dtype != PA_BF16) {
+    return a->dtype == PA_F32 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID;
+  }
+  if (a->kv_dtype != a->dtype && a->kv_dtype != PA_I8) return PA_ERR_INVALID;
+  if (a->num_seqs < 0 || a->num_tokens < 0 || a->num_q_heads <= 0 || a->num_kv_heads <= 0 ||
+      a->head_dim <= 0 || a->block_size <= 0 || a->num_blocks <= 0 ||
+      a->max_blocks_per_seq <= 0 || a->max_query_len < 0 || a->max_context_len < 0)
+    return PA_ERR_INVALID;
+  if (a->num_q_heads % a->num_kv_heads != 0) return PA_ERR_INVALID;
+  if ((int64_t)a->max_context_len > (int64_t)a->max_blocks_per_seq * a->block_size)
+    return PA_ERR_INVALID;
+  if (!isfinite(a->scale)) return PA_ERR_INVALID;
+  if (a->head_dim != 64 && a->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (a->block_size != 8 && a->block_size != 16 && a->block_size != 32 && a->block_size != 64)
+    return PA_ERR_UNSUPPORTED;
+  if (a->num_seqs == 0 || a->num_tokens == 0 || a->max_query_len == 0) return PA_OK;
+  if (!aligned16(a->out) || !aligned16(a->q) || !aligned16(a->k_cache) ||
+      !aligned16(a->v_cache) || !a->block_tables || !a->context_lens || !a->query_start)
+    return PA_ERR_INVALID;
+  const int64_t tiles =
+      ((int64_t)a->max_query_len * (a->num_q_heads / a->num_kv_heads) + 15) / 16;
+  if (a->num_seqs > 65535 || a->num_kv_heads > 65535 || tiles > 0x7FFFFFFF)
+    return PA_ERR_UNSUPPORTED;
+  hipStream_t hs = (hipStream_t)stream;
+  const bool kv8 = a->kv_dtype == PA_I8;
+  if (a->dtype == PA_F16) {
+    if (kv8) launch_prefill_dims<F16, true>(a, hs);
+    else launch_prefill_dims<F16, false>(a, hs);
+  } else {
+    if (kv8) launch_prefill_dims<BF16, true>(a, hs);
+    else launch_prefill_dims<BF16, false>(a, hs);
+  }
+  return launch_status();
 }
 
 PA_API pa_status pa_decode(const pa_decode_args* a, void* stream) {

@@ -56,6 +56,17 @@ class pa_decode_args(ctypes.Structure):
     ]
 
 
+class pa_prefill_args(ctypes.Structure):
+    _fields_ = [
+        ("out", _P), ("q", _P), ("k_cache", _P), ("v_cache", _P),
+        ("block_tables", _P), ("context_lens", _P), ("query_start", _P),
+        ("num_seqs", _I32), ("num_tokens", _I32), ("num_q_heads", _I32), ("num_kv_heads", _I32),
+        ("head_dim", _I32), ("block_size", _I32), ("num_blocks", _I32),
+        ("max_blocks_per_seq", _I32), ("max_query_len", _I32), ("max_context_len", _I32),
+        ("scale", ctypes.c_float), ("dtype", _I32), ("kv_dtype", _I32),
+    ]
+
+
 def lib():
     """Load libpagedattn.so and declare its signatures (raises if not built)."""
     global _lib
@@ -70,6 +81,7 @@ def lib():
         "pa_decode_workspace_bytes": (ctypes.c_size_t, [A]),
         "pa_decode_partition_size": (_I32, [A]),
         "pa_decode": (ctypes.c_int, [A, _P]),
+        "pa_prefill": (ctypes.c_int, [ctypes.POINTER(pa_prefill_args), _P]),
         "pa_write_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
         "pa_write_kv_i8": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                           _P]),
@@ -235,6 +247,54 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         a.workspace_bytes = need
     _check(lib().pa_decode(ctypes.byref(a), _stream(stream)), "pa_decode")
     return out
+
+
+def make_prefill_args(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                      max_query_len, max_context_len):
+    """Fill a pa_prefill_args from tensors (no call into the library)."""
+    T, Hq, Dq = q.shape
+    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, Dq)
+    i8 = is_i8(k_cache)
+    if (Dq != D or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or
+            (q.dtype != k_cache.dtype and not i8)):
+        raise ValueError("q / out must be [T, Hq, D] of the cache's dtype")
+    torch = _torch()
+    S = context_lens.shape[0]
+    for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                    (query_start, "query_start")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(query_start.shape) != (S + 1,):
+        raise ValueError("block_tables must be [S, max_blocks] and query_start [S + 1]")
+    a = pa_prefill_args()
+    a.out, a.q, a.k_cache, a.v_cache = _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache)
+    a.block_tables, a.context_lens, a.query_start = _ptr(block_tables), _ptr(context_lens), _ptr(query_start)
+    a.num_seqs, a.num_tokens, a.num_q_heads, a.num_kv_heads = S, T, Hq, Hkv
+    a.head_dim, a.block_size, a.num_blocks, a.max_blocks_per_seq = D, BS, NB, block_tables.shape[1]
+    a.max_query_len, a.max_context_len = int(max_query_len), int(max_context_len)
+    a.scale = float(scale)
+    a.dtype = _dtype_code(q)
+    a.kv_dtype = PA_I8 if i8 else _dtype_code(k_cache)
+    return a
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+               max_query_len, max_context_len, stream=None):
+    """Paged (chunked) prefill into `out` [T, Hq, D]: row r of sequence s sits
+    at position context_lens[s] - n_s + (r - query_start[s]) and attends
+    causally to its sequence's positions up to its own."""
+    a = make_prefill_args(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                          max_query_len, max_context_len)
+    _check(lib().pa_prefill(ctypes.byref(a), _stream(stream)), "pa_prefill")
+    return out
+
+
+def prepare_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                    max_query_len, max_context_len, stream=None):
+    a = make_prefill_args(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                          max_query_len, max_context_len)
+    return PreparedCall("pa_prefill", lib().pa_prefill, (ctypes.byref(a), _stream(stream)),
+                        (a, out, q, k_cache, v_cache, block_tables, context_lens, query_start))
 
 
 class PreparedCall:

@@ -32,7 +32,8 @@ import numpy as np
 
 NP_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
-CONFIG_INDEX = {"tiny_f32": 1, "llama13b_f16": 2, "mixed_gqa_bf16": 3, "cow_bf16": 4, "long_bf16": 5}
+CONFIG_INDEX = {"tiny_f32": 1, "llama13b_f16": 2, "mixed_gqa_bf16": 3, "cow_bf16": 4, "long_bf16": 5,
+                "prefill_llama13b_f16": 6}
 
 
 def base_seed(name):
@@ -232,33 +233,37 @@ def tiny_f32(seed=None, replicas=1, fill=True):
     return _finish(name, "f32", 4, 2, 2, 64, BS, NB, 0, lens, tables, rngs, fill, True)
 
 
-def llama13b_f16(seed=None, replicas=1, fill=True, num_blocks=20000, kv_dtype=None):
+def llama13b_f16(seed=None, replicas=1, fill=True, num_blocks=None, kv_dtype=None, block_size=16):
+    """num_blocks defaults to 20,000 blocks of 16 tokens (the same pool bytes
+    at any block size)."""
     name = "llama13b_f16"
     rngs = _rngs(base_seed(name) if seed is None else seed)
     lens = rngs["lens"].integers(1024, 1280, size=16, endpoint=True).tolist()
-    BS = 16
+    BS = block_size
+    num_blocks = num_blocks or 20000 * 16 // BS
     perm = rngs["perm"].permutation(num_blocks)
     tables = _permutation_tables(lens, BS, perm, replicas)
     return _finish(name, "f16", 16, 40, 40, 128, BS, num_blocks, 0, lens, tables, rngs, fill, True,
                    kv_dtype)
 
 
-def long_bf16(seed=None, replicas=1, fill=True, kv_dtype=None):
+def long_bf16(seed=None, replicas=1, fill=True, kv_dtype=None, block_size=16):
     name = "long_bf16"
     rngs = _rngs(base_seed(name) if seed is None else seed)
     lens = [16384, 32768, 65536, 131072]
-    BS = 16
-    NB = 16384 * replicas
+    BS = block_size
+    NB = 16384 * 16 // BS * replicas
     perm = rngs["perm"].permutation(NB)
     tables = _permutation_tables(lens, BS, perm, replicas)
-    return _finish(name, "bf16", 4, 64, 8, 128, BS, NB, 512, lens, tables, rngs, fill, True, kv_dtype)
+    return _finish(name, "bf16", 4, 64, 8, 128, BS, NB, max(512, BS), lens, tables, rngs, fill, True,
+                   kv_dtype)
 
 
 def _log_uniform_lens(rng, n, lo, hi):
     return np.clip(np.rint(np.exp(rng.uniform(math.log(lo), math.log(hi), size=n))), lo, hi).astype(int).tolist()
 
 
-def mixed_gqa_bf16(seed=None, replicas=1, fill=True, kv_dtype=None):
+def mixed_gqa_bf16(seed=None, replicas=1, fill=True, kv_dtype=None, block_size=16):
     """Fragmented pool: the free pool starts as a seeded permutation used as a
     stack; dummy sequences take blocks until 60% of the pool is in use, a
     seeded half of them is released, then the real sequences take their
@@ -266,7 +271,7 @@ def mixed_gqa_bf16(seed=None, replicas=1, fill=True, kv_dtype=None):
     scattered between live dummy blocks and recycled holes."""
     name = "mixed_gqa_bf16"
     rngs = _rngs(base_seed(name) if seed is None else seed)
-    S, BS = 64, 16
+    S, BS = 64, block_size
     lens = _log_uniform_lens(rngs["lens"], S, 32, 8192)
     need_one = sum(_blocks_needed(lens, BS))
     NB = int(math.ceil(2.0 * need_one * replicas / 1024.0)) * 1024
@@ -328,6 +333,76 @@ def random_case(seed, S, Hq, Hkv, D, BS, dtype, lens, NB=None, partition_size=0,
     tables = _permutation_tables(lens, BS, perm, 1)
     return _finish("random", dtype, S, Hq, Hkv, D, BS, NB, partition_size, lens, tables, rngs, fill, True,
                    kv_dtype)
+
+
+@dataclass
+class PrefillCase:
+    """A paged (chunked) prefill step: sequence s has context_lens[s] cached
+    tokens, the last chunks[s] of which are the chunk being prefilled (its
+    K/V already in the pool); q holds the chunks' rows back to back."""
+    name: str
+    dtype: str
+    kv_dtype: str
+    S: int
+    Hq: int
+    Hkv: int
+    D: int
+    BS: int
+    NB: int
+    scale: float
+    context_lens: np.ndarray
+    query_start: np.ndarray
+    block_tables: np.ndarray  # [S, max_blocks]
+    q: np.ndarray             # [T, Hq, D] storage
+    k_cache: np.ndarray = None
+    v_cache: np.ndarray = None
+
+    @property
+    def max_query_len(self):
+        return int(np.max(np.diff(self.query_start))) if self.S else 0
+
+    @property
+    def max_context(self):
+        return int(self.context_lens.max()) if self.S else 0
+
+    def flops(self):
+        """Multiply-adds of QK and PV counted as 2 flops each: 4 * D per (row,
+        head, key) pair, keys 0..p for a row at position p."""
+        tot = 0
+        for c, n in zip(self.context_lens.tolist(), np.diff(self.query_start).tolist()):
+            tot += sum(range(c - n + 1, c + 1))  # keys seen by the chunk's rows
+        return 4 * self.D * self.Hq * tot
+
+
+def prefill_case(seed, priors, chunks, Hq, Hkv, D, BS, dtype, kv_dtype=None, NB=None, fill=True,
+                 name="prefill"):
+    """Sequence s: priors[s] earlier tokens plus a chunk of chunks[s] tokens
+    (context = prior + chunk).  Seeded permutation pool as for decode."""
+    rngs = _rngs(seed)
+    lens = [int(a) + int(b) for a, b in zip(priors, chunks)]
+    need = sum(_blocks_needed(lens, BS))
+    NB = NB if NB is not None else max(need + 2, 4)
+    perm = rngs["perm"].permutation(NB)
+    tables = _permutation_tables(lens, BS, perm, 1)
+    dec = _finish(name, dtype, len(lens), Hq, Hkv, D, BS, NB, 0, lens, tables, rngs, fill, False,
+                  kv_dtype)
+    qs = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = round_to_storage(rngs["q"].standard_normal((int(qs[-1]), Hq, D), dtype=np.float32), dtype)
+    return PrefillCase(name=name, dtype=dtype, kv_dtype=dec.kv_dtype, S=len(lens), Hq=Hq, Hkv=Hkv,
+                       D=D, BS=BS, NB=NB, scale=dec.scale, context_lens=dec.context_lens,
+                       query_start=qs, block_tables=dec.block_tables[0], q=q, k_cache=dec.k_cache,
+                       v_cache=dec.v_cache)
+
+
+def prefill_llama13b_f16(seed=None, fill=True, kv_dtype=None, block_size=16):
+    """Chunked prefill at LLaMA-13B shape: 8 sequences each prefill a 512-token
+    chunk on top of 0..1536 earlier tokens (seeded), 40 heads, head_dim 128."""
+    name = "prefill_llama13b_f16"
+    seed = base_seed(name) if seed is None else seed
+    rng = np.random.default_rng(seed)
+    priors = rng.integers(0, 1536, size=8, endpoint=True).tolist()
+    return prefill_case(seed + 1, priors, [512] * 8, 40, 40, 128, block_size, "f16", kv_dtype,
+                        fill=fill, name=name)
 
 
 BUILDERS = {

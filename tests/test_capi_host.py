@@ -42,7 +42,7 @@ def _args(**over):
 @pytest.mark.parametrize("over,status", [
     ({"num_q_heads": 7}, pa.PA_ERR_INVALID),            # Hq not a multiple of Hkv
     ({"head_dim": 96}, pa.PA_ERR_UNSUPPORTED),
-    ({"block_size": 8, "max_context_len": 80}, pa.PA_ERR_UNSUPPORTED),
+    ({"block_size": 24, "max_context_len": 240}, pa.PA_ERR_UNSUPPORTED),
     ({"dtype": 7}, pa.PA_ERR_INVALID),
     ({"partition_size": 48}, pa.PA_ERR_INVALID),        # not a multiple of 32
     ({"partition_size": -32}, pa.PA_ERR_INVALID),

@@ -167,7 +167,7 @@ EDGE_LENS = [0, 1, 2, 15, 16, 17, 32, 33, 64, 65, 100, 129, 257]
 
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("D,BS", [(64, 16), (64, 32), (128, 16), (128, 32)])
+@pytest.mark.parametrize("D,BS", [(64, 16), (64, 32), (128, 16), (128, 32), (64, 8), (128, 8), (128, 64)])
 @pytest.mark.parametrize("Hq,Hkv,P", [(4, 4, 0), (12, 4, 32), (40, 2, 64), (16, 2, 128)])
 def test_i8_edge_shapes(fused, dtype, D, BS, Hq, Hkv, P):
     if P and P % BS:
@@ -185,7 +185,7 @@ def test_i8_partition_sizes(P):
     run_i8_decode(case, f"i8 partition P={P}", fused=True)
 
 
-@pytest.mark.parametrize("BS,P", [(16, 8192), (32, 16384)])
+@pytest.mark.parametrize("BS,P", [(16, 8192), (32, 16384), (8, 4096), (64, 16384)])
 def test_i8_long_partitions(BS, P):
     """Partitions long enough that each wave reloads its block ids."""
     lens = [4095, 8193, 20000, 33000]

@@ -250,7 +250,7 @@ FUSED_LENS = [0, 1, 2, 16, 17, 32, 33, 64, 65, 100, 129, 257]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("D,BS", [(64, 16), (128, 16), (128, 32)])
+@pytest.mark.parametrize("D,BS", [(64, 16), (128, 16), (128, 32), (128, 8), (64, 64), (128, 64)])
 @pytest.mark.parametrize("Hq,Hkv,P", [(4, 4, 0), (12, 4, 32), (40, 2, 64), (8, 8, 128)])
 def test_fused_append_edge_shapes(dtype, D, BS, Hq, Hkv, P):
     if P and P % BS:
@@ -267,7 +267,7 @@ EDGE_LENS = [0, 1, 15, 16, 17, 33, 100, 257]
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("BS", [16, 32])
+@pytest.mark.parametrize("BS", [8, 16, 32, 64])
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (12, 4), (16, 2), (40, 2)])
 def test_edge_shapes_16bit(dtype, D, BS, Hq, Hkv):
     case = wl.random_case(500 + D + BS + Hq, len(EDGE_LENS), Hq, Hkv, D, BS, dtype, EDGE_LENS,
@@ -276,9 +276,11 @@ def test_edge_shapes_16bit(dtype, D, BS, Hq, Hkv):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("BS", [16, 32])
+@pytest.mark.parametrize("BS", [8, 16, 32, 64])
 @pytest.mark.parametrize("Hq,Hkv,P", [(2, 2, 0), (8, 2, 32), (3, 1, 64)])
 def test_edge_shapes_f32(D, BS, Hq, Hkv, P):
+    if P % BS:
+        pytest.skip("partition size must be a multiple of the block size")
     case = wl.random_case(700 + D + BS + Hq, len(EDGE_LENS), Hq, Hkv, D, BS, "f32", EDGE_LENS,
                           partition_size=P)
     run_decode_case(case, f"edge f32 D{D} BS{BS} {Hq}/{Hkv} P{P}", compare_pools=True)
@@ -291,12 +293,12 @@ def test_partition_sizes_all_match(P):
     run_decode_case(case, f"partition P={P}", gather_seqs=None)
 
 
-@pytest.mark.parametrize("BS,P", [(16, 8192), (32, 16384), (16, 4096)])
+@pytest.mark.parametrize("BS,P", [(16, 8192), (32, 16384), (16, 4096), (8, 4096), (64, 16384)])
 def test_long_partitions_reload_block_ids(BS, P):
     """A wave keeps the block ids of at most 64 blocks in registers and
-    fetches the next batch when it runs out: partitions of more than 4096
-    (BS 16) or 8192 (BS 32) tokens cross batches; 4096 at BS 16 ends exactly
-    at a batch boundary."""
+    fetches the next batch when it runs out: partitions of more than 2048
+    (BS 8), 4096 (BS 16) or 8192 (BS 32 and 64) tokens cross batches; 4096
+    at BS 16 ends exactly at a batch boundary."""
     lens = [4095, 4096, 4097, 8191, 8192, 8193, 20000, 33000]
     case = wl.random_case(950 + BS, len(lens), 8, 2, 128, BS, "bf16", lens, partition_size=P)
     run_decode_case(case, f"long partition BS={BS} P={P}", gather_seqs=None)
@@ -409,17 +411,18 @@ def test_large_logits_stay_finite():
     run_decode_case(case, "large logits", gather_seqs=None)
 
 
-def test_write_skips_padding_and_copy_is_bit_exact():
-    dtype, NB, Hkv, D, BS = "bf16", 12, 2, 128, 16
-    rng = np.random.default_rng(17)
+@pytest.mark.parametrize("dtype,BS", [("bf16", 16), ("f16", 8), ("bf16", 64), ("f32", 32)])
+def test_write_skips_padding_and_copy_is_bit_exact(dtype, BS):
+    NB, Hkv, D = 12, 2, 128
+    rng = np.random.default_rng(17 + BS)
     ks, vs = wl.pool_shapes(NB, Hkv, D, BS, dtype)
     kc = wl.round_to_storage(rng.standard_normal(ks, dtype=np.float32), dtype)
     vc = wl.round_to_storage(rng.standard_normal(vs, dtype=np.float32), dtype)
     kd, vd = to_dev(kc, dtype), to_dev(vc, dtype)
-    slots = np.array([3, -1, 11 * BS + 15, 7 * BS, -5, NB * BS + 3], np.int64)  # padding + out of pool
+    slots = np.array([3, -1, 11 * BS + BS - 1, 7 * BS, -5, NB * BS + 3], np.int64)  # padding + out of pool
     kn = wl.round_to_storage(rng.standard_normal((6, Hkv, D), dtype=np.float32), dtype)
     vn = wl.round_to_storage(rng.standard_normal((6, Hkv, D), dtype=np.float32), dtype)
-    announce("write/copy small: pa_write_kv")
+    announce(f"write/copy small {dtype} BS={BS}: pa_write_kv")
     pa.pa_write_kv(to_dev(kn, dtype), to_dev(vn, dtype), kd, vd, ints_to_dev(slots))
     oracle.write_kv(kn[:5], vn[:5], kc, vc, slots[:5], dtype)  # the oracle rejects the last slot
     pairs = np.array([[2, 9], [7, 4], [11, 0]], np.int32)
