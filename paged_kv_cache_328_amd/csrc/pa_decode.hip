@@ -305,16 +305,19 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   // not read (id 0 stands in; those tokens are dropped).
   constexpr int BPC = BS >= kChunk ? 1 : kChunk / BS;  // blocks per chunk
   constexpr int CPB = 64 / BPC;                         // chunks per batch
+  // Chunks are dealt to the waves round-robin (the intelliparadigm page's
+  // warp-to-block assignment, section 4.2, with a wave taking 32 tokens).
+  auto chunk_of = [&](int k) { return w + NW * k; };  // the wave's k-th chunk
   int tbl = 0;
   auto load_batch = [&](int k0) {
-    const int ch = w + NW * (k0 + lane / BPC);
+    const int ch = chunk_of(k0 + lane / BPC);
     const int t = t_begin + ch * kChunk + (lane % BPC) * BS;
     tbl = ch < n_chunks && t < cc ? clampi(trow[t / BS], 0, NB - 1) : 0;
   };
-  if (w < n_chunks) load_batch(0);
-  // Physical blocks of chunk `ch`, in token order (one block when BS >= 32).
-  auto block_ids = [&](int ch, int (&b)[BPC]) {
-    const int k = uniform((ch - w) / NW);
+  if (chunk_of(0) < n_chunks) load_batch(0);
+  // Physical blocks of the wave's k-th chunk, in token order (one block when
+  // BS >= 32).
+  auto block_ids = [&](int k, int (&b)[BPC]) {
     if (k > 0 && k % CPB == 0) load_batch(k);
     const int e = (k % CPB) * BPC;
 #pragma unroll
@@ -488,21 +491,23 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   // the table entries of the one after) are issued before the current chunk
   // is used: two chunks in flight per wave.
   int nb[BPC] = {};
-  int ch = w;
-  if (ch < n_chunks) block_ids(ch, nb);
+  int ch = chunk_of(0);
+  if (ch < n_chunks) block_ids(0, nb);
   Raw<KK, MM, KV8> cur, nxt;
   if (ch < n_chunks) {
     issue(nb, t_begin + ch * kChunk, cur);
-    if (ch + NW < n_chunks) block_ids(ch + NW, nb);
+    if (chunk_of(1) < n_chunks) block_ids(1, nb);
   }
-  for (; ch < n_chunks; ch += NW) {
-    if (ch + NW < n_chunks) {
-      issue(nb, t_begin + (ch + NW) * kChunk, nxt);
-      if (ch + 2 * NW < n_chunks) block_ids(ch + 2 * NW, nb);
+  for (int k = 0; ch < n_chunks; ++k) {
+    const int ch1 = chunk_of(k + 1);
+    if (ch1 < n_chunks) {
+      issue(nb, t_begin + ch1 * kChunk, nxt);
+      if (chunk_of(k + 2) < n_chunks) block_ids(k + 2, nb);
     }
     __builtin_amdgcn_sched_barrier(0);
     consume(t_begin + ch * kChunk, cur);
     cur = nxt;
+    ch = ch1;
   }
 
   // Fused append: that wave adds token c - 1 to its running state on the
