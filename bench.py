@@ -36,7 +36,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="llama13b_f16",
-                    choices=["llama13b_f16", "mixed_gqa_bf16", "long_bf16", "prefill_llama13b_f16"])
+                    choices=["llama13b_f16", "mixed_gqa_bf16", "long_bf16", "prefill_llama13b_f16",
+                             "shared_prefix_bf16"])
+    ap.add_argument("--no-prefix-groups", action="store_true",
+                    help="shared_prefix_bf16 only: decode with pa_decode (every sequence reads the "
+                         "shared prefix itself) instead of pa_decode_prefix")
     ap.add_argument("--replicas", type=int, default=0, help="0 = as many as the pool allows (max 16)")
     ap.add_argument("--partition-size", type=int, default=-1, help="-1 = the workload's own")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget; 0 = skip")
@@ -85,6 +89,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.config.startswith("prefill"):
         return bench_prefill(args, dev)
+    if args.config == "shared_prefix_bf16":
+        return bench_shared_prefix(args, dev)
     i8 = args.kv == "i8"
     case = build_case(args.config, args.replicas, "i8" if i8 else None, args.block_size)
     R, S, dtype = case.replicas, case.S, case.dtype
@@ -321,6 +327,92 @@ def bench_prefill(args, dev):
     }
     if args.cpu_seconds > 0 and not args.profile_steps:
         result["cpu_baseline"] = cpu_baseline_prefill(case, kd, vd, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def bench_shared_prefix(args, dev):
+    """One step = one decode step of 32 sequences that share a 2048-token
+    prefix (block size 32, private suffixes of 1..512 tokens, 32 query / 8 KV
+    heads, bf16), with the fused append: pa_decode_prefix reads the shared
+    blocks once for the group (--no-prefix-groups: pa_decode, every sequence
+    reads them).  R replicas (own prefix and suffix blocks) are cycled.
+    value = logical KV bytes (every sequence's whole context) per second."""
+    import torch
+    from paged_kv_cache_328_amd import pagedattn as pa
+    from paged_kv_cache_328_amd import workloads as wl
+    name = "shared_prefix_bf16"
+    seed = wl.base_seed("cow_bf16")
+    rng = np.random.default_rng(seed)
+    n, BS, R = 32, 32, args.replicas or 8
+    suffix = rng.integers(1, 512, size=n, endpoint=True).tolist()
+    case, gs, shared = wl.shared_prefix_case(seed + 1, [(2048 // BS, suffix)] * R, 32, 8, 128, BS,
+                                             "bf16", fill=False)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    ks, vs = wl.pool_shapes(case.NB, case.Hkv, case.D, case.BS, "bf16")
+    kd = torch.randn(ks, dtype=torch.bfloat16, device=dev, generator=g)
+    vd = torch.randn(vs, dtype=torch.bfloat16, device=dev, generator=g)
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    stream = torch.cuda.current_stream()
+    calls = []
+    lens_all = case.context_lens
+    use_groups = not args.no_prefix_groups
+    for r in range(R):
+        rows = slice(r * n, (r + 1) * n)
+        tables = torch.from_numpy(np.ascontiguousarray(case.block_tables[0][rows])).to(dev)
+        lens = torch.from_numpy(np.ascontiguousarray(lens_all[rows])).to(dev)
+        q = dev_bf16(case.q[0][rows])
+        out = torch.empty_like(q)
+        kn, vn = dev_bf16(case.new_k[0][rows]), dev_bf16(case.new_v[0][rows])
+        max_ctx = int(lens_all[rows].max())
+        if use_groups:
+            gst = torch.tensor([0, n], dtype=torch.int32, device=dev)
+            pl = torch.tensor([int(shared[r])], dtype=torch.int32, device=dev)
+            calls.append(pa.prepare_decode_prefix(out, q, kd, vd, tables, lens, case.scale, max_ctx,
+                                                  gst, pl, n, stream=stream, k_new=kn, v_new=vn))
+        else:
+            calls.append(pa.prepare_decode(out, q, kd, vd, tables, lens, case.scale, max_ctx,
+                                           stream=stream, k_new=kn, v_new=vn))
+    for i in range(args.warmup):
+        calls[i % R]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        calls[i % R]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    per_tok = 2 * case.Hkv * case.D * 2
+    logical = int(lens_all[:n].sum()) * per_tok
+    unique = (int(shared[0]) + sum(suffix)) * per_tok
+    alg = (unique if use_groups else logical) + 2 * n * case.Hq * case.D * 2 + 2 * n * case.Hkv * case.D * 2
+    result = {
+        "metric": "paged decode attention with a shared prefix: logical KV GB/s and seq-steps/s",
+        "value": round(logical / sec / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5), "gpu_ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "seq_steps_per_s": round(n / sec, 1),
+        "config": {"workload": name + ("" if use_groups else " (pa_decode, no prefix groups)"),
+                   "num_seqs": n, "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": case.D,
+                   "block_size": BS, "shared_prefix_tokens": int(shared[0]),
+                   "context_tokens": int(lens_all[:n].sum()), "replicas": R,
+                   "logical_kv_bytes_per_step": logical, "unique_kv_bytes_per_step": unique,
+                   "step": "pa_decode_prefix(fused append)" if use_groups else "pa_decode(fused append)"},
+        "roofline": {"kernel": ("decode_mfma_kernel prefix pass + suffix decode + merge_kernel"
+                                if use_groups else "decode_mfma_kernel (fused append) + merge_kernel"),
+                     "bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(ms, 5), "algorithmic_bytes_per_launch": alg},
+    }
     print(json.dumps(result), flush=True)
 
 

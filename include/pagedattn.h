@@ -167,6 +167,41 @@ PA_API int32_t pa_decode_partition_size(const pa_decode_args* args);
 PA_API pa_status pa_decode(const pa_decode_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
+ * pa_decode_prefix -- pa_decode for batches whose sequences share prefix
+ * blocks (prefix caching and parallel sampling: wiblog.cn, section
+ * "Copy-on-Write、并行采样与 Prefix Caching 不是同一件事"; kongchang.com,
+ * section "PagedAttention的三大核心优势", second advantage).  Sequences are
+ * ordered by group: group g is sequences [group_start[g], group_start[g+1])
+ * and its members share their first prefix_len[g] tokens -- the same
+ * physical slots through their tables, which the copy-on-write rules keep
+ * true for whole shared blocks.  The shared prefix is attended once per
+ * group (its K/V read once, every member's query heads as the matrix-core
+ * columns), each member's remaining tokens as in pa_decode, and the two
+ * parts merged with the log-sum-exp rule.  The output equals pa_decode's up
+ * to rounding order.
+ * Preconditions (device contents): group_start[0] = 0, non-decreasing,
+ * group_start[num_groups] = num_seqs; 0 <= prefix_len[g] <= the context of
+ * every member (minus the appended token when k_new is set); a group of one
+ * or prefix_len 0 is allowed (that member decodes as in pa_decode).
+ * max_group_size is a host-known bound of the group sizes.  Arguments of
+ * pa_decode otherwise (f16 / bf16 queries; fp32 returns
+ * PA_ERR_UNSUPPORTED); the workspace comes from
+ * pa_decode_prefix_workspace_bytes (never 0 when num_groups > 0).
+ * num_groups == 0 is pa_decode.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_prefix_groups {
+  const int32_t* group_start;   /* [num_groups + 1] device */
+  const int32_t* prefix_len;    /* [num_groups] device, tokens */
+  int32_t num_groups;
+  int32_t max_group_size;
+} pa_prefix_groups;
+
+PA_API size_t pa_decode_prefix_workspace_bytes(const pa_decode_args* args,
+                                               const pa_prefix_groups* groups);
+PA_API pa_status pa_decode_prefix(const pa_decode_args* args, const pa_prefix_groups* groups,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------
  * pa_prefill -- paged (chunked) prefill: attention for the prompt tokens of
  * each sequence, read through its block table (the prefill / chunked
  * prefill of wiblog.cn, section "如何判断服务瓶颈是否真的来自

@@ -172,7 +172,13 @@ struct Raw<KK, MM, true> {
   f32x4 sk[2], sv[2];  // K / V scales of tokens 4*g4..+3 of tile 0 / tile 1
 };
 
-template <typename Ty, int D, int BS, int NW, bool KV8, bool PRE>
+// Modes of the 16-bit kernel: decode (one query per sequence; with prefix
+// groups, the keys after the group's shared prefix), prefill (chunk rows,
+// causal) and the shared-prefix pass (the group's members over the shared
+// blocks).
+constexpr int kDecode = 0, kPrefill = 1, kPrefix = 2;
+
+template <typename Ty, int D, int BS, int NW, bool KV8, int MODE>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
     const void* __restrict__ vcv, const int32_t* __restrict__ tables,
@@ -180,7 +186,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     const uint16_t* __restrict__ v_new, int Hq, int Hkv, int G, int n_groups, int NB,
     int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
     float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs,
-    const int32_t* __restrict__ qstart, int max_q, int num_rows) {
+    const int32_t* __restrict__ qstart, int max_q, int num_rows,
+    const int32_t* __restrict__ grp_start, const int32_t* __restrict__ grp_len, int n_grp) {
+  constexpr bool PRE = MODE != kDecode;   // columns are slots with their own rows
+  constexpr bool GRP = MODE == kPrefix;
   static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
   static_assert(D % 32 == 0, "head_dim multiple of 32");
   using V8 = typename Ty::vec8;
@@ -199,8 +208,20 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   const int i = lane & 15;       // row (A operand) / column (B operand, output)
   const int g4 = lane >> 4;      // which 8-element slice of the reduction dim
   int hk, grp = 0, p = 0, s, c;
-  int q0 = 0, nq = 0, tile = 0;  // prefill: first row and rows of the chunk, slot tile
-  if constexpr (PRE) {
+  int q0 = 0, nq = 0, tile = 0;  // slot modes: first row, rows, slot tile
+  if constexpr (GRP) {
+    // Shared-prefix pass: x = tile of 16 (member, head) slots, y = KV head, z
+    // = group.  The members are sequences q0 .. q0 + nq - 1; the first one's
+    // table holds the shared blocks, keys [0, grp_len[g]).
+    tile = blockIdx.x;
+    hk = blockIdx.y;
+    const int g = blockIdx.z;
+    q0 = clampi(grp_start[g], 0, num_rows);
+    nq = clampi(grp_start[g + 1] - q0, 0, num_rows - q0);
+    if (tile * 16 >= nq * G) return;
+    s = q0;
+    c = clampi(grp_len[g], 0, min(max_ctx, max_blocks * BS));
+  } else if constexpr (PRE) {
     // Prefill: x = tile of 16 (query row, head) slots, y = KV head, z =
     // sequence.  Slot u = 16 * tile + i is row q0 + u / G, query head
     // hk * G + u % G, at position c - nq + u / G.
@@ -228,19 +249,37 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     s = blockIdx.z;
     c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
   }
-  const int n_p = PRE ? 1 : (c + P - 1) / P;
+  // Decode with prefix groups: tokens [0, skip) of sequence s belong to its
+  // group's shared prefix, attended by the prefix pass (partial 0); this
+  // launch covers [skip, c) in partitions 1, 2, ...
+  int skip = 0;
+  if (MODE == kDecode && n_grp > 0) {
+    int lo = 0, hi = n_grp - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (grp_start[mid] <= s) lo = mid;
+      else hi = mid - 1;
+    }
+    skip = uniform(clampi(grp_len[lo], 0, c));
+  }
+  const int pb = skip > 0 ? 1 : 0;  // first partial slot of this launch
+  // Chunks start on 32-token boundaries: the partitions run from the boundary
+  // at or below skip, and tokens below skip are dropped.
+  const int a_skip = skip & ~(kChunk - 1);
+  const int n_p = PRE ? 1 : (c - a_skip + P - 1) / P;
   if (!PRE && (p < 0 || p >= max(n_p, 1))) return;
-  const int t_begin = p * P;
+  const int t_begin = a_skip + p * P;
   // With a fused append the token at c - 1 comes from k_new / v_new, not from
   // the cache: the chunk loop reads [t_begin, cc) and the new token is added
   // afterwards by the workgroup whose partition holds it.  In prefill, slot
   // column i sees keys [0, lim) (its position + 1); the chunk loop reads up to
   // the tile's largest limit and masks per column from its smallest on.
   const bool append = !PRE && k_new != nullptr;
-  const int slots = PRE ? nq * G - tile * 16 : 0;  // valid slots of a prefill tile
-  const int cc = PRE ? c - nq + (tile * 16 + min(slots, 16) - 1) / G + 1
-                     : (append ? max(c - 1, 0) : c);
-  const int lim_min = PRE ? c - nq + (tile * 16) / G + 1 : cc;
+  const int slots = PRE ? nq * G - tile * 16 : 0;  // valid slots of a tile
+  const int cc = GRP ? c
+                 : PRE ? c - nq + (tile * 16 + min(slots, 16) - 1) / G + 1
+                       : (append ? max(c - 1, 0) : c);
+  const int lim_min = GRP ? c : PRE ? c - nq + (tile * 16) / G + 1 : cc;
   const bool has_new = append && c > 0 && c - 1 >= t_begin && c - 1 < t_begin + P;
   const int t_end = PRE ? cc : min(cc, t_begin + P);
   const int n_chunks = max(0, t_end - t_begin + kChunk - 1) / kChunk;
@@ -250,7 +289,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   const bool head_ok = i < Gv;
   const int qh0 = hk * G + grp * 16;     // first query head of the group (decode)
   const int u_i = tile * 16 + i;         // prefill slot of column i
-  const int lim = PRE ? (head_ok ? c - nq + u_i / G + 1 : cc) : cc;  // keys [0, lim) for column i
+  const int lim = GRP ? c : PRE ? (head_ok ? c - nq + u_i / G + 1 : cc) : cc;  // keys [0, lim) of column i
   // q / out row (times Hq, plus head) of column `col`
   auto out_row = [&](int col) -> int64_t {
     if constexpr (PRE) {
@@ -399,10 +438,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       x[j] = s0[j] * scale_log2;
       x[4 + j] = s1[j] * scale_log2;
     }
-    if (t0 + kChunk > lim_min) {  // drop tokens past the column's range by select
+    if (t0 + kChunk > lim_min || t0 < skip) {  // drop tokens outside [skip, lim) by select
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= lim) x[e] = -INFINITY;
+      for (int e = 0; e < 8; ++e) {
+        const int tok = t0 + 4 * g4 + (e & 3) + 16 * (e >> 2);
+        if (tok >= lim || tok < skip) x[e] = -INFINITY;
+      }
       if constexpr (!KV8) {  // zero the V bits of dropped tokens (they may hold NaN)
         uint32_t keep[4];  // V word wd holds tokens t0 + 8*g4 + 2*wd, +1
 #pragma unroll
@@ -666,7 +707,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   }
   __syncthreads();
 
-  const bool split = n_p > 1;
+  const bool split = GRP || skip > 0 || n_p > 1;
   for (int e = threadIdx.x; e < Gv * (D / 4); e += 64 * NW) {
     const int hh = e / (D / 4);
     const int d = 4 * (e - hh * (D / 4));
@@ -685,7 +726,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
                             (uint32_t)Ty::from_f32(r[2]) | ((uint32_t)Ty::from_f32(r[3]) << 16)};
       *reinterpret_cast<u32x2*>(out + row * D + d) = packed;
     } else {
-      const int64_t idx = row * max_parts + p;
+      const int64_t idx = row * max_parts + (GRP ? 0 : pb + p);
       *reinterpret_cast<f32x4*>(ws_acc + idx * D + d) = sum;
       if (d == 0) {
         float Mh = -INFINITY;
@@ -806,7 +847,8 @@ template <typename Store, int D, int NT>
 __global__ __launch_bounds__(NT) void merge_kernel(
     typename Store::T* __restrict__ out, const int32_t* __restrict__ lens,
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, int Hq, int max_ctx,
-    int max_blocks, int BS, int P, int max_parts) {
+    int max_blocks, int BS, int P, int max_parts, const int32_t* __restrict__ grp_start,
+    const int32_t* __restrict__ grp_len, int n_grp) {
   constexpr int C4 = D / 4;                   // threads per partition row
   constexpr int ROWS = NT / C4;               // partitions read at once
   constexpr int U = 8;                        // partitions per thread per batch
@@ -829,8 +871,20 @@ __global__ __launch_bounds__(NT) void merge_kernel(
     bo[k] = *reinterpret_cast<const f32x4*>(ws_acc + (base + pp) * D + 4 * c4);
   }
   const int c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
-  const int n_p = (c + P - 1) / P;
-  if (n_p <= 1) return;
+  // With prefix groups, partial 0 is the shared prefix (when the sequence's
+  // group has one) and the decode partitions follow.
+  int skip = 0;
+  if (n_grp > 0) {
+    int lo = 0, hi = n_grp - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (grp_start[mid] <= s) lo = mid;
+      else hi = mid - 1;
+    }
+    skip = clampi(grp_len[lo], 0, c);
+  }
+  const int n_p = (skip > 0 ? 1 : 0) + (c - (skip & ~(kChunk - 1)) + P - 1) / P;
+  if (n_p <= 1 && skip == 0) return;  // pass 1 stored the output itself
 #pragma unroll
   for (int k = 0; k < U; ++k)
     if (r + k * ROWS < n_p) lse_add(st, bm[k], bl[k], bo[k]);
@@ -855,7 +909,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(
 #pragma unroll
     for (int rr = 1; rr < ROWS; ++rr)
       if (rr < n_p) lse_add(tot, sm[rr][c4], sl[rr][c4], so[rr][c4]);
-    Store::put(out + ((int64_t)s * Hq + h) * D + 4 * c4, tot.o * (1.f / tot.l));
+    Store::put(out + ((int64_t)s * Hq + h) * D + 4 * c4, tot.o * (tot.l > 0.f ? 1.f / tot.l : 0.f));
   }
 }
 
@@ -885,6 +939,12 @@ struct Plan {
   int groups = 1;     // query-head groups of 16 per KV head (16-bit kernel)
   bool flat = true;   // flat (sequence, partition) work list (16-bit kernel)
   size_t ws_bytes = 0;
+  // shared-prefix groups (pa_decode_prefix): partial 0 of a member is its
+  // group's prefix, computed by the prefix pass
+  const int32_t* grp_start = nullptr;
+  const int32_t* grp_len = nullptr;
+  int n_grp = 0;
+  int max_group = 0;
 };
 
 pa_status validate(const pa_decode_args* a) {
@@ -969,12 +1029,45 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
             flat ? (unsigned)((int64_t)a->num_seqs * max(pl.max_parts, 1))
                  : (unsigned)max(pl.max_parts, 1),
             flat ? 1u : (unsigned)a->num_seqs);
-  decode_mfma_kernel<Ty, D, BS, NW, KV8, false><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
+  decode_mfma_kernel<Ty, D, BS, NW, KV8, kDecode><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
       (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
       a->context_lens, (const uint16_t*)a->k_new, (const uint16_t*)a->v_new, a->num_q_heads,
       a->num_kv_heads, G, pl.groups, a->num_blocks, a->max_blocks_per_seq, a->max_context_len,
       a->scale * kLog2e, pl.P, max(pl.max_parts, 1), ws_acc, ws_ml, flat ? a->num_seqs : 0,
-      nullptr, 0, 0);
+      nullptr, 0, 0, pl.grp_start, pl.grp_len, pl.n_grp);
+}
+
+// Shared-prefix pass: grid x = tiles of 16 (member, head) slots of the
+// largest group, y = KV head, z = group; writes partial 0 of every member.
+template <typename Ty, int D, int BS, int NW, bool KV8>
+void launch_prefix(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* ws_ml,
+                   hipStream_t st) {
+  const int G = a->num_q_heads / a->num_kv_heads;
+  const int64_t tiles = ((int64_t)pl.max_group * G + 15) / 16;
+  dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)pl.n_grp);
+  decode_mfma_kernel<Ty, D, BS, NW, KV8, kPrefix><<<grid, 64 * NW, merge_lds_bytes(NW, 16, D), st>>>(
+      (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
+      a->context_lens, nullptr, nullptr, a->num_q_heads, a->num_kv_heads, G, 1, a->num_blocks,
+      a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, kChunk, pl.max_parts, ws_acc,
+      ws_ml, 0, nullptr, 0, a->num_seqs, pl.grp_start, pl.grp_len, pl.n_grp);
+}
+
+template <typename Ty, bool KV8, int D>
+void launch_prefix_bs(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
+                      hipStream_t st) {
+  switch (a->block_size) {
+    case 8: launch_prefix<Ty, D, 8, kWaves, KV8>(a, pl, wa, wm, st); break;
+    case 16: launch_prefix<Ty, D, 16, kWaves, KV8>(a, pl, wa, wm, st); break;
+    case 32: launch_prefix<Ty, D, 32, kWaves, KV8>(a, pl, wa, wm, st); break;
+    default: launch_prefix<Ty, D, 64, kWaves, KV8>(a, pl, wa, wm, st); break;
+  }
+}
+
+template <typename Ty, bool KV8>
+void launch_prefix_dims(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
+                        hipStream_t st) {
+  if (a->head_dim == 128) launch_prefix_bs<Ty, KV8, 128>(a, pl, wa, wm, st);
+  else launch_prefix_bs<Ty, KV8, 64>(a, pl, wa, wm, st);
 }
 
 // Prefill: grid x = tiles of 16 (row, head) slots of the longest chunk, y =
@@ -984,11 +1077,11 @@ void launch_prefill(const pa_prefill_args* a, hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
   const int64_t tiles = ((int64_t)a->max_query_len * G + 15) / 16;
   dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
-  decode_mfma_kernel<Ty, D, BS, NW, KV8, true><<<grid, 64 * NW, merge_lds_bytes(NW, 16, D), st>>>(
+  decode_mfma_kernel<Ty, D, BS, NW, KV8, kPrefill><<<grid, 64 * NW, merge_lds_bytes(NW, 16, D), st>>>(
       (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
       a->context_lens, nullptr, nullptr, a->num_q_heads, a->num_kv_heads, G, 1, a->num_blocks,
       a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, kChunk, 1, nullptr, nullptr, 0,
-      a->query_start, a->max_query_len, a->num_tokens);
+      a->query_start, a->max_query_len, a->num_tokens, nullptr, nullptr, 0);
 }
 
 template <typename Ty, bool KV8, int D>
@@ -1055,11 +1148,13 @@ void launch_merge(const pa_decode_args* a, const Plan& pl, const float* wa, cons
   if (pl.max_parts <= 16)
     merge_kernel<Store, D, 128><<<grid, 128, 0, st>>>(
         (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
-        a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts);
+        a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts, pl.grp_start, pl.grp_len,
+        pl.n_grp);
   else
     merge_kernel<Store, D, 512><<<grid, 512, 0, st>>>(
         (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
-        a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts);
+        a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts, pl.grp_start, pl.grp_len,
+        pl.n_grp);
 }
 
 template <typename Store>
@@ -1078,6 +1173,15 @@ pa_status run_plan(const pa_decode_args* a, const Plan& pl, hipStream_t hs) {
     ws_ml = ws_acc + (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * a->head_dim;
   }
   const bool kv8 = a->kv_dtype == PA_I8;
+  if (pl.n_grp > 0) {  // shared prefixes first: partial 0 of every member
+    if (a->dtype == PA_F16) {
+      if (kv8) launch_prefix_dims<F16, true>(a, pl, ws_acc, ws_ml, hs);
+      else launch_prefix_dims<F16, false>(a, pl, ws_acc, ws_ml, hs);
+    } else {
+      if (kv8) launch_prefix_dims<BF16, true>(a, pl, ws_acc, ws_ml, hs);
+      else launch_prefix_dims<BF16, false>(a, pl, ws_acc, ws_ml, hs);
+    }
+  }
   switch (a->dtype) {
     case PA_F16:
       if (kv8) launch_mfma_dims<F16, true>(a, pl, ws_acc, ws_ml, hs);
@@ -1093,7 +1197,7 @@ pa_status run_plan(const pa_decode_args* a, const Plan& pl, hipStream_t hs) {
   }
   pa_status st = launch_status();
   if (st != PA_OK) return st;
-  if (pl.max_parts > 1) {
+  if (pl.max_parts > 1 || pl.n_grp > 0) {
     switch (a->dtype) {
       case PA_F16: launch_merge_dims<Store16<F16>>(a, pl, ws_acc, ws_ml, hs); break;
       case PA_BF16: launch_merge_dims<Store16<BF16>>(a, pl, ws_acc, ws_ml, hs); break;
@@ -1119,6 +1223,29 @@ PA_API size_t pa_decode_workspace_bytes(const pa_decode_args* args) {
 PA_API int32_t pa_decode_partition_size(const pa_decode_args* args) {
   if (validate(args) != PA_OK) return -1;
   return make_plan(args).P;
+}
+
+// Plan of a decode with shared-prefix groups: one partial slot for the
+// prefix plus the decode partitions; always merged; no flat work list.
+static pa_status prefix_plan(const pa_decode_args* a, const pa_prefix_groups* g, Plan& pl) {
+  pa_status st = validate(a);
+  if (st != PA_OK) return st;
+  if (!g || g->num_groups < 0 || g->max_group_size < 0) return PA_ERR_INVALID;
+  if (a->dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  pl = make_plan(a);
+  if (g->num_groups == 0) return PA_OK;  // plain decode
+  if (!g->group_start || !g->prefix_len || g->max_group_size == 0 ||
+      g->max_group_size > a->num_seqs)
+    return PA_ERR_INVALID;
+  if (g->num_groups > 65535) return PA_ERR_UNSUPPORTED;
+  pl.grp_start = g->group_start;
+  pl.grp_len = g->prefix_len;
+  pl.n_grp = g->num_groups;
+  pl.max_group = g->max_group_size;
+  pl.flat = false;
+  pl.max_parts = 1 + (a->max_context_len + pl.P - 1) / pl.P;
+  pl.ws_bytes = (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * (a->head_dim + 2) * 4;
+  return PA_OK;
 }
 
 PA_API pa_status pa_prefill(const pa_prefill_args* a, void* stream) {
@@ -1156,6 +1283,31 @@ PA_API pa_status pa_prefill(const pa_prefill_args* a, void* stream) {
     else launch_prefill_dims<BF16, false>(a, hs);
   }
   return launch_status();
+}
+
+PA_API size_t pa_decode_prefix_workspace_bytes(const pa_decode_args* a,
+                                               const pa_prefix_groups* g) {
+  Plan pl;
+  return prefix_plan(a, g, pl) == PA_OK ? pl.ws_bytes : 0;
+}
+
+PA_API pa_status pa_decode_prefix(const pa_decode_args* a, const pa_prefix_groups* g,
+                                  void* stream) {
+  Plan pl;
+  pa_status st = prefix_plan(a, g, pl);
+  if (st != PA_OK) return st;
+  if (a->num_seqs == 0) return PA_OK;
+  if (!aligned16(a->out) || !aligned16(a->q) || !aligned16(a->k_cache) ||
+      !aligned16(a->v_cache) || !a->block_tables || !a->context_lens)
+    return PA_ERR_INVALID;
+  if (a->num_seqs > 65535 || pl.max_parts > 65535 || a->num_q_heads > 65535)
+    return PA_ERR_UNSUPPORTED;
+  if ((a->k_new == nullptr) != (a->v_new == nullptr)) return PA_ERR_INVALID;
+  if (a->k_new && (!aligned16(a->k_new) || !aligned16(a->v_new))) return PA_ERR_INVALID;
+  if (pl.ws_bytes &&
+      (!a->workspace || a->workspace_bytes < pl.ws_bytes || !aligned16(a->workspace)))
+    return PA_ERR_WORKSPACE;
+  return run_plan(a, pl, (hipStream_t)stream);
 }
 
 PA_API pa_status pa_decode(const pa_decode_args* a, void* stream) {

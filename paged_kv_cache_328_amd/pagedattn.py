@@ -67,6 +67,11 @@ class pa_prefill_args(ctypes.Structure):
     ]
 
 
+class pa_prefix_groups(ctypes.Structure):
+    _fields_ = [("group_start", _P), ("prefix_len", _P), ("num_groups", _I32),
+                ("max_group_size", _I32)]
+
+
 def lib():
     """Load libpagedattn.so and declare its signatures (raises if not built)."""
     global _lib
@@ -82,6 +87,8 @@ def lib():
         "pa_decode_partition_size": (_I32, [A]),
         "pa_decode": (ctypes.c_int, [A, _P]),
         "pa_prefill": (ctypes.c_int, [ctypes.POINTER(pa_prefill_args), _P]),
+        "pa_decode_prefix_workspace_bytes": (ctypes.c_size_t, [A, ctypes.POINTER(pa_prefix_groups)]),
+        "pa_decode_prefix": (ctypes.c_int, [A, ctypes.POINTER(pa_prefix_groups), _P]),
         "pa_write_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
         "pa_write_kv_i8": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                           _P]),
@@ -295,6 +302,62 @@ def prepare_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_
                           max_query_len, max_context_len)
     return PreparedCall("pa_prefill", lib().pa_prefill, (ctypes.byref(a), _stream(stream)),
                         (a, out, q, k_cache, v_cache, block_tables, context_lens, query_start))
+
+
+def make_prefix_groups(group_start, prefix_len, max_group_size):
+    """pa_prefix_groups from int32 device tensors: group_start [G + 1],
+    prefix_len [G] (tokens)."""
+    torch = _torch()
+    if group_start.dtype != torch.int32 or prefix_len.dtype != torch.int32:
+        raise TypeError("group_start and prefix_len must be int32")
+    G = prefix_len.shape[0]
+    if tuple(group_start.shape) != (G + 1,):
+        raise ValueError("group_start must be [num_groups + 1]")
+    g = pa_prefix_groups()
+    g.group_start, g.prefix_len = _ptr(group_start), _ptr(prefix_len)
+    g.num_groups, g.max_group_size = G, int(max_group_size)
+    return g
+
+
+def pa_decode_prefix_workspace_bytes(args, groups):
+    return int(lib().pa_decode_prefix_workspace_bytes(ctypes.byref(args), ctypes.byref(groups)))
+
+
+def pa_decode_prefix(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                     group_start, prefix_len, max_group_size, partition_size=0, workspace=None,
+                     stream=None, k_new=None, v_new=None):
+    """pa_decode for sequences ordered by shared-prefix group: group g is
+    sequences group_start[g]..group_start[g+1]-1 sharing their first
+    prefix_len[g] tokens; the prefix is read once per group."""
+    a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                         max_context_len, partition_size, workspace, k_new, v_new)
+    g = make_prefix_groups(group_start, prefix_len, max_group_size)
+    need = pa_decode_prefix_workspace_bytes(a, g)
+    if need and workspace is None:
+        workspace = _torch().zeros(need, dtype=_torch().uint8, device=q.device)
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = need
+    _check(lib().pa_decode_prefix(ctypes.byref(a), ctypes.byref(g), _stream(stream)),
+           "pa_decode_prefix")
+    return out
+
+
+def prepare_decode_prefix(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                          max_context_len, group_start, prefix_len, max_group_size,
+                          partition_size=0, stream=None, k_new=None, v_new=None):
+    a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                         max_context_len, partition_size, None, k_new, v_new)
+    g = make_prefix_groups(group_start, prefix_len, max_group_size)
+    need = pa_decode_prefix_workspace_bytes(a, g)
+    workspace = None
+    if need:
+        workspace = _torch().zeros(need, dtype=_torch().uint8, device=q.device)
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = need
+    return PreparedCall("pa_decode_prefix", lib().pa_decode_prefix,
+                        (ctypes.byref(a), ctypes.byref(g), _stream(stream)),
+                        (a, g, workspace, out, q, k_cache, v_cache, block_tables, context_lens,
+                         group_start, prefix_len, k_new, v_new))
 
 
 class PreparedCall:

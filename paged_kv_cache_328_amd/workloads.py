@@ -335,6 +335,33 @@ def random_case(seed, S, Hq, Hkv, D, BS, dtype, lens, NB=None, partition_size=0,
                    kv_dtype)
 
 
+def shared_prefix_case(seed, groups, Hq, Hkv, D, BS, dtype, kv_dtype=None, fill=True):
+    """Decode batch whose sequences share prefix blocks.  groups is a list of
+    (shared_blocks, [suffix tokens of each member]): a group's members point
+    their first shared_blocks table entries at the same physical blocks and
+    have private blocks for their own suffix.  Sequences are numbered group
+    by group.  Returns (DecodeCase, group_start, shared_tokens) with
+    shared_tokens[g] = shared_blocks * BS."""
+    rngs = _rngs(seed)
+    lens, starts, shared = [], [0], []
+    for nb, suffixes in groups:
+        for x in suffixes:
+            lens.append(nb * BS + int(x))
+        starts.append(starts[-1] + len(suffixes))
+        shared.append(nb * BS)
+    need = sum(nb for nb, _ in groups) + sum(-(-int(x) // BS) for _, sfx in groups for x in sfx)
+    NB = need + 4
+    it = iter(rngs["perm"].permutation(NB).tolist())
+    lists = []
+    for nb, suffixes in groups:
+        prefix = [next(it) for _ in range(nb)]
+        for x in suffixes:
+            lists.append(prefix + [next(it) for _ in range(-(-int(x) // BS))])
+    case = _finish("shared_prefix", dtype, len(lens), Hq, Hkv, D, BS, NB, 0, lens, [lists], rngs,
+                   fill, True, kv_dtype)
+    return case, np.asarray(starts, np.int32), np.asarray(shared, np.int32)
+
+
 @dataclass
 class PrefillCase:
     """A paged (chunked) prefill step: sequence s has context_lens[s] cached

@@ -258,3 +258,41 @@ def test_allocator_error_codes():
             call()
         assert e.value.status == status
     assert a.pa_seq_len(9) == -1 and a.pa_block_refcount(4) == -1
+
+
+def test_prefill_and_prefix_validation(L):
+    import ctypes
+    a = pa.pa_prefill_args()
+    a.num_seqs, a.num_tokens, a.num_q_heads, a.num_kv_heads = 2, 4, 8, 2
+    a.head_dim, a.block_size, a.num_blocks, a.max_blocks_per_seq = 128, 16, 10, 4
+    a.max_query_len, a.max_context_len, a.scale = 3, 64, 0.1
+    a.dtype = a.kv_dtype = pa.PA_BF16
+    assert L.pa_prefill(a, None) == pa.PA_ERR_INVALID          # null tensors
+    a.num_tokens = 0
+    assert L.pa_prefill(a, None) == pa.PA_OK                   # nothing to do
+    a.num_tokens = 4
+    a.dtype = a.kv_dtype = pa.PA_F32
+    assert L.pa_prefill(a, None) == pa.PA_ERR_UNSUPPORTED
+    a.dtype, a.kv_dtype = pa.PA_BF16, pa.PA_F16
+    assert L.pa_prefill(a, None) == pa.PA_ERR_INVALID          # mixed 16-bit types
+    a.kv_dtype, a.block_size = pa.PA_I8, 24
+    assert L.pa_prefill(a, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_prefill(None, None) == pa.PA_ERR_INVALID
+
+    d = _args(partition_size=32)
+    g = pa.pa_prefix_groups()
+    assert L.pa_decode_prefix(d, None, None) == pa.PA_ERR_INVALID
+    g.num_groups, g.max_group_size = 2, 2
+    assert L.pa_decode_prefix(d, ctypes.byref(g), None) == pa.PA_ERR_INVALID  # null group arrays
+    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 0
+    buf = (ctypes.c_int32 * 4)()
+    g.group_start = g.prefix_len = ctypes.addressof(buf)
+    # one partial slot for the prefix plus 160 / 32 = 5 partitions
+    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 4 * 8 * 6 * 130 * 4
+    g.max_group_size = 5  # more than num_seqs
+    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 0
+    g.num_groups, g.max_group_size = 0, 0  # plain decode
+    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == L.pa_decode_workspace_bytes(d)
+    f = _args(dtype=pa.PA_F32)
+    g.num_groups, g.max_group_size = 1, 1
+    assert L.pa_decode_prefix(f, ctypes.byref(g), None) == pa.PA_ERR_UNSUPPORTED
