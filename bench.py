@@ -372,7 +372,8 @@ def bench_shared_prefix(args, dev):
             gst = torch.tensor([0, n], dtype=torch.int32, device=dev)
             pl = torch.tensor([int(shared[r])], dtype=torch.int32, device=dev)
             calls.append(pa.prepare_decode_prefix(out, q, kd, vd, tables, lens, case.scale, max_ctx,
-                                                  gst, pl, n, stream=stream, k_new=kn, v_new=vn))
+                                                  gst, pl, n, int(shared[r]), stream=stream,
+                                                  k_new=kn, v_new=vn))
         else:
             calls.append(pa.prepare_decode(out, q, kd, vd, tables, lens, case.scale, max_ctx,
                                            stream=stream, k_new=kn, v_new=vn))

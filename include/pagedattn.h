@@ -176,8 +176,9 @@ PA_API pa_status pa_decode(const pa_decode_args* args, void* stream);
  * physical slots through their tables, which the copy-on-write rules keep
  * true for whole shared blocks.  The shared prefix is attended once per
  * group (its K/V read once, every member's query heads as the matrix-core
- * columns), each member's remaining tokens as in pa_decode, and the two
- * parts merged with the log-sum-exp rule.  The output equals pa_decode's up
+ * columns, split into partitions like a long context), each member's
+ * remaining tokens as in pa_decode, and the parts merged with the
+ * log-sum-exp rule.  The output equals pa_decode's up
  * to rounding order.
  * Preconditions (device contents): group_start[0] = 0, non-decreasing,
  * group_start[num_groups] = num_seqs; 0 <= prefix_len[g] <= the context of
@@ -193,7 +194,8 @@ typedef struct pa_prefix_groups {
   const int32_t* group_start;   /* [num_groups + 1] device */
   const int32_t* prefix_len;    /* [num_groups] device, tokens */
   int32_t num_groups;
-  int32_t max_group_size;
+  int32_t max_group_size;       /* host bound of the group sizes */
+  int32_t max_prefix_len;       /* host bound of prefix_len, <= max_context_len */
 } pa_prefix_groups;
 
 PA_API size_t pa_decode_prefix_workspace_bytes(const pa_decode_args* args,

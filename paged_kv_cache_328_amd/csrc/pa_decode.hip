@@ -210,17 +210,20 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   int hk, grp = 0, p = 0, s, c;
   int q0 = 0, nq = 0, tile = 0;  // slot modes: first row, rows, slot tile
   if constexpr (GRP) {
-    // Shared-prefix pass: x = tile of 16 (member, head) slots, y = KV head, z
-    // = group.  The members are sequences q0 .. q0 + nq - 1; the first one's
-    // table holds the shared blocks, keys [0, grp_len[g]).
+    // Shared-prefix pass: x = tile of 16 (member, head) slots, y = partition
+    // of the prefix, z = group * Hkv + KV head.  The members are sequences
+    // q0 .. q0 + nq - 1; the first one's table holds the shared blocks, keys
+    // [0, grp_len[g]) in partitions of P tokens.
     tile = blockIdx.x;
-    hk = blockIdx.y;
-    const int g = blockIdx.z;
+    p = blockIdx.y;
+    const int g = blockIdx.z / Hkv;
+    hk = blockIdx.z - g * Hkv;
     q0 = clampi(grp_start[g], 0, num_rows);
     nq = clampi(grp_start[g + 1] - q0, 0, num_rows - q0);
     if (tile * 16 >= nq * G) return;
     s = q0;
-    c = clampi(grp_len[g], 0, min(max_ctx, max_blocks * BS));
+    c = clampi(grp_len[g], 0, min(min(max_ctx, max_blocks * BS), (int)gridDim.y * P));
+    if (p * P >= c) return;
   } else if constexpr (PRE) {
     // Prefill: x = tile of 16 (query row, head) slots, y = KV head, z =
     // sequence.  Slot u = 16 * tile + i is row q0 + u / G, query head
@@ -260,9 +263,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       if (grp_start[mid] <= s) lo = mid;
       else hi = mid - 1;
     }
-    skip = uniform(clampi(grp_len[lo], 0, c));
+    // (max_q carries the prefix's partial slots here: skip never needs more)
+    skip = uniform(clampi(grp_len[lo], 0, min(c, max_q * P)));
   }
-  const int pb = skip > 0 ? 1 : 0;  // first partial slot of this launch
+  const int pb = (skip + P - 1) / P;  // partial slots of the prefix come first
   // Chunks start on 32-token boundaries: the partitions run from the boundary
   // at or below skip, and tokens below skip are dropped.
   const int a_skip = skip & ~(kChunk - 1);
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
                        : (append ? max(c - 1, 0) : c);
   const int lim_min = GRP ? c : PRE ? c - nq + (tile * 16) / G + 1 : cc;
   const bool has_new = append && c > 0 && c - 1 >= t_begin && c - 1 < t_begin + P;
-  const int t_end = PRE ? cc : min(cc, t_begin + P);
+  const int t_end = PRE && !GRP ? cc : min(cc, t_begin + P);
   const int n_chunks = max(0, t_end - t_begin + kChunk - 1) / kChunk;
 
   // Columns: decode, query heads qh0 + i of the group; prefill, slots.
@@ -726,7 +730,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
                             (uint32_t)Ty::from_f32(r[2]) | ((uint32_t)Ty::from_f32(r[3]) << 16)};
       *reinterpret_cast<u32x2*>(out + row * D + d) = packed;
     } else {
-      const int64_t idx = row * max_parts + (GRP ? 0 : pb + p);
+      const int64_t idx = row * max_parts + (GRP ? p : pb + p);
       *reinterpret_cast<f32x4*>(ws_acc + idx * D + d) = sum;
       if (d == 0) {
         float Mh = -INFINITY;
@@ -848,7 +852,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(
     typename Store::T* __restrict__ out, const int32_t* __restrict__ lens,
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, int Hq, int max_ctx,
     int max_blocks, int BS, int P, int max_parts, const int32_t* __restrict__ grp_start,
-    const int32_t* __restrict__ grp_len, int n_grp) {
+    const int32_t* __restrict__ grp_len, int n_grp, int pre_parts) {
   constexpr int C4 = D / 4;                   // threads per partition row
   constexpr int ROWS = NT / C4;               // partitions read at once
   constexpr int U = 8;                        // partitions per thread per batch
@@ -881,9 +885,9 @@ __global__ __launch_bounds__(NT) void merge_kernel(
       if (grp_start[mid] <= s) lo = mid;
       else hi = mid - 1;
     }
-    skip = clampi(grp_len[lo], 0, c);
+    skip = clampi(grp_len[lo], 0, min(c, pre_parts * P));
   }
-  const int n_p = (skip > 0 ? 1 : 0) + (c - (skip & ~(kChunk - 1)) + P - 1) / P;
+  const int n_p = (skip + P - 1) / P + (c - (skip & ~(kChunk - 1)) + P - 1) / P;
   if (n_p <= 1 && skip == 0) return;  // pass 1 stored the output itself
 #pragma unroll
   for (int k = 0; k < U; ++k)
@@ -945,6 +949,7 @@ struct Plan {
   const int32_t* grp_len = nullptr;
   int n_grp = 0;
   int max_group = 0;
+  int pre_parts = 0;  // partitions of the longest shared prefix
 };
 
 pa_status validate(const pa_decode_args* a) {
@@ -1034,7 +1039,7 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
       a->context_lens, (const uint16_t*)a->k_new, (const uint16_t*)a->v_new, a->num_q_heads,
       a->num_kv_heads, G, pl.groups, a->num_blocks, a->max_blocks_per_seq, a->max_context_len,
       a->scale * kLog2e, pl.P, max(pl.max_parts, 1), ws_acc, ws_ml, flat ? a->num_seqs : 0,
-      nullptr, 0, 0, pl.grp_start, pl.grp_len, pl.n_grp);
+      nullptr, pl.pre_parts, 0, pl.grp_start, pl.grp_len, pl.n_grp);
 }
 
 // Shared-prefix pass: grid x = tiles of 16 (member, head) slots of the
@@ -1044,11 +1049,11 @@ void launch_prefix(const pa_decode_args* a, const Plan& pl, float* ws_acc, float
                    hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
   const int64_t tiles = ((int64_t)pl.max_group * G + 15) / 16;
-  dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)pl.n_grp);
+  dim3 grid((unsigned)tiles, (unsigned)pl.pre_parts, (unsigned)(pl.n_grp * a->num_kv_heads));
   decode_mfma_kernel<Ty, D, BS, NW, KV8, kPrefix><<<grid, 64 * NW, merge_lds_bytes(NW, 16, D), st>>>(
       (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
       a->context_lens, nullptr, nullptr, a->num_q_heads, a->num_kv_heads, G, 1, a->num_blocks,
-      a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, kChunk, pl.max_parts, ws_acc,
+      a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, pl.P, pl.max_parts, ws_acc,
       ws_ml, 0, nullptr, 0, a->num_seqs, pl.grp_start, pl.grp_len, pl.n_grp);
 }
 
@@ -1149,12 +1154,12 @@ void launch_merge(const pa_decode_args* a, const Plan& pl, const float* wa, cons
     merge_kernel<Store, D, 128><<<grid, 128, 0, st>>>(
         (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
         a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts, pl.grp_start, pl.grp_len,
-        pl.n_grp);
+        pl.n_grp, pl.pre_parts);
   else
     merge_kernel<Store, D, 512><<<grid, 512, 0, st>>>(
         (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
         a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts, pl.grp_start, pl.grp_len,
-        pl.n_grp);
+        pl.n_grp, pl.pre_parts);
 }
 
 template <typename Store>
@@ -1235,15 +1240,17 @@ static pa_status prefix_plan(const pa_decode_args* a, const pa_prefix_groups* g,
   pl = make_plan(a);
   if (g->num_groups == 0) return PA_OK;  // plain decode
   if (!g->group_start || !g->prefix_len || g->max_group_size == 0 ||
-      g->max_group_size > a->num_seqs)
+      g->max_group_size > a->num_seqs || g->max_prefix_len < 0 ||
+      g->max_prefix_len > a->max_context_len)
     return PA_ERR_INVALID;
-  if (g->num_groups > 65535) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)g->num_groups * a->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   pl.grp_start = g->group_start;
   pl.grp_len = g->prefix_len;
   pl.n_grp = g->num_groups;
   pl.max_group = g->max_group_size;
   pl.flat = false;
-  pl.max_parts = 1 + (a->max_context_len + pl.P - 1) / pl.P;
+  pl.pre_parts = max(1, (g->max_prefix_len + pl.P - 1) / pl.P);
+  pl.max_parts = pl.pre_parts + (a->max_context_len + pl.P - 1) / pl.P;
   pl.ws_bytes = (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * (a->head_dim + 2) * 4;
   return PA_OK;
 }

@@ -287,8 +287,12 @@ def test_prefill_and_prefix_validation(L):
     assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 0
     buf = (ctypes.c_int32 * 4)()
     g.group_start = g.prefix_len = ctypes.addressof(buf)
-    # one partial slot for the prefix plus 160 / 32 = 5 partitions
-    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 4 * 8 * 6 * 130 * 4
+    g.max_prefix_len = 64
+    # 64 / 32 = 2 partial slots for the prefix plus 160 / 32 = 5 partitions
+    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 4 * 8 * 7 * 130 * 4
+    g.max_prefix_len = 161  # beyond max_context_len
+    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 0
+    g.max_prefix_len = 64
     g.max_group_size = 5  # more than num_seqs
     assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 0
     g.num_groups, g.max_group_size = 0, 0  # plain decode

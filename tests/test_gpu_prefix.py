@@ -56,7 +56,7 @@ def run_prefix_case(case, group_start, prefix_len, label, fused=False, partition
     announce(f"{label}: pa_decode_prefix max_group={max_group} P={partition_size}")
     pa.pa_decode_prefix(out, qd, kd, vd, ints_to_dev(tables), ints_to_dev(lens), case.scale,
                         case.max_context, ints_to_dev(group_start), ints_to_dev(prefix_len),
-                        max_group, partition_size=partition_size, **extra)
+                        max_group, int(np.max(prefix_len)), partition_size=partition_size, **extra)
     _sync()
     if fused:
         live = slots >= 0
