@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
     q0 = clampi(qstart[s], 0, num_rows);
     nq = clampi(qstart[s + 1] - q0, 0, min(min(max_q, c), num_rows - q0));
-    if (tile * 16 >= nq * G) return;
+    if (tile * 16 * NW >= nq * G) return;
   } else if (num_seqs > 0) {
     hk = blockIdx.x / n_groups;
     grp = blockIdx.x - hk * n_groups;
@@ -279,11 +279,17 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   // column i sees keys [0, lim) (its position + 1); the chunk loop reads up to
   // the tile's largest limit and masks per column from its smallest on.
   const bool append = !PRE && k_new != nullptr;
-  const int slots = PRE ? nq * G - tile * 16 : 0;  // valid slots of a tile
+  // First slot of this wave's columns: in prefill each wave owns 16 slots of
+  // the workgroup's 16 * NW and reads all of their keys itself (the waves
+  // stream the same K/V lines together, so the CU's L1 serves most of them);
+  // the other modes share 16 slots among the waves, which split the keys.
+  const int sb = MODE == kPrefill ? (tile * NW + w) * 16 : tile * 16;
+  if (MODE == kPrefill && sb >= nq * G) return;  // no barrier follows in prefill
+  const int slots = PRE ? nq * G - sb : 0;  // valid slots of this wave's tile
   const int cc = GRP ? c
-                 : PRE ? c - nq + (tile * 16 + min(slots, 16) - 1) / G + 1
+                 : PRE ? c - nq + (sb + min(slots, 16) - 1) / G + 1
                        : (append ? max(c - 1, 0) : c);
-  const int lim_min = GRP ? c : PRE ? c - nq + (tile * 16) / G + 1 : cc;
+  const int lim_min = GRP ? c : PRE ? c - nq + sb / G + 1 : cc;
   const bool has_new = append && c > 0 && c - 1 >= t_begin && c - 1 < t_begin + P;
   const int t_end = PRE && !GRP ? cc : min(cc, t_begin + P);
   const int n_chunks = max(0, t_end - t_begin + kChunk - 1) / kChunk;
@@ -292,12 +298,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   const int Gv = PRE ? min(slots, 16) : min(16, G - grp * 16);  // valid columns
   const bool head_ok = i < Gv;
   const int qh0 = hk * G + grp * 16;     // first query head of the group (decode)
-  const int u_i = tile * 16 + i;         // prefill slot of column i
+  const int u_i = sb + i;                // slot of column i
   const int lim = GRP ? c : PRE ? (head_ok ? c - nq + u_i / G + 1 : cc) : cc;  // keys [0, lim) of column i
   // q / out row (times Hq, plus head) of column `col`
   auto out_row = [&](int col) -> int64_t {
     if constexpr (PRE) {
-      const int u = tile * 16 + col;
+      const int u = sb + col;
       return (int64_t)(q0 + u / G) * Hq + hk * G + u % G;
     } else {
       return (int64_t)s * Hq + qh0 + col;
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   constexpr int CPB = 64 / BPC;                         // chunks per batch
   // Chunks are dealt to the waves round-robin (the intelliparadigm page's
   // warp-to-block assignment, section 4.2, with a wave taking 32 tokens).
-  auto chunk_of = [&](int k) { return w + NW * k; };  // the wave's k-th chunk
+  auto chunk_of = [&](int k) { return MODE == kPrefill ? k : w + NW * k; };  // the wave's k-th chunk
   int tbl = 0;
   auto load_batch = [&](int k0) {
     const int ch = chunk_of(k0 + lane / BPC);
@@ -372,6 +378,20 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
   // Token tau of the chunk (0..31) sits in block tau / BS of the chunk at row
   // tau % BS; a block of 64 tokens holds the whole chunk from row t0 % 64.
   auto issue = [&](const int (&b)[BPC], int t0, Raw<KK, MM, KV8>& r) {
+    // prefill: ordinary loads (the waves of a workgroup read the same lines);
+    // otherwise non-temporal (each byte is read once per step)
+    auto ld16 = [](const void* a) -> u32x4 {
+      if constexpr (MODE == kPrefill) return load16(a);
+      else return stream16(a);
+    };
+    auto ld8 = [](const void* a) -> u32x2 {
+      if constexpr (MODE == kPrefill) return *reinterpret_cast<const u32x2*>(a);
+      else return stream8(a);
+    };
+    auto ldf4 = [](const void* a) -> f32x4 {
+      if constexpr (MODE == kPrefill) return *reinterpret_cast<const f32x4*>(a);
+      else return stream_f4(a);
+    };
     const int r0 = BS > kChunk ? t0 % BS : 0;
     auto at = [&](int tau, int64_t& off, int& row) {  // tile offset and row of token tau
       int id = b[0];
@@ -391,30 +411,30 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
     if constexpr (!KV8) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        r.k[0][kk] = stream16(kc + ok0 + ((4 * kk + g4) * BS + rk0) * 8);
-        r.k[1][kk] = stream16(kc + ok1 + ((4 * kk + g4) * BS + rk1) * 8);
+        r.k[0][kk] = ld16(kc + ok0 + ((4 * kk + g4) * BS + rk0) * 8);
+        r.k[1][kk] = ld16(kc + ok1 + ((4 * kk + g4) * BS + rk1) * 8);
       }
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream16(vc + ov + (16 * mm + i) * BS + rv);
+      for (int mm = 0; mm < MM; ++mm) r.v[mm] = ld16(vc + ov + (16 * mm + i) * BS + rv);
     } else {
       // K codes: one 16-byte x-vector 4*k2 + g4 (channels 16*(4*k2+g4)..+16)
       // of the token's row feeds products 2*k2 and 2*k2 + 1.
 #pragma unroll
       for (int k2 = 0; k2 < KK / 2; ++k2) {
-        const u32x4 a = stream16(kc + ok0 + ((4 * k2 + g4) * BS + rk0) * 16);
-        const u32x4 c = stream16(kc + ok1 + ((4 * k2 + g4) * BS + rk1) * 16);
+        const u32x4 a = ld16(kc + ok0 + ((4 * k2 + g4) * BS + rk0) * 16);
+        const u32x4 c = ld16(kc + ok1 + ((4 * k2 + g4) * BS + rk1) * 16);
         r.k[0][2 * k2] = u32x2{a[0], a[1]};
         r.k[0][2 * k2 + 1] = u32x2{a[2], a[3]};
         r.k[1][2 * k2] = u32x2{c[0], c[1]};
         r.k[1][2 * k2 + 1] = u32x2{c[2], c[3]};
       }
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream8(vc + ov + (16 * mm + i) * BS + rv);
+      for (int mm = 0; mm < MM; ++mm) r.v[mm] = ld8(vc + ov + (16 * mm + i) * BS + rv);
       constexpr int SC = I8Tile<D, BS>::kScales;
-      r.sk[0] = stream_f4(kc + os0 + SC + 4 * rs0);
-      r.sk[1] = stream_f4(kc + os1 + SC + 4 * rs1);
-      r.sv[0] = stream_f4(vc + os0 + SC + 4 * rs0);
-      r.sv[1] = stream_f4(vc + os1 + SC + 4 * rs1);
+      r.sk[0] = ldf4(kc + os0 + SC + 4 * rs0);
+      r.sk[1] = ldf4(kc + os1 + SC + 4 * rs1);
+      r.sv[0] = ldf4(vc + os0 + SC + 4 * rs0);
+      r.sv[1] = ldf4(vc + os1 + SC + 4 * rs1);
     }
   };
   // Both products and the online-softmax update for the chunk at token t0.
@@ -689,6 +709,21 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
 
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
+
+  if constexpr (MODE == kPrefill) {
+    // The wave's columns are its own: normalise and store (lane (i, g4)
+    // holds output channels 16*mm + 4*g4 .. +3 of column i).
+    if (head_ok) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* orow = out + out_row(i) * D + 4 * g4;
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm) {
+        const f32x4 r = acc[mm] * inv;
+        *reinterpret_cast<u32x2*>(orow + 16 * mm) = u32x2{Ty::pack2(r[0], r[1]), Ty::pack2(r[2], r[3])};
+      }
+    }
+    return;
+  }
 
   // Merge the NW waves: M = max_w m_w per head, then every wave rescales its
   // sum and output by 2^(m_w - M) into LDS and the workgroup adds them up in
@@ -1080,9 +1115,9 @@ void launch_prefix_dims(const pa_decode_args* a, const Plan& pl, float* wa, floa
 template <typename Ty, int D, int BS, int NW, bool KV8>
 void launch_prefill(const pa_prefill_args* a, hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
-  const int64_t tiles = ((int64_t)a->max_query_len * G + 15) / 16;
+  const int64_t tiles = ((int64_t)a->max_query_len * G + 16 * NW - 1) / (16 * NW);
   dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
-  decode_mfma_kernel<Ty, D, BS, NW, KV8, kPrefill><<<grid, 64 * NW, merge_lds_bytes(NW, 16, D), st>>>(
+  decode_mfma_kernel<Ty, D, BS, NW, KV8, kPrefill><<<grid, 64 * NW, 0, st>>>(
       (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
       a->context_lens, nullptr, nullptr, a->num_q_heads, a->num_kv_heads, G, 1, a->num_blocks,
       a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, kChunk, 1, nullptr, nullptr, 0,
