@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64],
                     help="tokens per cache block (the workloads are defined at 16; the pool keeps "
                          "its bytes)")
+    ap.add_argument("--no-host-lens", action="store_true",
+                    help="do not pass the host copy of the context lengths (the library then "
+                         "launches every (sequence, partition) pair max_context_len allows)")
     ap.add_argument("--calib-bytes", type=int, default=0,
                     help="first run one plain device-to-device copy of this many bytes (a "
                          "known-size reference for hardware byte counters)")
@@ -133,9 +136,13 @@ def main():
     # arguments are marshalled once per replica; the timed loop only enqueues
     outs = [torch.empty_like(qs[0]) for _ in range(R)]
     fused = not args.separate_write
+    # the scheduler's host copy of the lengths lets the library launch only
+    # the (sequence, partition) units that exist
+    host_lens = None if args.no_host_lens else case.context_lens
     decode = [pa.prepare_decode(outs[r], qs[r], kd, vd, tables[r], lens, case.scale, max_ctx,
                                 partition_size=P, stream=stream,
-                                k_new=knew[r] if fused else None, v_new=vnew[r] if fused else None)
+                                k_new=knew[r] if fused else None, v_new=vnew[r] if fused else None,
+                                context_lens_host=host_lens)
               for r in range(R)]
     write = [pa.prepare_write_kv(knew[r], vnew[r], kd, vd, slots[r], stream=stream) for r in range(R)]
     if fused:
@@ -233,6 +240,7 @@ def main():
                    "head_dim": case.D, "block_size": case.BS, "num_blocks": case.NB,
                    "context_tokens": int(case.context_lens.sum()),
                    "max_context": max_ctx, "partition_size": P_eff, "replicas": R,
+                   "host_context_lens": host_lens is not None,
                    "kv_bytes_per_step": kv_bytes,
                    "step": ("pa_copy_blocks(0 pairs) + pa_decode(fused append of the new token)"
                             if fused else "pa_copy_blocks(0 pairs) + %s + pa_decode"
@@ -376,7 +384,9 @@ def bench_shared_prefix(args, dev):
                                                   k_new=kn, v_new=vn))
         else:
             calls.append(pa.prepare_decode(out, q, kd, vd, tables, lens, case.scale, max_ctx,
-                                           stream=stream, k_new=kn, v_new=vn))
+                                           stream=stream, k_new=kn, v_new=vn,
+                                           context_lens_host=None if args.no_host_lens
+                                           else lens_all[rows]))
     for i in range(args.warmup):
         calls[i % R]()
     torch.cuda.synchronize()

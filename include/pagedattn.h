@@ -154,9 +154,21 @@ typedef struct pa_decode_args {
    * pa_dtype) with f16 / bf16 queries.  With PA_I8 a fused append quantises
    * the new token as pa_write_kv_i8 does; k_new / v_new stay of dtype. */
   int32_t kv_dtype;
+  /* Optional host copy of context_lens ([num_seqs] int32 in host memory,
+   * NULL = none), read during the call.  From the device lengths the library
+   * knows only the bound max_context_len, so it launches a workgroup for
+   * every (sequence, partition) pair that bound allows and the surplus ones
+   * exit at once; given the host copy, the 16-bit and INT8 kernels launch
+   * only the pairs that exist.  Values outside [0, max_context_len] return
+   * PA_ERR_INVALID.  The values must equal the device ones: where they
+   * differ, the outputs are undefined (no access leaves the arguments'
+   * buffers either way).  A launch recorded into a graph keeps the shape it
+   * was recorded with, so leave this NULL under capture. */
+  const int32_t* context_lens_host;
 } pa_decode_args;
 
-/* Bytes of workspace pa_decode needs for these sizes (pointers are not read).
+/* Bytes of workspace pa_decode needs for these sizes (device pointers are
+ * not read; a context_lens_host copy is checked).
  * 0 when the step needs none, or when the arguments are invalid. */
 PA_API size_t pa_decode_workspace_bytes(const pa_decode_args* args);
 

@@ -985,6 +985,9 @@ struct Plan {
   int n_grp = 0;
   int max_group = 0;
   int pre_parts = 0;  // partitions of the longest shared prefix
+  // (sequence, partition) units of the flat work list, from the host copy of
+  // the context lengths (0 = unknown: the grid covers num_seqs * max_parts)
+  int64_t units = 0;
 };
 
 pa_status validate(const pa_decode_args* a) {
@@ -1008,6 +1011,10 @@ pa_status validate(const pa_decode_args* a) {
   if (a->block_size != 8 && a->block_size != 16 && a->block_size != 32 && a->block_size != 64)
     return PA_ERR_UNSUPPORTED;
   if (a->dtype == PA_F32 && a->partition_size > kMaxF32Part) return PA_ERR_UNSUPPORTED;
+  if (a->context_lens_host)
+    for (int s = 0; s < a->num_seqs; ++s)
+      if (a->context_lens_host[s] < 0 || a->context_lens_host[s] > a->max_context_len)
+        return PA_ERR_INVALID;
   return PA_OK;
 }
 
@@ -1047,6 +1054,11 @@ Plan make_plan(const pa_decode_args* a) {
   // (sequence, partition) slot.
   pl.flat = pl.max_parts >= 4 && a->num_seqs <= 1024 &&
             (int64_t)a->num_seqs * pl.max_parts <= 65535;
+  if (pl.flat && a->context_lens_host) {
+    // the kernel's own count: every sequence has max(ceil(c / P), 1) units
+    for (int s = 0; s < a->num_seqs; ++s)
+      pl.units += max((a->context_lens_host[s] + pl.P - 1) / pl.P, 1);
+  }
   if (pl.max_parts > 1)
     pl.ws_bytes = (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * (a->head_dim + 2) * 4;
   return pl;
@@ -1066,7 +1078,7 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
   const int G = a->num_q_heads / a->num_kv_heads;
   const bool flat = pl.flat;
   dim3 grid((unsigned)(a->num_kv_heads * pl.groups),
-            flat ? (unsigned)((int64_t)a->num_seqs * max(pl.max_parts, 1))
+            flat ? (unsigned)(pl.units > 0 ? pl.units : (int64_t)a->num_seqs * max(pl.max_parts, 1))
                  : (unsigned)max(pl.max_parts, 1),
             flat ? 1u : (unsigned)a->num_seqs);
   decode_mfma_kernel<Ty, D, BS, NW, KV8, kDecode><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(

@@ -52,7 +52,7 @@ class pa_decode_args(ctypes.Structure):
         ("block_size", _I32), ("num_blocks", _I32), ("max_blocks_per_seq", _I32),
         ("max_context_len", _I32), ("scale", ctypes.c_float), ("dtype", _I32),
         ("partition_size", _I32), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
-        ("k_new", _P), ("v_new", _P), ("kv_dtype", _I32),
+        ("k_new", _P), ("v_new", _P), ("kv_dtype", _I32), ("context_lens_host", _P),
     ]
 
 
@@ -192,10 +192,14 @@ def cache_geometry(k_cache, v_cache, head_dim=None):
 
 
 def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                     max_context_len, partition_size=0, workspace=None, k_new=None, v_new=None):
+                     max_context_len, partition_size=0, workspace=None, k_new=None, v_new=None,
+                     context_lens_host=None):
     """Fill a pa_decode_args from tensors (no call into the library).
     k_new / v_new ([S, Hkv, D], optional): the step's new token of every
-    sequence, appended at position context_lens[s] - 1 by pa_decode itself."""
+    sequence, appended at position context_lens[s] - 1 by pa_decode itself.
+    context_lens_host (optional): the context lengths as a host sequence,
+    equal to the device ones; the library then launches only the work that
+    exists.  The struct keeps the int32 copy it points to alive."""
     S, Hq, Dq = q.shape
     NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, Dq)
     i8 = is_i8(k_cache)
@@ -228,6 +232,13 @@ def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale
         if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
             raise TypeError("k_new / v_new must have q's dtype")
         a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
+    if context_lens_host is not None:
+        import numpy as np
+        host = np.ascontiguousarray(np.asarray(context_lens_host, dtype=np.int32))
+        if host.shape != (S,):
+            raise ValueError("context_lens_host must hold num_seqs lengths")
+        a._lens_host = host
+        a.context_lens_host = host.ctypes.data
     return a
 
 
@@ -240,13 +251,15 @@ def pa_decode_partition_size(args):
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-              partition_size=0, workspace=None, stream=None, k_new=None, v_new=None):
+              partition_size=0, workspace=None, stream=None, k_new=None, v_new=None,
+              context_lens_host=None):
     """Paged decode attention into `out` (with k_new / v_new: fused append of
     the step's token at position context_lens[s] - 1).  When the step needs
     split-K partials and no workspace is given, a byte tensor is allocated with
     torch on q's device."""
     a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                         max_context_len, partition_size, workspace, k_new, v_new)
+                         max_context_len, partition_size, workspace, k_new, v_new,
+                         context_lens_host)
     need = pa_decode_workspace_bytes(a)
     if need and workspace is None:
         workspace = _torch().zeros(need, dtype=_torch().uint8, device=q.device)
@@ -375,11 +388,13 @@ class PreparedCall:
 
 
 def prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-                   partition_size=0, workspace=None, stream=None, k_new=None, v_new=None):
+                   partition_size=0, workspace=None, stream=None, k_new=None, v_new=None,
+                   context_lens_host=None):
     """pa_decode with its argument struct filled once; the workspace (when
     the step needs one) is allocated here."""
     a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                         max_context_len, partition_size, workspace, k_new, v_new)
+                         max_context_len, partition_size, workspace, k_new, v_new,
+                         context_lens_host)
     need = pa_decode_workspace_bytes(a)
     if need and workspace is None:
         workspace = _torch().zeros(need, dtype=_torch().uint8, device=q.device)

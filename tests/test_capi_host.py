@@ -58,6 +58,24 @@ def _args(**over):
 def test_decode_rejects_bad_arguments_before_launch(L, over, status):
     a = _args(**over)
     assert L.pa_decode(a, None) == status
+
+
+def test_decode_checks_the_host_copy_of_context_lens(L):
+    """A host copy of the context lengths must lie in [0, max_context_len];
+    it does not change the workspace size."""
+    import numpy as np
+    base = L.pa_decode_workspace_bytes(_args(partition_size=32))
+    assert base > 0
+    good = np.array([0, 5, 160, 33], np.int32)
+    a = _args(partition_size=32, context_lens_host=good.ctypes.data)
+    assert L.pa_decode_workspace_bytes(a) == base
+    assert L.pa_decode_partition_size(a) == 32
+    for bad in ([0, 5, 161, 33], [0, -1, 3, 3]):
+        arr = np.array(bad, np.int32)
+        a = _args(partition_size=32, context_lens_host=arr.ctypes.data)
+        assert L.pa_decode_workspace_bytes(a) == 0
+        assert L.pa_decode_partition_size(a) == -1
+        assert L.pa_decode(a, None) == pa.PA_ERR_INVALID
     assert L.pa_decode_workspace_bytes(a) == 0
     assert L.pa_decode_partition_size(a) == -1
 

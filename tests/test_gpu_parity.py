@@ -16,7 +16,7 @@ from paged_kv_cache_328_amd import pagedattn as pa
 from paged_kv_cache_328_amd import workloads as wl
 import tests._gpu as _g
 from tests._gpu import (TOL, announce, check_attention, ints_to_dev, poison_tails, same_bits,
-                        to_dev, to_host, torch_dtype)
+                        tail_slots, to_dev, to_host, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -401,6 +401,55 @@ def test_split_merge_repeats_bit_for_bit():
             first = got
             check_attention(got, want, dtype, "split merge repeats")
         assert same_bits(got, first), f"launch {rep} differs from launch 0"
+
+
+@pytest.mark.parametrize("kv", [None, "i8"])
+@pytest.mark.parametrize("P", [0, 256])
+def test_host_context_lens_size_the_grid_bit_identical(kv, P):
+    """With the host copy of the context lengths the library launches only the
+    (sequence, partition) units that exist; the units compute what they
+    computed in the full grid, so the output is bit-identical to the call
+    without it, and matches the oracle (lengths 0..6000, log-uniform, with
+    the fused append)."""
+    import torch
+    from tests.test_gpu_int8 import poison_scales
+    rng = np.random.default_rng(78)
+    lens = np.exp(rng.uniform(np.log(2), np.log(6000), size=62)).astype(int).tolist() + [0, 1]
+    dtype, i8 = "bf16", kv == "i8"
+    case = wl.random_case(905, len(lens), 32, 8, 128, 16, dtype, lens, partition_size=P, kv_dtype=kv)
+    t0 = np.ascontiguousarray(case.block_tables[0])
+    if i8:
+        poison_scales(case.k_cache, case.v_cache, tail_slots(t0, case.context_lens, case.BS),
+                      case.Hkv, case.D, case.BS)
+    else:
+        poison_tails(oracle, case.k_cache, case.v_cache, t0, case.context_lens, dtype)
+    pool_t = "u8" if i8 else dtype
+    kd, vd = to_dev(case.k_cache, pool_t), to_dev(case.v_cache, pool_t)
+    qd = to_dev(case.q[0], dtype)
+    kn, vn = to_dev(case.new_k[0], dtype), to_dev(case.new_v[0], dtype)
+    td, ld = ints_to_dev(t0), ints_to_dev(case.context_lens)
+    outs = []
+    for host in (None, case.context_lens):
+        announce(f"host lens kv={kv} P={P} host={'yes' if host is not None else 'no'}")
+        out = torch.empty_like(qd)
+        pa.pa_decode(out, qd, kd, vd, td, ld, case.scale, case.max_context, partition_size=P,
+                     k_new=kn, v_new=vn, context_lens_host=host)
+        _sync()
+        outs.append(to_host(out, dtype))
+    assert same_bits(outs[0], outs[1]), "host copy of the lengths changed the output"
+    q = np.ascontiguousarray(case.q[0])
+    slots = np.ascontiguousarray(case.slot_mapping[0])
+    if i8:
+        oracle.write_kv_i8(np.ascontiguousarray(case.new_k[0]), np.ascontiguousarray(case.new_v[0]),
+                           dtype, case.k_cache, case.v_cache, slots, case.D, case.BS)
+        want = oracle.decode_i8(q, dtype, case.k_cache, case.v_cache, t0, case.context_lens,
+                                case.scale, case.D, case.BS, num_threads=16)
+    else:
+        oracle.write_kv(np.ascontiguousarray(case.new_k[0]), np.ascontiguousarray(case.new_v[0]),
+                        case.k_cache, case.v_cache, slots, dtype)
+        want = oracle.decode(q, case.k_cache, case.v_cache, t0, case.context_lens, case.scale, dtype,
+                             num_threads=16)
+    check_attention(outs[1], want, dtype, f"host lens kv={kv} P={P}")
 
 
 def test_large_logits_stay_finite():
