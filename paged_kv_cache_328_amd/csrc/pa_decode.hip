@@ -126,8 +126,8 @@ __device__ __forceinline__ u32x2 stream8(const void* p) {
 __device__ __forceinline__ uint32_t stream4(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
-__device__ __forceinline__ f32x4 stream_f4(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+__device__ __forceinline__ float stream_f1(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const float*>(p));
 }
 
 // INT8 codes -> 16-bit operand values (8 codes, exact: Ty::codes4).
@@ -169,7 +169,7 @@ struct Raw<KK, MM, true> {
   u32x2 k[2][KK];  // 8 codes of tile-0 / tile-1 token i, channels 8*m..+8 with
                    // m = 8*(kk/2) + 2*g4 + kk%2 (half kk%2 of one 16-byte x-vector)
   u32x2 v[MM];     // 8 codes: channel 16*mm + i, tokens 8*g4..+8
-  f32x4 sk[2], sv[2];  // K / V scales of tokens 4*g4..+3 of tile 0 / tile 1
+  float sc;        // lane L < 32: K scale of the chunk's token L; else V scale of token L - 32
 };
 
 // Modes of the 16-bit kernel: decode (one query per sequence; with prefix
@@ -179,7 +179,7 @@ struct Raw<KK, MM, true> {
 constexpr int kDecode = 0, kPrefill = 1, kPrefix = 2;
 
 template <typename Ty, int D, int BS, int NW, bool KV8, int MODE>
-__global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3 : 1))) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
     const void* __restrict__ vcv, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_new,
@@ -388,9 +388,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       if constexpr (MODE == kPrefill) return *reinterpret_cast<const u32x2*>(a);
       else return stream8(a);
     };
-    auto ldf4 = [](const void* a) -> f32x4 {
-      if constexpr (MODE == kPrefill) return *reinterpret_cast<const f32x4*>(a);
-      else return stream_f4(a);
+    auto ldf1 = [](const void* a) -> float {
+      if constexpr (MODE == kPrefill) return *reinterpret_cast<const float*>(a);
+      else return stream_f1(a);
     };
     const int r0 = BS > kChunk ? t0 % BS : 0;
     auto at = [&](int tau, int64_t& off, int& row) {  // tile offset and row of token tau
@@ -401,13 +401,11 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       off = (int64_t)id * blk_stride + head_off;
       row = BS >= kChunk ? r0 + tau : tau % BS;
     };
-    int64_t ok0, ok1, ov, os0, os1;
-    int rk0, rk1, rv, rs0, rs1;
+    int64_t ok0, ok1, ov;
+    int rk0, rk1, rv;
     at(i, ok0, rk0);               // K operand of tile 0: token i
     at(16 + i, ok1, rk1);          // tile 1: token 16 + i
     at(8 * g4, ov, rv);            // V^T operand: tokens 8*g4..+8 (one block row)
-    at(4 * g4, os0, rs0);          // scales of tokens 4*g4..+3 of tile 0
-    at(16 + 4 * g4, os1, rs1);     // and of tile 1
     if constexpr (!KV8) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
@@ -430,11 +428,14 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       }
 #pragma unroll
       for (int mm = 0; mm < MM; ++mm) r.v[mm] = ld8(vc + ov + (16 * mm + i) * BS + rv);
+      // Scales: one per lane (the chunk's 32 K scales, then its 32 V
+      // scales); consume hands each lane the ones it needs by lane shuffles,
+      // which keeps one register per chunk in flight instead of sixteen.
       constexpr int SC = I8Tile<D, BS>::kScales;
-      r.sk[0] = ldf4(kc + os0 + SC + 4 * rs0);
-      r.sk[1] = ldf4(kc + os1 + SC + 4 * rs1);
-      r.sv[0] = ldf4(vc + os0 + SC + 4 * rs0);
-      r.sv[1] = ldf4(vc + os1 + SC + 4 * rs1);
+      int64_t osc;
+      int rsc;
+      at(lane & 31, osc, rsc);
+      r.sc = ldf1((lane < 32 ? kc : vc) + osc + SC + 4 * rsc);
     }
   };
   // Both products and the online-softmax update for the chunk at token t0.
@@ -450,9 +451,16 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
         s1 = Ty::mma(__builtin_bit_cast(V8, codes_to_operand<Ty>(r.k[1][kk])), qop[kk], s1);
       }
     }
+    // INT8: V scales of this lane's tokens 4*g4 + (e & 3) + 16 * (e >> 2)
+    float sv[8];
     if constexpr (KV8) {  // logits of INT8 keys: code dot q times the token's scale
-      s0 *= r.sk[0];
-      s1 *= r.sk[1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s0[j] *= __shfl(r.sc, 4 * g4 + j);
+        s1[j] *= __shfl(r.sc, 16 + 4 * g4 + j);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = __shfl(r.sc, 32 + 16 * (e >> 2) + 4 * g4 + (e & 3));
     }
     // x[e]: base-2 logit for head i of token t0 + 4*g4 + e (e < 4) or
     // t0 + 16 + 4*g4 + e - 4 (e >= 4): reduction index 8*g4 + e of the PV product.
@@ -481,7 +489,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       } else {  // and their V scales (codes are finite; a scale may be NaN)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (x[e] == -INFINITY) r.sv[e >> 2][e & 3] = 0.f;
+          if (x[e] == -INFINITY) sv[e] = 0.f;
       }
     }
 
@@ -525,7 +533,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(
       for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(x[e] - m_use);
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
-        const float s0 = r.sv[wd >> 1][(2 * wd) & 3], s1 = r.sv[wd >> 1][(2 * wd + 1) & 3];
+        const float s0 = sv[2 * wd], s1 = sv[2 * wd + 1];
         pw[wd] = Ty::pack2(pr[2 * wd] * s0, pr[2 * wd + 1] * s1);
         psum += s0 != 0.f ? Ty::lo_f32(pw[wd]) * __builtin_amdgcn_rcpf(s0) : pr[2 * wd];
         psum += s1 != 0.f ? Ty::hi_f32(pw[wd]) * __builtin_amdgcn_rcpf(s1) : pr[2 * wd + 1];
