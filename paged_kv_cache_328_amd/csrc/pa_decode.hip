@@ -560,27 +560,42 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
 
   // Chunk loop.  All loads of a chunk are issued before any of them is used
   // (the scheduling barrier keeps the compiler from interleaving the
-  // products with the loads), and the loads of the wave's next chunk (and
-  // the table entries of the one after) are issued before the current chunk
-  // is used: two chunks in flight per wave.
+  // products with the loads).  16-bit caches: the loads of the wave's next
+  // chunk (and the table entries of the one after) are issued before the
+  // current chunk is used, two chunks in flight per wave.  INT8 caches: one
+  // chunk at a time (measured on MI355X: with half the bytes per chunk, the
+  // look-ahead made the step 4% slower; without it the kernel needs fewer
+  // registers and more waves fit).
   int nb[BPC] = {};
   int ch = chunk_of(0);
   if (ch < n_chunks) block_ids(0, nb);
-  Raw<KK, MM, KV8> cur, nxt;
-  if (ch < n_chunks) {
-    issue(nb, t_begin + ch * kChunk, cur);
-    if (chunk_of(1) < n_chunks) block_ids(1, nb);
-  }
-  for (int k = 0; ch < n_chunks; ++k) {
-    const int ch1 = chunk_of(k + 1);
-    if (ch1 < n_chunks) {
-      issue(nb, t_begin + ch1 * kChunk, nxt);
-      if (chunk_of(k + 2) < n_chunks) block_ids(k + 2, nb);
+  if constexpr (KV8) {
+    for (int k = 0; ch < n_chunks; ++k) {
+      Raw<KK, MM, KV8> one;
+      issue(nb, t_begin + ch * kChunk, one);
+      const int ch1 = chunk_of(k + 1);
+      if (ch1 < n_chunks) block_ids(k + 1, nb);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(t_begin + ch * kChunk, one);
+      ch = ch1;
     }
-    __builtin_amdgcn_sched_barrier(0);
-    consume(t_begin + ch * kChunk, cur);
-    cur = nxt;
-    ch = ch1;
+  } else {
+    Raw<KK, MM, KV8> cur, nxt;
+    if (ch < n_chunks) {
+      issue(nb, t_begin + ch * kChunk, cur);
+      if (chunk_of(1) < n_chunks) block_ids(1, nb);
+    }
+    for (int k = 0; ch < n_chunks; ++k) {
+      const int ch1 = chunk_of(k + 1);
+      if (ch1 < n_chunks) {
+        issue(nb, t_begin + ch1 * kChunk, nxt);
+        if (chunk_of(k + 2) < n_chunks) block_ids(k + 2, nb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      consume(t_begin + ch * kChunk, cur);
+      cur = nxt;
+      ch = ch1;
+    }
   }
 
   // Fused append: that wave adds token c - 1 to its running state on the
