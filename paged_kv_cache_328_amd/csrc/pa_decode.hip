@@ -802,6 +802,264 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
 }
 
 // ----------------------------------------------------------------------------
+// Paged prefill with K/V staged through LDS (16-bit caches).  A workgroup of
+// NW waves takes 16 * NC * NW (row, head) slots of one sequence and KV head;
+// wave w owns slots sb .. sb + 16*NC - 1 (NC column groups of 16).  The
+// workgroup walks the keys in 32-token chunks: all threads load a chunk's K
+// and V (16-byte vectors in the pool's order, coalesced) into registers,
+// store them into one of two LDS buffers, and every wave reads its matrix-core
+// operands from there, so each K/V byte crosses L1 once per workgroup rather
+// than once per wave.  Two chunks are in flight while one is computed.
+// The LDS order is swizzled so that the operand reads (16 bytes per lane,
+// 16 lanes on 16 tokens or channels) hit distinct banks:
+//   K vector (token tau, x-vector j) at tau * XV + (j ^ (tau % XV)),
+//   V vector (channel d, tokens 8*qd..+8) at d * 4 + (qd ^ ((d / 2) % 4)).
+// Arithmetic per column as in decode_mfma_kernel's prefill mode.
+// ----------------------------------------------------------------------------
+template <typename Ty, int D, int BS, int NW, int NC>
+__global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ lens, const int32_t* __restrict__ qstart, int Hq, int Hkv, int G,
+    int NB, int max_blocks, int max_ctx, int max_q, int num_rows, float scale_log2) {
+  static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
+  using V8 = typename Ty::vec8;
+  constexpr int KK = D / 32;           // QK products along head_dim
+  constexpr int MM = D / 16;           // PV products along head_dim
+  constexpr int XV = D / 8;            // 16-byte vectors per K row (one token)
+  constexpr int CV = kChunk * XV;      // 16-byte vectors of a chunk's K (and of its V)
+  constexpr int PER = CV / (64 * NW);  // K (and V) vectors each thread moves per chunk
+  static_assert(PER * 64 * NW == CV, "chunk vectors split evenly over the threads");
+  constexpr int TILE = D * BS;
+  constexpr int BPC = BS >= kChunk ? 1 : kChunk / BS;  // blocks per chunk
+  constexpr int CPB = 64 / BPC;                         // chunks per batch of table entries
+  __shared__ u32x4 lk[2][CV];
+  __shared__ u32x4 lv[2][CV];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
+  const int i = lane & 15;
+  const int g4 = lane >> 4;
+  const int tile = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
+  const int c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
+  const int q0 = clampi(qstart[s], 0, num_rows);
+  const int nq = clampi(qstart[s + 1] - q0, 0, min(min(max_q, c), num_rows - q0));
+  const int swg = tile * NW * NC * 16;  // first slot of the workgroup
+  if (swg >= nq * G) return;            // the whole workgroup: no barrier reached yet
+  // Slot u is chunk row u / G (position c - nq + u / G), query head hk*G + u % G.
+  const int last = min(nq * G, swg + NW * NC * 16) - 1;  // last slot of the workgroup
+  const int n_chunks = (c - nq + last / G + 1 + kChunk - 1) / kChunk;  // chunks the workgroup loads
+  const int sb = swg + w * NC * 16;                // the wave's first slot
+  const int slots = nq * G - sb;                   // may be <= 0: the wave only loads
+  const int cc = slots > 0 ? c - nq + (sb + min(slots, 16 * NC) - 1) / G + 1 : 0;  // keys it needs
+  const int lim_min = slots > 0 ? c - nq + sb / G + 1 : 0;
+  const int n_mine = (cc + kChunk - 1) / kChunk;   // chunks this wave computes
+
+  int Gv[NC], lim[NC];
+  bool head_ok[NC];
+#pragma unroll
+  for (int nc = 0; nc < NC; ++nc) {
+    Gv[nc] = clampi(slots - 16 * nc, 0, 16);
+    head_ok[nc] = i < Gv[nc];
+    lim[nc] = head_ok[nc] ? c - nq + (sb + 16 * nc + i) / G + 1 : cc;
+  }
+  auto out_row = [&](int col) -> int64_t {
+    const int u = sb + col;
+    return (int64_t)(q0 + u / G) * Hq + hk * G + u % G;
+  };
+  V8 qop[NC][KK];
+#pragma unroll
+  for (int nc = 0; nc < NC; ++nc) {
+    const uint16_t* qrow = q + out_row(head_ok[nc] ? 16 * nc + i : 0) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4 raw = head_ok[nc] ? load16(qrow + 8 * (4 * kk + g4)) : u32x4{0u, 0u, 0u, 0u};
+      qop[nc][kk] = __builtin_bit_cast(V8, raw);
+    }
+  }
+  f32x4 acc[NC][MM];
+  float m_run[NC], l_run[NC];
+#pragma unroll
+  for (int nc = 0; nc < NC; ++nc) {
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) acc[nc][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[nc] = -INFINITY;
+    l_run[nc] = 0.f;
+  }
+
+  // Block ids in registers, as in decode: lane j holds block j % BPC of chunk
+  // (batch start) + j / BPC; entries past the loaded range read as block 0.
+  const int32_t* trow = tables + (int64_t)s * max_blocks;
+  const int64_t blk_stride = (int64_t)Hkv * TILE;
+  const int64_t head_off = (int64_t)hk * TILE;
+  const int c_load = c - nq + last / G + 1;  // tokens the workgroup loads
+  int tbl = 0;
+  auto load_batch = [&](int k0) {
+    const int ch = k0 + lane / BPC;
+    const int t = ch * kChunk + (lane % BPC) * BS;
+    tbl = ch < n_chunks && t < c_load ? clampi(trow[t / BS], 0, NB - 1) : 0;
+  };
+  load_batch(0);
+
+  // This thread's share of chunk k: vector g = tid + 64*NW*r of K (x-vector
+  // g / 32, token g % 32: 16 consecutive lanes read 16 consecutive tokens of
+  // one x-vector, 256 contiguous bytes) and of V (channel g / 4, tokens
+  // 8*(g % 4)..+8: consecutive lanes read consecutive bytes of a block row).
+  auto gload = [&](int k, u32x4 (&kr)[PER], u32x4 (&vr)[PER]) {
+    if (k > 0 && k % CPB == 0) load_batch(k);
+    const int e = (k % CPB) * BPC;
+    int b[BPC];
+#pragma unroll
+    for (int j = 0; j < BPC; ++j) b[j] = __builtin_amdgcn_readlane(tbl, e + j);
+    const int r0 = BS > kChunk ? (k * kChunk) % BS : 0;
+    auto at = [&](int tau, int64_t& off, int& row) {  // tile offset and row of token tau
+      int id = b[0];
+#pragma unroll
+      for (int j = 1; j < BPC; ++j)
+        if (tau / BS == j) id = b[j];
+      off = (int64_t)id * blk_stride + head_off;
+      row = BS >= kChunk ? r0 + tau : tau % BS;
+    };
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int g = tid + 64 * NW * r;
+      int64_t off;
+      int row;
+      at(g % kChunk, off, row);
+      kr[r] = load16(kc + off + ((g / kChunk) * BS + row) * 8);
+      at(8 * (g & 3), off, row);
+      vr[r] = load16(vc + off + (g >> 2) * BS + row);
+    }
+  };
+  auto swrite = [&](int buf, const u32x4 (&kr)[PER], const u32x4 (&vr)[PER]) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int g = tid + 64 * NW * r;
+      const int tau = g % kChunk, j = g / kChunk;
+      lk[buf][tau * XV + (j ^ (tau % XV))] = kr[r];
+      const int d = g >> 2, qd = g & 3;
+      lv[buf][d * 4 + (qd ^ ((d >> 1) & 3))] = vr[r];
+    }
+  };
+
+  // The wave's products and online-softmax update for chunk k (in buf).
+  auto compute = [&](int k, int buf) {
+    const int t0 = k * kChunk;
+    u32x4 kop[2][KK], vop[MM];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int tau = 16 * t + i, j = 4 * kk + g4;
+        kop[t][kk] = lk[buf][tau * XV + (j ^ (tau % XV))];
+      }
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) {
+      const int d = 16 * mm + i;
+      vop[mm] = lv[buf][d * 4 + (g4 ^ ((d >> 1) & 3))];
+    }
+    const bool edge = t0 + kChunk > lim_min;
+    if (edge) {  // zero the V bits of tokens past the wave's keys (they may hold NaN)
+      uint32_t keep[4];  // V word wd holds tokens t0 + 8*g4 + 2*wd, +1
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd)
+        keep[wd] = (t0 + 8 * g4 + 2 * wd < cc ? 0x0000FFFFu : 0u) |
+                   (t0 + 8 * g4 + 2 * wd + 1 < cc ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm)
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) vop[mm][wd] &= keep[wd];
+    }
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) {
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s0 = Ty::mma(__builtin_bit_cast(V8, kop[0][kk]), qop[nc][kk], s0);
+        s1 = Ty::mma(__builtin_bit_cast(V8, kop[1][kk]), qop[nc][kk], s1);
+      }
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = s0[j] * scale_log2;
+        x[4 + j] = s1[j] * scale_log2;
+      }
+      if (edge) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= lim[nc]) x[e] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (__builtin_amdgcn_ballot_w64(mx > m_run[nc] + kSlack) != 0) {
+        const float m_new = fmaxf(m_run[nc], mx);
+        const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run[nc] - m_new);
+        m_run[nc] = m_new;
+        l_run[nc] *= alpha;
+#pragma unroll
+        for (int mm = 0; mm < MM; ++mm) acc[nc][mm] *= alpha;
+      }
+      const float m_use = m_run[nc] == -INFINITY ? 0.f : m_run[nc];
+      uint32_t pw[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        pw[wd] = Ty::pack2(exp2_fast(x[2 * wd] - m_use), exp2_fast(x[2 * wd + 1] - m_use));
+        psum += Ty::lo_f32(pw[wd]) + Ty::hi_f32(pw[wd]);
+      }
+      l_run[nc] += psum;
+      const auto a32 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+      const auto b32 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+      const auto a16 = __builtin_amdgcn_permlane16_swap(a32[0], a32[1], false, false);
+      const auto b16 = __builtin_amdgcn_permlane16_swap(b32[0], b32[1], false, false);
+      const V8 pop = __builtin_bit_cast(V8, u32x4{a16[0], b16[0], a16[1], b16[1]});
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm)
+        acc[nc][mm] = Ty::mma(__builtin_bit_cast(V8, vop[mm]), pop, acc[nc][mm]);
+    }
+  };
+
+  // Chunk k is computed from buffer k % 2 while chunks k + 1 (in registers)
+  // and k + 2 (being loaded) are in flight; the barrier after each step makes
+  // the next chunk visible and frees the buffer just read.  Every wave takes
+  // every barrier (n_chunks is the workgroup's).
+  u32x4 ka[PER], va[PER], kb[PER], vb[PER];
+  gload(0, ka, va);
+  if (1 < n_chunks) gload(1, kb, vb);
+  swrite(0, ka, va);
+  __syncthreads();
+  for (int k = 0; k < n_chunks; k += 2) {
+    if (k + 2 < n_chunks) gload(k + 2, ka, va);
+    if (k < n_mine) compute(k, 0);
+    if (k + 1 < n_chunks) swrite(1, kb, vb);
+    __syncthreads();
+    if (k + 1 >= n_chunks) break;
+    if (k + 3 < n_chunks) gload(k + 3, kb, vb);
+    if (k + 1 < n_mine) compute(k + 1, 1);
+    if (k + 2 < n_chunks) swrite(0, ka, va);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int nc = 0; nc < NC; ++nc) {
+    float l_tot = l_run[nc] + __shfl_xor(l_run[nc], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (head_ok[nc]) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* orow = out + out_row(16 * nc + i) * D + 4 * g4;
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm) {
+        const f32x4 r = acc[nc][mm] * inv;
+        *reinterpret_cast<u32x2*>(orow + 16 * mm) = u32x2{Ty::pack2(r[0], r[1]), Ty::pack2(r[2], r[3])};
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // fp32 pass 1 (vector ALU).  One wave per (partition, query head, sequence).
 // Logits of the partition go to LDS, then the weights, then each lane
 // accumulates whole channels.  K layout for fp32: [NB, Hkv, D/4, BS, 4].
@@ -1147,16 +1405,33 @@ void launch_prefix_dims(const pa_decode_args* a, const Plan& pl, float* wa, floa
 
 // Prefill: grid x = tiles of 16 (row, head) slots of the longest chunk, y =
 // KV head, z = sequence; no split-K (each tile's key range is its own).
+// Column groups of 16 slots per wave of the LDS prefill kernel.
+#ifndef PA_PREFILL_GROUPS
+#define PA_PREFILL_GROUPS 2
+#endif
+constexpr int kLdsGroups = PA_PREFILL_GROUPS;
+
 template <typename Ty, int D, int BS, int NW, bool KV8>
 void launch_prefill(const pa_prefill_args* a, hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
-  const int64_t tiles = ((int64_t)a->max_query_len * G + 16 * NW - 1) / (16 * NW);
-  dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
-  decode_mfma_kernel<Ty, D, BS, NW, KV8, kPrefill><<<grid, 64 * NW, 0, st>>>(
-      (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
-      a->context_lens, nullptr, nullptr, a->num_q_heads, a->num_kv_heads, G, 1, a->num_blocks,
-      a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, kChunk, 1, nullptr, nullptr, 0,
-      a->query_start, a->max_query_len, a->num_tokens, nullptr, nullptr, 0);
+  if constexpr (!KV8) {
+    // 16-bit caches: K/V staged through LDS, 16 * kLdsGroups slots per wave
+    const int64_t tiles = ((int64_t)a->max_query_len * G + 16 * kLdsGroups * NW - 1) / (16 * kLdsGroups * NW);
+    dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
+    prefill_lds_kernel<Ty, D, BS, NW, kLdsGroups><<<grid, 64 * NW, 0, st>>>(
+        (uint16_t*)a->out, (const uint16_t*)a->q, (const uint16_t*)a->k_cache,
+        (const uint16_t*)a->v_cache, a->block_tables, a->context_lens, a->query_start,
+        a->num_q_heads, a->num_kv_heads, G, a->num_blocks, a->max_blocks_per_seq,
+        a->max_context_len, a->max_query_len, a->num_tokens, a->scale * kLog2e);
+  } else {
+    const int64_t tiles = ((int64_t)a->max_query_len * G + 16 * NW - 1) / (16 * NW);
+    dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
+    decode_mfma_kernel<Ty, D, BS, NW, KV8, kPrefill><<<grid, 64 * NW, 0, st>>>(
+        (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
+        a->context_lens, nullptr, nullptr, a->num_q_heads, a->num_kv_heads, G, 1, a->num_blocks,
+        a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, kChunk, 1, nullptr, nullptr, 0,
+        a->query_start, a->max_query_len, a->num_tokens, nullptr, nullptr, 0);
+  }
 }
 
 template <typename Ty, bool KV8, int D>
