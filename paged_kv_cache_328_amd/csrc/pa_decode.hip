@@ -57,6 +57,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 32;          // tokens per step of the 16-bit kernel
 constexpr int kMaxF32Part = 1024;   // largest partition of the fp32 kernel
 constexpr float kSlack = 8.f;       // base-2 headroom of the 16-bit kernel's running max
+constexpr int kXcds = 8;            // accelerator dies (each with its own L2) of an MI355X
 
 __device__ __forceinline__ u32x2 load8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
@@ -841,7 +842,25 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
   const int w = uniform(tid >> 6);
   const int i = lane & 15;
   const int g4 = lane >> 4;
-  const int tile = blockIdx.x, hk = blockIdx.y, s = blockIdx.z;
+  // Workgroups are dealt to the 8 XCDs round-robin, and each XCD has its own
+  // L2.  The linear id is remapped so that the consecutive workgroups of one
+  // XCD are the slot tiles of one (sequence, KV head) -- they read the same
+  // K/V lines at about the same time, through one L2 -- while the (sequence,
+  // KV head) pairs are dealt to the XCDs round-robin (balanced work).
+  int tile, hk, s;
+  {
+    const int X = gridDim.x, Y = gridDim.y;
+    const int L = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
+    int grp = L / X;
+    tile = L % X;
+    if ((Y * (int)gridDim.z) % kXcds == 0) {
+      const int n = L / kXcds;  // the workgroup's place on its XCD
+      tile = n % X;
+      grp = (n / X) * kXcds + L % kXcds;
+    }
+    hk = grp % Y;
+    s = grp / Y;
+  }
   const int c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
   const int q0 = clampi(qstart[s], 0, num_rows);
   const int nq = clampi(qstart[s + 1] - q0, 0, min(min(max_q, c), num_rows - q0));
@@ -1004,13 +1023,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
       }
       const float m_use = m_run[nc] == -INFINITY ? 0.f : m_run[nc];
       uint32_t pw[4];
-      float psum = 0.f;
+      float psum = l_run[nc];
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
         pw[wd] = Ty::pack2(exp2_fast(x[2 * wd] - m_use), exp2_fast(x[2 * wd + 1] - m_use));
-        psum += Ty::lo_f32(pw[wd]) + Ty::hi_f32(pw[wd]);
+        psum = Ty::sum2(pw[wd], psum);  // the weights the PV product sees
       }
-      l_run[nc] += psum;
+      l_run[nc] = psum;
       const auto a32 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
       const auto b32 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
       const auto a16 = __builtin_amdgcn_permlane16_swap(a32[0], a32[1], false, false);

@@ -34,6 +34,11 @@ struct F16 {
   }
   static __device__ __forceinline__ float lo_f32(uint32_t w) { return to_f32((uint16_t)w); }
   static __device__ __forceinline__ float hi_f32(uint32_t w) { return to_f32((uint16_t)(w >> 16)); }
+  // acc + both halves of a packed pair, in one dot-product instruction
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), f16x2{(_Float16)1.f, (_Float16)1.f},
+                                  acc, false);
+  }
   // four signed bytes -> four f16 (two packed words), exactly: with the sign
   // bit flipped a byte is c + 128 in [1, 255]; as the mantissa under 0x64 it
   // reads 1024 + c + 128, and subtracting 1152 leaves c (all values exact).
@@ -63,6 +68,10 @@ struct BF16 {
   }
   static __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
   static __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+  static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
+  }
   // four signed bytes -> four bf16, exactly (|c| <= 128 needs 8 significant bits)
   static __device__ __forceinline__ u32x2 codes4(uint32_t c) {
     return u32x2{pack2((float)(int8_t)c, (float)(int8_t)(c >> 8)),
