@@ -250,7 +250,8 @@ def main():
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(case.name + (":i8" if i8 else "")
-                                                 + (f":bs{case.BS}" if case.BS != 16 else ""), P_eff, fused),
+                                                 + (f":bs{case.BS}" if case.BS != 16 else ""), P_eff, fused,
+                                                 host_lens is not None),
                      "avg_launch_ms": round(decode_ms, 5),
                      "algorithmic_bytes_per_launch": decode_bytes},
         "host_bookkeeping_us": round(host_us, 2),
@@ -464,17 +465,19 @@ def cpu_baseline_prefill(case, kd, vd, budget_s):
                       f"{cores} OpenMP threads"}
 
 
-def measured_traffic(workload, partition_size, fused):
-    """HBM bytes per pa_decode launch from the committed rocprofv3 byte
-    counters (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE, each scaled by
-    what the counter reads for a plain copy of known size), or None when no
-    record matches this launch or the kernel sources changed since."""
+def measured_traffic(workload, partition_size, fused, host_lens):
+    """HBM bytes per pa_decode call (pass 1 and, when split, the merge) from
+    the committed rocprofv3 byte counters (profiles/traffic.json: FETCH_SIZE
+    and WRITE_SIZE, each scaled by what the counter reads for a plain copy of
+    known size), or None when no record matches this launch or the kernel
+    sources changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(workload)
-    if not rec or rec.get("partition_size") != partition_size or rec.get("fused_append") != fused:
+    if (not rec or rec.get("partition_size") != partition_size or rec.get("fused_append") != fused
+            or rec.get("host_context_lens") != host_lens):
         return None
     h = hashlib.sha256()
     for f in ["paged_kv_cache_328_amd/csrc/pa_decode.hip", "paged_kv_cache_328_amd/csrc/pa_device.h"]:
