@@ -174,10 +174,9 @@ struct Raw<KK, MM, true> {
 };
 
 // Modes of the 16-bit kernel: decode (one query per sequence; with prefix
-// groups, the keys after the group's shared prefix), prefill (chunk rows,
-// causal) and the shared-prefix pass (the group's members over the shared
-// blocks).
-constexpr int kDecode = 0, kPrefill = 1, kPrefix = 2;
+// groups, the keys after the group's shared prefix) and the shared-prefix
+// pass (the group's members over the shared blocks).
+constexpr int kDecode = 0, kPrefix = 1;
 
 template <typename Ty, int D, int BS, int NW, bool KV8, int MODE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3 : 1))) void decode_mfma_kernel(
@@ -186,11 +185,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
     const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, int Hq, int Hkv, int G, int n_groups, int NB,
     int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
-    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs,
-    const int32_t* __restrict__ qstart, int max_q, int num_rows,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs, int max_q, int num_rows,
     const int32_t* __restrict__ grp_start, const int32_t* __restrict__ grp_len, int n_grp) {
-  constexpr bool PRE = MODE != kDecode;   // columns are slots with their own rows
-  constexpr bool GRP = MODE == kPrefix;
+  constexpr bool GRP = MODE == kPrefix;  // columns are (member, head) slots
   static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
   static_assert(D % 32 == 0, "head_dim multiple of 32");
   using V8 = typename Ty::vec8;
@@ -225,17 +222,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
     s = q0;
     c = clampi(grp_len[g], 0, min(min(max_ctx, max_blocks * BS), (int)gridDim.y * P));
     if (p * P >= c) return;
-  } else if constexpr (PRE) {
-    // Prefill: x = tile of 16 (query row, head) slots, y = KV head, z =
-    // sequence.  Slot u = 16 * tile + i is row q0 + u / G, query head
-    // hk * G + u % G, at position c - nq + u / G.
-    tile = blockIdx.x;
-    hk = blockIdx.y;
-    s = blockIdx.z;
-    c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
-    q0 = clampi(qstart[s], 0, num_rows);
-    nq = clampi(qstart[s + 1] - q0, 0, min(min(max_q, c), num_rows - q0));
-    if (tile * 16 * NW >= nq * G) return;
   } else if (num_seqs > 0) {
     hk = blockIdx.x / n_groups;
     grp = blockIdx.x - hk * n_groups;
@@ -271,39 +257,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
   // Chunks start on 32-token boundaries: the partitions run from the boundary
   // at or below skip, and tokens below skip are dropped.
   const int a_skip = skip & ~(kChunk - 1);
-  const int n_p = PRE ? 1 : (c - a_skip + P - 1) / P;
-  if (!PRE && (p < 0 || p >= max(n_p, 1))) return;
+  const int n_p = GRP ? 1 : (c - a_skip + P - 1) / P;
+  if (!GRP && (p < 0 || p >= max(n_p, 1))) return;
   const int t_begin = a_skip + p * P;
   // With a fused append the token at c - 1 comes from k_new / v_new, not from
   // the cache: the chunk loop reads [t_begin, cc) and the new token is added
-  // afterwards by the workgroup whose partition holds it.  In prefill, slot
-  // column i sees keys [0, lim) (its position + 1); the chunk loop reads up to
-  // the tile's largest limit and masks per column from its smallest on.
-  const bool append = !PRE && k_new != nullptr;
-  // First slot of this wave's columns: in prefill each wave owns 16 slots of
-  // the workgroup's 16 * NW and reads all of their keys itself (the waves
-  // stream the same K/V lines together, so the CU's L1 serves most of them);
-  // the other modes share 16 slots among the waves, which split the keys.
-  const int sb = MODE == kPrefill ? (tile * NW + w) * 16 : tile * 16;
-  if (MODE == kPrefill && sb >= nq * G) return;  // no barrier follows in prefill
-  const int slots = PRE ? nq * G - sb : 0;  // valid slots of this wave's tile
-  const int cc = GRP ? c
-                 : PRE ? c - nq + (sb + min(slots, 16) - 1) / G + 1
-                       : (append ? max(c - 1, 0) : c);
-  const int lim_min = GRP ? c : PRE ? c - nq + sb / G + 1 : cc;
+  // afterwards by the workgroup whose partition holds it.
+  const bool append = !GRP && k_new != nullptr;
+  const int sb = tile * 16;                 // shared-prefix pass: first slot of the tile
+  const int slots = GRP ? nq * G - sb : 0;  // valid slots of the tile
+  const int cc = GRP ? c : (append ? max(c - 1, 0) : c);  // keys [0, cc) come from the cache
   const bool has_new = append && c > 0 && c - 1 >= t_begin && c - 1 < t_begin + P;
-  const int t_end = PRE && !GRP ? cc : min(cc, t_begin + P);
+  const int t_end = min(cc, t_begin + P);
   const int n_chunks = max(0, t_end - t_begin + kChunk - 1) / kChunk;
 
-  // Columns: decode, query heads qh0 + i of the group; prefill, slots.
-  const int Gv = PRE ? min(slots, 16) : min(16, G - grp * 16);  // valid columns
+  // Columns: decode, query heads qh0 + i of the group; shared-prefix pass,
+  // (member, head) slots.
+  const int Gv = GRP ? min(slots, 16) : min(16, G - grp * 16);  // valid columns
   const bool head_ok = i < Gv;
   const int qh0 = hk * G + grp * 16;     // first query head of the group (decode)
-  const int u_i = sb + i;                // slot of column i
-  const int lim = GRP ? c : PRE ? (head_ok ? c - nq + u_i / G + 1 : cc) : cc;  // keys [0, lim) of column i
   // q / out row (times Hq, plus head) of column `col`
   auto out_row = [&](int col) -> int64_t {
-    if constexpr (PRE) {
+    if constexpr (GRP) {
       const int u = sb + col;
       return (int64_t)(q0 + u / G) * Hq + hk * G + u % G;
     } else {
@@ -357,7 +332,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
   constexpr int CPB = 64 / BPC;                         // chunks per batch
   // Chunks are dealt to the waves round-robin (the intelliparadigm page's
   // warp-to-block assignment, section 4.2, with a wave taking 32 tokens).
-  auto chunk_of = [&](int k) { return MODE == kPrefill ? k : w + NW * k; };  // the wave's k-th chunk
+  auto chunk_of = [&](int k) { return w + NW * k; };  // the wave's k-th chunk
   int tbl = 0;
   auto load_batch = [&](int k0) {
     const int ch = chunk_of(k0 + lane / BPC);
@@ -379,20 +354,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
   // Token tau of the chunk (0..31) sits in block tau / BS of the chunk at row
   // tau % BS; a block of 64 tokens holds the whole chunk from row t0 % 64.
   auto issue = [&](const int (&b)[BPC], int t0, Raw<KK, MM, KV8>& r) {
-    // prefill: ordinary loads (the waves of a workgroup read the same lines);
-    // otherwise non-temporal (each byte is read once per step)
-    auto ld16 = [](const void* a) -> u32x4 {
-      if constexpr (MODE == kPrefill) return load16(a);
-      else return stream16(a);
-    };
-    auto ld8 = [](const void* a) -> u32x2 {
-      if constexpr (MODE == kPrefill) return *reinterpret_cast<const u32x2*>(a);
-      else return stream8(a);
-    };
-    auto ldf1 = [](const void* a) -> float {
-      if constexpr (MODE == kPrefill) return *reinterpret_cast<const float*>(a);
-      else return stream_f1(a);
-    };
     const int r0 = BS > kChunk ? t0 % BS : 0;
     auto at = [&](int tau, int64_t& off, int& row) {  // tile offset and row of token tau
       int id = b[0];
@@ -410,25 +371,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
     if constexpr (!KV8) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        r.k[0][kk] = ld16(kc + ok0 + ((4 * kk + g4) * BS + rk0) * 8);
-        r.k[1][kk] = ld16(kc + ok1 + ((4 * kk + g4) * BS + rk1) * 8);
+        r.k[0][kk] = stream16(kc + ok0 + ((4 * kk + g4) * BS + rk0) * 8);
+        r.k[1][kk] = stream16(kc + ok1 + ((4 * kk + g4) * BS + rk1) * 8);
       }
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm) r.v[mm] = ld16(vc + ov + (16 * mm + i) * BS + rv);
+      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream16(vc + ov + (16 * mm + i) * BS + rv);
     } else {
       // K codes: one 16-byte x-vector 4*k2 + g4 (channels 16*(4*k2+g4)..+16)
       // of the token's row feeds products 2*k2 and 2*k2 + 1.
 #pragma unroll
       for (int k2 = 0; k2 < KK / 2; ++k2) {
-        const u32x4 a = ld16(kc + ok0 + ((4 * k2 + g4) * BS + rk0) * 16);
-        const u32x4 c = ld16(kc + ok1 + ((4 * k2 + g4) * BS + rk1) * 16);
+        const u32x4 a = stream16(kc + ok0 + ((4 * k2 + g4) * BS + rk0) * 16);
+        const u32x4 c = stream16(kc + ok1 + ((4 * k2 + g4) * BS + rk1) * 16);
         r.k[0][2 * k2] = u32x2{a[0], a[1]};
         r.k[0][2 * k2 + 1] = u32x2{a[2], a[3]};
         r.k[1][2 * k2] = u32x2{c[0], c[1]};
         r.k[1][2 * k2 + 1] = u32x2{c[2], c[3]};
       }
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm) r.v[mm] = ld8(vc + ov + (16 * mm + i) * BS + rv);
+      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream8(vc + ov + (16 * mm + i) * BS + rv);
       // Scales: one per lane (the chunk's 32 K scales, then its 32 V
       // scales); consume hands each lane the ones it needs by lane shuffles,
       // which keeps one register per chunk in flight instead of sixteen.
@@ -436,7 +397,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
       int64_t osc;
       int rsc;
       at(lane & 31, osc, rsc);
-      r.sc = ldf1((lane < 32 ? kc : vc) + osc + SC + 4 * rsc);
+      r.sc = stream_f1((lane < 32 ? kc : vc) + osc + SC + 4 * rsc);
     }
   };
   // Both products and the online-softmax update for the chunk at token t0.
@@ -471,11 +432,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
       x[j] = s0[j] * scale_log2;
       x[4 + j] = s1[j] * scale_log2;
     }
-    if (t0 + kChunk > lim_min || t0 < skip) {  // drop tokens outside [skip, lim) by select
+    if (t0 + kChunk > cc || t0 < skip) {  // drop tokens outside [skip, cc) by select
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tok = t0 + 4 * g4 + (e & 3) + 16 * (e >> 2);
-        if (tok >= lim || tok < skip) x[e] = -INFINITY;
+        if (tok >= cc || tok < skip) x[e] = -INFINITY;
       }
       if constexpr (!KV8) {  // zero the V bits of dropped tokens (they may hold NaN)
         uint32_t keep[4];  // V word wd holds tokens t0 + 8*g4 + 2*wd, +1
@@ -734,21 +695,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
 
-  if constexpr (MODE == kPrefill) {
-    // The wave's columns are its own: normalise and store (lane (i, g4)
-    // holds output channels 16*mm + 4*g4 .. +3 of column i).
-    if (head_ok) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      uint16_t* orow = out + out_row(i) * D + 4 * g4;
-#pragma unroll
-      for (int mm = 0; mm < MM; ++mm) {
-        const f32x4 r = acc[mm] * inv;
-        *reinterpret_cast<u32x2*>(orow + 16 * mm) = u32x2{Ty::pack2(r[0], r[1]), Ty::pack2(r[2], r[3])};
-      }
-    }
-    return;
-  }
-
   // Merge the NW waves: M = max_w m_w per head, then every wave rescales its
   // sum and output by 2^(m_w - M) into LDS and the workgroup adds them up in
   // wave order.  A wave that saw no token has m_w = -inf and weight 0.
@@ -802,8 +748,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
   }
 }
 
+// A thread's share of one prefill chunk on its way to LDS.
+template <int PER>
+struct Stage16 {
+  u32x4 k[PER], v[PER];
+};
+template <int PV8>
+struct StageI8 {
+  u32x4 k = {0u, 0u, 0u, 0u};
+  u32x2 v[PV8];
+  float sc = 0.f;
+};
+
 // ----------------------------------------------------------------------------
-// Paged prefill with K/V staged through LDS (16-bit caches).  A workgroup of
+// Paged prefill with K/V staged through LDS.  A workgroup of
 // NW waves takes 16 * NC * NW (row, head) slots of one sequence and KV head;
 // wave w owns slots sb .. sb + 16*NC - 1 (NC column groups of 16).  The
 // workgroup walks the keys in 32-token chunks: all threads load a chunk's K
@@ -815,12 +773,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
 // 16 lanes on 16 tokens or channels) hit distinct banks:
 //   K vector (token tau, x-vector j) at tau * XV + (j ^ (tau % XV)),
 //   V vector (channel d, tokens 8*qd..+8) at d * 4 + (qd ^ ((d / 2) % 4)).
-// Arithmetic per column as in decode_mfma_kernel's prefill mode.
+// INT8 caches (KV8): a chunk is its K codes (16-byte x-vectors, 4 KiB at
+// D = 128), its V codes (8-byte runs of 8 tokens, 4 KiB) and its 64 scales;
+//   K vector (token tau, x-vector j) at tau * XV8 + (j ^ (tau % XV8)),
+//   V run (channel d, tokens 8*qd..+8) at d * 4 + (qd ^ ((d / 4) % 4)),
+// and the codes are widened to the query type as the operands are read.
+// Arithmetic per column as in decode_mfma_kernel: base-2 online softmax with
+// the lazy reference maximum, fp32 accumulation, weights rounded to the
+// element type for the PV product.
 // ----------------------------------------------------------------------------
-template <typename Ty, int D, int BS, int NW, int NC>
+template <typename Ty, int D, int BS, int NW, int NC, bool KV8>
 __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
-    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, const int32_t* __restrict__ tables,
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
+    const void* __restrict__ vcv, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, const int32_t* __restrict__ qstart, int Hq, int Hkv, int G,
     int NB, int max_blocks, int max_ctx, int max_q, int num_rows, float scale_log2) {
   static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
@@ -831,11 +796,26 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
   constexpr int CV = kChunk * XV;      // 16-byte vectors of a chunk's K (and of its V)
   constexpr int PER = CV / (64 * NW);  // K (and V) vectors each thread moves per chunk
   static_assert(PER * 64 * NW == CV, "chunk vectors split evenly over the threads");
-  constexpr int TILE = D * BS;
+  constexpr int XV8 = D / 16;          // INT8: 16-byte code vectors per K row
+  constexpr int CK8 = kChunk * XV8;    // INT8: K code vectors of a chunk
+  constexpr int CV8 = D * 4;           // INT8: 8-byte V runs of a chunk
+  static_assert(!KV8 || (CK8 <= 64 * NW && CV8 % (64 * NW) == 0), "INT8 chunk split over the threads");
+  constexpr int PV8 = CV8 / (64 * NW);  // INT8: V runs each thread moves per chunk
+  constexpr int TILE = KV8 ? I8Tile<D, BS>::kBytes : D * BS;  // elements (16-bit) or bytes (INT8)
+  using Elem = typename std::conditional<KV8, uint8_t, uint16_t>::type;
+  const Elem* kc = reinterpret_cast<const Elem*>(kcv);
+  const Elem* vc = reinterpret_cast<const Elem*>(vcv);
   constexpr int BPC = BS >= kChunk ? 1 : kChunk / BS;  // blocks per chunk
   constexpr int CPB = 64 / BPC;                         // chunks per batch of table entries
-  __shared__ u32x4 lk[2][CV];
-  __shared__ u32x4 lv[2][CV];
+  // one LDS buffer: K then V (16-bit), or K codes, V codes and 64 scales (INT8)
+  constexpr int BUF = KV8 ? CK8 * 16 + CV8 * 8 + 64 * 4 : 2 * CV * 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[2 * BUF];
+  auto lk = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF); };
+  auto lv = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF + CV * 16); };
+  auto lk8 = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF); };
+  auto lv8 = [&](int buf) { return reinterpret_cast<u32x2*>(lds_raw + buf * BUF + CK8 * 16); };
+  auto lsc = [&](int buf) { return reinterpret_cast<float*>(lds_raw + buf * BUF + CK8 * 16 + CV8 * 8); };
+  using Stage = typename std::conditional<KV8, StageI8<(PV8 > 0 ? PV8 : 1)>, Stage16<PER>>::type;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -887,13 +867,17 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
     const int u = sb + col;
     return (int64_t)(q0 + u / G) * Hq + hk * G + u % G;
   };
+  // Q^T operand: lane feeds column i, channels 8*m..+8 with m = 4*kk + g4
+  // (INT8: 8*(kk/2) + 2*g4 + kk%2, so that one 16-byte code vector feeds two
+  // products)
+  auto qchunk = [&](int kk) { return KV8 ? 8 * (kk >> 1) + 2 * g4 + (kk & 1) : 4 * kk + g4; };
   V8 qop[NC][KK];
 #pragma unroll
   for (int nc = 0; nc < NC; ++nc) {
     const uint16_t* qrow = q + out_row(head_ok[nc] ? 16 * nc + i : 0) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const u32x4 raw = head_ok[nc] ? load16(qrow + 8 * (4 * kk + g4)) : u32x4{0u, 0u, 0u, 0u};
+      const u32x4 raw = head_ok[nc] ? load16(qrow + 8 * qchunk(kk)) : u32x4{0u, 0u, 0u, 0u};
       qop[nc][kk] = __builtin_bit_cast(V8, raw);
     }
   }
@@ -921,11 +905,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
   };
   load_batch(0);
 
-  // This thread's share of chunk k: vector g = tid + 64*NW*r of K (x-vector
+  // This thread's share of chunk k (16-bit): vector g = tid + 64*NW*r of K (x-vector
   // g / 32, token g % 32: 16 consecutive lanes read 16 consecutive tokens of
   // one x-vector, 256 contiguous bytes) and of V (channel g / 4, tokens
   // 8*(g % 4)..+8: consecutive lanes read consecutive bytes of a block row).
-  auto gload = [&](int k, u32x4 (&kr)[PER], u32x4 (&vr)[PER]) {
+  auto gload = [&](int k, Stage& st) {
     if (k > 0 && k % CPB == 0) load_batch(k);
     const int e = (k % CPB) * BPC;
     int b[BPC];
@@ -940,63 +924,133 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
       off = (int64_t)id * blk_stride + head_off;
       row = BS >= kChunk ? r0 + tau : tau % BS;
     };
+    if constexpr (!KV8) {
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int g = tid + 64 * NW * r;
+      for (int r = 0; r < PER; ++r) {
+        const int g = tid + 64 * NW * r;
+        int64_t off;
+        int row;
+        at(g % kChunk, off, row);
+        st.k[r] = load16(kc + off + ((g / kChunk) * BS + row) * 8);
+        at(8 * (g & 3), off, row);
+        st.v[r] = load16(vc + off + (g >> 2) * BS + row);
+      }
+    } else {
       int64_t off;
       int row;
-      at(g % kChunk, off, row);
-      kr[r] = load16(kc + off + ((g / kChunk) * BS + row) * 8);
-      at(8 * (g & 3), off, row);
-      vr[r] = load16(vc + off + (g >> 2) * BS + row);
+      if (tid < CK8) {  // K code vector: x-vector tid / 32, token tid % 32
+        at(tid % kChunk, off, row);
+        st.k = load16(kc + off + ((tid / kChunk) * BS + row) * 16);
+      }
+#pragma unroll
+      for (int r = 0; r < PV8; ++r) {  // V run: channel g / 4, tokens 8*(g % 4)..+8
+        const int g = tid + 64 * NW * r;
+        at(8 * (g & 3), off, row);
+        st.v[r] = load8(vc + off + (g >> 2) * BS + row);
+      }
+      if (tid < 64) {  // scales: K of token tid (tid < 32), V of token tid - 32
+        at(tid & 31, off, row);
+        st.sc = *reinterpret_cast<const float*>((tid < 32 ? kc : vc) + off + I8Tile<D, BS>::kScales + 4 * row);
+      }
     }
   };
-  auto swrite = [&](int buf, const u32x4 (&kr)[PER], const u32x4 (&vr)[PER]) {
+  auto swrite = [&](int buf, const Stage& st) {
+    if constexpr (!KV8) {
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      const int g = tid + 64 * NW * r;
-      const int tau = g % kChunk, j = g / kChunk;
-      lk[buf][tau * XV + (j ^ (tau % XV))] = kr[r];
-      const int d = g >> 2, qd = g & 3;
-      lv[buf][d * 4 + (qd ^ ((d >> 1) & 3))] = vr[r];
+      for (int r = 0; r < PER; ++r) {
+        const int g = tid + 64 * NW * r;
+        const int tau = g % kChunk, j = g / kChunk;
+        lk(buf)[tau * XV + (j ^ (tau % XV))] = st.k[r];
+        const int d = g >> 2, qd = g & 3;
+        lv(buf)[d * 4 + (qd ^ ((d >> 1) & 3))] = st.v[r];
+      }
+    } else {
+      if (tid < CK8) {
+        const int tau = tid % kChunk, j = tid / kChunk;
+        lk8(buf)[tau * XV8 + (j ^ (tau % XV8))] = st.k;
+      }
+#pragma unroll
+      for (int r = 0; r < PV8; ++r) {
+        const int g = tid + 64 * NW * r;
+        const int d = g >> 2, qd = g & 3;
+        lv8(buf)[d * 4 + (qd ^ ((d >> 2) & 3))] = st.v[r];
+      }
+      if (tid < 64) lsc(buf)[tid] = st.sc;
     }
   };
 
   // The wave's products and online-softmax update for chunk k (in buf).
   auto compute = [&](int k, int buf) {
     const int t0 = k * kChunk;
-    u32x4 kop[2][KK], vop[MM];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int tau = 16 * t + i, j = 4 * kk + g4;
-        kop[t][kk] = lk[buf][tau * XV + (j ^ (tau % XV))];
-      }
-#pragma unroll
-    for (int mm = 0; mm < MM; ++mm) {
-      const int d = 16 * mm + i;
-      vop[mm] = lv[buf][d * 4 + (g4 ^ ((d >> 1) & 3))];
-    }
     const bool edge = t0 + kChunk > lim_min;
-    if (edge) {  // zero the V bits of tokens past the wave's keys (they may hold NaN)
-      uint32_t keep[4];  // V word wd holds tokens t0 + 8*g4 + 2*wd, +1
+    // operands: 16-bit K rows / V runs, or INT8 code vectors and scales
+    u32x4 kop[2][KK], vop[MM];
+    u32x4 kv8[2][KK / 2 > 0 ? KK / 2 : 1];
+    u32x2 vv8[MM];
+    f32x4 sk[2], sv[2];
+    if constexpr (!KV8) {
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd)
-        keep[wd] = (t0 + 8 * g4 + 2 * wd < cc ? 0x0000FFFFu : 0u) |
-                   (t0 + 8 * g4 + 2 * wd + 1 < cc ? 0xFFFF0000u : 0u);
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm)
+        for (int kk = 0; kk < KK; ++kk) {
+          const int tau = 16 * t + i, j = 4 * kk + g4;
+          kop[t][kk] = lk(buf)[tau * XV + (j ^ (tau % XV))];
+        }
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) vop[mm][wd] &= keep[wd];
+      for (int mm = 0; mm < MM; ++mm) {
+        const int d = 16 * mm + i;
+        vop[mm] = lv(buf)[d * 4 + (g4 ^ ((d >> 1) & 3))];
+      }
+      if (edge) {  // zero the V bits of tokens past the wave's keys (they may hold NaN)
+        uint32_t keep[4];  // V word wd holds tokens t0 + 8*g4 + 2*wd, +1
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd)
+          keep[wd] = (t0 + 8 * g4 + 2 * wd < cc ? 0x0000FFFFu : 0u) |
+                     (t0 + 8 * g4 + 2 * wd + 1 < cc ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int mm = 0; mm < MM; ++mm)
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) vop[mm][wd] &= keep[wd];
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int k2 = 0; k2 < KK / 2; ++k2) {
+          const int tau = 16 * t + i, j = 4 * k2 + g4;
+          kv8[t][k2] = lk8(buf)[tau * XV8 + (j ^ (tau % XV8))];
+        }
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm) {
+        const int d = 16 * mm + i;
+        vv8[mm] = lv8(buf)[d * 4 + (g4 ^ ((d >> 2) & 3))];
+      }
+      // scales of tokens 16*t + 4*g4 .. +3 (K, then V)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sk[t] = *reinterpret_cast<const f32x4*>(lsc(buf) + 16 * t + 4 * g4);
+        sv[t] = *reinterpret_cast<const f32x4*>(lsc(buf) + 32 + 16 * t + 4 * g4);
+      }
     }
 #pragma unroll
     for (int nc = 0; nc < NC; ++nc) {
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        s0 = Ty::mma(__builtin_bit_cast(V8, kop[0][kk]), qop[nc][kk], s0);
-        s1 = Ty::mma(__builtin_bit_cast(V8, kop[1][kk]), qop[nc][kk], s1);
+        if constexpr (!KV8) {
+          s0 = Ty::mma(__builtin_bit_cast(V8, kop[0][kk]), qop[nc][kk], s0);
+          s1 = Ty::mma(__builtin_bit_cast(V8, kop[1][kk]), qop[nc][kk], s1);
+        } else {  // product kk takes half kk % 2 of code vector kk / 2
+          const u32x4 a = kv8[0][kk >> 1], b = kv8[1][kk >> 1];
+          const u32x2 ha = (kk & 1) ? u32x2{a[2], a[3]} : u32x2{a[0], a[1]};
+          const u32x2 hb = (kk & 1) ? u32x2{b[2], b[3]} : u32x2{b[0], b[1]};
+          s0 = Ty::mma(__builtin_bit_cast(V8, codes_to_operand<Ty>(ha)), qop[nc][kk], s0);
+          s1 = Ty::mma(__builtin_bit_cast(V8, codes_to_operand<Ty>(hb)), qop[nc][kk], s1);
+        }
+      }
+      if constexpr (KV8) {  // logits of INT8 keys: code dot q times the token's scale
+        s0 *= sk[0];
+        s1 *= sk[1];
       }
       float x[8];
 #pragma unroll
@@ -1004,10 +1058,16 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
         x[j] = s0[j] * scale_log2;
         x[4 + j] = s1[j] * scale_log2;
       }
+      float svc[8];  // INT8: V scales, 0 for dropped tokens (a scale may be NaN)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) svc[e] = KV8 ? sv[e >> 2][e & 3] : 0.f;
       if (edge) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= lim[nc]) x[e] = -INFINITY;
+          if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= lim[nc]) {
+            x[e] = -INFINITY;
+            svc[e] = 0.f;
+          }
       }
       float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                        fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -1024,10 +1084,26 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
       const float m_use = m_run[nc] == -INFINITY ? 0.f : m_run[nc];
       uint32_t pw[4];
       float psum = l_run[nc];
+      if constexpr (!KV8) {
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd) {
-        pw[wd] = Ty::pack2(exp2_fast(x[2 * wd] - m_use), exp2_fast(x[2 * wd + 1] - m_use));
-        psum = Ty::sum2(pw[wd], psum);  // the weights the PV product sees
+        for (int wd = 0; wd < 4; ++wd) {
+          pw[wd] = Ty::pack2(exp2_fast(x[2 * wd] - m_use), exp2_fast(x[2 * wd + 1] - m_use));
+          psum = Ty::sum2(pw[wd], psum);  // the weights the PV product sees
+        }
+      } else {
+        // INT8 values: the PV product sees weight * V scale per token; the sum
+        // takes rounded(p * s) / s, as in decode (a token with scale 0 counts
+        // with its weight p).
+        float pr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(x[e] - m_use);
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          const float s0w = svc[2 * wd], s1w = svc[2 * wd + 1];
+          pw[wd] = Ty::pack2(pr[2 * wd] * s0w, pr[2 * wd + 1] * s1w);
+          psum += s0w != 0.f ? Ty::lo_f32(pw[wd]) * __builtin_amdgcn_rcpf(s0w) : pr[2 * wd];
+          psum += s1w != 0.f ? Ty::hi_f32(pw[wd]) * __builtin_amdgcn_rcpf(s1w) : pr[2 * wd + 1];
+        }
       }
       l_run[nc] = psum;
       const auto a32 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
@@ -1036,8 +1112,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
       const auto b16 = __builtin_amdgcn_permlane16_swap(b32[0], b32[1], false, false);
       const V8 pop = __builtin_bit_cast(V8, u32x4{a16[0], b16[0], a16[1], b16[1]});
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm)
-        acc[nc][mm] = Ty::mma(__builtin_bit_cast(V8, vop[mm]), pop, acc[nc][mm]);
+      for (int mm = 0; mm < MM; ++mm) {
+        if constexpr (!KV8)
+          acc[nc][mm] = Ty::mma(__builtin_bit_cast(V8, vop[mm]), pop, acc[nc][mm]);
+        else
+          acc[nc][mm] = Ty::mma(__builtin_bit_cast(V8, codes_to_operand<Ty>(vv8[mm])), pop, acc[nc][mm]);
+      }
     }
   };
 
@@ -1045,20 +1125,20 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
   // and k + 2 (being loaded) are in flight; the barrier after each step makes
   // the next chunk visible and frees the buffer just read.  Every wave takes
   // every barrier (n_chunks is the workgroup's).
-  u32x4 ka[PER], va[PER], kb[PER], vb[PER];
-  gload(0, ka, va);
-  if (1 < n_chunks) gload(1, kb, vb);
-  swrite(0, ka, va);
+  Stage st_a, st_b;
+  gload(0, st_a);
+  if (1 < n_chunks) gload(1, st_b);
+  swrite(0, st_a);
   __syncthreads();
   for (int k = 0; k < n_chunks; k += 2) {
-    if (k + 2 < n_chunks) gload(k + 2, ka, va);
+    if (k + 2 < n_chunks) gload(k + 2, st_a);
     if (k < n_mine) compute(k, 0);
-    if (k + 1 < n_chunks) swrite(1, kb, vb);
+    if (k + 1 < n_chunks) swrite(1, st_b);
     __syncthreads();
     if (k + 1 >= n_chunks) break;
-    if (k + 3 < n_chunks) gload(k + 3, kb, vb);
+    if (k + 3 < n_chunks) gload(k + 3, st_b);
     if (k + 1 < n_mine) compute(k + 1, 1);
-    if (k + 2 < n_chunks) swrite(0, ka, va);
+    if (k + 2 < n_chunks) swrite(0, st_a);
     __syncthreads();
   }
 
@@ -1386,7 +1466,7 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
       a->context_lens, (const uint16_t*)a->k_new, (const uint16_t*)a->v_new, a->num_q_heads,
       a->num_kv_heads, G, pl.groups, a->num_blocks, a->max_blocks_per_seq, a->max_context_len,
       a->scale * kLog2e, pl.P, max(pl.max_parts, 1), ws_acc, ws_ml, flat ? a->num_seqs : 0,
-      nullptr, pl.pre_parts, 0, pl.grp_start, pl.grp_len, pl.n_grp);
+      pl.pre_parts, 0, pl.grp_start, pl.grp_len, pl.n_grp);
 }
 
 // Shared-prefix pass: grid x = tiles of 16 (member, head) slots of the
@@ -1401,7 +1481,7 @@ void launch_prefix(const pa_decode_args* a, const Plan& pl, float* ws_acc, float
       (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
       a->context_lens, nullptr, nullptr, a->num_q_heads, a->num_kv_heads, G, 1, a->num_blocks,
       a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, pl.P, pl.max_parts, ws_acc,
-      ws_ml, 0, nullptr, 0, a->num_seqs, pl.grp_start, pl.grp_len, pl.n_grp);
+      ws_ml, 0, 0, a->num_seqs, pl.grp_start, pl.grp_len, pl.n_grp);
 }
 
 template <typename Ty, bool KV8, int D>
@@ -1433,24 +1513,16 @@ constexpr int kLdsGroups = PA_PREFILL_GROUPS;
 template <typename Ty, int D, int BS, int NW, bool KV8>
 void launch_prefill(const pa_prefill_args* a, hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
-  if constexpr (!KV8) {
-    // 16-bit caches: K/V staged through LDS, 16 * kLdsGroups slots per wave
-    const int64_t tiles = ((int64_t)a->max_query_len * G + 16 * kLdsGroups * NW - 1) / (16 * kLdsGroups * NW);
-    dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
-    prefill_lds_kernel<Ty, D, BS, NW, kLdsGroups><<<grid, 64 * NW, 0, st>>>(
-        (uint16_t*)a->out, (const uint16_t*)a->q, (const uint16_t*)a->k_cache,
-        (const uint16_t*)a->v_cache, a->block_tables, a->context_lens, a->query_start,
-        a->num_q_heads, a->num_kv_heads, G, a->num_blocks, a->max_blocks_per_seq,
-        a->max_context_len, a->max_query_len, a->num_tokens, a->scale * kLog2e);
-  } else {
-    const int64_t tiles = ((int64_t)a->max_query_len * G + 16 * NW - 1) / (16 * NW);
-    dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
-    decode_mfma_kernel<Ty, D, BS, NW, KV8, kPrefill><<<grid, 64 * NW, 0, st>>>(
-        (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
-        a->context_lens, nullptr, nullptr, a->num_q_heads, a->num_kv_heads, G, 1, a->num_blocks,
-        a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, kChunk, 1, nullptr, nullptr, 0,
-        a->query_start, a->max_query_len, a->num_tokens, nullptr, nullptr, 0);
-  }
+  // K/V (or INT8 codes and scales) staged through LDS, 16 * NC slots per wave
+  // (INT8: one column group, so that the widened operands fit 2 waves per SIMD)
+  constexpr int NC = KV8 ? 1 : kLdsGroups;
+  const int64_t tiles = ((int64_t)a->max_query_len * G + 16 * NC * NW - 1) / (16 * NC * NW);
+  dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
+  prefill_lds_kernel<Ty, D, BS, NW, NC, KV8><<<grid, 64 * NW, 0, st>>>(
+      (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
+      a->context_lens, a->query_start, a->num_q_heads, a->num_kv_heads, G, a->num_blocks,
+      a->max_blocks_per_seq, a->max_context_len, a->max_query_len, a->num_tokens,
+      a->scale * kLog2e);
 }
 
 template <typename Ty, bool KV8, int D>
