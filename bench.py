@@ -329,7 +329,7 @@ def bench_prefill(args, dev):
                    "block_size": case.BS, "chunk_rows": rows,
                    "context_tokens": int(case.context_lens.sum()),
                    "flops_per_step": flops, "step": "pa_prefill"},
-        "roofline": {"kernel": "decode_mfma_kernel (prefill mode)", "bound": "mfma",
+        "roofline": {"kernel": "prefill_lds_kernel", "bound": "mfma",
                      "achieved": round(flops / (ms * 1e-3) / 1e12, 2), "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
                      "traffic": None, "avg_launch_ms": round(ms, 5), "algorithmic_flops_per_launch": flops},
