@@ -1712,9 +1712,13 @@ PA_API pa_status pa_prefill(const pa_prefill_args* a, void* stream) {
   if (!aligned16(a->out) || !aligned16(a->q) || !aligned16(a->k_cache) ||
       !aligned16(a->v_cache) || !a->block_tables || !a->context_lens || !a->query_start)
     return PA_ERR_INVALID;
+  // grid: slot tiles (at least 64 slots each) x KV heads x sequences; the
+  // kernel numbers its workgroups with 32-bit ints
   const int64_t tiles =
-      ((int64_t)a->max_query_len * (a->num_q_heads / a->num_kv_heads) + 15) / 16;
-  if (a->num_seqs > 65535 || a->num_kv_heads > 65535 || tiles > 0x7FFFFFFF)
+      ((int64_t)a->max_query_len * (a->num_q_heads / a->num_kv_heads) + 16 * kWaves - 1) /
+      (16 * kWaves);
+  if (a->num_seqs > 65535 || a->num_kv_heads > 65535 ||
+      tiles * a->num_kv_heads * a->num_seqs > 0x7FFFFFFF)
     return PA_ERR_UNSUPPORTED;
   hipStream_t hs = (hipStream_t)stream;
   const bool kv8 = a->kv_dtype == PA_I8;

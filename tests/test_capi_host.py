@@ -296,6 +296,14 @@ def test_prefill_and_prefix_validation(L):
     a.kv_dtype, a.block_size = pa.PA_I8, 24
     assert L.pa_prefill(a, None) == pa.PA_ERR_UNSUPPORTED
     assert L.pa_prefill(None, None) == pa.PA_ERR_INVALID
+    # a grid past 2^31 workgroups is refused before any launch (the pointers
+    # below are aligned stand-ins that are never dereferenced)
+    a.kv_dtype, a.block_size = pa.PA_BF16, 16
+    a.out = a.q = a.k_cache = a.v_cache = 0x100000
+    a.block_tables = a.context_lens = a.query_start = 0x100000
+    a.num_seqs, a.num_q_heads, a.num_kv_heads = 65535, 4096, 512
+    a.max_query_len, a.max_context_len, a.max_blocks_per_seq = 1 << 20, 1 << 20, 1 << 16
+    assert L.pa_prefill(a, None) == pa.PA_ERR_UNSUPPORTED
 
     d = _args(partition_size=32)
     g = pa.pa_prefix_groups()
