@@ -156,6 +156,8 @@ __global__ __launch_bounds__(256) void write_kv_i8_kernel(const void* __restrict
 }
 
 inline unsigned grid1d(int64_t n) { return (unsigned)((n + 255) / 256); }
+// whether n items at 256 per workgroup fit a 1-D grid
+inline bool fits1d(int64_t n) { return (n + 255) / 256 <= 0x7FFFFFFF; }
 
 }  // namespace
 }  // namespace pa
@@ -178,6 +180,7 @@ PA_API pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache
       !slot_mapping)
     return PA_ERR_INVALID;
   const int64_t items = (int64_t)num_tokens * num_kv_heads * (head_dim / (16 / es));
+  if (!fits1d(items)) return PA_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
   if (es == 2)
     write_kv_kernel<2><<<grid1d(items), 256, 0, st>>>(
@@ -203,6 +206,7 @@ PA_API pa_status pa_write_kv_i8(const void* k_new, const void* v_new, int32_t sr
       !slot_mapping)
     return PA_ERR_INVALID;
   const int64_t waves = (int64_t)num_tokens * num_kv_heads;
+  if ((waves + 3) / 4 > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
   const unsigned grid = (unsigned)((waves + 3) / 4);
   hipStream_t st = (hipStream_t)stream;
   uint8_t* kc = (uint8_t*)k_cache;
@@ -266,6 +270,7 @@ PA_API pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
       !block_tables || !context_lens)
     return PA_ERR_INVALID;
   const int64_t items = (int64_t)num_seqs * max_context_len * num_kv_heads * (head_dim / (16 / es));
+  if (!fits1d(items)) return PA_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
   if (es == 2)
     gather_kv_kernel<2><<<grid1d(items), 256, 0, st>>>(
