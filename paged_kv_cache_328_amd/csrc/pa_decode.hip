@@ -173,21 +173,19 @@ struct Raw<KK, MM, true> {
   float sc;        // lane L < 32: K scale of the chunk's token L; else V scale of token L - 32
 };
 
-// Modes of the 16-bit kernel: decode (one query per sequence; with prefix
-// groups, the keys after the group's shared prefix) and the shared-prefix
-// pass (the group's members over the shared blocks).
-constexpr int kDecode = 0, kPrefix = 1;
-
-template <typename Ty, int D, int BS, int NW, bool KV8, int MODE>
+// With prefix groups (pa_decode_prefix) the kernel takes each member's keys
+// after its group's shared prefix; the prefix itself is attended by
+// prefill_lds_kernel's shared-prefix pass, in pre_parts partitions of pre_P
+// tokens that fill the first partial slots of every member.
+template <typename Ty, int D, int BS, int NW, bool KV8>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3 : 1))) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
     const void* __restrict__ vcv, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, int Hq, int Hkv, int G, int n_groups, int NB,
     int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
-    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs, int max_q, int num_rows,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs, int pre_parts, int pre_P,
     const int32_t* __restrict__ grp_start, const int32_t* __restrict__ grp_len, int n_grp) {
-  constexpr bool GRP = MODE == kPrefix;  // columns are (member, head) slots
   static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
   static_assert(D % 32 == 0, "head_dim multiple of 32");
   using V8 = typename Ty::vec8;
@@ -206,23 +204,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
   const int i = lane & 15;       // row (A operand) / column (B operand, output)
   const int g4 = lane >> 4;      // which 8-element slice of the reduction dim
   int hk, grp = 0, p = 0, s, c;
-  int q0 = 0, nq = 0, tile = 0;  // slot modes: first row, rows, slot tile
-  if constexpr (GRP) {
-    // Shared-prefix pass: x = tile of 16 (member, head) slots, y = partition
-    // of the prefix, z = group * Hkv + KV head.  The members are sequences
-    // q0 .. q0 + nq - 1; the first one's table holds the shared blocks, keys
-    // [0, grp_len[g]) in partitions of P tokens.
-    tile = blockIdx.x;
-    p = blockIdx.y;
-    const int g = blockIdx.z / Hkv;
-    hk = blockIdx.z - g * Hkv;
-    q0 = clampi(grp_start[g], 0, num_rows);
-    nq = clampi(grp_start[g + 1] - q0, 0, num_rows - q0);
-    if (tile * 16 >= nq * G) return;
-    s = q0;
-    c = clampi(grp_len[g], 0, min(min(max_ctx, max_blocks * BS), (int)gridDim.y * P));
-    if (p * P >= c) return;
-  } else if (num_seqs > 0) {
+  if (num_seqs > 0) {
     hk = blockIdx.x / n_groups;
     grp = blockIdx.x - hk * n_groups;
     // Flat work list: y enumerates the (sequence, partition) units that exist,
@@ -239,52 +221,41 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
     s = blockIdx.z;
     c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
   }
-  // Decode with prefix groups: tokens [0, skip) of sequence s belong to its
-  // group's shared prefix, attended by the prefix pass (partial 0); this
-  // launch covers [skip, c) in partitions 1, 2, ...
+  // With prefix groups: tokens [0, skip) of sequence s belong to its group's
+  // shared prefix, attended by the prefix pass (partial slots 0 .. pb - 1);
+  // this launch covers [skip, c) in the slots after them.
   int skip = 0;
-  if (MODE == kDecode && n_grp > 0) {
+  if (n_grp > 0) {
     int lo = 0, hi = n_grp - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (grp_start[mid] <= s) lo = mid;
       else hi = mid - 1;
     }
-    // (max_q carries the prefix's partial slots here: skip never needs more)
-    skip = uniform(clampi(grp_len[lo], 0, min(c, max_q * P)));
+    skip = uniform(clampi(grp_len[lo], 0, min(c, pre_parts * pre_P)));
   }
-  const int pb = (skip + P - 1) / P;  // partial slots of the prefix come first
+  const int pb = n_grp > 0 ? (skip + pre_P - 1) / pre_P : 0;  // partial slots of the prefix
   // Chunks start on 32-token boundaries: the partitions run from the boundary
   // at or below skip, and tokens below skip are dropped.
   const int a_skip = skip & ~(kChunk - 1);
-  const int n_p = GRP ? 1 : (c - a_skip + P - 1) / P;
-  if (!GRP && (p < 0 || p >= max(n_p, 1))) return;
+  const int n_p = (c - a_skip + P - 1) / P;
+  if (p < 0 || p >= max(n_p, 1)) return;
   const int t_begin = a_skip + p * P;
   // With a fused append the token at c - 1 comes from k_new / v_new, not from
   // the cache: the chunk loop reads [t_begin, cc) and the new token is added
   // afterwards by the workgroup whose partition holds it.
-  const bool append = !GRP && k_new != nullptr;
-  const int sb = tile * 16;                 // shared-prefix pass: first slot of the tile
-  const int slots = GRP ? nq * G - sb : 0;  // valid slots of the tile
-  const int cc = GRP ? c : (append ? max(c - 1, 0) : c);  // keys [0, cc) come from the cache
+  const bool append = k_new != nullptr;
+  const int cc = append ? max(c - 1, 0) : c;  // keys [0, cc) come from the cache
   const bool has_new = append && c > 0 && c - 1 >= t_begin && c - 1 < t_begin + P;
   const int t_end = min(cc, t_begin + P);
   const int n_chunks = max(0, t_end - t_begin + kChunk - 1) / kChunk;
 
-  // Columns: decode, query heads qh0 + i of the group; shared-prefix pass,
-  // (member, head) slots.
-  const int Gv = GRP ? min(slots, 16) : min(16, G - grp * 16);  // valid columns
+  // Columns: query heads qh0 + i of the group of 16.
+  const int Gv = min(16, G - grp * 16);  // valid columns
   const bool head_ok = i < Gv;
-  const int qh0 = hk * G + grp * 16;     // first query head of the group (decode)
+  const int qh0 = hk * G + grp * 16;     // first query head of the group
   // q / out row (times Hq, plus head) of column `col`
-  auto out_row = [&](int col) -> int64_t {
-    if constexpr (GRP) {
-      const int u = sb + col;
-      return (int64_t)(q0 + u / G) * Hq + hk * G + u % G;
-    } else {
-      return (int64_t)s * Hq + qh0 + col;
-    }
-  };
+  auto out_row = [&](int col) -> int64_t { return (int64_t)s * Hq + qh0 + col; };
 
   // Q^T operand of the QK product: lane feeds head i, channels 8*m..+8 of the
   // K operand it meets (m = 4*kk + g4; INT8: 8*(kk/2) + 2*g4 + kk%2, so that
@@ -716,7 +687,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
   }
   __syncthreads();
 
-  const bool split = GRP || skip > 0 || n_p > 1;
+  const bool split = pb > 0 || n_p > 1;
   for (int e = threadIdx.x; e < Gv * (D / 4); e += 64 * NW) {
     const int hh = e / (D / 4);
     const int d = 4 * (e - hh * (D / 4));
@@ -735,7 +706,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
                             (uint32_t)Ty::from_f32(r[2]) | ((uint32_t)Ty::from_f32(r[3]) << 16)};
       *reinterpret_cast<u32x2*>(out + row * D + d) = packed;
     } else {
-      const int64_t idx = row * max_parts + (GRP ? p : pb + p);
+      const int64_t idx = row * max_parts + pb + p;
       *reinterpret_cast<f32x4*>(ws_acc + idx * D + d) = sum;
       if (d == 0) {
         float Mh = -INFINITY;
@@ -782,12 +753,21 @@ struct StageI8 {
 // the lazy reference maximum, fp32 accumulation, weights rounded to the
 // element type for the PV product.
 // ----------------------------------------------------------------------------
-template <typename Ty, int D, int BS, int NW, int NC, bool KV8>
+// PFX: the shared-prefix pass of pa_decode_prefix instead.  Grid x = slot
+// tiles of a group's (member, head) slots, y = partition of the prefix (P
+// tokens), z = group * Hkv + KV head; members are rows qstart[g] ..
+// qstart[g+1] - 1 (query rows of the decode), the keys [p*P, (p+1)*P) of
+// the prefix (grp_len[g] tokens) come through the first member's table, no
+// causal limit, and each column's partial (max, sum, unnormalised output)
+// goes to partial slot p of its row in the split-K workspace.
+template <typename Ty, int D, int BS, int NW, int NC, bool KV8, bool PFX>
 __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
     const void* __restrict__ vcv, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, const int32_t* __restrict__ qstart, int Hq, int Hkv, int G,
-    int NB, int max_blocks, int max_ctx, int max_q, int num_rows, float scale_log2) {
+    int NB, int max_blocks, int max_ctx, int max_q, int num_rows, float scale_log2,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int P, int max_parts,
+    const int32_t* __restrict__ grp_len) {
   static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
   using V8 = typename Ty::vec8;
   constexpr int KK = D / 32;           // QK products along head_dim
@@ -827,7 +807,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
   // XCD are the slot tiles of one (sequence, KV head) -- they read the same
   // K/V lines at about the same time, through one L2 -- while the (sequence,
   // KV head) pairs are dealt to the XCDs round-robin (balanced work).
-  int tile, hk, s;
+  int tile, ya, za;  // grid position after the reordering
   {
     const int X = gridDim.x, Y = gridDim.y;
     const int L = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
@@ -838,22 +818,43 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
       tile = n % X;
       grp = (n / X) * kXcds + L % kXcds;
     }
-    hk = grp % Y;
-    s = grp / Y;
+    ya = grp % Y;
+    za = grp / Y;
   }
-  const int c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
-  const int q0 = clampi(qstart[s], 0, num_rows);
-  const int nq = clampi(qstart[s + 1] - q0, 0, min(min(max_q, c), num_rows - q0));
+  // Rows q0 .. q0 + nq - 1; keys from t_begin on, up to c.
+  int hk, s, c, q0, nq, p = 0, t_begin = 0;
+  if constexpr (!PFX) {
+    hk = ya;
+    s = za;
+    c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
+    q0 = clampi(qstart[s], 0, num_rows);
+    nq = clampi(qstart[s + 1] - q0, 0, min(min(max_q, c), num_rows - q0));
+  } else {
+    p = ya;
+    const int g = za / Hkv;
+    hk = za - g * Hkv;
+    q0 = clampi(qstart[g], 0, num_rows);
+    nq = clampi(qstart[g + 1] - q0, 0, num_rows - q0);
+    s = q0;  // the first member's table holds the shared blocks
+    c = clampi(grp_len[g], 0, min(min(max_ctx, max_blocks * BS), (int)gridDim.y * P));
+    t_begin = p * P;
+    if (t_begin >= c) return;  // the whole workgroup: no barrier reached yet
+    c = min(c, t_begin + P);
+  }
   const int swg = tile * NW * NC * 16;  // first slot of the workgroup
   if (swg >= nq * G) return;            // the whole workgroup: no barrier reached yet
-  // Slot u is chunk row u / G (position c - nq + u / G), query head hk*G + u % G.
+  // Slot u is row q0 + u / G, query head hk*G + u % G; in prefill it sits at
+  // position c - nq + u / G and sees keys up to there, in the shared-prefix
+  // pass it sees all keys [t_begin, c).
+  auto key_end = [&](int u) { return PFX ? c : c - nq + u / G + 1; };
   const int last = min(nq * G, swg + NW * NC * 16) - 1;  // last slot of the workgroup
-  const int n_chunks = (c - nq + last / G + 1 + kChunk - 1) / kChunk;  // chunks the workgroup loads
+  const int c_load = key_end(last);                      // tokens the workgroup loads
+  const int n_chunks = (c_load - t_begin + kChunk - 1) / kChunk;
   const int sb = swg + w * NC * 16;                // the wave's first slot
   const int slots = nq * G - sb;                   // may be <= 0: the wave only loads
-  const int cc = slots > 0 ? c - nq + (sb + min(slots, 16 * NC) - 1) / G + 1 : 0;  // keys it needs
-  const int lim_min = slots > 0 ? c - nq + sb / G + 1 : 0;
-  const int n_mine = (cc + kChunk - 1) / kChunk;   // chunks this wave computes
+  const int cc = slots > 0 ? key_end(sb + min(slots, 16 * NC) - 1) : t_begin;  // keys it needs
+  const int lim_min = slots > 0 ? key_end(sb) : t_begin;
+  const int n_mine = (cc - t_begin + kChunk - 1) / kChunk;  // chunks this wave computes
 
   int Gv[NC], lim[NC];
   bool head_ok[NC];
@@ -861,7 +862,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
   for (int nc = 0; nc < NC; ++nc) {
     Gv[nc] = clampi(slots - 16 * nc, 0, 16);
     head_ok[nc] = i < Gv[nc];
-    lim[nc] = head_ok[nc] ? c - nq + (sb + 16 * nc + i) / G + 1 : cc;
+    lim[nc] = head_ok[nc] ? key_end(sb + 16 * nc + i) : cc;
   }
   auto out_row = [&](int col) -> int64_t {
     const int u = sb + col;
@@ -896,11 +897,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
   const int32_t* trow = tables + (int64_t)s * max_blocks;
   const int64_t blk_stride = (int64_t)Hkv * TILE;
   const int64_t head_off = (int64_t)hk * TILE;
-  const int c_load = c - nq + last / G + 1;  // tokens the workgroup loads
   int tbl = 0;
   auto load_batch = [&](int k0) {
     const int ch = k0 + lane / BPC;
-    const int t = ch * kChunk + (lane % BPC) * BS;
+    const int t = t_begin + ch * kChunk + (lane % BPC) * BS;
     tbl = ch < n_chunks && t < c_load ? clampi(trow[t / BS], 0, NB - 1) : 0;
   };
   load_batch(0);
@@ -915,7 +915,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
     int b[BPC];
 #pragma unroll
     for (int j = 0; j < BPC; ++j) b[j] = __builtin_amdgcn_readlane(tbl, e + j);
-    const int r0 = BS > kChunk ? (k * kChunk) % BS : 0;
+    const int r0 = BS > kChunk ? (t_begin + k * kChunk) % BS : 0;
     auto at = [&](int tau, int64_t& off, int& row) {  // tile offset and row of token tau
       int id = b[0];
 #pragma unroll
@@ -981,7 +981,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
 
   // The wave's products and online-softmax update for chunk k (in buf).
   auto compute = [&](int k, int buf) {
-    const int t0 = k * kChunk;
+    const int t0 = t_begin + k * kChunk;
     const bool edge = t0 + kChunk > lim_min;
     // operands: 16-bit K rows / V runs, or INT8 code vectors and scales
     u32x4 kop[2][KK], vop[MM];
@@ -1146,13 +1146,23 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
   for (int nc = 0; nc < NC; ++nc) {
     float l_tot = l_run[nc] + __shfl_xor(l_run[nc], 16);
     l_tot += __shfl_xor(l_tot, 32);
-    if (head_ok[nc]) {
+    if (!head_ok[nc]) continue;
+    if constexpr (!PFX) {  // the row's output
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       uint16_t* orow = out + out_row(16 * nc + i) * D + 4 * g4;
 #pragma unroll
       for (int mm = 0; mm < MM; ++mm) {
         const f32x4 r = acc[nc][mm] * inv;
         *reinterpret_cast<u32x2*>(orow + 16 * mm) = u32x2{Ty::pack2(r[0], r[1]), Ty::pack2(r[2], r[3])};
+      }
+    } else {  // partial slot p of the row: max, sum, unnormalised output
+      const int64_t idx = out_row(16 * nc + i) * max_parts + p;
+      float* arow = ws_acc + idx * D + 4 * g4;
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm) *reinterpret_cast<f32x4*>(arow + 16 * mm) = acc[nc][mm];
+      if (g4 == 0) {
+        ws_ml[2 * idx] = m_run[nc];
+        ws_ml[2 * idx + 1] = l_tot;
       }
     }
   }
@@ -1267,7 +1277,7 @@ __global__ __launch_bounds__(NT) void merge_kernel(
     typename Store::T* __restrict__ out, const int32_t* __restrict__ lens,
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, int Hq, int max_ctx,
     int max_blocks, int BS, int P, int max_parts, const int32_t* __restrict__ grp_start,
-    const int32_t* __restrict__ grp_len, int n_grp, int pre_parts) {
+    const int32_t* __restrict__ grp_len, int n_grp, int pre_parts, int pre_P) {
   constexpr int C4 = D / 4;                   // threads per partition row
   constexpr int ROWS = NT / C4;               // partitions read at once
   constexpr int U = 8;                        // partitions per thread per batch
@@ -1300,9 +1310,9 @@ __global__ __launch_bounds__(NT) void merge_kernel(
       if (grp_start[mid] <= s) lo = mid;
       else hi = mid - 1;
     }
-    skip = clampi(grp_len[lo], 0, min(c, pre_parts * P));
+    skip = clampi(grp_len[lo], 0, min(c, pre_parts * pre_P));
   }
-  const int n_p = (skip + P - 1) / P + (c - (skip & ~(kChunk - 1)) + P - 1) / P;
+  const int n_p = (n_grp > 0 ? (skip + pre_P - 1) / pre_P : 0) + (c - (skip & ~(kChunk - 1)) + P - 1) / P;
   if (n_p <= 1 && skip == 0) return;  // pass 1 stored the output itself
 #pragma unroll
   for (int k = 0; k < U; ++k)
@@ -1365,6 +1375,7 @@ struct Plan {
   int n_grp = 0;
   int max_group = 0;
   int pre_parts = 0;  // partitions of the longest shared prefix
+  int pre_P = 0;      // tokens per partition of the shared prefixes
   // (sequence, partition) units of the flat work list, from the host copy of
   // the context lengths (0 = unknown: the grid covers num_seqs * max_parts)
   int64_t units = 0;
@@ -1451,37 +1462,46 @@ size_t merge_lds_bytes(int NW, int G, int D) {
 // Waves per workgroup of the 16-bit kernel (measured best on MI355X among 1,
 // 2, 4 and 8 for the workloads of the tests and the benchmark).
 constexpr int kWaves = 4;
+// Column groups of 16 slots per wave of prefill_lds_kernel over 16-bit caches
+// (INT8 caches take one, so that the widened operands fit 3 waves per SIMD).
+constexpr int kLdsGroups = 2;
 
 template <typename Ty, int D, int BS, int NW, bool KV8>
 void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* ws_ml,
                  hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
   const bool flat = pl.flat;
+  // partitions of the longest context (with prefix groups, the partial
+  // slots also hold the prefix partitions, which this launch does not cover)
+  const int dec_parts = max((a->max_context_len + pl.P - 1) / pl.P, 1);
   dim3 grid((unsigned)(a->num_kv_heads * pl.groups),
-            flat ? (unsigned)(pl.units > 0 ? pl.units : (int64_t)a->num_seqs * max(pl.max_parts, 1))
-                 : (unsigned)max(pl.max_parts, 1),
+            flat ? (unsigned)(pl.units > 0 ? pl.units : (int64_t)a->num_seqs * dec_parts)
+                 : (unsigned)dec_parts,
             flat ? 1u : (unsigned)a->num_seqs);
-  decode_mfma_kernel<Ty, D, BS, NW, KV8, kDecode><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
+  decode_mfma_kernel<Ty, D, BS, NW, KV8><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
       (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
       a->context_lens, (const uint16_t*)a->k_new, (const uint16_t*)a->v_new, a->num_q_heads,
       a->num_kv_heads, G, pl.groups, a->num_blocks, a->max_blocks_per_seq, a->max_context_len,
       a->scale * kLog2e, pl.P, max(pl.max_parts, 1), ws_acc, ws_ml, flat ? a->num_seqs : 0,
-      pl.pre_parts, 0, pl.grp_start, pl.grp_len, pl.n_grp);
+      pl.pre_parts, pl.pre_P, pl.grp_start, pl.grp_len, pl.n_grp);
 }
 
-// Shared-prefix pass: grid x = tiles of 16 (member, head) slots of the
-// largest group, y = KV head, z = group; writes partial 0 of every member.
+// Shared-prefix pass: prefill_lds_kernel over each group's prefix, grid x =
+// slot tiles of the largest group, y = partition of the prefix, z = group *
+// Hkv + KV head; writes the prefix partials (slots 0 .. pre_parts - 1) of
+// every member.
 template <typename Ty, int D, int BS, int NW, bool KV8>
 void launch_prefix(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* ws_ml,
                    hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
-  const int64_t tiles = ((int64_t)pl.max_group * G + 15) / 16;
+  constexpr int NC = KV8 ? 1 : kLdsGroups;
+  const int64_t tiles = ((int64_t)pl.max_group * G + 16 * NC * NW - 1) / (16 * NC * NW);
   dim3 grid((unsigned)tiles, (unsigned)pl.pre_parts, (unsigned)(pl.n_grp * a->num_kv_heads));
-  decode_mfma_kernel<Ty, D, BS, NW, KV8, kPrefix><<<grid, 64 * NW, merge_lds_bytes(NW, 16, D), st>>>(
-      (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
-      a->context_lens, nullptr, nullptr, a->num_q_heads, a->num_kv_heads, G, 1, a->num_blocks,
-      a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, pl.P, pl.max_parts, ws_acc,
-      ws_ml, 0, 0, a->num_seqs, pl.grp_start, pl.grp_len, pl.n_grp);
+  prefill_lds_kernel<Ty, D, BS, NW, NC, KV8, true><<<grid, 64 * NW, 0, st>>>(
+      nullptr, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables, nullptr,
+      pl.grp_start, a->num_q_heads, a->num_kv_heads, G, a->num_blocks, a->max_blocks_per_seq,
+      a->max_context_len, 0, a->num_seqs, a->scale * kLog2e, ws_acc, ws_ml, pl.pre_P, pl.max_parts,
+      pl.grp_len);
 }
 
 template <typename Ty, bool KV8, int D>
@@ -1504,11 +1524,6 @@ void launch_prefix_dims(const pa_decode_args* a, const Plan& pl, float* wa, floa
 
 // Prefill: grid x = tiles of 16 (row, head) slots of the longest chunk, y =
 // KV head, z = sequence; no split-K (each tile's key range is its own).
-// Column groups of 16 slots per wave of the LDS prefill kernel.
-#ifndef PA_PREFILL_GROUPS
-#define PA_PREFILL_GROUPS 2
-#endif
-constexpr int kLdsGroups = PA_PREFILL_GROUPS;
 
 template <typename Ty, int D, int BS, int NW, bool KV8>
 void launch_prefill(const pa_prefill_args* a, hipStream_t st) {
@@ -1518,11 +1533,11 @@ void launch_prefill(const pa_prefill_args* a, hipStream_t st) {
   constexpr int NC = KV8 ? 1 : kLdsGroups;
   const int64_t tiles = ((int64_t)a->max_query_len * G + 16 * NC * NW - 1) / (16 * NC * NW);
   dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
-  prefill_lds_kernel<Ty, D, BS, NW, NC, KV8><<<grid, 64 * NW, 0, st>>>(
+  prefill_lds_kernel<Ty, D, BS, NW, NC, KV8, false><<<grid, 64 * NW, 0, st>>>(
       (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
       a->context_lens, a->query_start, a->num_q_heads, a->num_kv_heads, G, a->num_blocks,
       a->max_blocks_per_seq, a->max_context_len, a->max_query_len, a->num_tokens,
-      a->scale * kLog2e);
+      a->scale * kLog2e, nullptr, nullptr, 0, 0, nullptr);
 }
 
 template <typename Ty, bool KV8, int D>
@@ -1590,12 +1605,12 @@ void launch_merge(const pa_decode_args* a, const Plan& pl, const float* wa, cons
     merge_kernel<Store, D, 128><<<grid, 128, 0, st>>>(
         (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
         a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts, pl.grp_start, pl.grp_len,
-        pl.n_grp, pl.pre_parts);
+        pl.n_grp, pl.pre_parts, pl.pre_P);
   else
     merge_kernel<Store, D, 512><<<grid, 512, 0, st>>>(
         (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
         a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts, pl.grp_start, pl.grp_len,
-        pl.n_grp, pl.pre_parts);
+        pl.n_grp, pl.pre_parts, pl.pre_P);
 }
 
 template <typename Store>
@@ -1685,7 +1700,18 @@ static pa_status prefix_plan(const pa_decode_args* a, const pa_prefix_groups* g,
   pl.n_grp = g->num_groups;
   pl.max_group = g->max_group_size;
   pl.flat = false;
-  pl.pre_parts = max(1, (g->max_prefix_len + pl.P - 1) / pl.P);
+  // Prefix partitions: enough workgroups for the prefix pass (about 512 of
+  // them, each over at least 64 tokens), never longer than the decode's.
+  {
+    const int G = a->num_q_heads / a->num_kv_heads;
+    const int64_t tiles = ((int64_t)g->max_group_size * G + 16 * kLdsGroups * kWaves - 1) /
+                          (16 * kLdsGroups * kWaves);
+    const int64_t wgs = tiles * g->num_groups * a->num_kv_heads;  // per partition
+    int pp = pl.P;
+    while (pp > 64 && pp % 64 == 0 && wgs * ((g->max_prefix_len + pp - 1) / pp) < 256) pp /= 2;
+    pl.pre_P = pp;
+  }
+  pl.pre_parts = max(1, (g->max_prefix_len + pl.pre_P - 1) / pl.pre_P);
   pl.max_parts = pl.pre_parts + (a->max_context_len + pl.P - 1) / pl.P;
   pl.ws_bytes = (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * (a->head_dim + 2) * 4;
   return PA_OK;
