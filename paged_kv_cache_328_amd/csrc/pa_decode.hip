@@ -1,5 +1,7 @@
-// Paged decode attention for gfx950: pass 1 (per-partition attention over the
-// block table) and pass 2 (log-sum-exp merge of the partitions).
+// Paged attention for gfx950: decode pass 1 (per-partition attention over the
+// block table), pass 2 (log-sum-exp merge of the partitions), and paged
+// (chunked) prefill, whose kernel also runs the shared-prefix pass of
+// pa_decode_prefix.
 //
 // What is computed: for sequence s and query head h, the softmax attention of
 // q[s,h] over the sequence's cached keys/values, which sit in fixed-size
@@ -23,26 +25,34 @@
 // consecutive reduction-dimension elements 8*(l/16)..+7; the 16x16 result
 // leaves rows 4*(l/16)..+3 of column l%16 in lane l):
 //   QK:  S[token][head] = K[token][d] x Q^T[d][head], reduction over d.  Row i
-//        of the 16-token tile is token i, so for one 8-channel chunk the 16
+//        of a 16-token tile is token i, so for one 8-channel chunk the 16
 //        lanes of a row group read 16 consecutive 16-byte vectors: 256
-//        contiguous bytes, whole cache lines.
+//        contiguous bytes, whole cache lines.  A 32-token chunk is two tiles.
 //   PV:  O^T[d][head] += V^T[d][k] x P^T[k][head], reduction over the 32
-//        tokens of a chunk.  The reduction index k is ordered so that lane l
-//        already holds the weights it must feed: k = 8*(l/16) + j is token
-//        4*(l/16) + j of tile 0 for j < 4 and token 16 + 4*(l/16) + j - 4 of
-//        tile 1 otherwise.  The V^T operand follows the same order: two
-//        8-byte reads of 4 consecutive tokens of one channel.
-// So the softmax weights never move between lanes, and the running max / sum
-// of head l%16 stays lane-local apart from one reduction over the 4 row
-// groups of the wave.
+//        tokens of a chunk, k = token.  Lane l's V operand is tokens
+//        8*(l/16)..+7 of channel l%16 (one 16-byte load).  The QK result
+//        leaves lane row g = l/16 with tokens 4g..4g+3 and 16+4g..16+4g+3;
+//        two lane-row swaps (v_permlane32_swap, then v_permlane16_swap) of
+//        the packed weights regroup them to tokens 8g..8g+7.
+// The running max / sum of head l%16 stays lane-local apart from one
+// reduction over the 4 row groups of the wave.
 //
-// Work decomposition: one workgroup of NW waves per (KV head, group of up to
-// 16 query heads sharing that KV head, partition, sequence).  The group's
-// query heads are the N = 16 dimension of both products, so K/V bytes are read
-// once per KV head whatever the group size G is.  The partition is cut into
-// chunks of 32 tokens dealt round-robin to the waves (the warp-to-block
-// assignment of intelliparadigm.com, section "4.2 动态负载均衡"); each wave keeps its own
-// running (max, sum, output) and the waves are merged through LDS at the end.
+// Decode work decomposition: one workgroup of NW waves per (KV head, group
+// of up to 16 query heads sharing that KV head, partition, sequence).  The
+// group's query heads are the N = 16 dimension of both products, so K/V
+// bytes are read once per KV head whatever the group size G is.  The
+// partition is cut into chunks of 32 tokens dealt round-robin to the waves
+// (the warp-to-block assignment of intelliparadigm.com, section "4.2
+// 动态负载均衡"); each wave keeps its own running (max, sum, output) and the
+// waves are merged through LDS at the end.
+//
+// Prefill: one workgroup per (tile of 64 or 128 (row, head) slots, KV head,
+// sequence) walks the keys in 32-token chunks staged through LDS; every wave
+// computes its own slots' columns against each staged chunk.
+//
+// INT8 caches (codes plus one fp32 scale per token and KV head, in the block
+// tile): the codes are widened exactly to the query type for the same
+// products, the K scale multiplies the logit and the V scale the weight.
 #include <math.h>
 
 #include <type_traits>
