@@ -236,7 +236,10 @@ PA_API pa_status pa_decode_prefix(const pa_decode_args* args, const pa_prefix_gr
  * non-decreasing, query_start[num_seqs] = num_tokens and 0 <= n_s <=
  * min(c, max_query_len); the caches, tables and lengths as for pa_decode
  * (kv_dtype PA_I8 for INT8 pools).  No workspace.  Device contents are
- * preconditions; out-of-range lengths are clamped, never read past.
+ * preconditions; out-of-range lengths are clamped, never read past.  Sizes
+ * beyond the launch limits (num_seqs or num_kv_heads above 65535, or more
+ * than 2^31 - 1 workgroups of 64 (row, head) slots per sequence and KV head)
+ * return PA_ERR_UNSUPPORTED before anything is launched.
  * ------------------------------------------------------------------------ */
 typedef struct pa_prefill_args {
   void* out;
