@@ -1277,8 +1277,9 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
 // when every context fits in 16 partitions, else 512).
 // Thread (r, c4) walks partitions r, r + ROWS, ... keeping its own running
 // (max, sum, output for channels 4*c4..+3) with the log-sum-exp rule, so one
-// pass reads every partial once and all loads of a batch are independent; the
-// first batch is fetched together with the context length.  The ROWS states
+// pass reads every live partial once and all loads of a batch are independent
+// (they are issued once the context length gives the row's partition count).
+// The ROWS states
 // are then combined in LDS in row order, so the result depends only on the
 // partition contents, never on where the blocks sit.
 // ----------------------------------------------------------------------------
@@ -1297,18 +1298,6 @@ __global__ __launch_bounds__(NT) void merge_kernel(
   const int r = tid / C4, c4 = tid - r * C4;
   const int64_t base = ((int64_t)s * Hq + h) * max_parts;
 
-  Lse st = {-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
-  float bm[U], bl[U];
-  f32x4 bo[U];
-  // first batch: issued before the context length is known (indices stay
-  // below max_parts, so every read is inside the workspace)
-#pragma unroll
-  for (int k = 0; k < U; ++k) {
-    const int pp = min(r + k * ROWS, max_parts - 1);
-    bm[k] = ws_ml[2 * (base + pp)];
-    bl[k] = ws_ml[2 * (base + pp) + 1];
-    bo[k] = *reinterpret_cast<const f32x4*>(ws_acc + (base + pp) * D + 4 * c4);
-  }
   const int c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
   // With prefix groups, partial 0 is the shared prefix (when the sequence's
   // group has one) and the decode partitions follow.
@@ -1322,12 +1311,17 @@ __global__ __launch_bounds__(NT) void merge_kernel(
     }
     skip = clampi(grp_len[lo], 0, min(c, pre_parts * pre_P));
   }
-  const int n_p = (n_grp > 0 ? (skip + pre_P - 1) / pre_P : 0) + (c - (skip & ~(kChunk - 1)) + P - 1) / P;
+  const int n_p = min((n_grp > 0 ? (skip + pre_P - 1) / pre_P : 0) +
+                          (c - (skip & ~(kChunk - 1)) + P - 1) / P,
+                      max_parts);
   if (n_p <= 1 && skip == 0) return;  // pass 1 stored the output itself
-#pragma unroll
-  for (int k = 0; k < U; ++k)
-    if (r + k * ROWS < n_p) lse_add(st, bm[k], bl[k], bo[k]);
-  for (int p0 = r + U * ROWS; p0 < n_p; p0 += U * ROWS) {
+  // Only the row's own partials are read (the length is known first): a
+  // speculative batch over max_parts slots read several times the live
+  // bytes on mixed-length batches.
+  Lse st = {-INFINITY, 0.f, f32x4{0.f, 0.f, 0.f, 0.f}};
+  float bm[U], bl[U];
+  f32x4 bo[U];
+  for (int p0 = r; p0 < n_p; p0 += U * ROWS) {
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const int pp = min(p0 + k * ROWS, n_p - 1);
