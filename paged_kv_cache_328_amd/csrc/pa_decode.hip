@@ -1421,15 +1421,17 @@ pa_status validate(const pa_decode_args* a) {
 //   - contexts up to 2048 tokens are not split when the (sequence, KV head,
 //     head group) workgroups alone fill the chip (>= 512 of them);
 //   - otherwise P = max_context / 16 rounded up to a power of two within
-//     [256, 2048] tokens, halved (down to one 32-token chunk) while fewer
+//     [256, 4096] tokens, halved (down to one 32-token chunk) while fewer
 //     than 1024 workgroups would exist even if every context were maximal.
+// Measured on MI355X (4 sequences of 16k..128k tokens, 8 KV heads): P = 512
+// 185 us, 1024 171 us, 2048 162 us, 4096 156 us.
 int choose_partition(const pa_decode_args* a, int wg_per_part) {
   if (a->dtype == PA_F32) return 512;
   const int64_t base = (int64_t)a->num_seqs * wg_per_part;
   const int64_t max_ctx = a->max_context_len;
   if (max_ctx <= 2048 && base >= 512) return 2048;
   int P = 256;
-  while (P < 2048 && (int64_t)P * 16 < max_ctx) P *= 2;
+  while (P < 4096 && (int64_t)P * 16 < max_ctx) P *= 2;
   while (P > kChunk && base * ((max_ctx + P - 1) / P) < 1024) P /= 2;
   return max(P, a->block_size);  // a power of two >= 32: a multiple of the block size
 }

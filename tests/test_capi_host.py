@@ -80,6 +80,20 @@ def test_decode_checks_the_host_copy_of_context_lens(L):
     assert L.pa_decode_partition_size(a) == -1
 
 
+@pytest.mark.parametrize("S,Hq,Hkv,max_ctx,want", [
+    (16, 40, 40, 1280, 2048),     # LLaMA-13B-shaped: 640 workgroups, not split
+    (64, 32, 8, 8192, 512),       # mixed lengths up to 8k over 8 KV heads
+    (4, 64, 8, 131072, 4096),     # 16k..128k contexts: 1024 workgroups at 4096
+    (1, 8, 1, 131072, 128),       # one sequence, one KV head: halved to 1024 units
+])
+def test_library_partition_choice(L, S, Hq, Hkv, max_ctx, want):
+    """The heuristic behind partition_size = 0 at the benchmark shapes (a
+    host-side computation; no device memory is touched)."""
+    a = _args(num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv, max_context_len=max_ctx,
+              max_blocks_per_seq=max_ctx // 16, num_blocks=max_ctx // 16)
+    assert L.pa_decode_partition_size(a) == want
+
+
 def test_decode_rejects_null_pointers_and_missing_workspace(L):
     a = _args()
     assert L.pa_decode(a, None) == pa.PA_ERR_INVALID  # null tensors

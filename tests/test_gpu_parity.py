@@ -96,6 +96,13 @@ def test_long_bf16_full_size_p512():
     run_decode_case(case, "long_bf16", gather_seqs=[0])
 
 
+def test_long_bf16_full_size_library_partition():
+    """The same workload at the library's own partition size (4096 tokens for
+    contexts up to 128k over 8 KV heads), checked against the oracle."""
+    case = wl.long_bf16()
+    run_decode_case(case, "long_bf16 library P", partition_size=0, gather_seqs=None)
+
+
 def test_cow_shared_prefix_step():
     """32 sequences share a 2048-token prefix; each has a private suffix and a
     forked sibling that shares all its blocks.  One step appends a token to
