@@ -471,7 +471,6 @@ def measured_traffic(workload, partition_size, fused, host_lens):
     and WRITE_SIZE, each scaled by what the counter reads for a plain copy of
     known size), or None when no record matches this launch or the kernel
     sources changed since."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -479,10 +478,42 @@ def measured_traffic(workload, partition_size, fused, host_lens):
     if (not rec or rec.get("partition_size") != partition_size or rec.get("fused_append") != fused
             or rec.get("host_context_lens") != host_lens):
         return None
+    return rec["bytes_per_launch"] if kernel_source_digest() == rec["kernel_sources_sha256"] else None
+
+
+def kernel_source_digest():
+    """SHA-256 of the decode kernels' source with comments and blank space
+    removed: byte counters stay valid across comment-only edits and go stale
+    on any change of code."""
+    import hashlib
     h = hashlib.sha256()
     for f in ["paged_kv_cache_328_amd/csrc/pa_decode.hip", "paged_kv_cache_328_amd/csrc/pa_device.h"]:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    return rec["bytes_per_launch"] if h.hexdigest() == rec["kernel_sources_sha256"] else None
+        h.update(_strip_comments(open(os.path.join(ROOT, f), encoding="utf-8").read()).encode())
+    return h.hexdigest()
+
+
+def _strip_comments(src):
+    """C++ source without // and /* */ comments (string and character
+    literals kept), every run of white space folded to one blank."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
 
 
 def cpu_baseline(case, kd, vd, budget_s):

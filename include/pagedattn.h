@@ -189,9 +189,9 @@ PA_API pa_status pa_decode(const pa_decode_args* args, void* stream);
  * true for whole shared blocks.  The shared prefix is attended once per
  * group (its K/V read once, every member's query heads as the matrix-core
  * columns, split into partitions like a long context), each member's
- * remaining tokens as in pa_decode, and the parts merged with the
- * log-sum-exp rule.  The output equals pa_decode's up
- * to rounding order.
+ * remaining tokens as in pa_decode in the same launch, and the parts merged
+ * with the log-sum-exp rule by a second launch.  The output equals
+ * pa_decode's up to rounding order.
  * Preconditions (device contents): group_start[0] = 0, non-decreasing,
  * group_start[num_groups] = num_seqs; 0 <= prefix_len[g] <= the context of
  * every member (minus the appended token when k_new is set); a group of one

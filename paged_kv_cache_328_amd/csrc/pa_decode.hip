@@ -1,7 +1,7 @@
 // Paged attention for gfx950: decode pass 1 (per-partition attention over the
 // block table), pass 2 (log-sum-exp merge of the partitions), and paged
-// (chunked) prefill, whose kernel also runs the shared-prefix pass of
-// pa_decode_prefix.
+// (chunked) prefill.  pa_decode_prefix runs the prefill body (as a
+// shared-prefix pass) and the decode body in one launch, then the merge.
 //
 // What is computed: for sequence s and query head h, the softmax attention of
 // q[s,h] over the sequence's cached keys/values, which sit in fixed-size
@@ -187,8 +187,10 @@ struct Raw<KK, MM, true> {
 // after its group's shared prefix; the prefix itself is attended by
 // prefill_lds_kernel's shared-prefix pass, in pre_parts partitions of pre_P
 // tokens that fill the first partial slots of every member.
+// Body of the decode pass for the workgroup at grid position (bx, by, bz);
+// `lds` holds merge_lds_bytes(NW, G, D) bytes.
 template <typename Ty, int D, int BS, int NW, bool KV8>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3 : 1))) void decode_mfma_kernel(
+__device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* lds,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
     const void* __restrict__ vcv, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_new,
@@ -207,7 +209,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
   const Elem* kc = reinterpret_cast<const Elem*>(kcv);
   const Elem* vc = reinterpret_cast<const Elem*>(vcv);
   constexpr int DP = D + 4;      // padded LDS row of the merge buffer
-  extern __shared__ float lds[];
 
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
@@ -215,20 +216,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
   const int g4 = lane >> 4;      // which 8-element slice of the reduction dim
   int hk, grp = 0, p = 0, s, c;
   if (num_seqs > 0) {
-    hk = blockIdx.x / n_groups;
-    grp = blockIdx.x - hk * n_groups;
+    hk = bx / n_groups;
+    grp = bx - hk * n_groups;
     // Flat work list: y enumerates the (sequence, partition) units that exist,
     // sequence by sequence; each wave finds its unit from a prefix sum of the
     // sequences' partition counts, so grid slots past the real work sit at
     // the end of the grid instead of between sequences.
-    if (!flat_unit(lens, num_seqs, min(max_ctx, max_blocks * BS), P, (int)blockIdx.y, lane, s, p,
+    if (!flat_unit(lens, num_seqs, min(max_ctx, max_blocks * BS), P, by, lane, s, p,
                    c))
       return;
   } else {
-    hk = blockIdx.x / n_groups;
-    grp = blockIdx.x - hk * n_groups;
-    p = blockIdx.y;
-    s = blockIdx.z;
+    hk = bx / n_groups;
+    grp = bx - hk * n_groups;
+    p = by;
+    s = bz;
     c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
   }
   // With prefix groups: tokens [0, skip) of sequence s belong to its group's
@@ -729,6 +730,29 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
   }
 }
 
+template <typename Ty, int D, int BS, int NW, bool KV8>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3 : 1))) void decode_mfma_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
+    const void* __restrict__ vcv, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, int Hq, int Hkv, int G, int n_groups, int NB,
+    int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs, int pre_parts, int pre_P,
+    const int32_t* __restrict__ grp_start, const int32_t* __restrict__ grp_len, int n_grp) {
+  extern __shared__ float lds[];
+  decode_mfma_body<Ty, D, BS, NW, KV8>(blockIdx.x, blockIdx.y, blockIdx.z, lds, out, q, kcv, vcv, tables, lens, k_new, v_new, Hq, Hkv, G, n_groups, NB, max_blocks,
+      max_ctx, scale_log2, P, max_parts, ws_acc, ws_ml, num_seqs, pre_parts, pre_P, grp_start,
+      grp_len, n_grp);
+}
+
+// LDS of the prefill pass: two chunk buffers, each a 32-token chunk's K and
+// V (16-bit), or its K codes, V codes and 64 scales (INT8).
+template <int D, bool KV8>
+struct PrefillLds {
+  static constexpr int kBuf = KV8 ? kChunk * (D / 16) * 16 + D * 4 * 8 + 64 * 4 : 2 * kChunk * (D / 8) * 16;
+  static constexpr int kBytes = 2 * kBuf;
+};
+
 // A thread's share of one prefill chunk on its way to LDS.
 template <int PER>
 struct Stage16 {
@@ -770,9 +794,11 @@ struct StageI8 {
 // the prefix (grp_len[g] tokens) come through the first member's table, no
 // causal limit, and each column's partial (max, sum, unnormalised output)
 // goes to partial slot p of its row in the split-K workspace.
+// Body of the prefill pass for the workgroup at grid position (bx, by, bz) of
+// a (gx, gy, gz) grid; `lds_raw` holds PrefillLds<D, KV8>::kBytes bytes.
 template <typename Ty, int D, int BS, int NW, int NC, bool KV8, bool PFX>
-__global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
-    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
+__device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx, int gy, int gz,
+    uint8_t* lds_raw, uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
     const void* __restrict__ vcv, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, const int32_t* __restrict__ qstart, int Hq, int Hkv, int G,
     int NB, int max_blocks, int max_ctx, int max_q, int num_rows, float scale_log2,
@@ -799,7 +825,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
   constexpr int CPB = 64 / BPC;                         // chunks per batch of table entries
   // one LDS buffer: K then V (16-bit), or K codes, V codes and 64 scales (INT8)
   constexpr int BUF = KV8 ? CK8 * 16 + CV8 * 8 + 64 * 4 : 2 * CV * 16;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[2 * BUF];
+  static_assert(2 * BUF == PrefillLds<D, KV8>::kBytes, "LDS size of the prefill pass");
   auto lk = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF); };
   auto lv = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF + CV * 16); };
   auto lk8 = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF); };
@@ -819,11 +845,11 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
   // KV head) pairs are dealt to the XCDs round-robin (balanced work).
   int tile, ya, za;  // grid position after the reordering
   {
-    const int X = gridDim.x, Y = gridDim.y;
-    const int L = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
+    const int X = gx, Y = gy;
+    const int L = bx + X * (by + Y * bz);
     int grp = L / X;
     tile = L % X;
-    if ((Y * (int)gridDim.z) % kXcds == 0) {
+    if ((Y * gz) % kXcds == 0) {
       const int n = L / kXcds;  // the workgroup's place on its XCD
       tile = n % X;
       grp = (n / X) * kXcds + L % kXcds;
@@ -846,7 +872,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
     q0 = clampi(qstart[g], 0, num_rows);
     nq = clampi(qstart[g + 1] - q0, 0, num_rows - q0);
     s = q0;  // the first member's table holds the shared blocks
-    c = clampi(grp_len[g], 0, min(min(max_ctx, max_blocks * BS), (int)gridDim.y * P));
+    c = clampi(grp_len[g], 0, min(min(max_ctx, max_blocks * BS), gy * P));
     t_begin = p * P;
     if (t_begin >= c) return;  // the whole workgroup: no barrier reached yet
     c = min(c, t_begin + P);
@@ -1178,6 +1204,70 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
   }
 }
 
+template <typename Ty, int D, int BS, int NW, int NC, bool KV8, bool PFX>
+__global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
+    const void* __restrict__ vcv, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ lens, const int32_t* __restrict__ qstart, int Hq, int Hkv, int G,
+    int NB, int max_blocks, int max_ctx, int max_q, int num_rows, float scale_log2,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int P, int max_parts,
+    const int32_t* __restrict__ grp_len) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[PrefillLds<D, KV8>::kBytes];
+  prefill_lds_body<Ty, D, BS, NW, NC, KV8, PFX>(blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x,
+                                                gridDim.y, gridDim.z, lds_raw, out, q, kcv, vcv, tables, lens, qstart, Hq, Hkv, G, NB, max_blocks, max_ctx, max_q,
+      num_rows, scale_log2, ws_acc, ws_ml, P, max_parts, grp_len);
+}
+
+// Waves per workgroup of the 16-bit kernel (measured best on MI355X among 1,
+// 2, 4 and 8 for the workloads of the tests and the benchmark).
+constexpr int kWaves = 4;
+// Column groups of 16 slots per wave of prefill_lds_kernel over 16-bit caches
+// (INT8 caches take one, so that the widened operands fit 3 waves per SIMD).
+constexpr int kLdsGroups = 2;
+
+// ----------------------------------------------------------------------------
+// pa_decode_prefix in one launch.  The shared-prefix pass and the members'
+// own tokens are independent (they fill different partial slots), so one
+// grid holds both: workgroups 0 .. n_pre - 1 are the prefix pass over a
+// (px, py, pz) grid (prefill_lds_body with PFX), the rest the decode pass
+// over a (dx, dy, dz) grid (decode_mfma_body).  The short prefix
+// workgroups then run beside the decode ones instead of before them.  The
+// LDS is the larger of the two passes' needs.
+// ----------------------------------------------------------------------------
+template <int NW, int D>
+struct FusedLds {
+  static constexpr int kMerge = (2 * NW * 16 + NW * 16 * (D + 4)) * 4;  // merge_lds_bytes at G >= 16
+  static constexpr int kBytes = kMerge > PrefillLds<D, false>::kBytes ? kMerge : PrefillLds<D, false>::kBytes;
+};
+
+template <typename Ty, int D, int BS, int NW, bool KV8>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3 : 1))) void prefix_suffix_kernel(
+    int n_pre, int px, int py, int pz, int dx, int dy,
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
+    const void* __restrict__ vcv, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, int Hq, int Hkv, int G, int n_groups, int NB,
+    int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs, int pre_parts, int pre_P,
+    const int32_t* __restrict__ grp_start, const int32_t* __restrict__ grp_len, int n_grp) {
+  static_assert(PrefillLds<D, KV8>::kBytes <= FusedLds<NW, D>::kBytes, "LDS of the fused launch");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[FusedLds<NW, D>::kBytes];
+  const int L = blockIdx.x;
+  if (L < n_pre) {
+    constexpr int NC = KV8 ? 1 : kLdsGroups;
+    prefill_lds_body<Ty, D, BS, NW, NC, KV8, true>(
+        L % px, (L / px) % py, L / (px * py), px, py, pz, lds_raw, nullptr, q, kcv, vcv, tables,
+        nullptr, grp_start, Hq, Hkv, G, NB, max_blocks, max_ctx, 0, num_seqs, scale_log2, ws_acc,
+        ws_ml, pre_P, max_parts, grp_len);
+  } else {
+    const int M = L - n_pre;
+    decode_mfma_body<Ty, D, BS, NW, KV8>(M % dx, (M / dx) % dy, M / (dx * dy),
+                                         reinterpret_cast<float*>(lds_raw), out, q, kcv, vcv, tables, lens, k_new, v_new, Hq, Hkv, G, n_groups, NB, max_blocks,
+        max_ctx, scale_log2, P, max_parts, ws_acc, ws_ml, 0, pre_parts, pre_P, grp_start,
+        grp_len, n_grp);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // fp32 pass 1 (vector ALU).  One wave per (partition, query head, sequence).
 // Logits of the partition go to LDS, then the weights, then each lane
@@ -1465,12 +1555,6 @@ size_t merge_lds_bytes(int NW, int G, int D) {
   return (size_t)(2 * NW * 16 + NW * min(G, 16) * (D + 4)) * sizeof(float);
 }
 
-// Waves per workgroup of the 16-bit kernel (measured best on MI355X among 1,
-// 2, 4 and 8 for the workloads of the tests and the benchmark).
-constexpr int kWaves = 4;
-// Column groups of 16 slots per wave of prefill_lds_kernel over 16-bit caches
-// (INT8 caches take one, so that the widened operands fit 3 waves per SIMD).
-constexpr int kLdsGroups = 2;
 
 template <typename Ty, int D, int BS, int NW, bool KV8>
 void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* ws_ml,
@@ -1492,40 +1576,58 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
       pl.pre_parts, pl.pre_P, pl.grp_start, pl.grp_len, pl.n_grp);
 }
 
-// Shared-prefix pass: prefill_lds_kernel over each group's prefix, grid x =
-// slot tiles of the largest group, y = partition of the prefix, z = group *
-// Hkv + KV head; writes the prefix partials (slots 0 .. pre_parts - 1) of
-// every member.
-template <typename Ty, int D, int BS, int NW, bool KV8>
-void launch_prefix(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* ws_ml,
-                   hipStream_t st) {
+// pa_decode_prefix: prefix_suffix_kernel, one launch of the shared-prefix
+// pass (grid: slot tiles of the largest group x prefix partitions x group *
+// Hkv + KV head; it writes partial slots 0 .. pre_parts - 1 of every member)
+// followed in the same grid by the decode pass over each member's own tokens
+// (KV head * head group x partitions x sequences).
+int64_t fused_prefix_wgs(const pa_decode_args* a, const Plan& pl, int* px, int* py, int* pz) {
   const int G = a->num_q_heads / a->num_kv_heads;
-  constexpr int NC = KV8 ? 1 : kLdsGroups;
-  const int64_t tiles = ((int64_t)pl.max_group * G + 16 * NC * NW - 1) / (16 * NC * NW);
-  dim3 grid((unsigned)tiles, (unsigned)pl.pre_parts, (unsigned)(pl.n_grp * a->num_kv_heads));
-  prefill_lds_kernel<Ty, D, BS, NW, NC, KV8, true><<<grid, 64 * NW, 0, st>>>(
-      nullptr, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables, nullptr,
-      pl.grp_start, a->num_q_heads, a->num_kv_heads, G, a->num_blocks, a->max_blocks_per_seq,
-      a->max_context_len, 0, a->num_seqs, a->scale * kLog2e, ws_acc, ws_ml, pl.pre_P, pl.max_parts,
-      pl.grp_len);
+  const int NC = a->kv_dtype == PA_I8 ? 1 : kLdsGroups;
+  const int64_t tiles = ((int64_t)pl.max_group * G + 16 * NC * kWaves - 1) / (16 * NC * kWaves);
+  *px = (int)tiles;
+  *py = pl.pre_parts;
+  *pz = pl.n_grp * a->num_kv_heads;
+  return tiles * pl.pre_parts * pz[0];
+}
+
+int64_t fused_decode_wgs(const pa_decode_args* a, const Plan& pl, int* dx, int* dy) {
+  *dx = a->num_kv_heads * pl.groups;
+  *dy = max((a->max_context_len + pl.P - 1) / pl.P, 1);
+  return (int64_t)dx[0] * dy[0] * a->num_seqs;
+}
+
+template <typename Ty, int D, int BS, int NW, bool KV8>
+void launch_fused(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* ws_ml,
+                  hipStream_t st) {
+  const int G = a->num_q_heads / a->num_kv_heads;
+  int px, py, pz, dx, dy;
+  const int64_t n_pre = fused_prefix_wgs(a, pl, &px, &py, &pz);
+  const int64_t n_dec = fused_decode_wgs(a, pl, &dx, &dy);
+  prefix_suffix_kernel<Ty, D, BS, NW, KV8><<<dim3((unsigned)(n_pre + n_dec)), 64 * NW, 0, st>>>(
+      (int)n_pre, px, py, pz, dx, dy, (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache,
+      a->v_cache, a->block_tables, a->context_lens, (const uint16_t*)a->k_new,
+      (const uint16_t*)a->v_new, a->num_q_heads, a->num_kv_heads, G, pl.groups, a->num_blocks,
+      a->max_blocks_per_seq, a->max_context_len, a->scale * kLog2e, pl.P, max(pl.max_parts, 1),
+      ws_acc, ws_ml, a->num_seqs, pl.pre_parts, pl.pre_P, pl.grp_start, pl.grp_len, pl.n_grp);
 }
 
 template <typename Ty, bool KV8, int D>
-void launch_prefix_bs(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
-                      hipStream_t st) {
+void launch_fused_bs(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
+                     hipStream_t st) {
   switch (a->block_size) {
-    case 8: launch_prefix<Ty, D, 8, kWaves, KV8>(a, pl, wa, wm, st); break;
-    case 16: launch_prefix<Ty, D, 16, kWaves, KV8>(a, pl, wa, wm, st); break;
-    case 32: launch_prefix<Ty, D, 32, kWaves, KV8>(a, pl, wa, wm, st); break;
-    default: launch_prefix<Ty, D, 64, kWaves, KV8>(a, pl, wa, wm, st); break;
+    case 8: launch_fused<Ty, D, 8, kWaves, KV8>(a, pl, wa, wm, st); break;
+    case 16: launch_fused<Ty, D, 16, kWaves, KV8>(a, pl, wa, wm, st); break;
+    case 32: launch_fused<Ty, D, 32, kWaves, KV8>(a, pl, wa, wm, st); break;
+    default: launch_fused<Ty, D, 64, kWaves, KV8>(a, pl, wa, wm, st); break;
   }
 }
 
 template <typename Ty, bool KV8>
-void launch_prefix_dims(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
-                        hipStream_t st) {
-  if (a->head_dim == 128) launch_prefix_bs<Ty, KV8, 128>(a, pl, wa, wm, st);
-  else launch_prefix_bs<Ty, KV8, 64>(a, pl, wa, wm, st);
+void launch_fused_dims(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
+                       hipStream_t st) {
+  if (a->head_dim == 128) launch_fused_bs<Ty, KV8, 128>(a, pl, wa, wm, st);
+  else launch_fused_bs<Ty, KV8, 64>(a, pl, wa, wm, st);
 }
 
 // Prefill: grid x = tiles of 16 (row, head) slots of the longest chunk, y =
@@ -1635,16 +1737,15 @@ pa_status run_plan(const pa_decode_args* a, const Plan& pl, hipStream_t hs) {
     ws_ml = ws_acc + (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * a->head_dim;
   }
   const bool kv8 = a->kv_dtype == PA_I8;
-  if (pl.n_grp > 0) {  // shared prefixes first: partial 0 of every member
+  if (pl.n_grp > 0) {  // shared prefixes and own tokens in one launch (16-bit queries only)
     if (a->dtype == PA_F16) {
-      if (kv8) launch_prefix_dims<F16, true>(a, pl, ws_acc, ws_ml, hs);
-      else launch_prefix_dims<F16, false>(a, pl, ws_acc, ws_ml, hs);
+      if (kv8) launch_fused_dims<F16, true>(a, pl, ws_acc, ws_ml, hs);
+      else launch_fused_dims<F16, false>(a, pl, ws_acc, ws_ml, hs);
     } else {
-      if (kv8) launch_prefix_dims<BF16, true>(a, pl, ws_acc, ws_ml, hs);
-      else launch_prefix_dims<BF16, false>(a, pl, ws_acc, ws_ml, hs);
+      if (kv8) launch_fused_dims<BF16, true>(a, pl, ws_acc, ws_ml, hs);
+      else launch_fused_dims<BF16, false>(a, pl, ws_acc, ws_ml, hs);
     }
-  }
-  switch (a->dtype) {
+  } else switch (a->dtype) {
     case PA_F16:
       if (kv8) launch_mfma_dims<F16, true>(a, pl, ws_acc, ws_ml, hs);
       else launch_mfma_dims<F16, false>(a, pl, ws_acc, ws_ml, hs);
@@ -1706,15 +1807,17 @@ static pa_status prefix_plan(const pa_decode_args* a, const pa_prefix_groups* g,
   pl.n_grp = g->num_groups;
   pl.max_group = g->max_group_size;
   pl.flat = false;
-  // Prefix partitions: enough workgroups for the prefix pass (about 512 of
-  // them, each over at least 64 tokens), never longer than the decode's.
+  // Prefix partitions of 256 tokens, doubled (up to 2048) while a long
+  // prefix would leave more than 64 partials per row for the merge.  The
+  // prefix workgroups run in the same launch as the members' own tokens, so
+  // they need not fill the chip by themselves; a workgroup over 256 tokens
+  // of 128 columns takes about as long as a decode workgroup.  Measured on
+  // MI355X (32 members sharing 2048 tokens, 8 KV heads, G = 4): prefix
+  // partitions of 64 tokens 31.9 us per step, 128 28.8, 256 25.2, 512 29.6,
+  // 1024 44.9.
   {
-    const int G = a->num_q_heads / a->num_kv_heads;
-    const int64_t tiles = ((int64_t)g->max_group_size * G + 16 * kLdsGroups * kWaves - 1) /
-                          (16 * kLdsGroups * kWaves);
-    const int64_t wgs = tiles * g->num_groups * a->num_kv_heads;  // per partition
-    int pp = pl.P;
-    while (pp > 64 && pp % 64 == 0 && wgs * ((g->max_prefix_len + pp - 1) / pp) < 256) pp /= 2;
+    int pp = 256;
+    while (pp < 2048 && (g->max_prefix_len + pp - 1) / pp > 64) pp *= 2;
     pl.pre_P = pp;
   }
   pl.pre_parts = max(1, (g->max_prefix_len + pl.pre_P - 1) / pl.pre_P);
@@ -1781,6 +1884,11 @@ PA_API pa_status pa_decode_prefix(const pa_decode_args* a, const pa_prefix_group
     return PA_ERR_INVALID;
   if (a->num_seqs > 65535 || pl.max_parts > 65535 || a->num_q_heads > 65535)
     return PA_ERR_UNSUPPORTED;
+  if (pl.n_grp > 0) {  // one 1-D grid of both passes; the kernel numbers it with 32-bit ints
+    int px, py, pz, dx, dy;
+    const int64_t wgs = fused_prefix_wgs(a, pl, &px, &py, &pz) + fused_decode_wgs(a, pl, &dx, &dy);
+    if (wgs * 64 * kWaves > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+  }
   if ((a->k_new == nullptr) != (a->v_new == nullptr)) return PA_ERR_INVALID;
   if (a->k_new && (!aligned16(a->k_new) || !aligned16(a->v_new))) return PA_ERR_INVALID;
   if (pl.ws_bytes &&

@@ -328,8 +328,17 @@ def test_prefill_and_prefix_validation(L):
     buf = (ctypes.c_int32 * 4)()
     g.group_start = g.prefix_len = ctypes.addressof(buf)
     g.max_prefix_len = 64
-    # 64 / 32 = 2 partial slots for the prefix plus 160 / 32 = 5 partitions
-    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 4 * 8 * 7 * 130 * 4
+    # one partial slot for the prefix (256-token prefix partitions) plus
+    # 160 / 32 = 5 partitions
+    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 4 * 8 * 6 * 130 * 4
+    # long prefixes: 256-token partitions, doubled while more than 64 of them
+    # (4 sequences of up to 200,000 tokens at P = 4096: 49 decode partitions)
+    long_d = _args(partition_size=4096, max_context_len=200000, max_blocks_per_seq=12500,
+                   num_blocks=12500)
+    for plen, parts in [(2048, 8), (16384, 64), (16385, 33), (100000, 49), (200000, 98)]:
+        g.max_prefix_len = plen
+        assert L.pa_decode_prefix_workspace_bytes(long_d, ctypes.byref(g)) == \
+            4 * 8 * (parts + 49) * 130 * 4, plen
     g.max_prefix_len = 161  # beyond max_context_len
     assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 0
     g.max_prefix_len = 64

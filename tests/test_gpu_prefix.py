@@ -110,6 +110,16 @@ def test_prefix_with_partitions(P):
     run_prefix_case(case, gs, shared, f"prefix partitions P={P}", fused=True, partition_size=P)
 
 
+def test_long_prefix_doubled_partitions():
+    """Prefixes past 16,384 tokens take 512-token prefix partitions (at most
+    64 prefix partials per row reach the merge): two groups sharing 17,600 and
+    16,480 tokens."""
+    case, gs, shared = wl.shared_prefix_case(4600, [(1100, [1, 40, 300]), (1030, [5, 64])],
+                                             8, 2, 128, 16, "bf16")
+    assert int(np.max(shared)) > 16384
+    run_prefix_case(case, gs, shared, "long prefix", fused=True)
+
+
 def test_cow_shaped_batch_matches_plain_decode():
     """32 sequences sharing a 2048-token prefix (block size 32) with private
     suffixes of 1..512 tokens: pa_decode_prefix and pa_decode agree."""
