@@ -37,10 +37,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="llama13b_f16",
                     choices=["llama13b_f16", "mixed_gqa_bf16", "long_bf16", "prefill_llama13b_f16",
-                             "shared_prefix_bf16"])
+                             "shared_prefix_bf16", "cow_bf16"])
     ap.add_argument("--no-prefix-groups", action="store_true",
-                    help="shared_prefix_bf16 only: decode with pa_decode (every sequence reads the "
-                         "shared prefix itself) instead of pa_decode_prefix")
+                    help="shared_prefix_bf16 and cow_bf16: decode with pa_decode (every sequence "
+                         "reads the shared prefix itself) instead of pa_decode_prefix")
     ap.add_argument("--replicas", type=int, default=0, help="0 = as many as the pool allows (max 16)")
     ap.add_argument("--partition-size", type=int, default=-1, help="-1 = the workload's own")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget; 0 = skip")
@@ -94,6 +94,8 @@ def main():
         return bench_prefill(args, dev)
     if args.config == "shared_prefix_bf16":
         return bench_shared_prefix(args, dev)
+    if args.config == "cow_bf16":
+        return bench_cow(args, dev)
     i8 = args.kv == "i8"
     case = build_case(args.config, args.replicas, "i8" if i8 else None, args.block_size)
     R, S, dtype = case.replicas, case.S, case.dtype
@@ -424,6 +426,127 @@ def bench_shared_prefix(args, dev):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_launch_ms": round(ms, 5), "algorithmic_bytes_per_launch": alg},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def bench_cow(args, dev):
+    """One step of the copy-on-write workload: 32 sequences forked from one
+    2048-token prefix (block size 32, bf16, 32 query / 8 KV heads), each with a
+    private suffix of 1..512 tokens and forked once more (parallel sampling),
+    so every partly filled tail block is shared by two sequences.  The native
+    block manager builds this state and takes the step's append: it returns
+    one slot per sequence and a (source, copy) pair per shared partial tail.
+    One step = pa_copy_blocks over those pairs, then the decode, which stores
+    each new token into its slot (now in the copy) and attends:
+    pa_decode_prefix with the 2048 shared tokens as the group's prefix
+    (--no-prefix-groups: pa_decode).  R replicas of the whole arrangement sit
+    in disjoint block ranges of one pool and are cycled; a replica's copies
+    and token stores repeat with the same result each cycle, so every step
+    does the same work.  value = logical KV bytes (every sequence's whole
+    context) per second."""
+    import torch
+    from paged_kv_cache_328_amd import pagedattn as pa
+    from paged_kv_cache_328_amd import workloads as wl
+    plan = wl.cow_plan()
+    BS, NB, n, Hq, Hkv, D = plan["BS"], plan["NB"], plan["n"], plan["Hq"], plan["Hkv"], plan["D"]
+    R = args.replicas or 8
+    A = pa.Allocator(NB, BS, plan["init_free_order"])
+    A.pa_seq_add(0)
+    for _ in range(plan["prefix"]):
+        A.pa_seq_append_slot(0)
+    for i in range(1, n):
+        A.pa_seq_fork(0, i)
+    for i in range(n):
+        for _ in range(plan["suffix"][i]):
+            A.pa_seq_append_slot(i)
+    for i in range(n):
+        A.pa_seq_fork(i, 1000 + i)
+    th = time.perf_counter()
+    slots, pairs = A.pa_seq_append_slots(list(range(n)))
+    host_us = (time.perf_counter() - th) * 1e6
+    lens = np.array([A.pa_seq_len(i) for i in range(n)], np.int32)
+    tables = [A.pa_seq_block_table(i) for i in range(n)]
+    A.close()
+    table = np.zeros((n, max(len(t) for t in tables)), np.int32)
+    for i, t in enumerate(tables):
+        table[i, :len(t)] = t
+    pairs = np.asarray(pairs, np.int32).reshape(-1, 2)
+    shared = plan["prefix"]  # whole blocks shared by every sequence after the copies
+    max_ctx = int(lens.max())
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.base_seed("cow_bf16"))
+    ks, vs = wl.pool_shapes(NB * R, Hkv, D, BS, "bf16")
+    kd = torch.randn(ks, dtype=torch.bfloat16, device=dev, generator=g)
+    vd = torch.randn(vs, dtype=torch.bfloat16, device=dev, generator=g)
+    stream = torch.cuda.current_stream()
+    lens_d = torch.from_numpy(lens).to(dev)
+    use_groups = not args.no_prefix_groups
+    steps = []
+    for r in range(R):
+        tab_d = torch.from_numpy(table + r * NB).to(dev)
+        pairs_d = torch.from_numpy(pairs + r * NB).to(dev)
+        q = torch.randn((n, Hq, D), dtype=torch.bfloat16, device=dev, generator=g)
+        kn = torch.randn((n, Hkv, D), dtype=torch.bfloat16, device=dev, generator=g)
+        vn = torch.randn((n, Hkv, D), dtype=torch.bfloat16, device=dev, generator=g)
+        out = torch.empty_like(q)
+        copy = pa.prepare_copy_blocks(kd, vd, pairs_d, stream=stream, head_dim=D)
+        if use_groups:
+            gst = torch.tensor([0, n], dtype=torch.int32, device=dev)
+            pl = torch.tensor([shared], dtype=torch.int32, device=dev)
+            dec = pa.prepare_decode_prefix(out, q, kd, vd, tab_d, lens_d, plan["scale"], max_ctx, gst,
+                                           pl, n, shared, stream=stream, k_new=kn, v_new=vn)
+        else:
+            dec = pa.prepare_decode(out, q, kd, vd, tab_d, lens_d, plan["scale"], max_ctx,
+                                    stream=stream, k_new=kn, v_new=vn, context_lens_host=lens)
+        steps.append((copy, dec))
+
+    def step(i):
+        copy, dec = steps[i % R]
+        copy()
+        dec()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    per_tok = 2 * Hkv * D * 2
+    logical = int(lens.sum()) * per_tok
+    unique = (shared + int((lens - shared).sum())) * per_tok
+    copy_bytes = 2 * len(pairs) * 2 * Hkv * D * BS * 2  # K and V tiles, read and written
+    alg = (unique if use_groups else logical) + copy_bytes + 2 * n * Hq * D * 2 + n * per_tok
+    result = {
+        "metric": "paged decode attention: achieved KV GB/s (% HBM peak) and seq-steps/s",
+        "value": round(logical / sec / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5), "gpu_ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "seq_steps_per_s": round(n / sec, 1),
+        "unique_kv_gbs": round(unique / sec / 1e9, 2),
+        "config": {"workload": "cow_bf16" + ("" if use_groups else " (pa_decode, no prefix groups)"),
+                   "num_seqs": n, "forked_siblings": n, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                   "block_size": BS, "shared_prefix_tokens": shared, "cow_pairs": int(len(pairs)),
+                   "context_tokens": int(lens.sum()), "replicas": R,
+                   "logical_kv_bytes_per_step": logical, "unique_kv_bytes_per_step": unique,
+                   "step": "pa_copy_blocks(%d pairs) + %s(fused append)"
+                           % (len(pairs), "pa_decode_prefix" if use_groups else "pa_decode")},
+        "roofline": {"kernel": "copy_blocks_kernel + " + ("prefix_suffix_kernel" if use_groups
+                                                          else "decode_mfma_kernel") + " + merge_kernel",
+                     "bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(ms, 5), "algorithmic_bytes_per_launch": alg},
+        "host_bookkeeping_us": round(host_us, 2),
     }
     print(json.dumps(result), flush=True)
 

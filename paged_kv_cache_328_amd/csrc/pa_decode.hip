@@ -1364,7 +1364,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
 // ----------------------------------------------------------------------------
 // Pass 2: merge the partitions of every (sequence, query head) that has more
 // than one.  grid: x = query head, y = sequence; block = NT threads (128
-// when every context fits in 16 partitions, else 512).
+// when every row has at most 32 partials, else 512).
 // Thread (r, c4) walks partitions r, r + ROWS, ... keeping its own running
 // (max, sum, output for channels 4*c4..+3) with the log-sum-exp rule, so one
 // pass reads every live partial once and all loads of a batch are independent
@@ -1709,7 +1709,7 @@ template <typename Store, int D>
 void launch_merge(const pa_decode_args* a, const Plan& pl, const float* wa, const float* wm,
                   hipStream_t st) {
   dim3 grid((unsigned)a->num_q_heads, (unsigned)a->num_seqs);
-  if (pl.max_parts <= 16)
+  if (pl.max_parts <= 32)  // one batch of loads per thread at D = 128
     merge_kernel<Store, D, 128><<<grid, 128, 0, st>>>(
         (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
         a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts, pl.grp_start, pl.grp_len,
