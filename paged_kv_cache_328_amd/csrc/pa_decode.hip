@@ -742,17 +742,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
     int xcd_order) {
   extern __shared__ float lds[];
   // Workgroups are dealt to the XCDs round-robin (linear id L goes to XCD
-  // L % kXcds).  For 16-bit caches the grid is renumbered so that each XCD
+  // L % kXcds).  With xcd_order the grid is renumbered so that each XCD
   // takes one contiguous range of the (head, partition, sequence) order: the
   // workgroups of a sequence then run on one XCD, and each XCD touches the
-  // blocks of its own sequences only.  Measured on MI355X: LLaMA-13B-shaped
-  // step 65.7 -> 64.3 us, long context 184.5 -> 181.2 us, mixed lengths
-  // unchanged.  INT8 caches keep the hardware order: all of their workgroups
-  // fit at once (3 waves per SIMD), and contiguous ranges made the
-  // LLaMA-13B-shaped INT8 step 2.7% slower (uneven work per XCD).  The host
-  // clears xcd_order when the grid is a flat work list sized without the
-  // context lengths: its surplus workgroups sit at the end and would leave
-  // the last XCDs idle.
+  // blocks of its own sequences only.  The host sets it for 16-bit caches
+  // on the (head, partition, sequence) grid; measured on MI355X, the
+  // LLaMA-13B-shaped step went from 65.6 to 64.0 us.  It stays off:
+  //   - for INT8 caches: all of their workgroups fit at once (3 waves per
+  //     SIMD), and contiguous ranges made the LLaMA-13B-shaped INT8 step
+  //     2.7% slower (uneven work per XCD);
+  //   - for the flat work list.  In hardware order, with 8 KV heads, each
+  //     XCD takes one head of every sequence, so blocks shared by many
+  //     sequences (a common prefix) are re-read from that XCD's L2.
+  //     Renumbered, a 32-sequence batch sharing 2048 tokens decoded in
+  //     63.3 us instead of 45.7 (long context gained 2%, mixed lengths
+  //     nothing).  Without host context lengths the flat list's surplus
+  //     workgroups also sit at its end and would idle the last XCDs.
   int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
   if (!KV8 && xcd_order) {
     const int64_t X = gridDim.x, Y = gridDim.y;
@@ -1598,7 +1603,7 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
       a->context_lens, (const uint16_t*)a->k_new, (const uint16_t*)a->v_new, a->num_q_heads,
       a->num_kv_heads, G, pl.groups, a->num_blocks, a->max_blocks_per_seq, a->max_context_len,
       a->scale * kLog2e, pl.P, max(pl.max_parts, 1), ws_acc, ws_ml, flat ? a->num_seqs : 0,
-      pl.pre_parts, pl.pre_P, pl.grp_start, pl.grp_len, pl.n_grp, (int)(!flat || pl.units > 0));
+      pl.pre_parts, pl.pre_P, pl.grp_start, pl.grp_len, pl.n_grp, (int)!flat);
 }
 
 // pa_decode_prefix: prefix_suffix_kernel, one launch of the shared-prefix
