@@ -938,6 +938,11 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
   // (INT8: 8*(kk/2) + 2*g4 + kk%2, so that one 16-byte code vector feeds two
   // products)
   auto qchunk = [&](int kk) { return KV8 ? 8 * (kk >> 1) + 2 * g4 + (kk & 1) : 4 * kk + g4; };
+  // The softmax step takes its maximum over the raw products and scales it
+  // once, which needs a scale >= 0: a negative scale is moved onto q by
+  // flipping its sign bits (exact; every product and sum is negated exactly).
+  const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
+  const float sc = fabsf(scale_log2);
   V8 qop[NC][KK];
 #pragma unroll
   for (int nc = 0; nc < NC; ++nc) {
@@ -945,7 +950,7 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const u32x4 raw = head_ok[nc] ? load16(qrow + 8 * qchunk(kk)) : u32x4{0u, 0u, 0u, 0u};
-      qop[nc][kk] = __builtin_bit_cast(V8, raw);
+      qop[nc][kk] = __builtin_bit_cast(V8, raw ^ qsign);
     }
   }
   f32x4 acc[NC][MM];
@@ -1118,11 +1123,13 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
         s0 *= sk[0];
         s1 *= sk[1];
       }
-      float x[8];
+      // y[e]: unscaled logit of token t0 + 4*g4 + e (e < 4) or t0 + 16 + 4*g4
+      // + e - 4 (e >= 4); its base-2 logit is y[e] * sc.
+      float y[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        x[j] = s0[j] * scale_log2;
-        x[4 + j] = s1[j] * scale_log2;
+        y[j] = s0[j];
+        y[4 + j] = s1[j];
       }
       float svc[8];  // INT8: V scales, 0 for dropped tokens (a scale may be NaN)
 #pragma unroll
@@ -1131,14 +1138,24 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (t0 + 4 * g4 + (e & 3) + 16 * (e >> 2) >= lim[nc]) {
-            x[e] = -INFINITY;
+            y[e] = -INFINITY;
             svc[e] = 0.f;
           }
       }
-      float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float my = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
+                       fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+      // maximum over the 4 row groups (lanes i, i+16, i+32, i+48 hold column
+      // i): each lane-row swap of two copies leaves a lane's partner value in
+      // one of the pair
+      {
+        const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(my), __float_as_uint(my),
+                                                          false, false);
+        my = fmaxf(__uint_as_float(h32[0]), __uint_as_float(h32[1]));
+        const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(my), __float_as_uint(my),
+                                                          false, false);
+        my = fmaxf(__uint_as_float(h16[0]), __uint_as_float(h16[1]));
+      }
+      const float mx = my * sc;  // the column's largest base-2 logit of the chunk
       if (__builtin_amdgcn_ballot_w64(mx > m_run[nc] + kSlack) != 0) {
         const float m_new = fmaxf(m_run[nc], mx);
         const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run[nc] - m_new);
@@ -1147,22 +1164,21 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
 #pragma unroll
         for (int mm = 0; mm < MM; ++mm) acc[nc][mm] *= alpha;
       }
-      const float m_use = m_run[nc] == -INFINITY ? 0.f : m_run[nc];
+      const float neg_m = m_run[nc] == -INFINITY ? 0.f : -m_run[nc];
       uint32_t pw[4];
-      float psum = l_run[nc];
       if constexpr (!KV8) {
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          pw[wd] = Ty::pack2(exp2_fast(x[2 * wd] - m_use), exp2_fast(x[2 * wd + 1] - m_use));
-          psum = Ty::sum2(pw[wd], psum);  // the weights the PV product sees
-        }
+        for (int wd = 0; wd < 4; ++wd)
+          pw[wd] = Ty::pack2(exp2_fast(fmaf(y[2 * wd], sc, neg_m)),
+                             exp2_fast(fmaf(y[2 * wd + 1], sc, neg_m)));
       } else {
         // INT8 values: the PV product sees weight * V scale per token; the sum
         // takes rounded(p * s) / s, as in decode (a token with scale 0 counts
         // with its weight p).
         float pr[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(x[e] - m_use);
+        for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(fmaf(y[e], sc, neg_m));
+        float psum = l_run[nc];
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {
           const float s0w = svc[2 * wd], s1w = svc[2 * wd + 1];
@@ -1170,13 +1186,22 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
           psum += s0w != 0.f ? Ty::lo_f32(pw[wd]) * __builtin_amdgcn_rcpf(s0w) : pr[2 * wd];
           psum += s1w != 0.f ? Ty::hi_f32(pw[wd]) * __builtin_amdgcn_rcpf(s1w) : pr[2 * wd + 1];
         }
+        l_run[nc] = psum;
       }
-      l_run[nc] = psum;
       const auto a32 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
       const auto b32 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
       const auto a16 = __builtin_amdgcn_permlane16_swap(a32[0], a32[1], false, false);
       const auto b16 = __builtin_amdgcn_permlane16_swap(b32[0], b32[1], false, false);
-      const V8 pop = __builtin_bit_cast(V8, u32x4{a16[0], b16[0], a16[1], b16[1]});
+      const u32x4 pwords = {a16[0], b16[0], a16[1], b16[1]};
+      if constexpr (!KV8) {
+        // the weights the PV product sees, summed after the swaps: the four
+        // lanes of a column hold the same weights in another order
+        float psum = l_run[nc];
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) psum = Ty::sum2(pwords[wd], psum);
+        l_run[nc] = psum;
+      }
+      const V8 pop = __builtin_bit_cast(V8, pwords);
 #pragma unroll
       for (int mm = 0; mm < MM; ++mm) {
         if constexpr (!KV8)
