@@ -941,8 +941,12 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
   // The softmax step takes its maximum over the raw products and scales it
   // once, which needs a scale >= 0: a negative scale is moved onto q by
   // flipping its sign bits (exact; every product and sum is negated exactly).
+  // A zero scale is taken as the smallest normal float, so that a dropped
+  // token's -inf logit never meets a zero factor; every kept weight is then
+  // 1 up to rounding, as scale 0 means.
   const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
-  const float sc = fabsf(scale_log2);
+  const float sc = fmaxf(fabsf(scale_log2), 1.17549435e-38f);
+  const float inv_sc = 1.f / sc;
   V8 qop[NC][KK];
 #pragma unroll
   for (int nc = 0; nc < NC; ++nc) {
@@ -955,12 +959,16 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
   }
   f32x4 acc[NC][MM];
   float m_run[NC], l_run[NC];
+  // thr: unscaled logit above which a chunk moves the reference maximum,
+  // (m_run + kSlack) / scale, kept up to date with m_run
+  float thr[NC];
 #pragma unroll
   for (int nc = 0; nc < NC; ++nc) {
 #pragma unroll
     for (int mm = 0; mm < MM; ++mm) acc[nc][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[nc] = -INFINITY;
     l_run[nc] = 0.f;
+    thr[nc] = -INFINITY;
   }
 
   // Block ids in registers, as in decode: lane j holds block j % BPC of chunk
@@ -1142,27 +1150,33 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
             svc[e] = 0.f;
           }
       }
-      float my = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
-                       fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
-      // maximum over the 4 row groups (lanes i, i+16, i+32, i+48 hold column
-      // i): each lane-row swap of two copies leaves a lane's partner value in
-      // one of the pair
-      {
+      // The reference maximum moves only when some column's chunk maximum
+      // passes it by more than kSlack, that is when some unscaled logit
+      // exceeds the column's threshold; only then is the chunk maximum formed.
+      bool above = false;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) above |= y[e] > thr[nc];
+      if (__builtin_amdgcn_ballot_w64(above) != 0) {
+        float my = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
+                         fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+        // maximum over the 4 row groups (lanes i, i+16, i+32, i+48 hold
+        // column i): each lane-row swap of two copies leaves a lane's
+        // partner value in one of the pair
         const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(my), __float_as_uint(my),
                                                           false, false);
         my = fmaxf(__uint_as_float(h32[0]), __uint_as_float(h32[1]));
         const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(my), __float_as_uint(my),
                                                           false, false);
         my = fmaxf(__uint_as_float(h16[0]), __uint_as_float(h16[1]));
-      }
-      const float mx = my * sc;  // the column's largest base-2 logit of the chunk
-      if (__builtin_amdgcn_ballot_w64(mx > m_run[nc] + kSlack) != 0) {
-        const float m_new = fmaxf(m_run[nc], mx);
-        const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run[nc] - m_new);
-        m_run[nc] = m_new;
-        l_run[nc] *= alpha;
+        const float m_new = fmaxf(m_run[nc], my * sc);
+        if (m_new > m_run[nc]) {
+          const float alpha = m_run[nc] == -INFINITY ? 0.f : exp2_fast(m_run[nc] - m_new);
+          m_run[nc] = m_new;
+          thr[nc] = (m_new + kSlack) * inv_sc;
+          l_run[nc] *= alpha;
 #pragma unroll
-        for (int mm = 0; mm < MM; ++mm) acc[nc][mm] *= alpha;
+          for (int mm = 0; mm < MM; ++mm) acc[nc][mm] *= alpha;
+        }
       }
       const float neg_m = m_run[nc] == -INFINITY ? 0.f : -m_run[nc];
       uint32_t pw[4];

@@ -70,6 +70,17 @@ def test_prefill_edge_shapes(dtype, D, BS, Hq, Hkv):
     run_prefill(case, f"prefill {dtype} D{D} BS{BS} {Hq}/{Hkv}")
 
 
+@pytest.mark.parametrize("kv", [None, "i8"])
+@pytest.mark.parametrize("scale", [0.0, -0.0884, 0.7])
+def test_prefill_zero_negative_and_large_scale(kv, scale):
+    """The softmax step takes its maximum over the unscaled products: a zero
+    scale (uniform weights), a negative one (moved onto q as a sign flip) and
+    a large one (logits of order 100) must all match the oracle."""
+    case = wl.prefill_case(3300, PRIORS, CHUNKS, 16, 4, 128, 16, "bf16", kv_dtype=kv)
+    case.scale = float(np.float32(scale))
+    run_prefill(case, f"prefill scale={scale} kv={kv or 'bf16'}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("D,BS", [(128, 16), (64, 32), (128, 8), (128, 64)])
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 2)])
