@@ -1442,38 +1442,54 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
 // are then combined in LDS in row order, so the result depends only on the
 // partition contents, never on where the blocks sit.
 // ----------------------------------------------------------------------------
+// The rows a merge launch covers, from the host copy of the context lengths:
+// the sequences with more than one partition, with their partition counts.
+// Passed by value as a kernel argument; n = 0 means no list (the grid
+// covers every sequence, and each workgroup reads its length).
+constexpr int kMaxSplit = 512;
+struct SplitList {
+  int32_t n;
+  uint16_t seq[kMaxSplit];
+  uint16_t parts[kMaxSplit];
+};
+
 template <typename Store, int D, int NT>
 __global__ __launch_bounds__(NT) void merge_kernel(
     typename Store::T* __restrict__ out, const int32_t* __restrict__ lens,
     const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, int Hq, int max_ctx,
     int max_blocks, int BS, int P, int max_parts, const int32_t* __restrict__ grp_start,
-    const int32_t* __restrict__ grp_len, int n_grp, int pre_parts, int pre_P) {
+    const int32_t* __restrict__ grp_len, int n_grp, int pre_parts, int pre_P, SplitList split) {
   constexpr int C4 = D / 4;                   // threads per partition row
   constexpr int ROWS = NT / C4;               // partitions read at once
   constexpr int U = 8;                        // partitions per thread per batch
   __shared__ float sm[ROWS][C4], sl[ROWS][C4];
   __shared__ f32x4 so[ROWS][C4];
-  const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.x, tid = threadIdx.x;
   const int r = tid / C4, c4 = tid - r * C4;
-  const int64_t base = ((int64_t)s * Hq + h) * max_parts;
-
-  const int c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
-  // With prefix groups, partial 0 is the shared prefix (when the sequence's
-  // group has one) and the decode partitions follow.
-  int skip = 0;
-  if (n_grp > 0) {
-    int lo = 0, hi = n_grp - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (grp_start[mid] <= s) lo = mid;
-      else hi = mid - 1;
+  int s, n_p, skip = 0;
+  if (split.n > 0) {  // a split sequence of the host's list: no length to read
+    s = split.seq[blockIdx.y];
+    n_p = min((int)split.parts[blockIdx.y], max_parts);
+  } else {
+    s = blockIdx.y;
+    const int c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
+    // With prefix groups, partial 0 is the shared prefix (when the
+    // sequence's group has one) and the decode partitions follow.
+    if (n_grp > 0) {
+      int lo = 0, hi = n_grp - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (grp_start[mid] <= s) lo = mid;
+        else hi = mid - 1;
+      }
+      skip = clampi(grp_len[lo], 0, min(c, pre_parts * pre_P));
     }
-    skip = clampi(grp_len[lo], 0, min(c, pre_parts * pre_P));
+    n_p = min((n_grp > 0 ? (skip + pre_P - 1) / pre_P : 0) +
+                  (c - (skip & ~(kChunk - 1)) + P - 1) / P,
+              max_parts);
+    if (n_p <= 1 && skip == 0) return;  // pass 1 stored the output itself
   }
-  const int n_p = min((n_grp > 0 ? (skip + pre_P - 1) / pre_P : 0) +
-                          (c - (skip & ~(kChunk - 1)) + P - 1) / P,
-                      max_parts);
-  if (n_p <= 1 && skip == 0) return;  // pass 1 stored the output itself
+  const int64_t base = ((int64_t)s * Hq + h) * max_parts;
   // Only the row's own partials are read (the length is known first): a
   // speculative batch over max_parts slots read several times the live
   // bytes on mixed-length batches.
@@ -1777,17 +1793,43 @@ void launch_f32_bs(const pa_decode_args* a, const Plan& pl, float* wa, float* wm
 template <typename Store, int D>
 void launch_merge(const pa_decode_args* a, const Plan& pl, const float* wa, const float* wm,
                   hipStream_t st) {
-  dim3 grid((unsigned)a->num_q_heads, (unsigned)a->num_seqs);
+  // With the host copy of the context lengths (and no prefix groups) the
+  // grid covers only the split sequences; when none is split there is no
+  // merge launch at all.  Measured on MI355X (mixed-length batch): see the
+  // design notes of the merge.
+  SplitList sl;
+  sl.n = 0;
+  unsigned rows = (unsigned)a->num_seqs;
+  if (a->context_lens_host && pl.n_grp == 0) {
+    int n = 0;
+    for (int s = 0; s < a->num_seqs && n >= 0; ++s) {
+      const int parts = (a->context_lens_host[s] + pl.P - 1) / pl.P;
+      if (parts <= 1) continue;
+      if (n == kMaxSplit) {
+        n = -1;  // too many for the list: every sequence reads its length
+        break;
+      }
+      sl.seq[n] = (uint16_t)s;
+      sl.parts[n] = (uint16_t)parts;
+      ++n;
+    }
+    if (n == 0) return;
+    if (n > 0) {
+      sl.n = n;
+      rows = (unsigned)n;
+    }
+  }
+  dim3 grid((unsigned)a->num_q_heads, rows);
   if (pl.max_parts <= 32)  // one batch of loads per thread at D = 128
     merge_kernel<Store, D, 128><<<grid, 128, 0, st>>>(
         (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
         a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts, pl.grp_start, pl.grp_len,
-        pl.n_grp, pl.pre_parts, pl.pre_P);
+        pl.n_grp, pl.pre_parts, pl.pre_P, sl);
   else
     merge_kernel<Store, D, 512><<<grid, 512, 0, st>>>(
         (typename Store::T*)a->out, a->context_lens, wa, wm, a->num_q_heads, a->max_context_len,
         a->max_blocks_per_seq, a->block_size, pl.P, pl.max_parts, pl.grp_start, pl.grp_len,
-        pl.n_grp, pl.pre_parts, pl.pre_P);
+        pl.n_grp, pl.pre_parts, pl.pre_P, sl);
 }
 
 template <typename Store>

@@ -459,6 +459,48 @@ def test_host_context_lens_size_the_grid_bit_identical(kv, P):
     check_attention(outs[1], want, dtype, f"host lens kv={kv} P={P}")
 
 
+@pytest.mark.parametrize("name,S,lens_fn,dtype,P,max_ctx", [
+    # no context spans two partitions although max_context_len allows 16:
+    # with the host copy there is no merge launch at all
+    ("no split", 40, lambda rng, S: rng.integers(1, 257, size=S), "bf16", 256, 4096),
+    # 600 split sequences: more than the host list holds, so the merge falls
+    # back to one row per sequence that reads its own length
+    ("600 split", 600, lambda rng, S: rng.integers(257, 700, size=S), "f16", 256, 0),
+    # fp32 queries and cache: the fp32 pass 1 with the same merge
+    ("f32", 30, lambda rng, S: rng.integers(1, 2000, size=S), "f32", 512, 0),
+])
+def test_host_lens_merge_rows(name, S, lens_fn, dtype, P, max_ctx):
+    """The merge covers only the split sequences of the host copy of the
+    lengths; the output equals the call without the copy bit for bit and
+    matches the oracle."""
+    import torch
+    rng = np.random.default_rng(79)
+    lens = [int(x) for x in lens_fn(rng, S)]
+    case = wl.random_case(906 + S, S, 2, 1, 64, 16, dtype, lens, partition_size=P)
+    t0 = np.ascontiguousarray(case.block_tables[0])
+    poison_tails(oracle, case.k_cache, case.v_cache, t0, case.context_lens, dtype)
+    kd, vd = to_dev(case.k_cache, dtype), to_dev(case.v_cache, dtype)
+    qd = to_dev(case.q[0], dtype)
+    td, ld = ints_to_dev(t0), ints_to_dev(case.context_lens)
+    bound = max(max_ctx, case.max_context)
+    if bound > t0.shape[1] * case.BS:  # the table must reach max_context_len
+        t0 = np.pad(t0, ((0, 0), (0, -(-bound // case.BS) - t0.shape[1])))
+        td = ints_to_dev(np.ascontiguousarray(t0))
+    outs = []
+    for host in (None, case.context_lens):
+        announce(f"merge rows {name}: host={'yes' if host is not None else 'no'} S={S} P={P} "
+                 f"max_ctx={bound}")
+        out = torch.empty_like(qd)
+        pa.pa_decode(out, qd, kd, vd, td, ld, case.scale, bound, partition_size=P,
+                     context_lens_host=host)
+        _sync()
+        outs.append(to_host(out, dtype))
+    assert same_bits(outs[0], outs[1]), f"{name}: host copy of the lengths changed the output"
+    want = oracle.decode(np.ascontiguousarray(case.q[0]), case.k_cache, case.v_cache, t0,
+                         case.context_lens, case.scale, dtype, num_threads=16)
+    check_attention(outs[1], want, dtype, f"merge rows {name}")
+
+
 def test_large_logits_stay_finite():
     lens = [64, 300, 1000]
     case = wl.random_case(902, len(lens), 8, 2, 128, 16, "bf16", lens, partition_size=128)
