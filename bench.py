@@ -384,7 +384,7 @@ def bench_shared_prefix(args, dev):
             pl = torch.tensor([int(shared[r])], dtype=torch.int32, device=dev)
             calls.append(pa.prepare_decode_prefix(out, q, kd, vd, tables, lens, case.scale, max_ctx,
                                                   gst, pl, n, int(shared[r]), stream=stream,
-                                                  k_new=kn, v_new=vn))
+                                                  k_new=kn, v_new=vn, min_prefix_len=int(shared[r])))
         else:
             calls.append(pa.prepare_decode(out, q, kd, vd, tables, lens, case.scale, max_ctx,
                                            stream=stream, k_new=kn, v_new=vn,
@@ -496,7 +496,8 @@ def bench_cow(args, dev):
             gst = torch.tensor([0, n], dtype=torch.int32, device=dev)
             pl = torch.tensor([shared], dtype=torch.int32, device=dev)
             dec = pa.prepare_decode_prefix(out, q, kd, vd, tab_d, lens_d, plan["scale"], max_ctx, gst,
-                                           pl, n, shared, stream=stream, k_new=kn, v_new=vn)
+                                           pl, n, shared, stream=stream, k_new=kn, v_new=vn,
+                                           min_prefix_len=shared)
         else:
             dec = pa.prepare_decode(out, q, kd, vd, tab_d, lens_d, plan["scale"], max_ctx,
                                     stream=stream, k_new=kn, v_new=vn, context_lens_host=lens)

@@ -208,6 +208,11 @@ typedef struct pa_prefix_groups {
   int32_t num_groups;
   int32_t max_group_size;       /* host bound of the group sizes */
   int32_t max_prefix_len;       /* host bound of prefix_len, <= max_context_len */
+  int32_t min_prefix_len;       /* host lower bound of prefix_len, 0..max_prefix_len;
+                                   0 = none.  A member's own tokens then span at
+                                   most max_context_len - min_prefix_len tokens,
+                                   which sizes their part of the grid; a prefix
+                                   shorter than it is a precondition violation. */
 } pa_prefix_groups;
 
 PA_API size_t pa_decode_prefix_workspace_bytes(const pa_decode_args* args,

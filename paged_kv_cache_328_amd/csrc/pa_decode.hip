@@ -1555,6 +1555,7 @@ struct Plan {
   int max_group = 0;
   int pre_parts = 0;  // partitions of the longest shared prefix
   int pre_P = 0;      // tokens per partition of the shared prefixes
+  int own_parts = 0;  // partitions of the longest run of a member's own tokens
   // (sequence, partition) units of the flat work list, from the host copy of
   // the context lengths (0 = unknown: the grid covers num_seqs * max_parts)
   int64_t units = 0;
@@ -1678,7 +1679,7 @@ int64_t fused_prefix_wgs(const pa_decode_args* a, const Plan& pl, int* px, int* 
 
 int64_t fused_decode_wgs(const pa_decode_args* a, const Plan& pl, int* dx, int* dy) {
   *dx = a->num_kv_heads * pl.groups;
-  *dy = max((a->max_context_len + pl.P - 1) / pl.P, 1);
+  *dy = pl.own_parts;
   return (int64_t)dx[0] * dy[0] * a->num_seqs;
 }
 
@@ -1910,7 +1911,8 @@ static pa_status prefix_plan(const pa_decode_args* a, const pa_prefix_groups* g,
   if (g->num_groups == 0) return PA_OK;  // plain decode
   if (!g->group_start || !g->prefix_len || g->max_group_size == 0 ||
       g->max_group_size > a->num_seqs || g->max_prefix_len < 0 ||
-      g->max_prefix_len > a->max_context_len)
+      g->max_prefix_len > a->max_context_len || g->min_prefix_len < 0 ||
+      g->min_prefix_len > g->max_prefix_len)
     return PA_ERR_INVALID;
   if ((int64_t)g->num_groups * a->num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   pl.grp_start = g->group_start;
@@ -1932,6 +1934,10 @@ static pa_status prefix_plan(const pa_decode_args* a, const pa_prefix_groups* g,
     pl.pre_P = pp;
   }
   pl.pre_parts = max(1, (g->max_prefix_len + pl.pre_P - 1) / pl.pre_P);
+  // A member's own tokens start at the 32-token boundary at or below its
+  // prefix length, so with a host lower bound of the prefixes they span at
+  // most max_context_len - floor32(min_prefix_len) tokens.
+  pl.own_parts = max(1, (a->max_context_len - (g->min_prefix_len & ~(kChunk - 1)) + pl.P - 1) / pl.P);
   pl.max_parts = pl.pre_parts + (a->max_context_len + pl.P - 1) / pl.P;
   pl.ws_bytes = (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * (a->head_dim + 2) * 4;
   return PA_OK;

@@ -69,7 +69,7 @@ class pa_prefill_args(ctypes.Structure):
 
 class pa_prefix_groups(ctypes.Structure):
     _fields_ = [("group_start", _P), ("prefix_len", _P), ("num_groups", _I32),
-                ("max_group_size", _I32), ("max_prefix_len", _I32)]
+                ("max_group_size", _I32), ("max_prefix_len", _I32), ("min_prefix_len", _I32)]
 
 
 def lib():
@@ -317,10 +317,10 @@ def prepare_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_
                         (a, out, q, k_cache, v_cache, block_tables, context_lens, query_start))
 
 
-def make_prefix_groups(group_start, prefix_len, max_group_size, max_prefix_len):
+def make_prefix_groups(group_start, prefix_len, max_group_size, max_prefix_len, min_prefix_len=0):
     """pa_prefix_groups from int32 device tensors: group_start [G + 1],
     prefix_len [G] (tokens), with host bounds of the group sizes and the
-    prefix lengths."""
+    prefix lengths (min_prefix_len 0 = no lower bound)."""
     torch = _torch()
     if group_start.dtype != torch.int32 or prefix_len.dtype != torch.int32:
         raise TypeError("group_start and prefix_len must be int32")
@@ -330,6 +330,7 @@ def make_prefix_groups(group_start, prefix_len, max_group_size, max_prefix_len):
     g = pa_prefix_groups()
     g.group_start, g.prefix_len = _ptr(group_start), _ptr(prefix_len)
     g.num_groups, g.max_group_size, g.max_prefix_len = G, int(max_group_size), int(max_prefix_len)
+    g.min_prefix_len = int(min_prefix_len)
     return g
 
 
@@ -339,13 +340,13 @@ def pa_decode_prefix_workspace_bytes(args, groups):
 
 def pa_decode_prefix(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                      group_start, prefix_len, max_group_size, max_prefix_len, partition_size=0,
-                     workspace=None, stream=None, k_new=None, v_new=None):
+                     workspace=None, stream=None, k_new=None, v_new=None, min_prefix_len=0):
     """pa_decode for sequences ordered by shared-prefix group: group g is
     sequences group_start[g]..group_start[g+1]-1 sharing their first
     prefix_len[g] tokens; the prefix is read once per group."""
     a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                          max_context_len, partition_size, workspace, k_new, v_new)
-    g = make_prefix_groups(group_start, prefix_len, max_group_size, max_prefix_len)
+    g = make_prefix_groups(group_start, prefix_len, max_group_size, max_prefix_len, min_prefix_len)
     need = pa_decode_prefix_workspace_bytes(a, g)
     if need and workspace is None:
         workspace = _torch().zeros(need, dtype=_torch().uint8, device=q.device)
@@ -358,10 +359,11 @@ def pa_decode_prefix(out, q, k_cache, v_cache, block_tables, context_lens, scale
 
 def prepare_decode_prefix(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                           max_context_len, group_start, prefix_len, max_group_size,
-                          max_prefix_len, partition_size=0, stream=None, k_new=None, v_new=None):
+                          max_prefix_len, partition_size=0, stream=None, k_new=None, v_new=None,
+                          min_prefix_len=0):
     a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                          max_context_len, partition_size, None, k_new, v_new)
-    g = make_prefix_groups(group_start, prefix_len, max_group_size, max_prefix_len)
+    g = make_prefix_groups(group_start, prefix_len, max_group_size, max_prefix_len, min_prefix_len)
     need = pa_decode_prefix_workspace_bytes(a, g)
     workspace = None
     if need:

@@ -339,6 +339,14 @@ def test_prefill_and_prefix_validation(L):
         g.max_prefix_len = plen
         assert L.pa_decode_prefix_workspace_bytes(long_d, ctypes.byref(g)) == \
             4 * 8 * (parts + 49) * 130 * 4, plen
+    g.max_prefix_len = 64
+    g.min_prefix_len = 65   # a lower bound above the upper one
+    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 0
+    g.min_prefix_len = -1
+    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 0
+    g.min_prefix_len = 64   # the bound does not change the workspace
+    assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 4 * 8 * 6 * 130 * 4
+    g.min_prefix_len = 0
     g.max_prefix_len = 161  # beyond max_context_len
     assert L.pa_decode_prefix_workspace_bytes(d, ctypes.byref(g)) == 0
     g.max_prefix_len = 64

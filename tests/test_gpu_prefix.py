@@ -120,6 +120,42 @@ def test_long_prefix_doubled_partitions():
     run_prefix_case(case, gs, shared, "long prefix", fused=True)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_min_prefix_len_bounds_the_grid(fused):
+    """A host lower bound of the prefix lengths shrinks the grid of the
+    members' own tokens; every unit that exists computes what it computed
+    before, so the output is bit-identical to the call without the bound."""
+    import torch
+    groups = [(128, [1, 40, 300]), (64, [5, 700]), (70, [33])]
+    outs = []
+    for bound in (False, True):
+        case, gs, shared = wl.shared_prefix_case(4700, groups, 16, 4, 128, 16, "bf16")
+        tables = np.ascontiguousarray(case.block_tables[0])
+        poison_tails(oracle, case.k_cache, case.v_cache, tables, case.context_lens, "bf16")
+        kd, vd = to_dev(case.k_cache, "bf16"), to_dev(case.v_cache, "bf16")
+        qd = to_dev(np.ascontiguousarray(case.q[0]), "bf16")
+        extra = {}
+        if fused:
+            extra = dict(k_new=to_dev(np.ascontiguousarray(case.new_k[0]), "bf16"),
+                         v_new=to_dev(np.ascontiguousarray(case.new_v[0]), "bf16"))
+        out = torch.empty_like(qd)
+        lo = int(np.min(shared)) if bound else 0
+        announce(f"min prefix bound={lo} fused={fused}")
+        pa.pa_decode_prefix(out, qd, kd, vd, ints_to_dev(tables), ints_to_dev(case.context_lens),
+                            case.scale, case.max_context, ints_to_dev(gs), ints_to_dev(shared),
+                            int(np.max(np.diff(gs))), int(np.max(shared)), min_prefix_len=lo,
+                            **extra)
+        _sync()
+        outs.append(to_host(out, "bf16"))
+    assert same_bits(outs[0], outs[1]), "the lower bound of the prefixes changed the output"
+    if fused:
+        oracle.write_kv(np.ascontiguousarray(case.new_k[0]), np.ascontiguousarray(case.new_v[0]),
+                        case.k_cache, case.v_cache, np.ascontiguousarray(case.slot_mapping[0]), "bf16")
+    want = oracle.decode(np.ascontiguousarray(case.q[0]), case.k_cache, case.v_cache, tables,
+                         case.context_lens, case.scale, "bf16", num_threads=16)
+    check_attention(outs[1], want, "bf16", f"min prefix bound fused={fused}")
+
+
 def test_cow_shaped_batch_matches_plain_decode():
     """32 sequences sharing a 2048-token prefix (block size 32) with private
     suffixes of 1..512 tokens: pa_decode_prefix and pa_decode agree."""
