@@ -193,6 +193,73 @@ def test_cow_shared_prefix_step():
     check_attention(to_host(out, dtype), want_out, dtype, "cow_bf16")
 
 
+def test_cow_step_as_benchmarked():
+    """The copy-on-write step in the form bench.py times it: pa_copy_blocks
+    over the step's pairs, then pa_decode_prefix over the 32 sequences (one
+    group, the 2048 shared tokens as prefix_len and as min_prefix_len) with
+    the fused append of each new token into its copy.  The copied blocks carry
+    the source's NaN-poisoned unused rows, so the append must overwrite the
+    row it attends to.  Pools and output are checked against the oracle's
+    copy, write and decode."""
+    import torch
+    plan = wl.cow_plan()
+    BS, NB, n, dtype = plan["BS"], plan["NB"], plan["n"], plan["dtype"]
+    A = pa.Allocator(NB, BS, plan["init_free_order"])
+    A.pa_seq_add(0)
+    for _ in range(plan["prefix"]):
+        A.pa_seq_append_slot(0)
+    for i in range(1, n):
+        A.pa_seq_fork(0, i)
+    for i in range(n):
+        for _ in range(plan["suffix"][i]):
+            A.pa_seq_append_slot(i)
+    for i in range(n):
+        A.pa_seq_fork(i, 1000 + i)
+    kc, vc = plan["k_cache"], plan["v_cache"]
+    referenced = np.zeros(NB, bool)
+    for s in list(range(n)) + [1000 + i for i in range(n)]:
+        referenced[A.pa_seq_block_table(s)] = True
+    kc[~referenced] = wl.nan_bits(dtype)
+    vc[~referenced] = wl.nan_bits(dtype)
+    pre_len = np.asarray([A.pa_seq_len(i) for i in range(n)], np.int32)
+    pre_tabs = [A.pa_seq_block_table(i) for i in range(n)]
+    pre_t = np.zeros((n, max(len(t) for t in pre_tabs)), np.int32)
+    for i, t in enumerate(pre_tabs):
+        pre_t[i, :len(t)] = t
+    poison_tails(oracle, kc, vc, pre_t, pre_len, dtype)
+
+    slots, pairs = A.pa_seq_append_slots(list(range(n)))
+    lens = np.asarray([A.pa_seq_len(i) for i in range(n)], np.int32)
+    tabs = [A.pa_seq_block_table(i) for i in range(n)]
+    A.close()
+    tables = np.zeros((n, max(len(t) for t in tabs)), np.int32)
+    for i, t in enumerate(tabs):
+        tables[i, :len(t)] = t
+    pairs = np.asarray(pairs, np.int32).reshape(-1, 2)
+    shared = plan["prefix"]
+
+    announce(f"cow as benchmarked: upload NB={NB} pairs={len(pairs)}")
+    kd, vd = to_dev(kc, dtype), to_dev(vc, dtype)
+    announce("cow as benchmarked: pa_copy_blocks")
+    pa.pa_copy_blocks(kd, vd, ints_to_dev(pairs))
+    qd = to_dev(plan["q"], dtype)
+    out = torch.empty_like(qd)
+    announce(f"cow as benchmarked: pa_decode_prefix S={n} max_ctx={int(lens.max())}")
+    pa.pa_decode_prefix(out, qd, kd, vd, ints_to_dev(tables), ints_to_dev(lens), plan["scale"],
+                        int(lens.max()), ints_to_dev(np.array([0, n], np.int32)),
+                        ints_to_dev(np.array([shared], np.int32)), n, shared, min_prefix_len=shared,
+                        k_new=to_dev(plan["new_k"], dtype), v_new=to_dev(plan["new_v"], dtype))
+    _sync()
+    oracle.copy_blocks(kc, vc, pairs, dtype)
+    oracle.write_kv(plan["new_k"], plan["new_v"], kc, vc, np.asarray(slots, np.int64), dtype)
+    touched = np.unique(np.concatenate([pairs[:, 1], np.asarray(slots) // BS]))
+    idx = torch.from_numpy(touched.astype(np.int64)).to(_g.DEVICE)
+    assert same_bits(to_host(kd.index_select(0, idx), dtype), kc[touched]), "K blocks after the step"
+    assert same_bits(to_host(vd.index_select(0, idx), dtype), vc[touched]), "V blocks after the step"
+    want = oracle.decode(plan["q"], kc, vc, tables, lens, plan["scale"], dtype, num_threads=16)
+    check_attention(to_host(out, dtype), want, dtype, "cow as benchmarked")
+
+
 # ---------------------------------------------------------------------------- fused append
 
 def run_fused_case(case, label, partition_size=None, r=0):
