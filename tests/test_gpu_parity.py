@@ -262,7 +262,7 @@ def test_cow_step_as_benchmarked():
 
 # ---------------------------------------------------------------------------- fused append
 
-def run_fused_case(case, label, partition_size=None, r=0):
+def run_fused_case(case, label, partition_size=None, r=0, host_lens=False):
     """pa_decode with k_new / v_new: the step's token of every sequence is
     stored at position c - 1 and attended to in the same launch.  The device
     pool's slot c - 1 is poisoned with NaN first, so a read of the stale slot
@@ -287,10 +287,10 @@ def run_fused_case(case, label, partition_size=None, r=0):
     qd = to_dev(q, dtype)
     out = torch.empty_like(qd)
     P = case.partition_size if partition_size is None else partition_size
-    announce(f"{label}: pa_decode fused append P={P}")
+    announce(f"{label}: pa_decode fused append P={P} host lens={host_lens}")
     pa.pa_decode(out, qd, kd, vd, ints_to_dev(tables), ints_to_dev(lens), case.scale,
                  case.max_context, partition_size=P, k_new=to_dev(k_new, dtype),
-                 v_new=to_dev(v_new, dtype))
+                 v_new=to_dev(v_new, dtype), context_lens_host=lens if host_lens else None)
     _sync()
     touched = np.unique(slots[live] // case.BS)
     idx = torch.from_numpy(touched.astype(np.int64)).to(_g.DEVICE)
@@ -308,16 +308,25 @@ def test_fused_append_tiny_f32_equals_write_then_decode():
     assert same_bits(fused, separate)
 
 
-def test_fused_append_llama13b_f16_full_size():
-    run_fused_case(wl.llama13b_f16(), "llama13b_f16")
+@pytest.mark.parametrize("host_lens", [False, True])
+def test_fused_append_llama13b_f16_full_size(host_lens):
+    """Full size with the fused append; with host_lens, in the launch
+    configuration bench.py times (host copy of the context lengths)."""
+    run_fused_case(wl.llama13b_f16(), "llama13b_f16", host_lens=host_lens)
 
 
-def test_fused_append_mixed_gqa_bf16_full_size():
-    run_fused_case(wl.mixed_gqa_bf16(), "mixed_gqa_bf16")
+@pytest.mark.parametrize("host_lens", [False, True])
+def test_fused_append_mixed_gqa_bf16_full_size(host_lens):
+    """Full size with the fused append; with host_lens, in the launch
+    configuration bench.py times (host copy of the context lengths)."""
+    run_fused_case(wl.mixed_gqa_bf16(), "mixed_gqa_bf16", host_lens=host_lens)
 
 
-def test_fused_append_long_bf16_full_size_p512():
-    run_fused_case(wl.long_bf16(), "long_bf16")
+@pytest.mark.parametrize("host_lens", [False, True])
+def test_fused_append_long_bf16_full_size_p512(host_lens):
+    """Full size with the fused append; with host_lens, in the launch
+    configuration bench.py times (host copy of the context lengths)."""
+    run_fused_case(wl.long_bf16(), "long_bf16", host_lens=host_lens)
 
 
 FUSED_LENS = [0, 1, 2, 16, 17, 32, 33, 64, 65, 100, 129, 257]
