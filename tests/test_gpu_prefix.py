@@ -26,7 +26,8 @@ def _sync():
     torch.cuda.synchronize()
 
 
-def run_prefix_case(case, group_start, prefix_len, label, fused=False, partition_size=0):
+def run_prefix_case(case, group_start, prefix_len, label, fused=False, partition_size=0,
+                    min_prefix=False):
     import torch
     dtype, i8 = case.dtype, case.kv_dtype == "i8"
     tables = np.ascontiguousarray(case.block_tables[0])
@@ -56,7 +57,8 @@ def run_prefix_case(case, group_start, prefix_len, label, fused=False, partition
     announce(f"{label}: pa_decode_prefix max_group={max_group} P={partition_size}")
     pa.pa_decode_prefix(out, qd, kd, vd, ints_to_dev(tables), ints_to_dev(lens), case.scale,
                         case.max_context, ints_to_dev(group_start), ints_to_dev(prefix_len),
-                        max_group, int(np.max(prefix_len)), partition_size=partition_size, **extra)
+                        max_group, int(np.max(prefix_len)), partition_size=partition_size,
+                        min_prefix_len=int(np.min(prefix_len)) if min_prefix else 0, **extra)
     _sync()
     if fused:
         live = slots >= 0
@@ -88,9 +90,11 @@ def test_prefix_groups_edge_shapes(dtype, D, BS, Hq, Hkv, fused):
 
 @pytest.mark.parametrize("kv", ["i8"])
 @pytest.mark.parametrize("fused", [False, True])
-def test_prefix_groups_int8(kv, fused):
+@pytest.mark.parametrize("min_prefix", [False, True])
+def test_prefix_groups_int8(kv, fused, min_prefix):
     case, gs, shared = wl.shared_prefix_case(4200, GROUPS, 32, 8, 128, 16, "bf16", kv_dtype=kv)
-    run_prefix_case(case, gs, shared, f"prefix int8 fused={fused}", fused=fused)
+    run_prefix_case(case, gs, shared, f"prefix int8 fused={fused} min_prefix={min_prefix}",
+                    fused=fused, min_prefix=min_prefix)
 
 
 def test_prefix_shorter_than_the_shared_blocks_and_zero():
