@@ -159,7 +159,9 @@ typedef struct pa_decode_args {
    * knows only the bound max_context_len, so it launches a workgroup for
    * every (sequence, partition) pair that bound allows and the surplus ones
    * exit at once; given the host copy, the 16-bit and INT8 kernels launch
-   * only the pairs that exist.  Values outside [0, max_context_len] return
+   * only the pairs that exist, and the merge pass covers only the sequences
+   * that span more than one partition (none: no merge launch).  Values
+   * outside [0, max_context_len] return
    * PA_ERR_INVALID.  The values must equal the device ones: where they
    * differ, the outputs are undefined (no access leaves the arguments'
    * buffers either way).  A launch recorded into a graph keeps the shape it
