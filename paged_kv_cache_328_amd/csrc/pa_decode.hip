@@ -183,12 +183,12 @@ struct Raw<KK, MM, true> {
   float sc;        // lane L < 32: K scale of the chunk's token L; else V scale of token L - 32
 };
 
-// With prefix groups (pa_decode_prefix) the kernel takes each member's keys
-// after its group's shared prefix; the prefix itself is attended by
-// prefill_lds_kernel's shared-prefix pass, in pre_parts partitions of pre_P
-// tokens that fill the first partial slots of every member.
 // Body of the decode pass for the workgroup at grid position (bx, by, bz);
-// `lds` holds merge_lds_bytes(NW, G, D) bytes.
+// `lds` holds merge_lds_bytes(NW, G, D) bytes.  With prefix groups
+// (pa_decode_prefix, through prefix_suffix_kernel) it takes each member's
+// keys after its group's shared prefix; the prefix itself is attended by the
+// shared-prefix pass of the prefill body, in pre_parts partitions of pre_P
+// tokens that fill the first partial slots of every member.
 template <typename Ty, int D, int BS, int NW, bool KV8>
 __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* lds,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
@@ -817,15 +817,16 @@ struct StageI8 {
 // the lazy reference maximum, fp32 accumulation, weights rounded to the
 // element type for the PV product.
 // ----------------------------------------------------------------------------
-// PFX: the shared-prefix pass of pa_decode_prefix instead.  Grid x = slot
-// tiles of a group's (member, head) slots, y = partition of the prefix (P
-// tokens), z = group * Hkv + KV head; members are rows qstart[g] ..
-// qstart[g+1] - 1 (query rows of the decode), the keys [p*P, (p+1)*P) of
-// the prefix (grp_len[g] tokens) come through the first member's table, no
-// causal limit, and each column's partial (max, sum, unnormalised output)
-// goes to partial slot p of its row in the split-K workspace.
 // Body of the prefill pass for the workgroup at grid position (bx, by, bz) of
 // a (gx, gy, gz) grid; `lds_raw` holds PrefillLds<D, KV8>::kBytes bytes.
+// PFX: the shared-prefix pass of pa_decode_prefix instead (run by
+// prefix_suffix_kernel).  Grid x = slot tiles of a group's (member, head)
+// slots, y = partition of the prefix (P tokens), z = group * Hkv + KV head;
+// members are rows qstart[g] .. qstart[g+1] - 1 (query rows of the decode),
+// the keys [p*P, (p+1)*P) of the prefix (grp_len[g] tokens) come through the
+// first member's table, no causal limit, and each column's partial (max,
+// sum, unnormalised output) goes to partial slot p of its row in the split-K
+// workspace.
 template <typename Ty, int D, int BS, int NW, int NC, bool KV8, bool PFX>
 __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx, int gy, int gz,
     uint8_t* lds_raw, uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
