@@ -1754,6 +1754,21 @@ void launch_prefill_dims(const pa_prefill_args* a, hipStream_t st) {
 template <typename Ty, bool KV8, int D>
 void launch_mfma_bs(const pa_decode_args* a, const Plan& pl, float* wa, float* wm,
                     hipStream_t st) {
+  // INT8 caches on the flat work list with partitions of at most 512 tokens:
+  // two waves per workgroup, 8 chunks each (INT8 waves keep one chunk in
+  // flight, so four waves over 16 chunks spent much of their life in the
+  // prologue and the LDS merge).  Measured on MI355X: mixed-length INT8 step
+  // 47.4 -> 44.4 us, long context at P = 512 121.0 -> 118.1 us; at P = 4096
+  // two waves over 128 chunks took 145 us instead of 102, hence the limit.
+  if (KV8 && pl.flat && pl.P <= 512) {
+    switch (a->block_size) {
+      case 8: launch_mfma<Ty, D, 8, 2, KV8>(a, pl, wa, wm, st); break;
+      case 16: launch_mfma<Ty, D, 16, 2, KV8>(a, pl, wa, wm, st); break;
+      case 32: launch_mfma<Ty, D, 32, 2, KV8>(a, pl, wa, wm, st); break;
+      default: launch_mfma<Ty, D, 64, 2, KV8>(a, pl, wa, wm, st); break;
+    }
+    return;
+  }
   switch (a->block_size) {
     case 8: launch_mfma<Ty, D, 8, kWaves, KV8>(a, pl, wa, wm, st); break;
     case 16: launch_mfma<Ty, D, 16, kWaves, KV8>(a, pl, wa, wm, st); break;
