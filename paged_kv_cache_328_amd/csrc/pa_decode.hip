@@ -189,6 +189,18 @@ struct Raw<KK, MM, true> {
 // keys after its group's shared prefix; the prefix itself is attended by the
 // shared-prefix pass of the prefill body, in pre_parts partitions of pre_P
 // tokens that fill the first partial slots of every member.
+// Block id j (0 <= j < N) of a chunk's N wave-uniform block ids, for a
+// lane-dependent j.  The ids are taken as values (readfirstlane of a uniform
+// value is the value): written as a lookup in the array, the compiler turned
+// the selects into an indexed load, which left the array in scratch memory.
+template <int N>
+__device__ __forceinline__ int pick_block(const int (&b)[N], int j) {
+  int id = b[0];
+#pragma unroll
+  for (int t = 1; t < N; ++t) id = j == t ? __builtin_amdgcn_readfirstlane(b[t]) : id;
+  return id;
+}
+
 template <typename Ty, int D, int BS, int NW, bool KV8>
 __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* lds,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
@@ -338,10 +350,7 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
   auto issue = [&](const int (&b)[BPC], int t0, Raw<KK, MM, KV8>& r) {
     const int r0 = BS > kChunk ? t0 % BS : 0;
     auto at = [&](int tau, int64_t& off, int& row) {  // tile offset and row of token tau
-      int id = b[0];
-#pragma unroll
-      for (int j = 1; j < BPC; ++j)
-        if (tau / BS == j) id = b[j];
+      const int id = pick_block<BPC>(b, tau / BS);
       off = (int64_t)id * blk_stride + head_off;
       row = BS >= kChunk ? r0 + tau : tau % BS;
     };
@@ -1001,10 +1010,7 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
     for (int j = 0; j < BPC; ++j) b[j] = __builtin_amdgcn_readlane(tbl, e + j);
     const int r0 = BS > kChunk ? (t_begin + k * kChunk) % BS : 0;
     auto at = [&](int tau, int64_t& off, int& row) {  // tile offset and row of token tau
-      int id = b[0];
-#pragma unroll
-      for (int j = 1; j < BPC; ++j)
-        if (tau / BS == j) id = b[j];
+      const int id = pick_block<BPC>(b, tau / BS);
       off = (int64_t)id * blk_stride + head_off;
       row = BS >= kChunk ? r0 + tau : tau % BS;
     };
