@@ -41,19 +41,17 @@ def lib():
         L.oracle_k_index.argtypes = [_I64, _I, _I, _I, _I, _I, _I, _I]
         L.oracle_v_index.restype = _I64
         L.oracle_v_index.argtypes = [_I64, _I, _I, _I, _I, _I, _I]
-        L.oracle_gather.restype = _I
-        L.oracle_gather.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P]
         L.oracle_gather_raw.restype = _I
         L.oracle_gather_raw.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P]
         L.oracle_decode.restype = _I
         L.oracle_decode.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
-                                    ctypes.c_float, _I, _I, _P]
+                                    ctypes.c_float, _I, _I, _P, _P, _P, _P]
         L.oracle_prefill.restype = _I
         L.oracle_prefill.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
-                                     ctypes.c_float, _I, _I, _P]
+                                     ctypes.c_float, _I, _I, _P, _P, _P, _P]
         L.oracle_prefill_i8.restype = _I
         L.oracle_prefill_i8.argtypes = [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
-                                        ctypes.c_float, _I, _P]
+                                        ctypes.c_float, _I, _P, _P, _P, _P]
         L.oracle_write_kv.restype = _I
         L.oracle_write_kv.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I]
         L.oracle_copy_blocks.restype = _I
@@ -73,13 +71,43 @@ def lib():
         L.oracle_copy_blocks_i8.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I]
         L.oracle_decode_i8.restype = _I
         L.oracle_decode_i8.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
-                                       ctypes.c_float, _I, _P]
+                                       ctypes.c_float, _I, _P, _P, _P, _P]
         _lib = L
     return _lib
 
 
 def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Attention:
+    """Oracle attention result with the ingredients of a per-element error
+    bound (see pa_oracle.c, oracle_decode):
+      out    [rows, Hq, D]  the attention output (fp64);
+      spread [rows, Hq, D]  sum_t pi_t |v_t[d] - out[d]|;
+      devmax [rows, Hq, D]  max_t |v_t[d] - out[d]|;
+      lam    [rows, Hq]     max_t |scale| sum_d |q[d] k_t[d]|;
+      keys   [rows]         how many keys each row attends to.
+    Indexing by rows (an int array or a slice) selects the same rows of all."""
+
+    def __init__(self, out, spread, devmax, lam, keys):
+        self.out, self.spread, self.devmax, self.lam = out, spread, devmax, lam
+        self.keys = np.asarray(keys, np.int64)
+
+    def __getitem__(self, rows):
+        return Attention(self.out[rows], self.spread[rows], self.devmax[rows], self.lam[rows],
+                         self.keys[rows])
+
+
+def _bound_buffers(rows, Hq, D, bound):
+    """(spread, devmax, lam) output arrays, or three None."""
+    if not bound:
+        return None, None, None
+    return np.empty((rows, Hq, D)), np.empty((rows, Hq, D)), np.empty((rows, Hq))
+
+
+def _opt(a):
+    return None if a is None else _ptr(a)
 
 
 def _check(a, np_dtype, name):
@@ -113,21 +141,6 @@ def v_index(b, h, o, d, Hkv, D, BS):
     return lib().oracle_v_index(b, h, o, d, Hkv, D, BS)
 
 
-def gather(k_cache, v_cache, block_tables, context_lens, max_ctx, dtype):
-    """Logical K, V [S, max_ctx, Hkv, D] fp64 (zero past each context)."""
-    NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, dtype)
-    _check(block_tables, np.int32, "block_tables")
-    _check(context_lens, np.int32, "context_lens")
-    S, max_blocks = block_tables.shape
-    k = np.empty((S, max_ctx, Hkv, D), np.float64)
-    v = np.empty_like(k)
-    rc = lib().oracle_gather(_ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
-                             S, Hkv, D, BS, max_blocks, max_ctx, DTYPE_CODE[dtype], _ptr(k), _ptr(v))
-    if rc != 0:
-        raise ValueError("oracle_gather rejected its arguments")
-    return k, v
-
-
 def gather_raw(k_cache, v_cache, block_tables, context_lens, max_ctx, dtype, fill=0):
     """Bit copies of logical K, V [S, max_ctx, Hkv, D] in the cache's storage
     type; positions past a context keep `fill`."""
@@ -145,8 +158,10 @@ def gather_raw(k_cache, v_cache, block_tables, context_lens, max_ctx, dtype, fil
     return k, v
 
 
-def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype, num_threads=1):
-    """Paged decode attention, fp64 output [S, Hq, D]."""
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype, num_threads=1,
+           bound=False):
+    """Paged decode attention, fp64 output [S, Hq, D]; with bound=True an
+    Attention (output plus the bound ingredients)."""
     NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, dtype)
     _check(q, NP_STORAGE[dtype], "q")
     _check(block_tables, np.int32, "block_tables")
@@ -155,18 +170,21 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype, num_th
     if Dq != D:
         raise ValueError("q head_dim does not match the cache")
     out = np.empty((S, Hq, D), np.float64)
+    spread, devmax, lam = _bound_buffers(S, Hq, D, bound)
     rc = lib().oracle_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                              _ptr(context_lens), S, Hq, Hkv, D, BS, block_tables.shape[1],
-                             ctypes.c_float(scale), DTYPE_CODE[dtype], int(num_threads), _ptr(out))
+                             ctypes.c_float(scale), DTYPE_CODE[dtype], int(num_threads), _ptr(out),
+                             _opt(spread), _opt(devmax), _opt(lam))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
-    return out
+    return Attention(out, spread, devmax, lam, np.maximum(context_lens, 0)) if bound else out
 
 
 def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, dtype,
-            num_threads=1):
+            num_threads=1, bound=False):
     """Paged (chunked) prefill: causal attention of each query row over its
-    sequence's positions 0..p, fp64 output [T, Hq, D]."""
+    sequence's positions 0..p, fp64 output [T, Hq, D]; with bound=True an
+    Attention."""
     NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, dtype)
     _check(q, NP_STORAGE[dtype], "q")
     _check(block_tables, np.int32, "block_tables")
@@ -177,13 +195,14 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
     if Dq != D or query_start.shape != (S + 1,) or int(query_start[-1]) != T:
         raise ValueError("q must be [T, Hq, D] with T = query_start[S]")
     out = np.empty((T, Hq, D), np.float64)
+    spread, devmax, lam = _bound_buffers(T, Hq, D, bound)
     rc = lib().oracle_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                               _ptr(context_lens), _ptr(query_start), S, Hq, Hkv, D, BS,
                               block_tables.shape[1], ctypes.c_float(scale), DTYPE_CODE[dtype],
-                              int(num_threads), _ptr(out))
+                              int(num_threads), _ptr(out), _opt(spread), _opt(devmax), _opt(lam))
     if rc != 0:
         raise ValueError("oracle_prefill rejected its arguments")
-    return out
+    return Attention(out, spread, devmax, lam, _row_keys(context_lens, query_start)) if bound else out
 
 
 def write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, dtype):
@@ -269,8 +288,10 @@ def copy_blocks_i8(k_pool, v_pool, pairs, D, BS):
         raise ValueError("oracle_copy_blocks_i8 rejected its arguments")
 
 
-def decode_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, scale, D, BS, num_threads=1):
-    """Paged decode attention over INT8 pools, fp64 output [S, Hq, D]."""
+def decode_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, scale, D, BS, num_threads=1,
+              bound=False):
+    """Paged decode attention over INT8 pools, fp64 output [S, Hq, D]; with
+    bound=True an Attention."""
     NB, Hkv = i8_geometry(k_pool, v_pool, D, BS)
     _check(q, NP_STORAGE[q_dtype], "q")
     _check(block_tables, np.int32, "block_tables")
@@ -279,18 +300,20 @@ def decode_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, scale, D, 
     if Dq != D:
         raise ValueError("q head_dim does not match")
     out = np.empty((S, Hq, D), np.float64)
+    spread, devmax, lam = _bound_buffers(S, Hq, D, bound)
     rc = lib().oracle_decode_i8(_ptr(q), DTYPE_CODE[q_dtype], _ptr(k_pool), _ptr(v_pool),
                                 _ptr(block_tables), _ptr(context_lens), S, Hq, Hkv, D, BS,
                                 block_tables.shape[1], ctypes.c_float(scale), int(num_threads),
-                                _ptr(out))
+                                _ptr(out), _opt(spread), _opt(devmax), _opt(lam))
     if rc != 0:
         raise ValueError("oracle_decode_i8 rejected its arguments")
-    return out
+    return Attention(out, spread, devmax, lam, np.maximum(context_lens, 0)) if bound else out
 
 
 def prefill_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, query_start, scale, D, BS,
-               num_threads=1):
-    """Paged (chunked) prefill over INT8 pools, fp64 output [T, Hq, D]."""
+               num_threads=1, bound=False):
+    """Paged (chunked) prefill over INT8 pools, fp64 output [T, Hq, D]; with
+    bound=True an Attention."""
     NB, Hkv = i8_geometry(k_pool, v_pool, D, BS)
     _check(q, NP_STORAGE[q_dtype], "q")
     _check(block_tables, np.int32, "block_tables")
@@ -301,10 +324,21 @@ def prefill_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, query_sta
     if Dq != D or query_start.shape != (S + 1,) or int(query_start[-1]) != T:
         raise ValueError("q must be [T, Hq, D] with T = query_start[S]")
     out = np.empty((T, Hq, D), np.float64)
+    spread, devmax, lam = _bound_buffers(T, Hq, D, bound)
     rc = lib().oracle_prefill_i8(_ptr(q), DTYPE_CODE[q_dtype], _ptr(k_pool), _ptr(v_pool),
                                  _ptr(block_tables), _ptr(context_lens), _ptr(query_start), S, Hq,
                                  Hkv, D, BS, block_tables.shape[1], ctypes.c_float(scale),
-                                 int(num_threads), _ptr(out))
+                                 int(num_threads), _ptr(out), _opt(spread), _opt(devmax), _opt(lam))
     if rc != 0:
         raise ValueError("oracle_prefill_i8 rejected its arguments")
-    return out
+    return Attention(out, spread, devmax, lam, _row_keys(context_lens, query_start)) if bound else out
+
+
+def _row_keys(context_lens, query_start):
+    """Keys seen by each prefill row: position + 1 (chunk rows are the last
+    query_start[s+1] - query_start[s] positions of sequence s)."""
+    keys = []
+    for s in range(context_lens.shape[0]):
+        n = int(query_start[s + 1] - query_start[s])
+        keys.extend(range(int(context_lens[s]) - n + 1, int(context_lens[s]) + 1))
+    return np.asarray(keys, np.int64)

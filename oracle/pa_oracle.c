@@ -109,39 +109,10 @@ static int64_t block_of(const int32_t* block_tables, int max_blocks, int s, int 
   return block_tables[(int64_t)s * max_blocks + t / BS];
 }
 
-/* Gather through the block table, widened to fp64.  k_out / v_out are
- * [S, max_ctx, Hkv, D]; positions t >= c_s are set to 0.  Returns 0, or -1
- * on bad dimensions or a context longer than max_ctx. */
-int oracle_gather(const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                  const int32_t* context_lens, int S, int Hkv, int D, int BS, int max_blocks,
-                  int max_ctx, int dtype, double* k_out, double* v_out) {
-  if (!dims_ok(Hkv, D, BS, dtype) || S < 0 || max_ctx < 0) return -1;
-  for (int s = 0; s < S; ++s)
-    if (context_lens[s] > max_ctx || context_lens[s] > max_blocks * BS) return -1;
-  for (int s = 0; s < S; ++s) {
-    for (int t = 0; t < max_ctx; ++t) {
-      for (int h = 0; h < Hkv; ++h) {
-        double* kd = k_out + (((int64_t)s * max_ctx + t) * Hkv + h) * D;
-        double* vd = v_out + (((int64_t)s * max_ctx + t) * Hkv + h) * D;
-        if (t >= context_lens[s]) {
-          for (int d = 0; d < D; ++d) kd[d] = vd[d] = 0.0;
-          continue;
-        }
-        int64_t b = block_of(block_tables, max_blocks, s, t, BS);
-        int o = t % BS;
-        for (int d = 0; d < D; ++d) {
-          kd[d] = load_elem(k_cache, oracle_k_index(b, h, o, d, Hkv, D, BS, dtype), dtype);
-          vd[d] = load_elem(v_cache, oracle_v_index(b, h, o, d, Hkv, D, BS), dtype);
-        }
-      }
-    }
-  }
-  return 0;
-}
-
-/* Same gather, but copying the stored bits unchanged into k_out / v_out of
- * the cache's element type, [S, max_ctx, Hkv, D].  Positions t >= c_s are
- * left untouched.  Used for bit-exact comparison of a device-side gather. */
+/* Gather through the block table: the stored bits of logical K/V, copied
+ * unchanged into k_out / v_out of the cache's element type, [S, max_ctx,
+ * Hkv, D].  Positions t >= c_s are left untouched.  Used for bit-exact
+ * comparison of a device-side gather. */
 int oracle_gather_raw(const void* k_cache, const void* v_cache, const int32_t* block_tables,
                       const int32_t* context_lens, int S, int Hkv, int D, int BS, int max_blocks,
                       int max_ctx, int dtype, void* k_out, void* v_out) {
@@ -169,11 +140,20 @@ int oracle_gather_raw(const void* k_cache, const void* v_cache, const int32_t* b
  * q is [S, Hq, D] of the cache's element type; out is [S, Hq, D] fp64.
  * num_threads > 0 runs that many OpenMP threads over (s, h); the arithmetic
  * of each (s, h) is the same whatever the thread count.
+ *
+ * Optional outputs (NULL = not computed), the ingredients of a per-element
+ * error bound for an implementation that rounds or reorders this sum (the
+ * paging must leave the attention result unchanged: wiblog.cn, section
+ * "非连续 KV 为什么需要专门的 Attention Kernel"), with pi_t = w_t / sum_u w_u:
+ *   spread [S, Hq, D]  sum_t pi_t |v_t[d] - out[d]|  (weighted mean deviation)
+ *   devmax [S, Hq, D]  max_t |v_t[d] - out[d]|
+ *   lam    [S, Hq]     max_t |scale| * sum_d |q[d] k_t[d]|  (logit magnitude)
+ * An empty context gives zeros.
  * Returns 0, or -1 on bad dimensions. */
 int oracle_decode(const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* block_tables, const int32_t* context_lens, int S, int Hq,
                   int Hkv, int D, int BS, int max_blocks, float scale, int dtype, int num_threads,
-                  double* out) {
+                  double* out, double* spread, double* devmax, double* lam) {
   if (!dims_ok(Hkv, D, BS, dtype) || S < 0 || Hq <= 0 || Hq % Hkv != 0) return -1;
   int max_c = 0;
   for (int s = 0; s < S; ++s) {
@@ -191,6 +171,9 @@ int oracle_decode(const void* q, const void* k_cache, const void* v_cache,
     const int c = context_lens[s];
     double* o = out + sh * D;
     for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (spread)
+      for (int d = 0; d < D; ++d) spread[sh * D + d] = devmax[sh * D + d] = 0.0;
+    if (lam) lam[sh] = 0.0;
     if (c <= 0) continue;
     double* x = (double*)malloc(sizeof(double) * (size_t)c);
     if (!x) {
@@ -201,11 +184,15 @@ int oracle_decode(const void* q, const void* k_cache, const void* v_cache,
     /* logits over the gathered keys */
     for (int t = 0; t < c; ++t) {
       int64_t b = block_of(block_tables, max_blocks, s, t, BS);
-      double dot = 0.0;
-      for (int d = 0; d < D; ++d)
-        dot += load_elem(q, sh * D + d, dtype) *
-               load_elem(k_cache, oracle_k_index(b, g, t % BS, d, Hkv, D, BS, dtype), dtype);
+      double dot = 0.0, mag = 0.0;
+      for (int d = 0; d < D; ++d) {
+        double qk = load_elem(q, sh * D + d, dtype) *
+                    load_elem(k_cache, oracle_k_index(b, g, t % BS, d, Hkv, D, BS, dtype), dtype);
+        dot += qk;
+        mag += fabs(qk);
+      }
       x[t] = sc * dot;
+      if (lam && fabs(sc) * mag > lam[sh]) lam[sh] = fabs(sc) * mag;
     }
     /* softmax weights: subtract the maximum, exponentiate, normalise */
     double m = x[0];
@@ -223,6 +210,16 @@ int oracle_decode(const void* q, const void* k_cache, const void* v_cache,
         o[d] += x[t] * load_elem(v_cache, oracle_v_index(b, g, t % BS, d, Hkv, D, BS), dtype);
     }
     for (int d = 0; d < D; ++d) o[d] /= z;
+    /* deviation of the values from the result, under the same weights */
+    if (spread)
+      for (int t = 0; t < c; ++t) {
+        int64_t b = block_of(block_tables, max_blocks, s, t, BS);
+        for (int d = 0; d < D; ++d) {
+          double dv = fabs(load_elem(v_cache, oracle_v_index(b, g, t % BS, d, Hkv, D, BS), dtype) - o[d]);
+          spread[sh * D + d] += x[t] / z * dv;
+          if (dv > devmax[sh * D + d]) devmax[sh * D + d] = dv;
+        }
+      }
     free(x);
   }
   (void)max_c;
@@ -244,12 +241,14 @@ int oracle_decode(const void* q, const void* k_cache, const void* v_cache,
  * at logical position p = context_lens[s] - n_s + (r - query_start[s]) and
  * attends to positions 0..p of its own sequence through the block table:
  * out = sum_{t<=p} softmax_t(scale * <q, K_t>) V_t.  q and out are
- * [T, Hq, D], T = query_start[S].
+ * [T, Hq, D], T = query_start[S].  spread, devmax [T, Hq, D] and lam [T, Hq]
+ * are the optional bound ingredients of oracle_decode, per query row.
  * ------------------------------------------------------------------------ */
 int oracle_prefill(const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* block_tables, const int32_t* context_lens,
                    const int32_t* query_start, int S, int Hq, int Hkv, int D, int BS,
-                   int max_blocks, float scale, int dtype, int num_threads, double* out) {
+                   int max_blocks, float scale, int dtype, int num_threads, double* out,
+                   double* spread, double* devmax, double* lam) {
   if (!dims_ok(Hkv, D, BS, dtype) || S < 0 || Hq <= 0 || Hq % Hkv != 0) return -1;
   if (query_start[0] != 0) return -1;
   for (int s = 0; s < S; ++s) {
@@ -274,6 +273,9 @@ int oracle_prefill(const void* q, const void* k_cache, const void* v_cache,
     const int c = context_lens[s] - n + (r - query_start[s]) + 1; /* positions 0..p */
     double* o = out + rh * D;
     for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (spread)
+      for (int d = 0; d < D; ++d) spread[rh * D + d] = devmax[rh * D + d] = 0.0;
+    if (lam) lam[rh] = 0.0;
     double* x = (double*)malloc(sizeof(double) * (size_t)c);
     if (!x) {
 #pragma omp atomic write
@@ -282,11 +284,15 @@ int oracle_prefill(const void* q, const void* k_cache, const void* v_cache,
     }
     for (int t = 0; t < c; ++t) {
       int64_t b = block_of(block_tables, max_blocks, s, t, BS);
-      double dot = 0.0;
-      for (int d = 0; d < D; ++d)
-        dot += load_elem(q, rh * D + d, dtype) *
-               load_elem(k_cache, oracle_k_index(b, g, t % BS, d, Hkv, D, BS, dtype), dtype);
+      double dot = 0.0, mag = 0.0;
+      for (int d = 0; d < D; ++d) {
+        double qk = load_elem(q, rh * D + d, dtype) *
+                    load_elem(k_cache, oracle_k_index(b, g, t % BS, d, Hkv, D, BS, dtype), dtype);
+        dot += qk;
+        mag += fabs(qk);
+      }
       x[t] = sc * dot;
+      if (lam && fabs(sc) * mag > lam[rh]) lam[rh] = fabs(sc) * mag;
     }
     double m = x[0];
     for (int t = 1; t < c; ++t)
@@ -302,6 +308,15 @@ int oracle_prefill(const void* q, const void* k_cache, const void* v_cache,
         o[d] += x[t] * load_elem(v_cache, oracle_v_index(b, g, t % BS, d, Hkv, D, BS), dtype);
     }
     for (int d = 0; d < D; ++d) o[d] /= z;
+    if (spread)
+      for (int t = 0; t < c; ++t) {
+        int64_t b = block_of(block_tables, max_blocks, s, t, BS);
+        for (int d = 0; d < D; ++d) {
+          double dv = fabs(load_elem(v_cache, oracle_v_index(b, g, t % BS, d, Hkv, D, BS), dtype) - o[d]);
+          spread[rh * D + d] += x[t] / z * dv;
+          if (dv > devmax[rh * D + d]) devmax[rh * D + d] = dv;
+        }
+      }
     free(x);
   }
   free(seq_of);
@@ -485,11 +500,12 @@ static double i8_value(const uint8_t* pool, int64_t code_off, int64_t scale_off)
 
 /* Decode attention over INT8 pools: the same textbook single-query softmax
  * attention as oracle_decode, on the exact values code * scale (fp64).
- * q is [S, Hq, D] of q_dtype; out is [S, Hq, D] fp64. */
+ * q is [S, Hq, D] of q_dtype; out is [S, Hq, D] fp64; spread, devmax and lam
+ * are oracle_decode's optional bound ingredients, over the same values. */
 int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
                      const int32_t* block_tables, const int32_t* context_lens, int S, int Hq,
                      int Hkv, int D, int BS, int max_blocks, float scale, int num_threads,
-                     double* out) {
+                     double* out, double* spread, double* devmax, double* lam) {
   if (q_dtype < OR_F32 || q_dtype > OR_BF16 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
       D <= 0 || D % 16 || BS <= 0)
     return -1;
@@ -506,6 +522,9 @@ int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const ui
     const int c = context_lens[s];
     double* o = out + sh * D;
     for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (spread)
+      for (int d = 0; d < D; ++d) spread[sh * D + d] = devmax[sh * D + d] = 0.0;
+    if (lam) lam[sh] = 0.0;
     if (c <= 0) continue;
     double* x = (double*)malloc(sizeof(double) * (size_t)c);
     if (!x) {
@@ -516,11 +535,15 @@ int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const ui
     for (int t = 0; t < c; ++t) {
       int64_t b = block_of(block_tables, max_blocks, s, t, BS);
       int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
-      double dot = 0.0;
-      for (int d = 0; d < D; ++d)
-        dot += load_elem(q, sh * D + d, q_dtype) *
-               i8_value(k_pool, oracle_i8_k_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+      double dot = 0.0, mag = 0.0;
+      for (int d = 0; d < D; ++d) {
+        double qk = load_elem(q, sh * D + d, q_dtype) *
+                    i8_value(k_pool, oracle_i8_k_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+        dot += qk;
+        mag += fabs(qk);
+      }
       x[t] = sc * dot;
+      if (lam && fabs(sc) * mag > lam[sh]) lam[sh] = fabs(sc) * mag;
     }
     double m = x[0];
     for (int t = 1; t < c; ++t)
@@ -537,17 +560,29 @@ int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const ui
         o[d] += x[t] * i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff);
     }
     for (int d = 0; d < D; ++d) o[d] /= z;
+    if (spread)
+      for (int t = 0; t < c; ++t) {
+        int64_t b = block_of(block_tables, max_blocks, s, t, BS);
+        int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
+        for (int d = 0; d < D; ++d) {
+          double dv = fabs(i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff) - o[d]);
+          spread[sh * D + d] += x[t] / z * dv;
+          if (dv > devmax[sh * D + d]) devmax[sh * D + d] = dv;
+        }
+      }
     free(x);
   }
   return bad ? -1 : 0;
 }
 
 /* Paged prefill over INT8 pools: oracle_prefill's causal rows on the exact
- * values code * scale (fp64).  q is [T, Hq, D] of q_dtype. */
+ * values code * scale (fp64).  q is [T, Hq, D] of q_dtype; spread, devmax
+ * and lam as for oracle_prefill. */
 int oracle_prefill_i8(const void* q, int q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
                       const int32_t* block_tables, const int32_t* context_lens,
                       const int32_t* query_start, int S, int Hq, int Hkv, int D, int BS,
-                      int max_blocks, float scale, int num_threads, double* out) {
+                      int max_blocks, float scale, int num_threads, double* out,
+                      double* spread, double* devmax, double* lam) {
   if (q_dtype < OR_F32 || q_dtype > OR_BF16 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
       D <= 0 || D % 16 || BS <= 0 || query_start[0] != 0)
     return -1;
@@ -573,6 +608,9 @@ int oracle_prefill_i8(const void* q, int q_dtype, const uint8_t* k_pool, const u
     const int c = context_lens[s] - n + (r - query_start[s]) + 1;
     double* o = out + rh * D;
     for (int d = 0; d < D; ++d) o[d] = 0.0;
+    if (spread)
+      for (int d = 0; d < D; ++d) spread[rh * D + d] = devmax[rh * D + d] = 0.0;
+    if (lam) lam[rh] = 0.0;
     double* x = (double*)malloc(sizeof(double) * (size_t)c);
     if (!x) {
 #pragma omp atomic write
@@ -582,11 +620,15 @@ int oracle_prefill_i8(const void* q, int q_dtype, const uint8_t* k_pool, const u
     for (int t = 0; t < c; ++t) {
       int64_t b = block_of(block_tables, max_blocks, s, t, BS);
       int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
-      double dot = 0.0;
-      for (int d = 0; d < D; ++d)
-        dot += load_elem(q, rh * D + d, q_dtype) *
-               i8_value(k_pool, oracle_i8_k_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+      double dot = 0.0, mag = 0.0;
+      for (int d = 0; d < D; ++d) {
+        double qk = load_elem(q, rh * D + d, q_dtype) *
+                    i8_value(k_pool, oracle_i8_k_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+        dot += qk;
+        mag += fabs(qk);
+      }
       x[t] = sc * dot;
+      if (lam && fabs(sc) * mag > lam[rh]) lam[rh] = fabs(sc) * mag;
     }
     double m = x[0];
     for (int t = 1; t < c; ++t)
@@ -603,6 +645,16 @@ int oracle_prefill_i8(const void* q, int q_dtype, const uint8_t* k_pool, const u
         o[d] += x[t] * i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff);
     }
     for (int d = 0; d < D; ++d) o[d] /= z;
+    if (spread)
+      for (int t = 0; t < c; ++t) {
+        int64_t b = block_of(block_tables, max_blocks, s, t, BS);
+        int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
+        for (int d = 0; d < D; ++d) {
+          double dv = fabs(i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff) - o[d]);
+          spread[rh * D + d] += x[t] / z * dv;
+          if (dv > devmax[rh * D + d]) devmax[rh * D + d] = dv;
+        }
+      }
     free(x);
   }
   free(seq_of);

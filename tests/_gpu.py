@@ -5,6 +5,7 @@ import sys
 import numpy as np
 
 from paged_kv_cache_328_amd import workloads as wl
+from tests._bound import bound_violations
 
 DEVICE = "cuda"
 TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}  # max |gpu - oracle| on the attention output
@@ -67,10 +68,25 @@ def poison_tails(oracle, k_cache, v_cache, tables, lens, dtype):
         oracle.write_kv(nan, nan.copy(), k_cache, v_cache, slots, dtype)
 
 
-def check_attention(got_storage, want64, dtype, label):
+def i8_scale_min(v_pool, D, BS):
+    """Smallest positive finite V scale of an INT8 pool [NB, Hkv, D*BS + 4*BS]
+    (the weight times that scale is what the device rounds)."""
+    sc = np.ascontiguousarray(v_pool[:, :, D * BS:]).view(np.float32)
+    sc = sc[np.isfinite(sc) & (sc > 0)]
+    return float(sc.min()) if sc.size else 1.0
+
+
+def check_attention(got_storage, want, dtype, label, kv_scale_min=None):
+    """Device output against the oracle's Attention `want`: within the fixed
+    absolute tolerance (TOL) and, element by element, within the scale-aware
+    bound of tests/_bound.py."""
     got = wl.storage_to_f32(got_storage, dtype).astype(np.float64)
     assert np.all(np.isfinite(got)), f"{label}: non-finite output"
-    err = float(np.max(np.abs(got - want64))) if got.size else 0.0
-    print(f"[parity] {label}: max|gpu-oracle| = {err:.3e} (tol {TOL[dtype]:.0e})", file=sys.stderr, flush=True)
+    err = float(np.max(np.abs(got - want.out))) if got.size else 0.0
+    D = want.out.shape[-1]
+    nbad, ratio = bound_violations(got, want, dtype, D, kv_scale_min)
+    print(f"[parity] {label}: max|gpu-oracle| = {err:.3e} (tol {TOL[dtype]:.0e}), "
+          f"max err/bound = {ratio:.3f}", file=sys.stderr, flush=True)
     assert err <= TOL[dtype], f"{label}: max abs error {err} > {TOL[dtype]}"
+    assert nbad == 0, f"{label}: {nbad} elements outside the per-element bound (max ratio {ratio:.3f})"
     return err

@@ -15,8 +15,8 @@ from oracle.allocator_model import BlockManagerModel
 from paged_kv_cache_328_amd import pagedattn as pa
 from paged_kv_cache_328_amd import workloads as wl
 import tests._gpu as _g
-from tests._gpu import (TOL, announce, check_attention, ints_to_dev, poison_tails, same_bits,
-                        tail_slots, to_dev, to_host, torch_dtype)
+from tests._gpu import (TOL, announce, check_attention, i8_scale_min, ints_to_dev, poison_tails,
+                        same_bits, tail_slots, to_dev, to_host, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +69,7 @@ def run_decode_case(case, label, r=0, partition_size=None, write=True, gather_se
     announce(f"{label}: pa_decode P={P}")
     pa.pa_decode(out, qd, kd, vd, td, ld, case.scale, case.max_context, partition_size=P)
     _sync()
-    want = oracle.decode(q, kc, vc, tables, lens, case.scale, dtype, num_threads=16)
+    want = oracle.decode(q, kc, vc, tables, lens, case.scale, dtype, num_threads=16, bound=True)
     return check_attention(to_host(out, dtype), want, dtype, label), to_host(out, dtype)
 
 
@@ -189,7 +189,7 @@ def test_cow_shared_prefix_step():
     announce(f"cow: pa_decode S={n} max_ctx={int(lens.max())}")
     pa.pa_decode(out, qd, kd, vd, ints_to_dev(tables), ints_to_dev(lens), plan["scale"], int(lens.max()))
     _sync()
-    want_out = oracle.decode(plan["q"], kc, vc, tables, lens, plan["scale"], dtype, num_threads=16)
+    want_out = oracle.decode(plan["q"], kc, vc, tables, lens, plan["scale"], dtype, num_threads=16, bound=True)
     check_attention(to_host(out, dtype), want_out, dtype, "cow_bf16")
 
 
@@ -256,7 +256,7 @@ def test_cow_step_as_benchmarked():
     idx = torch.from_numpy(touched.astype(np.int64)).to(_g.DEVICE)
     assert same_bits(to_host(kd.index_select(0, idx), dtype), kc[touched]), "K blocks after the step"
     assert same_bits(to_host(vd.index_select(0, idx), dtype), vc[touched]), "V blocks after the step"
-    want = oracle.decode(plan["q"], kc, vc, tables, lens, plan["scale"], dtype, num_threads=16)
+    want = oracle.decode(plan["q"], kc, vc, tables, lens, plan["scale"], dtype, num_threads=16, bound=True)
     check_attention(to_host(out, dtype), want, dtype, "cow as benchmarked")
 
 
@@ -296,7 +296,7 @@ def run_fused_case(case, label, partition_size=None, r=0, host_lens=False):
     idx = torch.from_numpy(touched.astype(np.int64)).to(_g.DEVICE)
     assert same_bits(to_host(kd.index_select(0, idx), dtype), kc[touched]), f"{label}: K blocks"
     assert same_bits(to_host(vd.index_select(0, idx), dtype), vc[touched]), f"{label}: V blocks"
-    want = oracle.decode(q, kc, vc, tables, lens, case.scale, dtype, num_threads=16)
+    want = oracle.decode(q, kc, vc, tables, lens, case.scale, dtype, num_threads=16, bound=True)
     return check_attention(to_host(out, dtype), want, dtype, label + " fused"), to_host(out, dtype)
 
 
@@ -433,7 +433,7 @@ def test_one_workspace_serves_repeated_and_smaller_calls():
     assert need > 0
     ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=_g.DEVICE)
     want = oracle.decode(np.ascontiguousarray(case.q[0]), case.k_cache, case.v_cache, t0,
-                         case.context_lens, case.scale, dtype, num_threads=16)
+                         case.context_lens, case.scale, dtype, num_threads=16, bound=True)
     outs = []
     for rep in range(3):
         announce(f"workspace reuse: call {rep}")
@@ -469,7 +469,7 @@ def test_split_merge_repeats_bit_for_bit():
     qd = to_dev(case.q[0], dtype)
     td, ld = ints_to_dev(t0), ints_to_dev(case.context_lens)
     want = oracle.decode(np.ascontiguousarray(case.q[0]), case.k_cache, case.v_cache, t0,
-                         case.context_lens, case.scale, dtype, num_threads=16)
+                         case.context_lens, case.scale, dtype, num_threads=16, bound=True)
     a = pa.make_decode_args(torch.empty_like(qd), qd, kd, vd, td, ld, case.scale, case.max_context, P)
     ws = torch.empty(pa.pa_decode_workspace_bytes(a), dtype=torch.uint8, device=_g.DEVICE)
     first = None
@@ -526,13 +526,14 @@ def test_host_context_lens_size_the_grid_bit_identical(kv, P):
         oracle.write_kv_i8(np.ascontiguousarray(case.new_k[0]), np.ascontiguousarray(case.new_v[0]),
                            dtype, case.k_cache, case.v_cache, slots, case.D, case.BS)
         want = oracle.decode_i8(q, dtype, case.k_cache, case.v_cache, t0, case.context_lens,
-                                case.scale, case.D, case.BS, num_threads=16)
+                                case.scale, case.D, case.BS, num_threads=16, bound=True)
     else:
         oracle.write_kv(np.ascontiguousarray(case.new_k[0]), np.ascontiguousarray(case.new_v[0]),
                         case.k_cache, case.v_cache, slots, dtype)
         want = oracle.decode(q, case.k_cache, case.v_cache, t0, case.context_lens, case.scale, dtype,
-                             num_threads=16)
-    check_attention(outs[1], want, dtype, f"host lens kv={kv} P={P}")
+                             num_threads=16, bound=True)
+    check_attention(outs[1], want, dtype, f"host lens kv={kv} P={P}",
+                    kv_scale_min=i8_scale_min(case.v_cache, case.D, case.BS) if i8 else None)
 
 
 @pytest.mark.parametrize("name,S,lens_fn,dtype,P,max_ctx", [
@@ -573,7 +574,7 @@ def test_host_lens_merge_rows(name, S, lens_fn, dtype, P, max_ctx):
         outs.append(to_host(out, dtype))
     assert same_bits(outs[0], outs[1]), f"{name}: host copy of the lengths changed the output"
     want = oracle.decode(np.ascontiguousarray(case.q[0]), case.k_cache, case.v_cache, t0,
-                         case.context_lens, case.scale, dtype, num_threads=16)
+                         case.context_lens, case.scale, dtype, num_threads=16, bound=True)
     check_attention(outs[1], want, dtype, f"merge rows {name}")
 
 

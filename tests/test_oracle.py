@@ -223,6 +223,127 @@ def test_two_tokens_closed_form():
     np.testing.assert_allclose(out[0, 0], a * v[1] + (1 - a) * v[0], rtol=1e-13, atol=1e-15)
 
 
+# ---------------------------------------------------------------------------- bound ingredients
+# spread = sum_t pi_t |v_t - out|, devmax = max_t |v_t - out|, lam = max_t |scale| sum_d |q_d k_t,d|,
+# pinned by closed forms (one token, uniform weights, two tokens) and by the
+# scipy softmax on contiguous K/V.
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bound_ingredients_single_token(dtype):
+    """One token: out = v_0, so spread = devmax = 0; lam = |scale| sum |q k_0|."""
+    rng = np.random.default_rng(15)
+    k_log, v_log = random_logical(rng, [1, 1], 2, 64, dtype)
+    kc, vc, tables, cl = paged_from_logical(k_log, v_log, 16, 6, dtype, rng)
+    q = wl.round_to_storage(rng.standard_normal((2, 4, 64), dtype=np.float32), dtype)
+    a = oracle.decode(q, kc, vc, tables, cl, -0.125, dtype, bound=True)
+    assert np.all(a.spread == 0) and np.all(a.devmax == 0)
+    q64 = _to_f64(q, dtype)
+    for s in range(2):
+        for h in range(4):
+            k0 = _to_f64(k_log[s][0, h // 2], dtype)
+            assert a.lam[s, h] == pytest.approx(0.125 * float(np.sum(np.abs(q64[s, h] * k0))), rel=1e-14)
+    assert list(a.keys) == [1, 1]
+
+
+def test_bound_ingredients_zero_query_mean_absolute_deviation():
+    """q = 0: uniform weights, so spread is the mean absolute deviation of the
+    values about their mean, devmax the largest deviation, lam = 0."""
+    rng = np.random.default_rng(16)
+    lens = [3, 17, 64]
+    k_log, v_log = random_logical(rng, lens, 1, 64, "bf16")
+    kc, vc, tables, cl = paged_from_logical(k_log, v_log, 16, 8, "bf16", rng)
+    q = np.zeros((3, 1, 64), np.uint16)
+    a = oracle.decode(q, kc, vc, tables, cl, 0.125, "bf16", bound=True)
+    for s in range(3):
+        v = _to_f64(v_log[s][:, 0], "bf16")
+        dev = np.abs(v - v.mean(axis=0))
+        np.testing.assert_allclose(a.spread[s, 0], dev.mean(axis=0), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(a.devmax[s, 0], dev.max(axis=0), rtol=0, atol=1e-14)
+    assert np.all(a.lam == 0)
+
+
+def test_bound_ingredients_two_tokens_closed_form():
+    """Two tokens with weights sigma, 1 - sigma: spread = 2 sigma (1 - sigma)
+    |v1 - v0| and devmax = max(sigma, 1 - sigma) |v1 - v0|."""
+    rng = np.random.default_rng(18)
+    k_log, v_log = random_logical(rng, [2], 1, 64, "f32")
+    kc, vc, tables, cl = paged_from_logical(k_log, v_log, 16, 4, "f32", rng)
+    q = rng.standard_normal((1, 1, 64), dtype=np.float32)
+    a = oracle.decode(q, kc, vc, tables, cl, 0.125, "f32", bound=True)
+    k = k_log[0][:, 0].astype(np.float64)
+    v = v_log[0][:, 0].astype(np.float64)
+    qd = q[0, 0].astype(np.float64)
+    sig = expit(0.125 * (qd @ k[1]) - 0.125 * (qd @ k[0]))
+    d = np.abs(v[1] - v[0])
+    np.testing.assert_allclose(a.spread[0, 0], 2 * sig * (1 - sig) * d, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(a.devmax[0, 0], max(sig, 1 - sig) * d, rtol=1e-12, atol=1e-15)
+    assert a.lam[0, 0] == pytest.approx(0.125 * max(np.abs(qd * k[0]).sum(), np.abs(qd * k[1]).sum()),
+                                        rel=1e-14)
+
+
+@pytest.mark.parametrize("i8", [False, True])
+def test_bound_ingredients_match_dense_softmax(i8):
+    """Random GQA batch: spread / devmax / lam from the paged oracle equal the
+    same quantities from scipy's softmax over the contiguous logical K/V (for
+    INT8 pools, over the dequantised values)."""
+    rng = np.random.default_rng(19)
+    lens, Hq, Hkv, D, BS = [1, 31, 70], 4, 2, 64, 16
+    case = wl.random_case(19, 3, Hq, Hkv, D, BS, "bf16", lens, kv_dtype="i8" if i8 else None)
+    tab = np.ascontiguousarray(case.block_tables[0])
+    q = np.ascontiguousarray(case.q[0])
+    if i8:
+        a = oracle.decode_i8(q, "bf16", case.k_cache, case.v_cache, tab, case.context_lens, case.scale,
+                             D, BS, bound=True)
+        k_log = []
+        v_log = []
+        for s, c in enumerate(lens):
+            kk = np.zeros((c, Hkv, D))
+            vv = np.zeros((c, Hkv, D))
+            for t in range(c):
+                b, o = int(tab[s, t // BS]), t % BS
+                for h in range(Hkv):
+                    for d in range(D):
+                        ko, vo, so = oracle.i8_offsets(b, h, o, d, Hkv, D, BS)
+                        ksc = case.k_cache.reshape(-1)[so:so + 4].view(np.float32)[0]
+                        vsc = case.v_cache.reshape(-1)[so:so + 4].view(np.float32)[0]
+                        kk[t, h, d] = float(case.k_cache.reshape(-1)[ko].view(np.int8)) * float(ksc)
+                        vv[t, h, d] = float(case.v_cache.reshape(-1)[vo].view(np.int8)) * float(vsc)
+            k_log.append(kk)
+            v_log.append(vv)
+    else:
+        a = oracle.decode(q, case.k_cache, case.v_cache, tab, case.context_lens, case.scale, "bf16",
+                          bound=True)
+        raw_k, raw_v = oracle.gather_raw(case.k_cache, case.v_cache, tab, case.context_lens, max(lens), "bf16")
+        k_log = [_to_f64(raw_k[s, :c], "bf16") for s, c in enumerate(lens)]
+        v_log = [_to_f64(raw_v[s, :c], "bf16") for s, c in enumerate(lens)]
+    q64 = _to_f64(q, "bf16")
+    sc = float(np.float32(case.scale))
+    G = Hq // Hkv
+    for s, c in enumerate(lens):
+        for h in range(Hq):
+            k, v = k_log[s][:, h // G], v_log[s][:, h // G]
+            w = softmax(sc * (k @ q64[s, h]))
+            out = w @ v
+            np.testing.assert_allclose(a.out[s, h], out, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(a.spread[s, h], w @ np.abs(v - out), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(a.devmax[s, h], np.abs(v - out).max(axis=0), rtol=0, atol=1e-12)
+            assert a.lam[s, h] == pytest.approx(sc * np.abs(k * q64[s, h]).sum(axis=1).max(), rel=1e-12)
+
+
+def test_prefill_bound_ingredients_equal_decode_rows():
+    """A prefill row at position p sees keys 0..p, so its ingredients equal a
+    decode over a context of p + 1 tokens."""
+    case = wl.prefill_case(21, [20], [12], 4, 2, 64, 16, "bf16")
+    a = oracle.prefill(case.q, case.k_cache, case.v_cache, case.block_tables, case.context_lens,
+                       case.query_start, case.scale, "bf16", bound=True)
+    assert list(a.keys) == list(range(21, 33))
+    for r, p in enumerate(range(20, 32)):
+        d = oracle.decode(np.ascontiguousarray(case.q[r:r + 1]), case.k_cache, case.v_cache,
+                          case.block_tables, np.array([p + 1], np.int32), case.scale, "bf16", bound=True)
+        assert np.array_equal(a.spread[r], d.spread[0]) and np.array_equal(a.devmax[r], d.devmax[0])
+        assert np.array_equal(a.lam[r], d.lam[0])
+
+
 def test_output_is_a_convex_combination_and_tails_never_leak():
     """min_t v_t <= out <= max_t v_t per channel; the pools hold NaN outside
     the written slots, so any read past a context would show up."""
