@@ -11,10 +11,18 @@ own queries and new tokens) are cycled so that consecutive steps read
 different KV bytes, as successive layers would, and the 256 MB last-level
 cache cannot serve them.
 
+Protocol: untimed priming (every replica twice and at least --prime-seconds
+of back-to-back steps, so that no replica is first touched inside the timed
+region and the clocks have settled), --warmup untimed steps, then exactly
+--steps timed steps between two synchronizations.
+
 Prints one JSON line.  value = KV bytes read per step / seconds per step
 (GB/s); seq_steps_per_s = sequences / seconds per step.  roofline covers
-pa_decode, timed with HIP events on the stream it runs on.  cpu_baseline is
-the fp64 CPU oracle timed on this host's cores over a bounded sample.
+pa_decode, timed with HIP events on the stream it runs on.  read_ceiling
+times a loads-only probe of the same tiles.  cpu_baseline is the fp64 CPU
+oracle timed on this host's cores over a bounded sample.  The default
+(LLaMA-13B-shaped) run adds the mixed-length and long-context workloads
+under extra_configs, measured the same way.
 """
 import argparse
 import json
@@ -57,6 +65,14 @@ def parse():
     ap.add_argument("--no-host-lens", action="store_true",
                     help="do not pass the host copy of the context lengths (the library then "
                          "launches every (sequence, partition) pair max_context_len allows)")
+    ap.add_argument("--prime-seconds", type=float, default=0.3,
+                    help="untimed steps before the warm-up: every replica twice and at least this "
+                         "long (-1 = none)")
+    ap.add_argument("--no-extra-configs", dest="extra_configs", action="store_false",
+                    help="headline workload only (by default the LLaMA-13B-shaped run also measures "
+                         "the mixed-length and long-context workloads as extra keys)")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the read-ceiling probe (pa_probe_read) of the step's tiles")
     ap.add_argument("--calib-bytes", type=int, default=0,
                     help="first run one plain device-to-device copy of this many bytes (a "
                          "known-size reference for hardware byte counters)")
@@ -85,7 +101,6 @@ def main():
         sys.exit(2)
     import torch
     from paged_kv_cache_328_amd import pagedattn as pa
-    from paged_kv_cache_328_amd import workloads as wl
 
     pa.lib()  # fail loudly if the library is not built
     dev = torch.device("cuda", 0)
@@ -96,8 +111,77 @@ def main():
         return bench_shared_prefix(args, dev)
     if args.config == "cow_bf16":
         return bench_cow(args, dev)
+    result, keep = run_decode(args, dev, args.config)
+    if args.cpu_seconds > 0 and not args.profile_steps:
+        result["cpu_baseline"] = cpu_baseline(*keep, args.cpu_seconds)
+    del keep
+    torch.cuda.empty_cache()
+    # The headline run also measures the other two bandwidth-bound workloads
+    # (mixed lengths with GQA, long context) in the same process and the same
+    # protocol, reported as extra keys of the one JSON line.
+    if (args.config == "llama13b_f16" and args.extra_configs and not args.profile_steps
+            and args.kv == "same" and args.block_size == 16 and args.partition_size < 0):
+        extra = {}
+        for name in ("mixed_gqa_bf16", "long_bf16"):
+            r, keep = run_decode(args, dev, name)
+            del keep
+            torch.cuda.empty_cache()
+            extra[name] = {k: r[k] for k in ("ms_per_step", "gpu_ms_per_step", "value", "pct_hbm_peak",
+                                             "seq_steps_per_s", "prime")}
+            extra[name]["config"] = {k: r["config"][k] for k in ("workload", "num_seqs", "q_heads", "kv_heads",
+                                                                 "head_dim", "block_size", "context_tokens",
+                                                                 "partition_size", "replicas")}
+            extra[name]["roofline"] = {k: r["roofline"][k] for k in ("kernel", "achieved", "frac", "traffic",
+                                                                     "avg_launch_ms",
+                                                                     "algorithmic_bytes_per_launch")}
+            extra[name]["read_ceiling"] = r.get("read_ceiling")
+        result["extra_configs"] = extra
+    print(json.dumps(result), flush=True)
+
+
+def prime(step, R, min_seconds):
+    """Untimed steps before the warm-up: every replica at least twice, and
+    for at least min_seconds of back-to-back work, so that the timed steps
+    meet no first touch of a replica and the GPU's clocks have settled
+    whatever --warmup is.  Returns (steps, seconds)."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while n < 2 * R or time.perf_counter() - t0 < min_seconds:
+        step(n)
+        n += 1
+        if n % R == 0:
+            torch.cuda.synchronize()  # keep the launch queue short
+    torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
+
+
+def time_steps(step, steps, stream):
+    """K steps enqueued back to back between two synchronizations: (wall
+    seconds per step, GPU milliseconds per step from one pair of HIP events on
+    the launch stream).  No event sits between launches (an event record
+    between two kernels adds several microseconds of its own)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) / steps, e0.elapsed_time(e1) / steps
+
+
+def run_decode(args, dev, name):
+    """One decode workload on the protocol of the module docstring.  Returns
+    (result dict, (case, k pool, v pool) for the CPU baseline)."""
+    import torch
+    from paged_kv_cache_328_amd import pagedattn as pa
+    from paged_kv_cache_328_amd import workloads as wl
+
     i8 = args.kv == "i8"
-    case = build_case(args.config, args.replicas, "i8" if i8 else None, args.block_size)
+    case = build_case(name, args.replicas, "i8" if i8 else None, args.block_size)
     R, S, dtype = case.replicas, case.S, case.dtype
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
     P = case.partition_size if args.partition_size < 0 else args.partition_size
@@ -116,10 +200,12 @@ def main():
             p[:, :, cb:] = sc.view(torch.uint8)
             pools.append(p)
         kd, vd = pools
+        tile_bytes = tile
     else:
         ks, vs = wl.pool_shapes(case.NB, case.Hkv, case.D, case.BS, dtype)
         kd = torch.randn(ks, dtype=tdt, device=dev, generator=g)
         vd = torch.randn(vs, dtype=tdt, device=dev, generator=g)
+        tile_bytes = case.D * case.BS * wl.ELEM_BYTES[dtype]
 
     def dev_storage(a):
         if dtype == "bf16":
@@ -168,35 +254,16 @@ def main():
         write[r]()
         decode[r]()
 
+    primed = prime(step, R, args.prime_seconds) if args.prime_seconds >= 0 else (0, 0.0)
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    # Timed region: K steps enqueued back to back, bracketed by one pair of HIP
-    # events on the launch stream (no event between launches: an event record
-    # between two kernels adds several microseconds of its own).
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    sec_per_step = (t1 - t0) / args.steps
-    gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
+    sec_per_step, gpu_ms_per_step = time_steps(step, args.steps, stream)
     # The decode launch alone: in the fused step it is the step's only launch;
     # with --separate-write it is timed in a second loop of decode launches.
     if fused:
         decode_ms = gpu_ms_per_step
     else:
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(args.steps):
-            decode[i % R]()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        decode_ms = e0.elapsed_time(e1) / args.steps
+        decode_ms = time_steps(lambda i: decode[i % R](), args.steps, stream)[1]
 
     # ---- algorithmic bytes of one pa_decode launch
     esz = wl.ELEM_BYTES[dtype]
@@ -206,6 +273,10 @@ def main():
     if fused:  # the appended token is also written to its slot (INT8: codes and a scale)
         decode_bytes += 2 * S * case.Hkv * ((case.D + 4) if i8 else case.D * esz)
     achieved = decode_bytes / (decode_ms * 1e-3) / 1e9
+
+    ceiling = None
+    if not args.no_probe and not args.profile_steps:
+        ceiling = read_ceiling(args, case, kd, vd, tile_bytes, stream, decode_ms)
 
     # ---- host bookkeeping (allocator) for one step, reported separately
     A = pa.Allocator(case.NB, case.BS)
@@ -236,6 +307,8 @@ def main():
         "data": "synthetic",
         "pct_hbm_peak": round(100 * kv_bytes / sec_per_step / 1e9 / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(S / sec_per_step, 1),
+        "prime": {"primed_replicas": R if primed[0] >= R else primed[0], "steps": primed[0],
+                  "seconds": round(primed[1], 3)},
         "config": {"workload": case.name + (" (INT8 KV)" if i8 else "")
                    + (f" (block size {case.BS})" if case.BS != 16 else ""), "kv_dtype": case.kv_dtype,
                    "num_seqs": S, "q_heads": case.Hq, "kv_heads": case.Hkv,
@@ -258,9 +331,49 @@ def main():
                      "algorithmic_bytes_per_launch": decode_bytes},
         "host_bookkeeping_us": round(host_us, 2),
     }
-    if args.cpu_seconds > 0 and not args.profile_steps:
-        result["cpu_baseline"] = cpu_baseline(case, kd, vd, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    if ceiling is not None:
+        result["read_ceiling"] = ceiling
+    return result, (case, kd, vd)
+
+
+def read_ceiling(args, case, kd, vd, tile_bytes, stream, decode_ms):
+    """Read ceilings of the step's access pattern, from pa_probe_read (loads
+    only, no arithmetic), timed like the decode over the same replicas:
+      tiles:      every (block, KV head) K and V tile the decode step reads,
+                  in (sequence, KV head, block) order;
+      contiguous: the same number of bytes as consecutive tiles of the pools.
+    decode_vs_tiles = the tile probe's time / the decode launch's time."""
+    import torch
+    from paged_kv_cache_328_amd import pagedattn as pa
+    dev = kd.device
+    R, Hkv, BS = case.replicas, case.Hkv, case.BS
+    nblk = [-(-int(c) // BS) for c in case.context_lens]
+    offs = []
+    for r in range(R):
+        t = case.block_tables[r]
+        o = [(int(t[s, j]) * Hkv + h) * tile_bytes for s in range(case.S) for h in range(Hkv)
+             for j in range(nblk[s])]
+        offs.append(torch.tensor(o, dtype=torch.int64, device=dev))
+    n = offs[0].numel()
+    pool_bytes = kd.numel() * kd.element_size()
+    contig = []
+    span = n * tile_bytes
+    for r in range(R):
+        base = (r * span) % max(pool_bytes - span + 1, 1)
+        base -= base % tile_bytes
+        contig.append(torch.arange(n, dtype=torch.int64, device=dev) * tile_bytes + base)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    kb, vb = kd.view(-1).view(torch.uint8), vd.view(-1).view(torch.uint8)
+    out = {"range_bytes": tile_bytes, "ranges_per_step": n, "bytes_per_step": 2 * n * tile_bytes}
+    for label, lists in (("tiles", offs), ("contiguous", contig)):
+        calls = [pa.prepare_probe_read(kb, vb, lists[r], tile_bytes, sink, stream=stream) for r in range(R)]
+        step = lambda i: calls[i % R]()
+        prime(step, R, 0.05)
+        ms = time_steps(step, max(args.steps, 20), stream)[1]
+        out[label + "_gbs"] = round(2 * n * tile_bytes / (ms * 1e-3) / 1e9, 1)
+        out[label + "_ms"] = round(ms, 5)
+    out["decode_vs_tiles"] = round(out["tiles_ms"] / decode_ms, 4)
+    return out
 
 
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16 / bf16 matrix cores
@@ -640,9 +753,22 @@ def _strip_comments(src):
     return " ".join("".join(out).split())
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, kd, vd, budget_s):
     """The fp64 CPU oracle on a bounded sample: the first sequences of replica
-    0 (all heads), repeated until ~budget_s of CPU work."""
+    0 (all heads), repeated until ~2/3 of budget_s on every core of the
+    process's affinity mask, then until ~1/3 of it on one core."""
     import torch
     from oracle import oracle
     from paged_kv_cache_328_amd import workloads as wl
@@ -667,24 +793,34 @@ def cpu_baseline(case, kd, vd, budget_s):
     kc, vc = host(kd), host(vd)
     q = np.ascontiguousarray(case.q[0][:n])
     i8 = case.kv_dtype == "i8"
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        if i8:
-            oracle.decode_i8(q, dtype, kc, vc, tables, lens, case.scale, case.D, case.BS,
-                             num_threads=cores)
-        else:
-            oracle.decode(q, kc, vc, tables, lens, case.scale, dtype, num_threads=cores)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = (time.perf_counter() - t0) / reps
     per_tok = (case.D + 4) if i8 else case.D * wl.ELEM_BYTES[dtype]
-    kv = 2 * int(lens.sum()) * case.Hkv * per_tok
-    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "seq_steps_per_s": round(n / dt, 3),
+
+    def timed(rows, threads, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            if i8:
+                oracle.decode_i8(q[rows], dtype, kc, vc, tables[rows], lens[rows], case.scale, case.D,
+                                 case.BS, num_threads=threads)
+            else:
+                oracle.decode(q[rows], kc, vc, tables[rows], lens[rows], case.scale, dtype,
+                              num_threads=threads)
+            reps += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        nseq = rows.stop - rows.start
+        kv = 2 * int(lens[rows].sum()) * case.Hkv * per_tok
+        return kv / dt / 1e9, nseq / dt, reps, reps * dt
+
+    gbs, sps, reps, sec = timed(slice(0, n), cores, budget_s * 2 / 3)
+    gbs1, sps1, reps1, sec1 = timed(slice(0, 1), 1, budget_s / 3)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "seq_steps_per_s": round(sps, 3), "cpu_model": cpu_model(),
+            "value_1core": round(gbs1, 4), "seq_steps_per_s_1core": round(sps1, 3),
             "sample": f"pa_decode of sequences 0..{n - 1} of replica 0 ({int(lens.sum())} context "
-                      f"tokens, all {case.Hq} query heads), {reps} repetitions in {reps * dt:.1f} s, "
-                      f"{cores} OpenMP threads"}
+                      f"tokens, all {case.Hq} query heads), {reps} repetitions in {sec:.1f} s, "
+                      f"{cores} OpenMP threads; 1 core: sequence 0 ({int(lens[0])} tokens), "
+                      f"{reps1} repetitions in {sec1:.1f} s"}
 
 
 if __name__ == "__main__":

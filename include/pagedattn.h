@@ -341,6 +341,26 @@ PA_API pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
                               void* stream);
 
 /* ------------------------------------------------------------------------
+ * pa_probe_read -- diagnostic, not a step of the decode path: the read
+ * ceiling of an access pattern.  Decode is bound by reading the KV cache
+ * from HBM (kongchang.com, "PagedAttention原理详解", section "GPU显存层次结构
+ * 与带宽瓶颈"); this reads num_ranges byte ranges of range_bytes bytes at byte
+ * offsets offs[i] (device, int64) of BOTH device buffers a and b (a K tile
+ * and the V tile at the same offset), with the decode pass's non-temporal
+ * 16-byte loads and no arithmetic.  Fed the (block, KV head) tiles of a
+ * decode step it times the scattered-tile ceiling; fed consecutive offsets,
+ * a streaming read.  buf_bytes: size of each buffer; a range that would
+ * leave [0, buf_bytes) is skipped.  range_bytes: a multiple of 16, at most
+ * 16384.  ranges_in_flight: 1, 2 or 4 ranges per wave per round.
+ * workgroups: grid cap (0 = 2048).  sink: one device uint32 that is written
+ * only when the xor of all bytes read equals a fixed value.  a, b 16-byte
+ * aligned.  Caller-owned memory; asynchronous on `stream`.
+ * ------------------------------------------------------------------------ */
+PA_API pa_status pa_probe_read(const void* a, const void* b, size_t buf_bytes, const int64_t* offs,
+                               int64_t num_ranges, int32_t range_bytes, int32_t ranges_in_flight,
+                               int32_t workgroups, uint32_t* sink, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host block manager (the allocator, free pool, refcounts and block tables:
  * bmjup.com, section "PagedAttention 的核心工作机制与创新", item 3 "动态内存
  * 分配"; the wiblog.cn flowchart and its copy-on-write section; kongchang.com,

@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_decode.hip", "pa_cache_ops.hip", "pa_allocator.cpp"]
+SOURCES = ["pa_decode.hip", "pa_cache_ops.hip", "pa_probe.hip", "pa_allocator.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed-fp32 instructions off; matrix-core accumulators kept in ordinary VGPRs

@@ -95,6 +95,7 @@ def lib():
         "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
         "pa_gather_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _I32, _P]),
+        "pa_probe_read": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P, _I64, _I32, _I32, _I32, _P, _P]),
         "pa_alloc_create": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_P)]),
         "pa_alloc_destroy": (None, [_P]),
         "pa_alloc_num_free": (_I32, [_P]),
@@ -156,6 +157,19 @@ def _stream(stream):
     if stream is not None:
         return ctypes.c_void_p(stream if isinstance(stream, int) else stream.cuda_stream)
     return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _workspace(need, device, stream):
+    """Uninitialised byte tensor for split-K partials (the kernels write every
+    partial they read), allocated by torch's caching allocator on the stream
+    the call is enqueued on: a block freed after the call is then reused only
+    by work ordered after it on that stream."""
+    torch = _torch()
+    if stream is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    s = torch.cuda.ExternalStream(stream, device=device) if isinstance(stream, int) else stream
+    with torch.cuda.stream(s):
+        return torch.empty(need, dtype=torch.uint8, device=device)
 
 
 def is_i8(k_cache):
@@ -262,7 +276,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
                          context_lens_host)
     need = pa_decode_workspace_bytes(a)
     if need and workspace is None:
-        workspace = _torch().zeros(need, dtype=_torch().uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
         a.workspace = _ptr(workspace)
         a.workspace_bytes = need
     _check(lib().pa_decode(ctypes.byref(a), _stream(stream)), "pa_decode")
@@ -349,7 +363,7 @@ def pa_decode_prefix(out, q, k_cache, v_cache, block_tables, context_lens, scale
     g = make_prefix_groups(group_start, prefix_len, max_group_size, max_prefix_len, min_prefix_len)
     need = pa_decode_prefix_workspace_bytes(a, g)
     if need and workspace is None:
-        workspace = _torch().zeros(need, dtype=_torch().uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
         a.workspace = _ptr(workspace)
         a.workspace_bytes = need
     _check(lib().pa_decode_prefix(ctypes.byref(a), ctypes.byref(g), _stream(stream)),
@@ -367,7 +381,7 @@ def prepare_decode_prefix(out, q, k_cache, v_cache, block_tables, context_lens, 
     need = pa_decode_prefix_workspace_bytes(a, g)
     workspace = None
     if need:
-        workspace = _torch().zeros(need, dtype=_torch().uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
         a.workspace = _ptr(workspace)
         a.workspace_bytes = need
     return PreparedCall("pa_decode_prefix", lib().pa_decode_prefix,
@@ -399,7 +413,7 @@ def prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, 
                          context_lens_host)
     need = pa_decode_workspace_bytes(a)
     if need and workspace is None:
-        workspace = _torch().zeros(need, dtype=_torch().uint8, device=q.device)
+        workspace = _workspace(need, q.device, stream)
         a.workspace = _ptr(workspace)
         a.workspace_bytes = need
     return PreparedCall("pa_decode", lib().pa_decode, (ctypes.byref(a), _stream(stream)),
@@ -489,6 +503,21 @@ def pa_gather_kv(k_cache, v_cache, block_tables, context_lens, k_out, v_out, str
     _check(lib().pa_gather_kv(_ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
                               _ptr(k_out), _ptr(v_out), S, Hkv, D, BS, NB, block_tables.shape[1],
                               max_ctx, _dtype_code(k_cache), _stream(stream)), "pa_gather_kv")
+
+
+def prepare_probe_read(a, b, offs, range_bytes, sink, ranges_in_flight=2, workgroups=0, stream=None):
+    """pa_probe_read (read-ceiling diagnostic) with its arguments marshalled
+    once: reads the range_bytes-byte ranges at byte offsets offs (int64
+    device tensor) of both byte-addressed tensors a and b."""
+    torch = _torch()
+    if offs.dtype != torch.int64 or sink.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("offs must be int64 and sink a 32-bit tensor")
+    nbytes = min(a.numel() * a.element_size(), b.numel() * b.element_size())
+    return PreparedCall("pa_probe_read", lib().pa_probe_read,
+                        (_ptr(a), _ptr(b), ctypes.c_size_t(nbytes), _ptr(offs), ctypes.c_int64(offs.numel()),
+                         int(range_bytes), int(ranges_in_flight), int(workgroups), _ptr(sink),
+                         _stream(stream)),
+                        (a, b, offs, sink))
 
 
 # ---------------------------------------------------------------------------- block manager
