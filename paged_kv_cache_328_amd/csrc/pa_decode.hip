@@ -183,12 +183,6 @@ struct Raw<KK, MM, true> {
   float sc;        // lane L < 32: K scale of the chunk's token L; else V scale of token L - 32
 };
 
-// Body of the decode pass for the workgroup at grid position (bx, by, bz);
-// `lds` holds merge_lds_bytes(NW, G, D) bytes.  With prefix groups
-// (pa_decode_prefix, through prefix_suffix_kernel) it takes each member's
-// keys after its group's shared prefix; the prefix itself is attended by the
-// shared-prefix pass of the prefill body, in pre_parts partitions of pre_P
-// tokens that fill the first partial slots of every member.
 // Block id j (0 <= j < N) of a chunk's N wave-uniform block ids, for a
 // lane-dependent j.  The ids are taken as values (readfirstlane of a uniform
 // value is the value): written as a lookup in the array, the compiler turned
@@ -201,6 +195,12 @@ __device__ __forceinline__ int pick_block(const int (&b)[N], int j) {
   return id;
 }
 
+// Body of the decode pass for the workgroup at grid position (bx, by, bz);
+// `lds` holds merge_lds_bytes(NW, G, D) bytes.  With prefix groups
+// (pa_decode_prefix, through prefix_suffix_kernel) it takes each member's
+// keys after its group's shared prefix; the prefix itself is attended by the
+// shared-prefix pass of the prefill body, in pre_parts partitions of pre_P
+// tokens that fill the first partial slots of every member.
 template <typename Ty, int D, int BS, int NW, bool KV8>
 __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* lds,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
