@@ -27,7 +27,8 @@
  *
  * Conventions for every entry point:
  *   - Every pointer argument of a device op is device memory owned by the
- *     caller; the library allocates no device memory and frees none.
+ *     caller; the library allocates no device memory and frees none (the
+ *     one exception: pa_decode_static's fixed scratch array, below).
  *   - Device ops are enqueued on `stream` (a hipStream_t; NULL = the null
  *     stream) and return without synchronising it.  PA_ERR_HIP means the
  *     launch itself failed; errors inside a kernel surface on the caller's
@@ -179,6 +180,26 @@ PA_API size_t pa_decode_workspace_bytes(const pa_decode_args* args);
 PA_API int32_t pa_decode_partition_size(const pa_decode_args* args);
 
 PA_API pa_status pa_decode(const pa_decode_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * pa_decode_static -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and results as pa_decode, with the
+ * split-K partials in a scratch array the library holds in device memory
+ * (PA_DECODE_STATIC_SCRATCH_BYTES per GPU it runs on, kept until the process
+ * ends) instead of args->workspace, which is ignored.  It calls no hipMalloc,
+ * hipFree or allocating routine.  The caller still owns every input and
+ * output.  Returns PA_ERR_WORKSPACE when the step needs more partial storage
+ * than the scratch holds (pa_decode_workspace_bytes(args) >
+ * PA_DECODE_STATIC_SCRATCH_BYTES), PA_ERR_INVALID when `stream` belongs to
+ * another device than the current one, otherwise as pa_decode.  Every call
+ * on one GPU shares that GPU's scratch: calls that overlap in time on one
+ * GPU (other streams, other threads) race; calls on one stream are ordered.
+ * The scratch keeps the last call's partials; nothing in it must start at
+ * zero (every partial read is written first by the same call).
+ * ------------------------------------------------------------------------ */
+#define PA_DECODE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+PA_API pa_status pa_decode_static(const pa_decode_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
  * pa_decode_prefix -- pa_decode for batches whose sequences share prefix

@@ -55,6 +55,7 @@
 // products, the K scale multiplies the logit and the V scale the weight.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -1913,6 +1914,48 @@ pa_status run_plan(const pa_decode_args* a, const Plan& pl, hipStream_t hs) {
 }  // namespace
 }  // namespace pa
 
+// ----------------------------------------------------------------------------
+// Allocation-free decode (pa_decode_static): the split-K partials go to a
+// file-scope device array instead of a caller workspace.  In host code the
+// array's name is only a host-side stand-in; its device address is taken
+// once per device with hipGetSymbolAddress (with that device current) and
+// only that address is passed to the kernels.
+// ----------------------------------------------------------------------------
+namespace pa {
+namespace {
+
+constexpr size_t kScratchBytes = PA_DECODE_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device).
+pa_status scratch_on_current_device(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return PA_ERR_HIP;
+    if (sdev != dev) return PA_ERR_INVALID;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return PA_ERR_HIP;
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
 using namespace pa;
 
 extern "C" {
@@ -2057,6 +2100,30 @@ PA_API pa_status pa_decode(const pa_decode_args* a, void* stream) {
       (!a->workspace || a->workspace_bytes < pl.ws_bytes || !aligned16(a->workspace)))
     return PA_ERR_WORKSPACE;
   return run_plan(a, pl, (hipStream_t)stream);
+}
+
+PA_API pa_status pa_decode_static(const pa_decode_args* a, void* stream) {
+  pa_status st = validate(a);
+  if (st != PA_OK) return st;
+  if (a->num_seqs == 0) return PA_OK;
+  if (!aligned16(a->out) || !aligned16(a->q) || !aligned16(a->k_cache) ||
+      !aligned16(a->v_cache) || !a->block_tables || !a->context_lens)
+    return PA_ERR_INVALID;
+  const Plan pl = make_plan(a);
+  if (a->num_seqs > 65535 || pl.max_parts > 65535 || a->num_q_heads > 65535)
+    return PA_ERR_UNSUPPORTED;
+  if ((a->k_new == nullptr) != (a->v_new == nullptr)) return PA_ERR_INVALID;
+  if (a->k_new && (!aligned16(a->k_new) || !aligned16(a->v_new))) return PA_ERR_INVALID;
+  if (pl.ws_bytes > kScratchBytes) return PA_ERR_WORKSPACE;
+  pa_decode_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (pl.ws_bytes) {
+    st = scratch_on_current_device((hipStream_t)stream, &b.workspace);
+    if (st != PA_OK) return st;
+    b.workspace_bytes = kScratchBytes;
+  }
+  return run_plan(&b, pl, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -86,6 +86,7 @@ def lib():
         "pa_decode_workspace_bytes": (ctypes.c_size_t, [A]),
         "pa_decode_partition_size": (_I32, [A]),
         "pa_decode": (ctypes.c_int, [A, _P]),
+        "pa_decode_static": (ctypes.c_int, [A, _P]),
         "pa_prefill": (ctypes.c_int, [ctypes.POINTER(pa_prefill_args), _P]),
         "pa_decode_prefix_workspace_bytes": (ctypes.c_size_t, [A, ctypes.POINTER(pa_prefix_groups)]),
         "pa_decode_prefix": (ctypes.c_int, [A, ctypes.POINTER(pa_prefix_groups), _P]),
@@ -280,6 +281,21 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_c
         a.workspace = _ptr(workspace)
         a.workspace_bytes = need
     _check(lib().pa_decode(ctypes.byref(a), _stream(stream)), "pa_decode")
+    return out
+
+
+PA_DECODE_STATIC_SCRATCH_BYTES = 64 << 20  # include/pagedattn.h
+
+
+def pa_decode_static(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                     partition_size=0, stream=None, k_new=None, v_new=None, context_lens_host=None):
+    """pa_decode without a workspace argument: the library keeps the split-K
+    partials in its own fixed device scratch (PA_DECODE_STATIC_SCRATCH_BYTES
+    per GPU), so the call allocates nothing.  Calls that overlap in time on
+    one GPU share that scratch and race."""
+    a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                         max_context_len, partition_size, None, k_new, v_new, context_lens_host)
+    _check(lib().pa_decode_static(ctypes.byref(a), _stream(stream)), "pa_decode_static")
     return out
 
 

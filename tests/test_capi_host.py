@@ -108,6 +108,27 @@ def test_decode_rejects_null_pointers_and_missing_workspace(L):
     assert L.pa_decode(None, None) == pa.PA_ERR_INVALID
 
 
+def test_decode_static_rejects_before_touching_the_device(L):
+    """pa_decode_static validates like pa_decode, and a step whose split-K
+    partials exceed the fixed scratch is refused with PA_ERR_WORKSPACE
+    before any device call."""
+    import ctypes
+    buf = (ctypes.c_uint8 * 64)()
+    addr = (ctypes.addressof(buf) + 15) // 16 * 16
+    assert L.pa_decode_static(None, None) == pa.PA_ERR_INVALID
+    assert L.pa_decode_static(_args(num_q_heads=7), None) == pa.PA_ERR_INVALID
+    assert L.pa_decode_static(_args(head_dim=96), None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_decode_static(_args(), None) == pa.PA_ERR_INVALID  # null tensors
+    # 512 sequences x 64 heads x 256 partitions of 512 tokens: 4.4 GB of partials
+    big = _args(num_seqs=512, num_q_heads=64, num_kv_heads=8, max_context_len=131072,
+                max_blocks_per_seq=8192, num_blocks=8192, partition_size=512)
+    assert L.pa_decode_workspace_bytes(big) > pa.PA_DECODE_STATIC_SCRATCH_BYTES
+    big.out = big.q = big.k_cache = big.v_cache = addr
+    big.block_tables = big.context_lens = addr
+    assert L.pa_decode_static(big, None) == pa.PA_ERR_WORKSPACE
+    assert L.pa_status_string(pa.PA_ERR_WORKSPACE)
+
+
 def test_fused_append_needs_both_tensors(L):
     import ctypes
     buf = (ctypes.c_uint8 * 64)()
