@@ -196,98 +196,64 @@ __device__ __forceinline__ int pick_block(const int (&b)[N], int j) {
   return id;
 }
 
-// Body of the decode pass for the workgroup at grid position (bx, by, bz);
-// `lds` holds merge_lds_bytes(NW, G, D) bytes.  With prefix groups
-// (pa_decode_prefix, through prefix_suffix_kernel) it takes each member's
-// keys after its group's shared prefix; the prefix itself is attended by the
-// shared-prefix pass of the prefill body, in pre_parts partitions of pre_P
-// tokens that fill the first partial slots of every member.
-template <typename Ty, int D, int BS, int NW, bool KV8>
-__device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* lds,
-    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
-    const void* __restrict__ vcv, const int32_t* __restrict__ tables,
-    const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new, int Hq, int Hkv, int G, int n_groups, int NB,
-    int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
-    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs, int pre_parts, int pre_P,
-    const int32_t* __restrict__ grp_start, const int32_t* __restrict__ grp_len, int n_grp) {
+// One wave's share of the decode pass: q held as the B operand of both
+// products, the running (max, sum, output) of the 16 columns (query heads
+// i = lane % 16 of a group), the block ids of its coming chunks, and the
+// per-chunk steps:
+//   issue    -- every K and V load of one 32-token chunk (per lane: 2 x KK
+//               16-byte K vectors and MM 16-byte V rows, or for INT8 codes
+//               2 x KK/2 16-byte K vectors, MM 8-byte V rows and one scale);
+//   consume  -- both products and the online-softmax update for that chunk;
+//   add_token -- the fused append's new token, on the vector ALU.
+// Token tau of a chunk (0..31) sits in block tau / BS of the chunk at row
+// tau % BS; a block of 64 tokens holds the whole chunk from row t0 % 64.
+template <typename Ty, int D, int BS, bool KV8>
+struct WaveDecoder {
   static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
   static_assert(D % 32 == 0, "head_dim multiple of 32");
   using V8 = typename Ty::vec8;
-  constexpr int KK = D / 32;     // QK products along head_dim (32 channels each)
-  constexpr int MM = D / 16;     // PV products along head_dim (16 channels each)
+  static constexpr int KK = D / 32;  // QK products along head_dim (32 channels each)
+  static constexpr int MM = D / 16;  // PV products along head_dim (16 channels each)
   // one (block, KV head) tile: D*BS 16-bit elements, or an INT8 tile (bytes)
-  constexpr int TILE = KV8 ? I8Tile<D, BS>::kBytes : D * BS;
+  static constexpr int TILE = KV8 ? I8Tile<D, BS>::kBytes : D * BS;
+  static constexpr int BPC = BS >= kChunk ? 1 : kChunk / BS;  // blocks per chunk
+  static constexpr int CPB = 64 / BPC;                         // chunks per batch of block ids
   using Elem = typename std::conditional<KV8, uint8_t, uint16_t>::type;
-  const Elem* kc = reinterpret_cast<const Elem*>(kcv);
-  const Elem* vc = reinterpret_cast<const Elem*>(vcv);
-  constexpr int DP = D + 4;      // padded LDS row of the merge buffer
+  using RawT = Raw<KK, MM, KV8>;
 
-  const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
-  const int i = lane & 15;       // row (A operand) / column (B operand, output)
-  const int g4 = lane >> 4;      // which 8-element slice of the reduction dim
-  int hk, grp = 0, p = 0, s, c;
-  if (num_seqs > 0) {
-    hk = bx / n_groups;
-    grp = bx - hk * n_groups;
-    // Flat work list: y enumerates the (sequence, partition) units that exist,
-    // sequence by sequence; each wave finds its unit from a prefix sum of the
-    // sequences' partition counts, so grid slots past the real work sit at
-    // the end of the grid instead of between sequences.
-    if (!flat_unit(lens, num_seqs, min(max_ctx, max_blocks * BS), P, by, lane, s, p,
-                   c))
-      return;
-  } else {
-    hk = bx / n_groups;
-    grp = bx - hk * n_groups;
-    p = by;
-    s = bz;
-    c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
+  const Elem* kc;
+  const Elem* vc;
+  int lane, i, g4;     // lane; row (A operand) / column (B operand, output); reduction slice
+  int64_t blk_stride;  // elements (bytes for INT8) from one block to the next
+  int64_t head_off;    // offset of the KV head's tile inside a block
+  float scale_log2;
+  V8 qop[KK];          // Q^T operand: head i, channels 8*qchunk(kk)..+8
+  f32x4 acc[MM];       // O^T[d = 16*mm + 4*g4 + j][head i]
+  float m_run;         // running max of the base-2 logits (head i)
+  float l_run;         // this lane's share of the running sum
+  int tbl;             // block ids of the current batch (lane e: entry e)
+
+  __device__ __forceinline__ WaveDecoder(const void* kcv, const void* vcv, int Hkv, float sl2)
+      : kc(reinterpret_cast<const Elem*>(kcv)), vc(reinterpret_cast<const Elem*>(vcv)),
+        lane(threadIdx.x & 63), i(threadIdx.x & 15), g4((threadIdx.x & 63) >> 4),
+        blk_stride((int64_t)Hkv * TILE), head_off(0), scale_log2(sl2), tbl(0) {}
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
   }
-  // With prefix groups: tokens [0, skip) of sequence s belong to its group's
-  // shared prefix, attended by the prefix pass (partial slots 0 .. pb - 1);
-  // this launch covers [skip, c) in the slots after them.
-  int skip = 0;
-  if (n_grp > 0) {
-    int lo = 0, hi = n_grp - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (grp_start[mid] <= s) lo = mid;
-      else hi = mid - 1;
-    }
-    skip = uniform(clampi(grp_len[lo], 0, min(c, pre_parts * pre_P)));
+
+  // Channels 8*m..+8 of the K operand that product kk meets (m = 4*kk + g4;
+  // INT8: 8*(kk/2) + 2*g4 + kk%2, so that one 16-byte load of codes feeds
+  // two products).
+  __device__ __forceinline__ int qchunk(int kk) const {
+    return KV8 ? 8 * (kk >> 1) + 2 * g4 + (kk & 1) : 4 * kk + g4;
   }
-  const int pb = n_grp > 0 ? (skip + pre_P - 1) / pre_P : 0;  // partial slots of the prefix
-  // Chunks start on 32-token boundaries: the partitions run from the boundary
-  // at or below skip, and tokens below skip are dropped.
-  const int a_skip = skip & ~(kChunk - 1);
-  const int n_p = (c - a_skip + P - 1) / P;
-  if (p < 0 || p >= max(n_p, 1)) return;
-  const int t_begin = a_skip + p * P;
-  // With a fused append the token at c - 1 comes from k_new / v_new, not from
-  // the cache: the chunk loop reads [t_begin, cc) and the new token is added
-  // afterwards by the workgroup whose partition holds it.
-  const bool append = k_new != nullptr;
-  const int cc = append ? max(c - 1, 0) : c;  // keys [0, cc) come from the cache
-  const bool has_new = append && c > 0 && c - 1 >= t_begin && c - 1 < t_begin + P;
-  const int t_end = min(cc, t_begin + P);
-  const int n_chunks = max(0, t_end - t_begin + kChunk - 1) / kChunk;
 
-  // Columns: query heads qh0 + i of the group of 16.
-  const int Gv = min(16, G - grp * 16);  // valid columns
-  const bool head_ok = i < Gv;
-  const int qh0 = hk * G + grp * 16;     // first query head of the group
-  // q / out row (times Hq, plus head) of column `col`
-  auto out_row = [&](int col) -> int64_t { return (int64_t)s * Hq + qh0 + col; };
-
-  // Q^T operand of the QK product: lane feeds head i, channels 8*m..+8 of the
-  // K operand it meets (m = 4*kk + g4; INT8: 8*(kk/2) + 2*g4 + kk%2, so that
-  // one 16-byte load of codes feeds two products).
-  auto qchunk = [&](int kk) { return KV8 ? 8 * (kk >> 1) + 2 * g4 + (kk & 1) : 4 * kk + g4; };
-  V8 qop[KK];
-  {
-    const uint16_t* qrow = q + out_row(head_ok ? i : 0) * D;
+  // q row of this lane's column (zeros for a column past the group).
+  __device__ __forceinline__ void load_q(const uint16_t* __restrict__ qrow, bool head_ok) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 raw = head_ok ? load16(qrow + 8 * qchunk(kk)) : u32x4{0u, 0u, 0u, 0u};
@@ -295,60 +261,30 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
     }
   }
 
-  // Fused append: wave 0 of the workgroup whose partition holds token c - 1
-  // fetches the new K row and V row up front, 8 bytes per lane (lanes
-  // [0, D/4) hold K elements 4*lane..+3, lanes [D/4, D/2) hold V elements
-  // 4*(lane - D/4)..+3), so the data is in registers when the token is added.
-  const bool new_here = has_new && w == 0;
-  u32x2 nv = {0u, 0u};
-  if (new_here && lane < D / 2) {
-    const int64_t row = ((int64_t)s * Hkv + hk) * D;
-    nv = lane < D / 4 ? load8(k_new + row + 4 * lane) : load8(v_new + row + 4 * (lane - D / 4));
-  }
-
-  f32x4 acc[MM];
-#pragma unroll
-  for (int mm = 0; mm < MM; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max of the base-2 logits (head i)
-  float l_run = 0.f;        // this lane's share of the running sum
-
-  const int32_t* trow = tables + (int64_t)s * max_blocks;
-  const int64_t blk_stride = (int64_t)Hkv * TILE;
-  const int64_t head_off = (int64_t)hk * TILE;
-
-  // Block ids of this wave's chunks (w, w + NW, ...), held in registers: lane
-  // j has the id of block j % BPC of the wave's chunk number j / BPC of the
-  // current batch of CPB chunks.  One vector load fetches a batch before the
-  // first K/V load is issued, so no chunk waits on a table read (a chunk
-  // whose block ids came from a load in the loop would also wait for every
-  // K/V load issued before that read).  Entries past the cached range are
-  // not read (id 0 stands in; those tokens are dropped).
-  constexpr int BPC = BS >= kChunk ? 1 : kChunk / BS;  // blocks per chunk
-  constexpr int CPB = 64 / BPC;                         // chunks per batch
-  // Chunks are dealt to the waves round-robin (the intelliparadigm page's
-  // warp-to-block assignment, section 4.2, with a wave taking 32 tokens).
-  auto chunk_of = [&](int k) { return w + NW * k; };  // the wave's k-th chunk
-  int tbl = 0;
-  auto load_batch = [&](int k0) {
-    const int ch = chunk_of(k0 + lane / BPC);
+  // Loads the table entries of the chunks ch(k0), ch(k0 + 1), ... (ch(k) =
+  // c0 + stride * k), one block id per lane: lane e holds block e % BPC of
+  // the chunk k0 + e / BPC.  Entries past the cached range [0, cc) or past
+  // n_chunks are not read (id 0 stands in; those tokens are dropped).
+  __device__ __forceinline__ void load_batch(const int32_t* __restrict__ trow, int t_begin,
+                                             int n_chunks, int cc, int NB, int c0, int stride,
+                                             int k0) {
+    const int ch = c0 + stride * (k0 + lane / BPC);
     const int t = t_begin + ch * kChunk + (lane % BPC) * BS;
     tbl = ch < n_chunks && t < cc ? clampi(trow[t / BS], 0, NB - 1) : 0;
-  };
-  if (chunk_of(0) < n_chunks) load_batch(0);
-  // Physical blocks of the wave's k-th chunk, in token order (one block when
-  // BS >= 32).
-  auto block_ids = [&](int k, int (&b)[BPC]) {
-    if (k > 0 && k % CPB == 0) load_batch(k);
+  }
+
+  // Physical blocks of the k-th chunk of the current walk, in token order
+  // (one block when BS >= 32); a new batch is loaded every CPB chunks.
+  __device__ __forceinline__ void block_ids(int k, int (&b)[BPC], const int32_t* __restrict__ trow,
+                                            int t_begin, int n_chunks, int cc, int NB, int c0,
+                                            int stride) {
+    if (k > 0 && k % CPB == 0) load_batch(trow, t_begin, n_chunks, cc, NB, c0, stride, k);
     const int e = (k % CPB) * BPC;
 #pragma unroll
     for (int j = 0; j < BPC; ++j) b[j] = __builtin_amdgcn_readlane(tbl, e + j);
-  };
-  // Issue every K and V load of the chunk at token t0 (per lane: 2 x KK
-  // 16-byte K vectors and MM 16-byte V rows, or for INT8 codes 2 x KK/2
-  // 16-byte K vectors, MM 8-byte V rows and four 16-byte groups of scales).
-  // Token tau of the chunk (0..31) sits in block tau / BS of the chunk at row
-  // tau % BS; a block of 64 tokens holds the whole chunk from row t0 % 64.
-  auto issue = [&](const int (&b)[BPC], int t0, Raw<KK, MM, KV8>& r) {
+  }
+
+  __device__ __forceinline__ void issue(const int (&b)[BPC], int t0, RawT& r) const {
     const int r0 = BS > kChunk ? t0 % BS : 0;
     auto at = [&](int tau, int64_t& off, int& row) {  // tile offset and row of token tau
       const int id = pick_block<BPC>(b, tau / BS);
@@ -391,9 +327,11 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
       at(lane & 31, osc, rsc);
       r.sc = stream_f1((lane < 32 ? kc : vc) + osc + SC + 4 * rsc);
     }
-  };
-  // Both products and the online-softmax update for the chunk at token t0.
-  auto consume = [&](int t0, Raw<KK, MM, KV8>& r) {
+  }
+
+  // Both products and the online-softmax update for the chunk at token t0;
+  // tokens outside [skip, cc) are dropped.
+  __device__ __forceinline__ void consume(int t0, RawT& r, int cc, int skip) {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -487,10 +425,10 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
       for (int e = 0; e < 8; ++e) pr[e] = exp2_fast(x[e] - m_use);
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
-        const float s0 = sv[2 * wd], s1 = sv[2 * wd + 1];
-        pw[wd] = Ty::pack2(pr[2 * wd] * s0, pr[2 * wd + 1] * s1);
-        psum += s0 != 0.f ? Ty::lo_f32(pw[wd]) * __builtin_amdgcn_rcpf(s0) : pr[2 * wd];
-        psum += s1 != 0.f ? Ty::hi_f32(pw[wd]) * __builtin_amdgcn_rcpf(s1) : pr[2 * wd + 1];
+        const float sa = sv[2 * wd], sb = sv[2 * wd + 1];
+        pw[wd] = Ty::pack2(pr[2 * wd] * sa, pr[2 * wd + 1] * sb);
+        psum += sa != 0.f ? Ty::lo_f32(pw[wd]) * __builtin_amdgcn_rcpf(sa) : pr[2 * wd];
+        psum += sb != 0.f ? Ty::hi_f32(pw[wd]) * __builtin_amdgcn_rcpf(sb) : pr[2 * wd + 1];
       }
     }
     l_run += psum;
@@ -510,76 +448,79 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
       else
         acc[mm] = Ty::mma(__builtin_bit_cast(V8, codes_to_operand<Ty>(r.v[mm])), pop, acc[mm]);
     }
-  };
+  }
 
-  // Chunk loop.  All loads of a chunk are issued before any of them is used
-  // (the scheduling barrier keeps the compiler from interleaving the
-  // products with the loads).  16-bit caches: the loads of the wave's next
-  // chunk (and the table entries of the one after) are issued before the
-  // current chunk is used, two chunks in flight per wave.  INT8 caches: one
-  // chunk at a time (measured on MI355X: with half the bytes per chunk, the
-  // look-ahead made the step 4% slower; without it the kernel needs fewer
-  // registers and more waves fit).
-  int nb[BPC] = {};
-  int ch = chunk_of(0);
-  if (ch < n_chunks) block_ids(0, nb);
-  if constexpr (KV8) {
-    for (int k = 0; ch < n_chunks; ++k) {
-      Raw<KK, MM, KV8> one;
-      issue(nb, t_begin + ch * kChunk, one);
-      const int ch1 = chunk_of(k + 1);
-      if (ch1 < n_chunks) block_ids(k + 1, nb);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(t_begin + ch * kChunk, one);
-      ch = ch1;
-    }
-  } else {
-    Raw<KK, MM, KV8> cur, nxt;
-    if (ch < n_chunks) {
-      issue(nb, t_begin + ch * kChunk, cur);
-      if (chunk_of(1) < n_chunks) block_ids(1, nb);
-    }
-    for (int k = 0; ch < n_chunks; ++k) {
-      const int ch1 = chunk_of(k + 1);
-      if (ch1 < n_chunks) {
-        issue(nb, t_begin + ch1 * kChunk, nxt);
-        if (chunk_of(k + 2) < n_chunks) block_ids(k + 2, nb);
+  // Streams the chunks k = 0 .. n - 1 of a walk (chunk k starts at token
+  // t0_of(k); ids(k, b) gives its block ids, reading the table in batches).
+  // All loads of a chunk are issued before any of them is used: the
+  // scheduling barrier keeps the compiler from interleaving the products
+  // with the loads.  AHEAD: the loads of chunk k + 1 are issued before chunk
+  // k is consumed.  The compiler turns `cur = nxt` into register copies,
+  // which wait for those loads at the end of the iteration, so in effect one
+  // chunk is in flight while the previous one is computed.  Measured on
+  // MI355X, this form at 218 VGPRs (two waves per SIMD) beat two register
+  // sets used in turn (no copies, two chunks really in flight): 264 VGPRs
+  // and one wave per SIMD, 70.0 against 63.8 us on the LLaMA-13B-shaped
+  // step; capped at 256 VGPRs that form spills and took 76 us.
+  template <bool AHEAD, typename T0, typename Ids>
+  __device__ __forceinline__ void walk(int n, T0 t0_of, Ids ids, int cc, int skip) {
+    if (n <= 0) return;
+    int nb[BPC] = {};
+    ids(0, nb);
+    if constexpr (AHEAD) {
+      RawT cur, nxt;
+      issue(nb, t0_of(0), cur);
+      if (n > 1) ids(1, nb);
+      for (int k = 0; k < n; ++k) {
+        if (k + 1 < n) {
+          issue(nb, t0_of(k + 1), nxt);
+          if (k + 2 < n) ids(k + 2, nb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        consume(t0_of(k), cur, cc, skip);
+        cur = nxt;
       }
-      __builtin_amdgcn_sched_barrier(0);
-      consume(t_begin + ch * kChunk, cur);
-      cur = nxt;
-      ch = ch1;
+    } else {
+      for (int k = 0; k < n; ++k) {
+        RawT one;
+        issue(nb, t0_of(k), one);
+        if (k + 1 < n) ids(k + 1, nb);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(t0_of(k), one, cc, skip);
+      }
     }
   }
 
-  // Fused append: that wave adds token c - 1 to its running state on the
-  // vector ALU (one logit per head: each lane of a head takes 32 channels and
-  // the 4 row groups are added), rounding the weight to the element type as
-  // the matrix-core path does.  The group-0 workgroup also stores the token
-  // into the cache slot of position c - 1, bit for bit.
-  if (new_here) {
+  // Fused append: adds the token whose K row and V row this wave fetched
+  // into nv (lanes [0, D/4) hold K elements 4*lane..+3, lanes [D/4, D/2) V
+  // elements 4*(lane - D/4)..+3) to its running state on the vector ALU
+  // (one logit per head: each lane of a head takes 32 channels and the 4 row
+  // groups are added), rounding the weight to the element type as the
+  // matrix-core path does.  With `store` the token also goes bit for bit
+  // (INT8: quantised) into the cache slot at row o of block b.
+  __device__ __forceinline__ void add_token(u32x2 nv, bool store, int64_t b, int o) {
     if constexpr (!KV8) {
       // operands gathered from the lanes holding them: K chunk 4*kk+g4 (16 B)
       // sits in lanes 2*chunk, 2*chunk+1; V channels 16*mm+4*g4..+3 (8 B) in
       // lane D/4 + 4*mm + g4.
       u32x4 kx[KK];
       u32x2 vx[MM];
-  #pragma unroll
+#pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const int src = 2 * (4 * kk + g4);
         kx[kk] = u32x4{(uint32_t)__shfl((int)nv[0], src), (uint32_t)__shfl((int)nv[1], src),
                        (uint32_t)__shfl((int)nv[0], src + 1), (uint32_t)__shfl((int)nv[1], src + 1)};
       }
-  #pragma unroll
+#pragma unroll
       for (int mm = 0; mm < MM; ++mm) {
         const int src = D / 4 + 4 * mm + g4;
         vx[mm] = u32x2{(uint32_t)__shfl((int)nv[0], src), (uint32_t)__shfl((int)nv[1], src)};
       }
       float dot = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const u32x4 qw = __builtin_bit_cast(u32x4, qop[kk]);
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 8; ++e)
           dot = fmaf(Ty::to_f32((uint16_t)(qw[e / 2] >> (16 * (e & 1)))),
                      Ty::to_f32((uint16_t)(kx[kk][e / 2] >> (16 * (e & 1)))), dot);
@@ -593,23 +534,20 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
       m_run = m_new;
       l_run = l_run * alpha + (g4 == 0 ? pn : 0.f);
       // lane holds O^T[d = 16*mm + 4*g4 + j][head i]; vx[mm] holds v_new[16*mm + 4*g4 + j]
-  #pragma unroll
+#pragma unroll
       for (int mm = 0; mm < MM; ++mm)
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[mm][j] = fmaf(pn, Ty::to_f32((uint16_t)(vx[mm][j / 2] >> (16 * (j & 1)))),
                             acc[mm][j] * alpha);
-      if (grp == 0 && lane < D / 2) {
-        const int tn = c - 1;
-        const int64_t b = clampi(trow[tn / BS], 0, NB - 1);
-        const int o = tn % BS;
+      if (store && lane < D / 2) {
         if (lane < D / 4) {  // K elements 4*lane..+3: half of chunk lane/2's 16-byte row piece
           uint16_t* kd = const_cast<Elem*>(kc) + b * blk_stride + head_off;
           *reinterpret_cast<u32x2*>(kd + ((lane / 2) * BS + o) * 8 + 4 * (lane & 1)) = nv;
         } else {             // V channels 4*(lane - D/4)..+3 of row o
           uint16_t* vd = const_cast<Elem*>(vc) + b * blk_stride + head_off;
           const int d0 = 4 * (lane - D / 4);
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 4; ++j)
             vd[(d0 + j) * BS + o] = (uint16_t)(nv[j / 2] >> (16 * (j & 1)));
         }
@@ -618,8 +556,7 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
       // INT8 caches: quantise the token's K and V rows in fp32 (scale =
       // max|x| / 127, code = rint(x / scale) clamped to +-127), then add the
       // token with the values code * scale, as a cache write followed by a
-      // read would.  Lanes [0, D/4) hold K elements 4*lane..+3, lanes
-      // [D/4, D/2) V elements; each half finds its row maximum.
+      // read would.  Each half of the lanes finds its row maximum.
       float xv[4];
       float am = 0.f;
 #pragma unroll
@@ -633,8 +570,8 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
       uint32_t cw = 0;  // this lane's 4 codes
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float r = qsc > 0.f ? fminf(fmaxf(rintf(xv[j] / qsc), -127.f), 127.f) : 0.f;
-        cw |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * j);
+        const float rr = qsc > 0.f ? fminf(fmaxf(rintf(xv[j] / qsc), -127.f), 127.f) : 0.f;
+        cw |= (uint32_t)(uint8_t)(int8_t)(int)rr << (8 * j);
       }
       const float sk_new = __shfl(qsc, 0);
       const float sv_new = __shfl(qsc, D / 4);
@@ -664,10 +601,7 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[mm][j] = fmaf(pv, (float)sbyte(vq, j), acc[mm][j] * alpha);
       }
-      if (grp == 0 && lane < D / 2) {
-        const int tn = c - 1;
-        const int64_t b = clampi(trow[tn / BS], 0, NB - 1);
-        const int o = tn % BS;
+      if (store && lane < D / 2) {
         constexpr int SC = I8Tile<D, BS>::kScales;
         if (lane < D / 4) {  // K codes of channels 4*lane..+3: bytes 4*(lane%4).. of x-vector lane/4
           uint8_t* kd = const_cast<Elem*>(kc) + b * blk_stride + head_off;
@@ -683,9 +617,135 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
       }
     }
   }
+};
 
-  float l_tot = l_run + __shfl_xor(l_run, 16);
+// Body of the decode pass for the workgroup at grid position (bx, by, bz);
+// `lds` holds merge_lds_bytes(NW, G, D) bytes.  With prefix groups
+// (pa_decode_prefix, through prefix_suffix_kernel) it takes each member's
+// keys after its group's shared prefix; the prefix itself is attended by the
+// shared-prefix pass of the prefill body, in pre_parts partitions of pre_P
+// tokens that fill the first partial slots of every member.
+template <typename Ty, int D, int BS, int NW, bool KV8>
+__device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* lds,
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
+    const void* __restrict__ vcv, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ lens, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, int Hq, int Hkv, int G, int n_groups, int NB,
+    int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs, int pre_parts, int pre_P,
+    const int32_t* __restrict__ grp_start, const int32_t* __restrict__ grp_len, int n_grp) {
+  using W = WaveDecoder<Ty, D, BS, KV8>;
+  constexpr int MM = W::MM;
+  constexpr int BPC = W::BPC;
+  constexpr int DP = D + 4;      // padded LDS row of the merge buffer
+
+  W wd(kcv, vcv, Hkv, scale_log2);
+  const int lane = wd.lane, i = wd.i, g4 = wd.g4;
+  const int w = uniform(threadIdx.x >> 6);
+  int hk, grp = 0, p = 0, s, c;
+  if (num_seqs > 0) {
+    hk = bx / n_groups;
+    grp = bx - hk * n_groups;
+    // Flat work list: y enumerates the (sequence, partition) units that exist,
+    // sequence by sequence; each wave finds its unit from a prefix sum of the
+    // sequences' partition counts, so grid slots past the real work sit at
+    // the end of the grid instead of between sequences.
+    if (!flat_unit(lens, num_seqs, min(max_ctx, max_blocks * BS), P, by, lane, s, p,
+                   c))
+      return;
+  } else {
+    hk = bx / n_groups;
+    grp = bx - hk * n_groups;
+    p = by;
+    s = bz;
+    c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
+  }
+  // With prefix groups: tokens [0, skip) of sequence s belong to its group's
+  // shared prefix, attended by the prefix pass (partial slots 0 .. pb - 1);
+  // this launch covers [skip, c) in the slots after them.
+  int skip = 0;
+  if (n_grp > 0) {
+    int lo = 0, hi = n_grp - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (grp_start[mid] <= s) lo = mid;
+      else hi = mid - 1;
+    }
+    skip = uniform(clampi(grp_len[lo], 0, min(c, pre_parts * pre_P)));
+  }
+  const int pb = n_grp > 0 ? (skip + pre_P - 1) / pre_P : 0;  // partial slots of the prefix
+  // Chunks start on 32-token boundaries: the partitions run from the boundary
+  // at or below skip, and tokens below skip are dropped.
+  const int a_skip = skip & ~(kChunk - 1);
+  const int n_p = (c - a_skip + P - 1) / P;
+  if (p < 0 || p >= max(n_p, 1)) return;
+  const int t_begin = a_skip + p * P;
+  // With a fused append the token at c - 1 comes from k_new / v_new, not from
+  // the cache: the chunk loop reads [t_begin, cc) and the new token is added
+  // afterwards by the workgroup whose partition holds it.
+  const bool append = k_new != nullptr;
+  const int cc = append ? max(c - 1, 0) : c;  // keys [0, cc) come from the cache
+  const bool has_new = append && c > 0 && c - 1 >= t_begin && c - 1 < t_begin + P;
+  const int t_end = min(cc, t_begin + P);
+  const int n_chunks = max(0, t_end - t_begin + kChunk - 1) / kChunk;
+
+  // Columns: query heads qh0 + i of the group of 16.
+  const int Gv = min(16, G - grp * 16);  // valid columns
+  const bool head_ok = i < Gv;
+  const int qh0 = hk * G + grp * 16;     // first query head of the group
+  // q / out row (times Hq, plus head) of column `col`
+  auto out_row = [&](int col) -> int64_t { return (int64_t)s * Hq + qh0 + col; };
+
+  wd.load_q(q + out_row(head_ok ? i : 0) * D, head_ok);
+
+  // Fused append: wave 0 of the workgroup whose partition holds token c - 1
+  // fetches the new K row and V row up front, 8 bytes per lane (lanes
+  // [0, D/4) hold K elements 4*lane..+3, lanes [D/4, D/2) hold V elements
+  // 4*(lane - D/4)..+3), so the data is in registers when the token is added.
+  const bool new_here = has_new && w == 0;
+  u32x2 nv = {0u, 0u};
+  if (new_here && lane < D / 2) {
+    const int64_t row = ((int64_t)s * Hkv + hk) * D;
+    nv = lane < D / 4 ? load8(k_new + row + 4 * lane) : load8(v_new + row + 4 * (lane - D / 4));
+  }
+
+  wd.reset();
+  const int32_t* trow = tables + (int64_t)s * max_blocks;
+  wd.head_off = (int64_t)hk * W::TILE;
+
+  // Block ids of this wave's chunks (w, w + NW, ...), held in registers: one
+  // vector load fetches a batch of table entries before the first K/V load is
+  // issued, so no chunk waits on a table read (a chunk whose block ids came
+  // from a load in the loop would also wait for every K/V load issued before
+  // that read).  Chunks are dealt to the waves round-robin (the
+  // intelliparadigm page's warp-to-block assignment, section 4.2, with a wave
+  // taking 32 tokens).
+  auto chunk_of = [&](int k) { return w + NW * k; };  // the wave's k-th chunk
+  if (chunk_of(0) < n_chunks) wd.load_batch(trow, t_begin, n_chunks, cc, NB, w, NW, 0);
+  auto block_ids = [&](int k, int (&b)[BPC]) {
+    wd.block_ids(k, b, trow, t_begin, n_chunks, cc, NB, w, NW);
+  };
+
+  // Chunk loop over the wave's chunks w, w + NW, ... of the partition.
+  // 16-bit caches keep the next chunk in flight; INT8 caches load one chunk
+  // at a time (measured on MI355X: with half the bytes per chunk, the
+  // look-ahead made the step slower; without it the kernel needs fewer
+  // registers and more waves fit).
+  const int n_mine = w < n_chunks ? (n_chunks - w + NW - 1) / NW : 0;
+  wd.template walk<!KV8>(n_mine, [&](int k) { return t_begin + chunk_of(k) * kChunk; }, block_ids,
+                         cc, skip);
+
+  // Fused append: that wave adds token c - 1 to its running state; the
+  // group-0 workgroup also stores the token into the cache slot of position
+  // c - 1.
+  if (new_here) {
+    const int tn = c - 1;
+    wd.add_token(nv, grp == 0, clampi(trow[tn / BS], 0, NB - 1), tn % BS);
+  }
+
+  float l_tot = wd.l_run + __shfl_xor(wd.l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
+  const float m_run = wd.m_run;
 
   // Merge the NW waves: M = max_w m_w per head, then every wave rescales its
   // sum and output by 2^(m_w - M) into LDS and the workgroup adds them up in
@@ -704,7 +764,7 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
     // lane holds O^T[d = 16*mm + 4*g4 + j][head i], j = 0..3
     float* arow = a_sh + (w * Gv + i) * DP + 4 * g4;
 #pragma unroll
-    for (int mm = 0; mm < MM; ++mm) *reinterpret_cast<f32x4*>(arow + 16 * mm) = acc[mm] * f;
+    for (int mm = 0; mm < MM; ++mm) *reinterpret_cast<f32x4*>(arow + 16 * mm) = wd.acc[mm] * f;
   }
   __syncthreads();
 
@@ -1456,14 +1516,13 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(
 // partition contents, never on where the blocks sit.
 // ----------------------------------------------------------------------------
 // The rows a merge launch covers, from the host copy of the context lengths:
-// the sequences with more than one partition, with their partition counts.
-// Passed by value as a kernel argument; n = 0 means no list (the grid
+// the sequences with more than one partition, one packed entry s | parts << 16
+// each.  Passed by value as a kernel argument; n = 0 means no list (the grid
 // covers every sequence, and each workgroup reads its length).
 constexpr int kMaxSplit = 512;
 struct SplitList {
   int32_t n;
-  uint16_t seq[kMaxSplit];
-  uint16_t parts[kMaxSplit];
+  uint32_t e[kMaxSplit];
 };
 
 template <typename Store, int D, int NT>
@@ -1481,8 +1540,8 @@ __global__ __launch_bounds__(NT) void merge_kernel(
   const int r = tid / C4, c4 = tid - r * C4;
   int s, n_p, skip = 0;
   if (split.n > 0) {  // a split sequence of the host's list: no length to read
-    s = split.seq[blockIdx.y];
-    n_p = min((int)split.parts[blockIdx.y], max_parts);
+    s = (int)(split.e[blockIdx.y] & 0xFFFFu);
+    n_p = min((int)(split.e[blockIdx.y] >> 16), max_parts);
   } else {
     s = blockIdx.y;
     const int c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
@@ -1838,8 +1897,7 @@ void launch_merge(const pa_decode_args* a, const Plan& pl, const float* wa, cons
         n = -1;  // too many for the list: every sequence reads its length
         break;
       }
-      sl.seq[n] = (uint16_t)s;
-      sl.parts[n] = (uint16_t)parts;
+      sl.e[n] = (uint32_t)s | ((uint32_t)parts << 16);
       ++n;
     }
     if (n == 0) return;

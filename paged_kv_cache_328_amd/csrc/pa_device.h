@@ -94,7 +94,7 @@ __device__ __forceinline__ float exp2_fast(float x) {
   return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0
 }
 
-__device__ __forceinline__ int clampi(int v, int lo, int hi) {
+__host__ __device__ __forceinline__ int clampi(int v, int lo, int hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 

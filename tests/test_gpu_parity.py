@@ -492,8 +492,8 @@ def test_host_context_lens_size_the_grid_bit_identical(kv, P):
     """With the host copy of the context lengths the library launches only the
     (sequence, partition) units that exist; the units compute what they
     computed in the full grid, so the output is bit-identical to the call
-    without it, and matches the oracle (lengths 0..6000, log-uniform, with
-    the fused append)."""
+    without it, and both match the oracle (lengths 0..6000, log-uniform,
+    with the fused append)."""
     import torch
     from tests.test_gpu_int8 import poison_scales
     rng = np.random.default_rng(78)
@@ -532,8 +532,9 @@ def test_host_context_lens_size_the_grid_bit_identical(kv, P):
                         case.k_cache, case.v_cache, slots, dtype)
         want = oracle.decode(q, case.k_cache, case.v_cache, t0, case.context_lens, case.scale, dtype,
                              num_threads=16, bound=True)
-    check_attention(outs[1], want, dtype, f"host lens kv={kv} P={P}",
-                    kv_scale_min=i8_scale_min(case.v_cache, case.D, case.BS) if i8 else None)
+    for host, got in zip(("no", "yes"), outs):
+        check_attention(got, want, dtype, f"host lens kv={kv} P={P} host={host}",
+                        kv_scale_min=i8_scale_min(case.v_cache, case.D, case.BS) if i8 else None)
 
 
 @pytest.mark.parametrize("name,S,lens_fn,dtype,P,max_ctx", [

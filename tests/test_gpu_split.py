@@ -1,0 +1,144 @@
+"""GPU parity of pa_decode at the library's own split (partition_size = 0)
+with the host copy of the context lengths: the flat (sequence, partition)
+work list sized from the host lengths, and the merge over the split
+sequences only.
+
+Each case poisons the unused tail slots (NaN rows, or NaN INT8 scales), runs
+pa_decode with partition_size = 0 and context_lens_host, checks the stored
+new tokens bit for bit when the append is fused, and compares the output
+with the fp64 oracle under the parity bound.  The workloads' own shapes run
+at full size; small cases cover the edges of the split: contexts of 0, 1,
+32 and 33 tokens, one sequence split into many partitions (more than 32
+partials per row), more than 16 query heads per KV head, every block size
+and head_dim 64.
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle
+from paged_kv_cache_328_amd import pagedattn as pa
+from paged_kv_cache_328_amd import workloads as wl
+from tests import _gpu as _g
+from tests._gpu import (announce, check_attention, i8_scale_min, ints_to_dev, poison_tails, same_bits,
+                        tail_slots, to_dev, to_host)
+from tests.test_gpu_int8 import poison_scales
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def split_case(case, label, fused=True, repeat=False):
+    """pa_decode over `case` at the library's split with host lengths;
+    returns the output."""
+    import torch
+    dtype, i8 = case.dtype, case.kv_dtype == "i8"
+    tables = np.ascontiguousarray(case.block_tables[0])
+    lens = case.context_lens
+    kc, vc = case.k_cache, case.v_cache
+    slots = np.ascontiguousarray(case.slot_mapping[0])
+    live = slots >= 0
+    if i8:
+        poison_scales(kc, vc, tail_slots(tables, lens, case.BS), case.Hkv, case.D, case.BS)
+        if fused:
+            poison_scales(kc, vc, slots[live], case.Hkv, case.D, case.BS)
+    else:
+        poison_tails(oracle, kc, vc, tables, lens, dtype)
+        if fused:
+            nan = np.full((int(live.sum()), case.Hkv, case.D), wl.nan_bits(dtype), wl.NP_STORAGE[dtype])
+            oracle.write_kv(nan, nan.copy(), kc, vc, slots[live], dtype)
+    pool_t = "u8" if i8 else dtype
+    announce(f"{label}: upload pools NB={case.NB} S={case.S} Hq={case.Hq} Hkv={case.Hkv} D={case.D} "
+             f"BS={case.BS} kv={case.kv_dtype} max_ctx={case.max_context}")
+    kd, vd = to_dev(kc, pool_t), to_dev(vc, pool_t)
+    q = np.ascontiguousarray(case.q[0])
+    qd, td, ld = to_dev(q, dtype), ints_to_dev(tables), ints_to_dev(lens)
+    extra = {}
+    if fused:
+        k_new, v_new = np.ascontiguousarray(case.new_k[0]), np.ascontiguousarray(case.new_v[0])
+        extra = dict(k_new=to_dev(k_new, dtype), v_new=to_dev(v_new, dtype))
+    out = torch.empty_like(qd)
+    a = pa.make_decode_args(out, qd, kd, vd, td, ld, case.scale, case.max_context, 0,
+                            context_lens_host=lens, **extra)
+    announce(f"{label}: pa_decode P=0 (library: {pa.pa_decode_partition_size(a)}) fused={fused} "
+             f"workspace={pa.pa_decode_workspace_bytes(a)} B")
+    pa.pa_decode(out, qd, kd, vd, td, ld, case.scale, case.max_context, partition_size=0,
+                 context_lens_host=lens, **extra)
+    _sync()
+    got = to_host(out, dtype)
+    if repeat:  # same inputs again (the fused store rewrites the same bits): same output bits
+        out2 = torch.empty_like(qd)
+        pa.pa_decode(out2, qd, kd, vd, td, ld, case.scale, case.max_context, partition_size=0,
+                     context_lens_host=lens, **extra)
+        _sync()
+        assert same_bits(to_host(out2, dtype), got), f"{label}: repeated call differs"
+    if fused:
+        touched = np.unique(slots[live] // case.BS)
+        idx = torch.from_numpy(touched.astype(np.int64)).to(_g.DEVICE)
+        if i8:
+            oracle.write_kv_i8(k_new, v_new, dtype, kc, vc, slots, case.D, case.BS)
+        else:
+            oracle.write_kv(k_new, v_new, kc, vc, slots, dtype)
+        assert same_bits(to_host(kd.index_select(0, idx), pool_t), kc[touched]), f"{label}: K blocks"
+        assert same_bits(to_host(vd.index_select(0, idx), pool_t), vc[touched]), f"{label}: V blocks"
+    if i8:
+        want = oracle.decode_i8(q, dtype, kc, vc, tables, lens, case.scale, case.D, case.BS,
+                                num_threads=16, bound=True)
+    else:
+        want = oracle.decode(q, kc, vc, tables, lens, case.scale, dtype, num_threads=16, bound=True)
+    check_attention(got, want, dtype, label, kv_scale_min=i8_scale_min(vc, case.D, case.BS) if i8 else None)
+    return got
+
+
+@pytest.mark.parametrize("kv", [None, "i8"])
+@pytest.mark.parametrize("fused", [True, False])
+def test_mixed_lengths_full_size(kv, fused):
+    split_case(wl.mixed_gqa_bf16(kv_dtype=kv), f"split mixed_gqa_bf16 kv={kv}", fused=fused,
+              repeat=fused and kv is None)
+
+
+@pytest.mark.parametrize("kv", [None, "i8"])
+def test_long_context_full_size(kv):
+    """The long-context workload at the library's split (4096-token
+    partitions, up to 32 partials per row)."""
+    split_case(wl.long_bf16(kv_dtype=kv), f"split long_bf16 kv={kv}")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,BS,lens", [
+    # edges: empty, one token, exactly one chunk, one chunk and one token
+    ("bf16", 32, 8, 128, 16, [0, 1, 32, 33] + [2100] * 12 + [4000, 7000]),
+    ("f16", 16, 4, 128, 8, [1, 2, 31, 64, 65, 3000, 5000, 8192]),
+    ("bf16", 40, 2, 128, 32, [33, 900, 6000, 6001, 12000]),       # G = 20: two head groups
+    ("f16", 8, 8, 64, 64, [5, 130, 7000, 9000, 16000]),
+    ("bf16", 8, 1, 128, 16, [131072]),                             # one unit over every wave
+])
+def test_edges(dtype, Hq, Hkv, D, BS, lens):
+    case = wl.random_case(930 + len(lens), len(lens), Hq, Hkv, D, BS, dtype, lens)
+    assert case.max_context > 4 * 256  # the library splits these contexts
+    split_case(case, f"split edges {dtype} {Hq}/{Hkv} D{D} BS{BS} S={len(lens)}")
+
+
+def test_static_entry_at_the_library_split():
+    """pa_decode_static with the host copy of the lengths: the split-K
+    partials in the library's scratch, bit-identical to pa_decode."""
+    import torch
+    case = wl.random_case(940, 6, 32, 8, 128, 16, "bf16", [33, 5000, 12000, 1, 700, 9000])
+    dtype = case.dtype
+    tables = np.ascontiguousarray(case.block_tables[0])
+    kd, vd = to_dev(case.k_cache, dtype), to_dev(case.v_cache, dtype)
+    qd, td, ld = to_dev(case.q[0], dtype), ints_to_dev(tables), ints_to_dev(case.context_lens)
+    outs = []
+    for fn in (pa.pa_decode, pa.pa_decode_static):
+        announce(f"split static: {fn.__name__}")
+        out = torch.empty_like(qd)
+        fn(out, qd, kd, vd, td, ld, case.scale, case.max_context, partition_size=0,
+           context_lens_host=case.context_lens)
+        _sync()
+        outs.append(to_host(out, dtype))
+    assert same_bits(outs[0], outs[1])
+    want = oracle.decode(np.ascontiguousarray(case.q[0]), case.k_cache, case.v_cache, tables,
+                         case.context_lens, case.scale, dtype, num_threads=16, bound=True)
+    check_attention(outs[1], want, dtype, "split static")
