@@ -73,6 +73,9 @@ def parse():
                          "the mixed-length and long-context workloads as extra keys)")
     ap.add_argument("--no-probe", action="store_true",
                     help="skip the read-ceiling probe (pa_probe_read) of the step's tiles")
+    ap.add_argument("--products", default="auto", choices=["auto", "matrix", "valu"],
+                    help="one query head per KV head: compute both products on the matrix cores "
+                         "or on the vector ALU (default: the library's choice)")
     ap.add_argument("--calib-bytes", type=int, default=0,
                     help="first run one plain device-to-device copy of this many bytes (a "
                          "known-size reference for hardware byte counters)")
@@ -230,14 +233,16 @@ def run_decode(args, dev, name):
     decode = [pa.prepare_decode(outs[r], qs[r], kd, vd, tables[r], lens, case.scale, max_ctx,
                                 partition_size=P, stream=stream,
                                 k_new=knew[r] if fused else None, v_new=vnew[r] if fused else None,
-                                context_lens_host=host_lens)
+                                context_lens_host=host_lens, products=args.products)
               for r in range(R)]
     write = [pa.prepare_write_kv(knew[r], vnew[r], kd, vd, slots[r], stream=stream) for r in range(R)]
     if fused:
         write = [lambda: None] * R
     copy = pa.prepare_copy_blocks(kd, vd, no_pairs, stream=stream, head_dim=case.D)
-    a0 = pa.make_decode_args(outs[0], qs[0], kd, vd, tables[0], lens, case.scale, max_ctx, P)
+    a0 = pa.make_decode_args(outs[0], qs[0], kd, vd, tables[0], lens, case.scale, max_ctx, P,
+                             products=args.products)
     P_eff = pa.pa_decode_partition_size(a0)
+    valu = pa.pa_decode_products(a0) == pa.PA_PRODUCTS_VALU
     split = P_eff < max_ctx
 
     if args.calib_bytes > 0:
@@ -320,7 +325,8 @@ def run_decode(args, dev, name):
                    "step": ("pa_copy_blocks(0 pairs) + pa_decode(fused append of the new token)"
                             if fused else "pa_copy_blocks(0 pairs) + %s + pa_decode"
                             % ("pa_write_kv_i8" if i8 else "pa_write_kv"))},
-        "roofline": {"kernel": "decode_mfma_kernel" + (" (fused append)" if fused else "")
+        "roofline": {"kernel": "decode_mfma_kernel" + (" (vector-ALU products)" if valu else "")
+                     + (" (fused append)" if fused else "")
                      + (" + merge_kernel (split-K)" if split else ""),
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

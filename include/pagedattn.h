@@ -168,7 +168,19 @@ typedef struct pa_decode_args {
    * buffers either way).  A launch recorded into a graph keeps the shape it
    * was recorded with, so leave this NULL under capture. */
   const int32_t* context_lens_host;
+  /* Which units compute the two products (q . K and weights . V) when every
+   * KV head is read by one query head (num_q_heads == num_kv_heads) and the
+   * caches are 16-bit: PA_PRODUCTS_MATRIX (the gfx950 matrix cores, the
+   * query heads of a KV head as the columns of the tile), PA_PRODUCTS_VALU
+   * (packed dot products on the vector ALU), or PA_PRODUCTS_AUTO (the
+   * library's choice, measured: see the design notes).  With more query heads per KV
+   * head the matrix cores always take the products; PA_PRODUCTS_VALU there,
+   * or with INT8 or fp32 caches, returns PA_ERR_UNSUPPORTED.  The results
+   * agree within the same error bound (same rounding of the weights). */
+  int32_t products;
 } pa_decode_args;
+
+enum { PA_PRODUCTS_AUTO = 0, PA_PRODUCTS_MATRIX = 1, PA_PRODUCTS_VALU = 2 };
 
 /* Bytes of workspace pa_decode needs for these sizes (device pointers are
  * not read; a context_lens_host copy is checked).
@@ -178,6 +190,10 @@ PA_API size_t pa_decode_workspace_bytes(const pa_decode_args* args);
 /* The partition size pa_decode will use for these arguments, or -1 when
  * they are invalid. */
 PA_API int32_t pa_decode_partition_size(const pa_decode_args* args);
+
+/* The products pa_decode will use for these arguments (PA_PRODUCTS_MATRIX
+ * or PA_PRODUCTS_VALU), or -1 when they are invalid. */
+PA_API int32_t pa_decode_products(const pa_decode_args* args);
 
 PA_API pa_status pa_decode(const pa_decode_args* args, void* stream);
 

@@ -196,6 +196,86 @@ __device__ __forceinline__ int pick_block(const int (&b)[N], int j) {
   return id;
 }
 
+// The block-table side of one wave's walk over 32-token chunks, shared by
+// the decoders below (Derived supplies RawT, issue and consume): the block
+// ids of the coming chunks are held one per lane, a batch fetched by one
+// vector load before the first K/V load is issued, so no chunk waits on a
+// table read (a chunk whose block ids came from a load in the loop would
+// also wait for every K/V load issued before that read).
+template <typename Derived, int BS>
+struct ChunkWalker {
+  static constexpr int BPC = BS >= kChunk ? 1 : kChunk / BS;  // blocks per chunk
+  static constexpr int CPB = 64 / BPC;                         // chunks per batch of block ids
+  int tbl = 0;  // block ids of the current batch (lane e: entry e)
+
+  // Loads the table entries of the chunks ch(k0), ch(k0 + 1), ... (ch(k) =
+  // c0 + stride * k), one block id per lane: lane e holds block e % BPC of
+  // the chunk k0 + e / BPC.  Entries past the cached range [0, cc) or past
+  // n_chunks are not read (id 0 stands in; those tokens are dropped).
+  __device__ __forceinline__ void load_batch(const int32_t* __restrict__ trow, int t_begin,
+                                             int n_chunks, int cc, int NB, int c0, int stride,
+                                             int k0) {
+    const int lane = threadIdx.x & 63;
+    const int ch = c0 + stride * (k0 + lane / BPC);
+    const int t = t_begin + ch * kChunk + (lane % BPC) * BS;
+    tbl = ch < n_chunks && t < cc ? clampi(trow[t / BS], 0, NB - 1) : 0;
+  }
+
+  // Physical blocks of the k-th chunk of the current walk, in token order
+  // (one block when BS >= 32); a new batch is loaded every CPB chunks.
+  __device__ __forceinline__ void block_ids(int k, int (&b)[BPC], const int32_t* __restrict__ trow,
+                                            int t_begin, int n_chunks, int cc, int NB, int c0,
+                                            int stride) {
+    if (k > 0 && k % CPB == 0) load_batch(trow, t_begin, n_chunks, cc, NB, c0, stride, k);
+    const int e = (k % CPB) * BPC;
+#pragma unroll
+    for (int j = 0; j < BPC; ++j) b[j] = __builtin_amdgcn_readlane(tbl, e + j);
+  }
+
+  // Streams the chunks k = 0 .. n - 1 of a walk (chunk k starts at token
+  // t0_of(k); ids(k, b) gives its block ids, reading the table in batches).
+  // All loads of a chunk are issued before any of them is used: the
+  // scheduling barrier keeps the compiler from interleaving the products
+  // with the loads.  AHEAD: the loads of chunk k + 1 are issued before chunk
+  // k is consumed.  The compiler turns `cur = nxt` into register copies,
+  // which wait for those loads at the end of the iteration, so in effect one
+  // chunk is in flight while the previous one is computed.  Measured on
+  // MI355X, this form at 218 VGPRs (two waves per SIMD) beat two register
+  // sets used in turn (no copies, two chunks really in flight): 264 VGPRs
+  // and one wave per SIMD, 70.0 against 63.8 us on the LLaMA-13B-shaped
+  // step; capped at 256 VGPRs that form spills and took 76 us.
+  template <bool AHEAD, typename T0, typename Ids>
+  __device__ __forceinline__ void walk(int n, T0 t0_of, Ids ids, int cc, int skip) {
+    Derived& d = static_cast<Derived&>(*this);
+    using RawT = typename Derived::RawT;
+    if (n <= 0) return;
+    int nb[BPC] = {};
+    ids(0, nb);
+    if constexpr (AHEAD) {
+      RawT cur, nxt;
+      d.issue(nb, t0_of(0), cur);
+      if (n > 1) ids(1, nb);
+      for (int k = 0; k < n; ++k) {
+        if (k + 1 < n) {
+          d.issue(nb, t0_of(k + 1), nxt);
+          if (k + 2 < n) ids(k + 2, nb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        d.consume(t0_of(k), cur, cc, skip);
+        cur = nxt;
+      }
+    } else {
+      for (int k = 0; k < n; ++k) {
+        RawT one;
+        d.issue(nb, t0_of(k), one);
+        if (k + 1 < n) ids(k + 1, nb);
+        __builtin_amdgcn_sched_barrier(0);
+        d.consume(t0_of(k), one, cc, skip);
+      }
+    }
+  }
+};
+
 // One wave's share of the decode pass: q held as the B operand of both
 // products, the running (max, sum, output) of the 16 columns (query heads
 // i = lane % 16 of a group), the block ids of its coming chunks, and the
@@ -208,7 +288,7 @@ __device__ __forceinline__ int pick_block(const int (&b)[N], int j) {
 // Token tau of a chunk (0..31) sits in block tau / BS of the chunk at row
 // tau % BS; a block of 64 tokens holds the whole chunk from row t0 % 64.
 template <typename Ty, int D, int BS, bool KV8>
-struct WaveDecoder {
+struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
   static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
   static_assert(D % 32 == 0, "head_dim multiple of 32");
   using V8 = typename Ty::vec8;
@@ -231,12 +311,11 @@ struct WaveDecoder {
   f32x4 acc[MM];       // O^T[d = 16*mm + 4*g4 + j][head i]
   float m_run;         // running max of the base-2 logits (head i)
   float l_run;         // this lane's share of the running sum
-  int tbl;             // block ids of the current batch (lane e: entry e)
 
   __device__ __forceinline__ WaveDecoder(const void* kcv, const void* vcv, int Hkv, float sl2)
       : kc(reinterpret_cast<const Elem*>(kcv)), vc(reinterpret_cast<const Elem*>(vcv)),
         lane(threadIdx.x & 63), i(threadIdx.x & 15), g4((threadIdx.x & 63) >> 4),
-        blk_stride((int64_t)Hkv * TILE), head_off(0), scale_log2(sl2), tbl(0) {}
+        blk_stride((int64_t)Hkv * TILE), head_off(0), scale_log2(sl2) {}
 
   __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -259,29 +338,6 @@ struct WaveDecoder {
       u32x4 raw = head_ok ? load16(qrow + 8 * qchunk(kk)) : u32x4{0u, 0u, 0u, 0u};
       qop[kk] = __builtin_bit_cast(V8, raw);
     }
-  }
-
-  // Loads the table entries of the chunks ch(k0), ch(k0 + 1), ... (ch(k) =
-  // c0 + stride * k), one block id per lane: lane e holds block e % BPC of
-  // the chunk k0 + e / BPC.  Entries past the cached range [0, cc) or past
-  // n_chunks are not read (id 0 stands in; those tokens are dropped).
-  __device__ __forceinline__ void load_batch(const int32_t* __restrict__ trow, int t_begin,
-                                             int n_chunks, int cc, int NB, int c0, int stride,
-                                             int k0) {
-    const int ch = c0 + stride * (k0 + lane / BPC);
-    const int t = t_begin + ch * kChunk + (lane % BPC) * BS;
-    tbl = ch < n_chunks && t < cc ? clampi(trow[t / BS], 0, NB - 1) : 0;
-  }
-
-  // Physical blocks of the k-th chunk of the current walk, in token order
-  // (one block when BS >= 32); a new batch is loaded every CPB chunks.
-  __device__ __forceinline__ void block_ids(int k, int (&b)[BPC], const int32_t* __restrict__ trow,
-                                            int t_begin, int n_chunks, int cc, int NB, int c0,
-                                            int stride) {
-    if (k > 0 && k % CPB == 0) load_batch(trow, t_begin, n_chunks, cc, NB, c0, stride, k);
-    const int e = (k % CPB) * BPC;
-#pragma unroll
-    for (int j = 0; j < BPC; ++j) b[j] = __builtin_amdgcn_readlane(tbl, e + j);
   }
 
   __device__ __forceinline__ void issue(const int (&b)[BPC], int t0, RawT& r) const {
@@ -450,54 +506,50 @@ struct WaveDecoder {
     }
   }
 
-  // Streams the chunks k = 0 .. n - 1 of a walk (chunk k starts at token
-  // t0_of(k); ids(k, b) gives its block ids, reading the table in batches).
-  // All loads of a chunk are issued before any of them is used: the
-  // scheduling barrier keeps the compiler from interleaving the products
-  // with the loads.  AHEAD: the loads of chunk k + 1 are issued before chunk
-  // k is consumed.  The compiler turns `cur = nxt` into register copies,
-  // which wait for those loads at the end of the iteration, so in effect one
-  // chunk is in flight while the previous one is computed.  Measured on
-  // MI355X, this form at 218 VGPRs (two waves per SIMD) beat two register
-  // sets used in turn (no copies, two chunks really in flight): 264 VGPRs
-  // and one wave per SIMD, 70.0 against 63.8 us on the LLaMA-13B-shaped
-  // step; capped at 256 VGPRs that form spills and took 76 us.
-  template <bool AHEAD, typename T0, typename Ids>
-  __device__ __forceinline__ void walk(int n, T0 t0_of, Ids ids, int cc, int skip) {
-    if (n <= 0) return;
-    int nb[BPC] = {};
-    ids(0, nb);
-    if constexpr (AHEAD) {
-      RawT cur, nxt;
-      issue(nb, t0_of(0), cur);
-      if (n > 1) ids(1, nb);
-      for (int k = 0; k < n; ++k) {
-        if (k + 1 < n) {
-          issue(nb, t0_of(k + 1), nxt);
-          if (k + 2 < n) ids(k + 2, nb);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        consume(t0_of(k), cur, cc, skip);
-        cur = nxt;
-      }
-    } else {
-      for (int k = 0; k < n; ++k) {
-        RawT one;
-        issue(nb, t0_of(k), one);
-        if (k + 1 < n) ids(k + 1, nb);
-        __builtin_amdgcn_sched_barrier(0);
-        consume(t0_of(k), one, cc, skip);
-      }
+  // Fused append: the new token's K row and V row, 8 bytes per lane (lanes
+  // [0, D/4) hold K elements 4*lane..+3, lanes [D/4, D/2) hold V elements
+  // 4*(lane - D/4)..+3), fetched early so the data is in registers when the
+  // token is added.
+  using Token = u32x2;
+  __device__ __forceinline__ Token fetch_token(const uint16_t* __restrict__ krow,
+                                               const uint16_t* __restrict__ vrow) const {
+    Token nv = {0u, 0u};
+    if (lane < D / 2) nv = lane < D / 4 ? load8(krow + 4 * lane) : load8(vrow + 4 * (lane - D / 4));
+    return nv;
+  }
+
+  // LDS merge of a workgroup's waves, in the layout the body reads: the
+  // wave's running max of column c at m_row[c]; then its sum and output
+  // rescaled by 2^(m_w - M), M the max over the NW waves of m_sh (row v at
+  // m_sh + 16 v), at l_row[c] and a_base[c * DP + d].  A wave that saw no
+  // token has m_w = -inf and weight 0.
+  __device__ __forceinline__ void stash_max(float* m_row) const {
+    if (g4 == 0) m_row[i] = m_run;
+  }
+  template <int NW>
+  __device__ __forceinline__ void stash_scaled(const float* m_sh, float* l_row, float* a_base, int Gv,
+                                               int DP) const {
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, m_sh[v * 16 + i]);
+    const float f = m_run > -INFINITY ? exp2_fast(m_run - M) : 0.f;
+    if (i < Gv) {
+      if (g4 == 0) l_row[i] = l_tot * f;
+      // lane holds O^T[d = 16*mm + 4*g4 + j][head i], j = 0..3
+      float* arow = a_base + i * DP + 4 * g4;
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm) *reinterpret_cast<f32x4*>(arow + 16 * mm) = acc[mm] * f;
     }
   }
 
-  // Fused append: adds the token whose K row and V row this wave fetched
-  // into nv (lanes [0, D/4) hold K elements 4*lane..+3, lanes [D/4, D/2) V
-  // elements 4*(lane - D/4)..+3) to its running state on the vector ALU
-  // (one logit per head: each lane of a head takes 32 channels and the 4 row
-  // groups are added), rounding the weight to the element type as the
-  // matrix-core path does.  With `store` the token also goes bit for bit
-  // (INT8: quantised) into the cache slot at row o of block b.
+  // Fused append: adds the token fetched into nv (fetch_token) to the
+  // running state on the vector ALU (one logit per head: each lane of a head
+  // takes 32 channels and the 4 row groups are added), rounding the weight
+  // to the element type as the matrix-core path does.  With `store` the
+  // token also goes bit for bit (INT8: quantised) into the cache slot at row
+  // o of block b.
   __device__ __forceinline__ void add_token(u32x2 nv, bool store, int64_t b, int o) {
     if constexpr (!KV8) {
       // operands gathered from the lanes holding them: K chunk 4*kk+g4 (16 B)
@@ -619,13 +671,216 @@ struct WaveDecoder {
   }
 };
 
+// One wave's share of the decode pass on the vector ALU, for a KV head read
+// by a single query head (G = 1: the matrix-core path would leave 15 of its
+// 16 columns empty).  Same interface as WaveDecoder; per 32-token chunk:
+//   QK -- lane l takes token l % 32 and half l / 32 of head_dim: its K
+//         x-vectors (16 bytes each, 16 lanes on 16 consecutive tokens read
+//         256 contiguous bytes) meet q in packed dot products (v_dot2, fp32
+//         accumulation), and the two halves are added across lanes;
+//   PV -- each 16-byte V load is 8 consecutive tokens of one channel row;
+//         lane l takes piece pc = l % PPB of a row (PPB pieces per row of the
+//         chunk) for channels CPI * n + l / PPB, so one load instruction reads
+//         whole rows, contiguous.  The lane keeps partial sums per channel
+//         over its own tokens; the PPB lanes of a channel are added at the end.
+//         The chunk's weights (rounded to the element type, packed in pairs)
+//         reach each lane's piece by lane shuffles.
+// Same arithmetic contract as the matrix-core path: fp32 logits from exact
+// products, base-2 online softmax with the lazy reference maximum, weights
+// rounded to the element type for PV and for the running sum.
+template <typename Ty, int D, int BS>
+struct VaWaveDecoder : ChunkWalker<VaWaveDecoder<Ty, D, BS>, BS> {
+  static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64, "block size 8, 16, 32 or 64");
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static constexpr int XH = D / 16;   // 16-byte K x-vectors per half of a row
+  static constexpr int TILE = D * BS;
+  static constexpr int BPC = BS >= kChunk ? 1 : kChunk / BS;  // blocks per chunk
+  static constexpr int RT = BS >= kChunk ? kChunk : BS;       // tokens of a row in one chunk
+  static constexpr int PPB = RT / 8;                          // 16-byte pieces of such a row
+  static constexpr int CPI = 64 / PPB;                        // channel rows per load instruction
+  static constexpr int NCH = D / CPI;                         // channels per lane
+  struct RawT {
+    u32x4 k[XH];         // token t's x-vectors h2*XH .. h2*XH + XH - 1
+    u32x4 v[BPC][NCH];   // block bb of the chunk, channel CPI*n + lane/PPB, piece lane % PPB
+  };
+  struct Token {         // fused append: q, k, v of the lane's channels (piece 0 lanes)
+    uint16_t q[NCH], k[NCH], v[NCH];
+  };
+
+  const uint16_t* kc;
+  const uint16_t* vc;
+  int lane, i, g4;     // lane; the column (always 0: one query head); unused
+  int t, h2;           // the lane's token of a chunk and its half of head_dim
+  int pc, ch0;         // the lane's piece of a row and its first channel
+  int64_t blk_stride, head_off;
+  float scale_log2;
+  u32x4 qh[XH];        // q channels 8*(h2*XH) .. of the query head
+  const uint16_t* qrow;
+  float acc[NCH];      // unnormalised output over the lane's tokens, channels ch0 + CPI*n
+  float m_run;         // running max of the base-2 logits (wave-uniform)
+  float l_run;         // running sum over this lane's tokens (lanes of half 0)
+
+  __device__ __forceinline__ VaWaveDecoder(const void* kcv, const void* vcv, int Hkv, float sl2)
+      : kc(reinterpret_cast<const uint16_t*>(kcv)), vc(reinterpret_cast<const uint16_t*>(vcv)),
+        lane(threadIdx.x & 63), i(0), g4(0), t(threadIdx.x & 31), h2((threadIdx.x & 63) >> 5),
+        pc((threadIdx.x & 63) % PPB), ch0((threadIdx.x & 63) / PPB),
+        blk_stride((int64_t)Hkv * TILE), head_off(0), scale_log2(sl2) {}
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int n = 0; n < NCH; ++n) acc[n] = 0.f;
+    m_run = -INFINITY;
+    l_run = 0.f;
+  }
+
+  __device__ __forceinline__ void load_q(const uint16_t* __restrict__ q_row, bool) {
+    qrow = q_row;
+#pragma unroll
+    for (int j = 0; j < XH; ++j) qh[j] = load16(q_row + 8 * (h2 * XH + j));
+  }
+
+  __device__ __forceinline__ void issue(const int (&b)[BPC], int t0, RawT& r) const {
+    const int r0 = BS > kChunk ? t0 % BS : 0;  // the chunk's first row of a 64-token block
+    {  // K row of token t
+      const int id = pick_block<BPC>(b, t / BS);
+      const int row = BS >= kChunk ? r0 + t : t % BS;
+      const uint16_t* base = kc + (int64_t)id * blk_stride + head_off;
+#pragma unroll
+      for (int j = 0; j < XH; ++j) r.k[j] = stream16(base + ((h2 * XH + j) * BS + row) * 8);
+    }
+#pragma unroll
+    for (int bb = 0; bb < BPC; ++bb) {  // V rows: piece pc of channel ch0 + CPI*n
+      const uint16_t* base = vc + (int64_t)b[bb] * blk_stride + head_off + r0 + 8 * pc;
+#pragma unroll
+      for (int n = 0; n < NCH; ++n) r.v[bb][n] = stream16(base + (ch0 + CPI * n) * BS);
+    }
+  }
+
+  __device__ __forceinline__ void consume(int t0, RawT& r, int cc, int skip) {
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < XH; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) part = Ty::dot2(r.k[j][w], qh[j][w], part);
+    float x = (part + __shfl_xor(part, 32)) * scale_log2;
+    if (t0 + kChunk > cc || t0 < skip) {  // drop tokens outside [skip, cc) (wave-uniform test)
+      const int tok = t0 + t;
+      if (tok >= cc || tok < skip) x = -INFINITY;
+#pragma unroll
+      for (int bb = 0; bb < BPC; ++bb)
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {  // zero the V bits of tokens past cc (they may hold NaN)
+          const int tk = t0 + bb * RT + 8 * pc + 2 * wd;
+          const uint32_t keep = (tk < cc ? 0x0000FFFFu : 0u) | (tk + 1 < cc ? 0xFFFF0000u : 0u);
+#pragma unroll
+          for (int n = 0; n < NCH; ++n) r.v[bb][n][wd] &= keep;
+        }
+    }
+    float mx = x;
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));  // both halves agree
+    if (mx > m_run + kSlack) {  // as in WaveDecoder: rescale only when the max moves far
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NCH; ++n) acc[n] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    const float p = Ty::to_f32(Ty::from_f32(exp2_fast(x - m_use)));  // the weight PV sees
+    l_run += h2 == 0 ? p : 0.f;
+    // lane 2k holds the packed weights of tokens 2k, 2k + 1
+    const int pp = (int)Ty::pack2(p, __shfl_xor(p, 1));
+#pragma unroll
+    for (int bb = 0; bb < BPC; ++bb)
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const uint32_t wv = (uint32_t)__shfl(pp, bb * RT + 8 * pc + 2 * wd);
+#pragma unroll
+        for (int n = 0; n < NCH; ++n) acc[n] = Ty::dot2(r.v[bb][n][wd], wv, acc[n]);
+      }
+  }
+
+  __device__ __forceinline__ Token fetch_token(const uint16_t* __restrict__ krow,
+                                               const uint16_t* __restrict__ vrow) const {
+    Token tk{};
+    if (pc == 0) {
+#pragma unroll
+      for (int n = 0; n < NCH; ++n) {
+        const int d = ch0 + CPI * n;
+        tk.q[n] = qrow[d];
+        tk.k[n] = krow[d];
+        tk.v[n] = vrow[d];
+      }
+    }
+    return tk;
+  }
+
+  // Fused append on the vector ALU: the lanes of piece 0 hold every channel
+  // once; their dot products add up to the logit, and they add the token's
+  // value to their partial sums.
+  __device__ __forceinline__ void add_token(const Token& tk, bool store, int64_t b, int o) {
+    float dot = 0.f;
+    if (pc == 0) {
+#pragma unroll
+      for (int n = 0; n < NCH; ++n) dot = fmaf(Ty::to_f32(tk.q[n]), Ty::to_f32(tk.k[n]), dot);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+    const float xn = dot * scale_log2;
+    const float m_new = fmaxf(m_run, xn);
+    const float alpha = exp2_fast(m_run - m_new);  // 0 when the wave saw no cached token
+    const float pn = Ty::to_f32(Ty::from_f32(exp2_fast(xn - m_new)));
+    m_run = m_new;
+    l_run = l_run * alpha + (lane == 0 ? pn : 0.f);
+#pragma unroll
+    for (int n = 0; n < NCH; ++n)
+      acc[n] = pc == 0 ? fmaf(pn, Ty::to_f32(tk.v[n]), acc[n] * alpha) : acc[n] * alpha;
+    if (store && pc == 0) {
+      uint16_t* kd = const_cast<uint16_t*>(kc) + b * blk_stride + head_off;
+      uint16_t* vd = const_cast<uint16_t*>(vc) + b * blk_stride + head_off;
+#pragma unroll
+      for (int n = 0; n < NCH; ++n) {  // channel d: x-vector d / 8, element d % 8; V row d
+        const int d = ch0 + CPI * n;
+        kd[((d / 8) * BS + o) * 8 + d % 8] = tk.k[n];
+        vd[d * BS + o] = tk.v[n];
+      }
+    }
+  }
+
+  __device__ __forceinline__ void stash_max(float* m_row) const {
+    if (lane == 0) m_row[0] = m_run;
+  }
+  template <int NW>
+  __device__ __forceinline__ void stash_scaled(const float* m_sh, float* l_row, float* a_base, int,
+                                               int) const {
+    float l_tot = l_run;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) l_tot += __shfl_xor(l_tot, off);
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, m_sh[v * 16]);
+    const float f = m_run > -INFINITY ? exp2_fast(m_run - M) : 0.f;
+    if (lane == 0) l_row[0] = l_tot * f;
+#pragma unroll
+    for (int n = 0; n < NCH; ++n) {  // add the PPB pieces of each channel
+      float a = acc[n];
+#pragma unroll
+      for (int off = 1; off < PPB; off <<= 1) a += __shfl_xor(a, off);
+      if (pc == 0) a_base[ch0 + CPI * n] = a * f;
+    }
+  }
+};
+
 // Body of the decode pass for the workgroup at grid position (bx, by, bz);
 // `lds` holds merge_lds_bytes(NW, G, D) bytes.  With prefix groups
 // (pa_decode_prefix, through prefix_suffix_kernel) it takes each member's
 // keys after its group's shared prefix; the prefix itself is attended by the
 // shared-prefix pass of the prefill body, in pre_parts partitions of pre_P
 // tokens that fill the first partial slots of every member.
-template <typename Ty, int D, int BS, int NW, bool KV8>
+template <typename Ty, int D, int BS, int NW, bool KV8, bool VALU = false>
 __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* lds,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
     const void* __restrict__ vcv, const int32_t* __restrict__ tables,
@@ -634,13 +889,13 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
     int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
     float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs, int pre_parts, int pre_P,
     const int32_t* __restrict__ grp_start, const int32_t* __restrict__ grp_len, int n_grp) {
-  using W = WaveDecoder<Ty, D, BS, KV8>;
-  constexpr int MM = W::MM;
+  static_assert(!VALU || !KV8, "the vector-ALU decoder reads 16-bit caches");
+  using W = typename std::conditional<VALU, VaWaveDecoder<Ty, D, BS>, WaveDecoder<Ty, D, BS, KV8>>::type;
   constexpr int BPC = W::BPC;
   constexpr int DP = D + 4;      // padded LDS row of the merge buffer
 
   W wd(kcv, vcv, Hkv, scale_log2);
-  const int lane = wd.lane, i = wd.i, g4 = wd.g4;
+  const int lane = wd.lane, i = wd.i;
   const int w = uniform(threadIdx.x >> 6);
   int hk, grp = 0, p = 0, s, c;
   if (num_seqs > 0) {
@@ -699,14 +954,13 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
   wd.load_q(q + out_row(head_ok ? i : 0) * D, head_ok);
 
   // Fused append: wave 0 of the workgroup whose partition holds token c - 1
-  // fetches the new K row and V row up front, 8 bytes per lane (lanes
-  // [0, D/4) hold K elements 4*lane..+3, lanes [D/4, D/2) hold V elements
-  // 4*(lane - D/4)..+3), so the data is in registers when the token is added.
+  // fetches the new K row and V row up front, so the data is in registers
+  // when the token is added.
   const bool new_here = has_new && w == 0;
-  u32x2 nv = {0u, 0u};
-  if (new_here && lane < D / 2) {
+  typename W::Token nv{};
+  if (new_here) {
     const int64_t row = ((int64_t)s * Hkv + hk) * D;
-    nv = lane < D / 4 ? load8(k_new + row + 4 * lane) : load8(v_new + row + 4 * (lane - D / 4));
+    nv = wd.fetch_token(k_new + row, v_new + row);
   }
 
   wd.reset();
@@ -743,29 +997,15 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
     wd.add_token(nv, grp == 0, clampi(trow[tn / BS], 0, NB - 1), tn % BS);
   }
 
-  float l_tot = wd.l_run + __shfl_xor(wd.l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const float m_run = wd.m_run;
-
   // Merge the NW waves: M = max_w m_w per head, then every wave rescales its
   // sum and output by 2^(m_w - M) into LDS and the workgroup adds them up in
-  // wave order.  A wave that saw no token has m_w = -inf and weight 0.
+  // wave order.
   float* m_sh = lds;                  // [NW][16]
   float* l_sh = lds + NW * 16;        // [NW][16]
   float* a_sh = lds + 2 * NW * 16;    // [NW][Gv][DP]
-  if (g4 == 0) m_sh[w * 16 + i] = m_run;
+  wd.stash_max(m_sh + w * 16);
   __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) M = fmaxf(M, m_sh[v * 16 + i]);
-  const float f = m_run > -INFINITY ? exp2_fast(m_run - M) : 0.f;
-  if (head_ok) {
-    if (g4 == 0) l_sh[w * 16 + i] = l_tot * f;
-    // lane holds O^T[d = 16*mm + 4*g4 + j][head i], j = 0..3
-    float* arow = a_sh + (w * Gv + i) * DP + 4 * g4;
-#pragma unroll
-    for (int mm = 0; mm < MM; ++mm) *reinterpret_cast<f32x4*>(arow + 16 * mm) = wd.acc[mm] * f;
-  }
+  wd.template stash_scaled<NW>(m_sh, l_sh + w * 16, a_sh + w * Gv * DP, Gv, DP);
   __syncthreads();
 
   const bool split = pb > 0 || n_p > 1;
@@ -800,7 +1040,7 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
   }
 }
 
-template <typename Ty, int D, int BS, int NW, bool KV8>
+template <typename Ty, int D, int BS, int NW, bool KV8, bool VALU>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3 : 1))) void decode_mfma_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
     const void* __restrict__ vcv, const int32_t* __restrict__ tables,
@@ -839,7 +1079,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
     by = (int)((lam / X) % Y);
     bz = (int)(lam / (X * Y));
   }
-  decode_mfma_body<Ty, D, BS, NW, KV8>(bx, by, bz, lds, out, q, kcv, vcv, tables, lens, k_new,
+  decode_mfma_body<Ty, D, BS, NW, KV8, VALU>(bx, by, bz, lds, out, q, kcv, vcv, tables, lens, k_new,
                                        v_new, Hq, Hkv, G, n_groups, NB, max_blocks, max_ctx,
                                        scale_log2, P, max_parts, ws_acc, ws_ml, num_seqs, pre_parts,
                                        pre_P, grp_start, grp_len, n_grp);
@@ -1631,6 +1871,8 @@ struct Plan {
   // (sequence, partition) units of the flat work list, from the host copy of
   // the context lengths (0 = unknown: the grid covers num_seqs * max_parts)
   int64_t units = 0;
+  // both products on the vector ALU (decode_mfma_kernel with VaWaveDecoder)
+  bool valu = false;
 };
 
 pa_status validate(const pa_decode_args* a) {
@@ -1654,6 +1896,10 @@ pa_status validate(const pa_decode_args* a) {
   if (a->block_size != 8 && a->block_size != 16 && a->block_size != 32 && a->block_size != 64)
     return PA_ERR_UNSUPPORTED;
   if (a->dtype == PA_F32 && a->partition_size > kMaxF32Part) return PA_ERR_UNSUPPORTED;
+  if (a->products < PA_PRODUCTS_AUTO || a->products > PA_PRODUCTS_VALU) return PA_ERR_INVALID;
+  if (a->products == PA_PRODUCTS_VALU &&
+      (a->num_q_heads != a->num_kv_heads || a->kv_dtype == PA_I8 || a->dtype == PA_F32))
+    return PA_ERR_UNSUPPORTED;
   if (a->context_lens_host)
     for (int s = 0; s < a->num_seqs; ++s)
       if (a->context_lens_host[s] < 0 || a->context_lens_host[s] > a->max_context_len)
@@ -1684,6 +1930,9 @@ int choose_partition(const pa_decode_args* a, int wg_per_part) {
   return max(P, a->block_size);  // a power of two >= 32: a multiple of the block size
 }
 
+// Products of the G = 1 case when the caller leaves the choice to the library.
+constexpr bool kValuForMha = false;
+
 Plan make_plan(const pa_decode_args* a) {
   Plan pl;
   const int G = a->num_q_heads / a->num_kv_heads;
@@ -1706,6 +1955,8 @@ Plan make_plan(const pa_decode_args* a) {
   }
   if (pl.max_parts > 1)
     pl.ws_bytes = (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * (a->head_dim + 2) * 4;
+  pl.valu = G == 1 && a->kv_dtype != PA_I8 && a->dtype != PA_F32 &&
+            (a->products == PA_PRODUCTS_VALU || (a->products == PA_PRODUCTS_AUTO && kValuForMha));
   return pl;
 }
 
@@ -1714,7 +1965,7 @@ size_t merge_lds_bytes(int NW, int G, int D) {
 }
 
 
-template <typename Ty, int D, int BS, int NW, bool KV8>
+template <typename Ty, int D, int BS, int NW, bool KV8, bool VALU = false>
 void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* ws_ml,
                  hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
@@ -1726,7 +1977,7 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
             flat ? (unsigned)(pl.units > 0 ? pl.units : (int64_t)a->num_seqs * dec_parts)
                  : (unsigned)dec_parts,
             flat ? 1u : (unsigned)a->num_seqs);
-  decode_mfma_kernel<Ty, D, BS, NW, KV8><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
+  decode_mfma_kernel<Ty, D, BS, NW, KV8, VALU><<<grid, 64 * NW, merge_lds_bytes(NW, G, D), st>>>(
       (uint16_t*)a->out, (const uint16_t*)a->q, a->k_cache, a->v_cache, a->block_tables,
       a->context_lens, (const uint16_t*)a->k_new, (const uint16_t*)a->v_new, a->num_q_heads,
       a->num_kv_heads, G, pl.groups, a->num_blocks, a->max_blocks_per_seq, a->max_context_len,
@@ -1839,6 +2090,17 @@ void launch_mfma_bs(const pa_decode_args* a, const Plan& pl, float* wa, float* w
       default: launch_mfma<Ty, D, 64, 2, KV8>(a, pl, wa, wm, st); break;
     }
     return;
+  }
+  if constexpr (!KV8) {
+    if (pl.valu) {  // one query head per KV head: both products on the vector ALU
+      switch (a->block_size) {
+        case 8: launch_mfma<Ty, D, 8, kWaves, false, true>(a, pl, wa, wm, st); break;
+        case 16: launch_mfma<Ty, D, 16, kWaves, false, true>(a, pl, wa, wm, st); break;
+        case 32: launch_mfma<Ty, D, 32, kWaves, false, true>(a, pl, wa, wm, st); break;
+        default: launch_mfma<Ty, D, 64, kWaves, false, true>(a, pl, wa, wm, st); break;
+      }
+      return;
+    }
   }
   switch (a->block_size) {
     case 8: launch_mfma<Ty, D, 8, kWaves, KV8>(a, pl, wa, wm, st); break;
@@ -2026,6 +2288,11 @@ PA_API size_t pa_decode_workspace_bytes(const pa_decode_args* args) {
 PA_API int32_t pa_decode_partition_size(const pa_decode_args* args) {
   if (validate(args) != PA_OK) return -1;
   return make_plan(args).P;
+}
+
+PA_API int32_t pa_decode_products(const pa_decode_args* args) {
+  if (validate(args) != PA_OK) return -1;
+  return make_plan(args).valu ? PA_PRODUCTS_VALU : PA_PRODUCTS_MATRIX;
 }
 
 // Plan of a decode with shared-prefix groups: one partial slot for the

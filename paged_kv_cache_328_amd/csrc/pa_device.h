@@ -39,6 +39,11 @@ struct F16 {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), f16x2{(_Float16)1.f, (_Float16)1.f},
                                   acc, false);
   }
+  // acc + a.lo * b.lo + a.hi * b.hi of two packed pairs (products exact in fp32)
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc,
+                                  false);
+  }
   // four signed bytes -> four f16 (two packed words), exactly: with the sign
   // bit flipped a byte is c + 128 in [1, 255]; as the mantissa under 0x64 it
   // reads 1024 + c + 128, and subtracting 1152 leaves c (all values exact).
@@ -71,6 +76,10 @@ struct BF16 {
   static __device__ __forceinline__ float sum2(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
                                            __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
+  }
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                           acc, false);
   }
   // four signed bytes -> four bf16, exactly (|c| <= 128 needs 8 significant bits)
   static __device__ __forceinline__ u32x2 codes4(uint32_t c) {

@@ -29,6 +29,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pagedattn.h")
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS = 0, 1, 2, 3
 PA_ERR_HIP, PA_ERR_WORKSPACE, PA_ERR_UNKNOWN_SEQ, PA_ERR_EXISTS = 4, 5, 6, 7
 PA_F32, PA_F16, PA_BF16, PA_I8 = 0, 1, 2, 3
+PA_PRODUCTS_AUTO, PA_PRODUCTS_MATRIX, PA_PRODUCTS_VALU = 0, 1, 2
+PRODUCTS = {"auto": PA_PRODUCTS_AUTO, "matrix": PA_PRODUCTS_MATRIX, "valu": PA_PRODUCTS_VALU}
 DTYPE_NAMES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "i8": PA_I8}
 
 _P = ctypes.c_void_p
@@ -53,6 +55,7 @@ class pa_decode_args(ctypes.Structure):
         ("max_context_len", _I32), ("scale", ctypes.c_float), ("dtype", _I32),
         ("partition_size", _I32), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
         ("k_new", _P), ("v_new", _P), ("kv_dtype", _I32), ("context_lens_host", _P),
+        ("products", _I32),
     ]
 
 
@@ -86,6 +89,7 @@ def lib():
         "pa_decode_workspace_bytes": (ctypes.c_size_t, [A]),
         "pa_decode_partition_size": (_I32, [A]),
         "pa_decode": (ctypes.c_int, [A, _P]),
+        "pa_decode_products": (_I32, [A]),
         "pa_decode_static": (ctypes.c_int, [A, _P]),
         "pa_prefill": (ctypes.c_int, [ctypes.POINTER(pa_prefill_args), _P]),
         "pa_decode_prefix_workspace_bytes": (ctypes.c_size_t, [A, ctypes.POINTER(pa_prefix_groups)]),
@@ -208,7 +212,7 @@ def cache_geometry(k_cache, v_cache, head_dim=None):
 
 def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                      max_context_len, partition_size=0, workspace=None, k_new=None, v_new=None,
-                     context_lens_host=None):
+                     context_lens_host=None, products="auto"):
     """Fill a pa_decode_args from tensors (no call into the library).
     k_new / v_new ([S, Hkv, D], optional): the step's new token of every
     sequence, appended at position context_lens[s] - 1 by pa_decode itself.
@@ -236,6 +240,7 @@ def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale
     a.dtype = _dtype_code(q)
     a.kv_dtype = PA_I8 if i8 else _dtype_code(k_cache)
     a.partition_size = int(partition_size)
+    a.products = PRODUCTS[products]
     if workspace is not None:
         a.workspace = _ptr(workspace)
         a.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -265,16 +270,21 @@ def pa_decode_partition_size(args):
     return int(lib().pa_decode_partition_size(ctypes.byref(args)))
 
 
+def pa_decode_products(args):
+    """PA_PRODUCTS_MATRIX or PA_PRODUCTS_VALU: what pa_decode will use."""
+    return int(lib().pa_decode_products(ctypes.byref(args)))
+
+
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
               partition_size=0, workspace=None, stream=None, k_new=None, v_new=None,
-              context_lens_host=None):
+              context_lens_host=None, products="auto"):
     """Paged decode attention into `out` (with k_new / v_new: fused append of
     the step's token at position context_lens[s] - 1).  When the step needs
     split-K partials and no workspace is given, a byte tensor is allocated with
     torch on q's device."""
     a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                          max_context_len, partition_size, workspace, k_new, v_new,
-                         context_lens_host)
+                         context_lens_host, products)
     need = pa_decode_workspace_bytes(a)
     if need and workspace is None:
         workspace = _workspace(need, q.device, stream)
@@ -288,13 +298,15 @@ PA_DECODE_STATIC_SCRATCH_BYTES = 64 << 20  # include/pagedattn.h
 
 
 def pa_decode_static(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-                     partition_size=0, stream=None, k_new=None, v_new=None, context_lens_host=None):
+                     partition_size=0, stream=None, k_new=None, v_new=None, context_lens_host=None,
+                     products="auto"):
     """pa_decode without a workspace argument: the library keeps the split-K
     partials in its own fixed device scratch (PA_DECODE_STATIC_SCRATCH_BYTES
     per GPU), so the call allocates nothing.  Calls that overlap in time on
     one GPU share that scratch and race."""
     a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
-                         max_context_len, partition_size, None, k_new, v_new, context_lens_host)
+                         max_context_len, partition_size, None, k_new, v_new, context_lens_host,
+                         products)
     _check(lib().pa_decode_static(ctypes.byref(a), _stream(stream)), "pa_decode_static")
     return out
 
@@ -421,12 +433,12 @@ class PreparedCall:
 
 def prepare_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                    partition_size=0, workspace=None, stream=None, k_new=None, v_new=None,
-                   context_lens_host=None):
+                   context_lens_host=None, products="auto"):
     """pa_decode with its argument struct filled once; the workspace (when
     the step needs one) is allocated here."""
     a = make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                          max_context_len, partition_size, workspace, k_new, v_new,
-                         context_lens_host)
+                         context_lens_host, products)
     need = pa_decode_workspace_bytes(a)
     if need and workspace is None:
         workspace = _workspace(need, q.device, stream)

@@ -54,10 +54,28 @@ def _args(**over):
     ({"dtype": pa.PA_I8}, pa.PA_ERR_INVALID),           # INT8 is a cache type only
     ({"dtype": pa.PA_F32, "kv_dtype": pa.PA_I8}, pa.PA_ERR_INVALID),
     ({"kv_dtype": pa.PA_I8, "head_dim": 96}, pa.PA_ERR_UNSUPPORTED),
+    ({"products": 3}, pa.PA_ERR_INVALID),
+    ({"products": -1}, pa.PA_ERR_INVALID),
+    ({"products": pa.PA_PRODUCTS_VALU}, pa.PA_ERR_UNSUPPORTED),          # 8 q heads on 2 KV heads
+    ({"products": pa.PA_PRODUCTS_VALU, "num_q_heads": 2, "kv_dtype": pa.PA_I8}, pa.PA_ERR_UNSUPPORTED),
+    ({"products": pa.PA_PRODUCTS_VALU, "num_q_heads": 2, "dtype": pa.PA_F32}, pa.PA_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects_bad_arguments_before_launch(L, over, status):
     a = _args(**over)
     assert L.pa_decode(a, None) == status
+
+
+def test_products_choice(L):
+    """Which units take the products: the matrix cores whenever several query
+    heads share a KV head; at one query head per KV head the caller's choice
+    or the library's."""
+    assert L.pa_decode_products(_args()) == pa.PA_PRODUCTS_MATRIX  # G = 4
+    mha = dict(num_q_heads=2)
+    assert L.pa_decode_products(_args(products=pa.PA_PRODUCTS_VALU, **mha)) == pa.PA_PRODUCTS_VALU
+    assert L.pa_decode_products(_args(products=pa.PA_PRODUCTS_MATRIX, **mha)) == pa.PA_PRODUCTS_MATRIX
+    assert L.pa_decode_products(_args(**mha)) in (pa.PA_PRODUCTS_MATRIX, pa.PA_PRODUCTS_VALU)
+    assert L.pa_decode_products(_args(kv_dtype=pa.PA_I8, **mha)) == pa.PA_PRODUCTS_MATRIX
+    assert L.pa_decode_products(_args(products=7)) == -1
 
 
 def test_decode_checks_the_host_copy_of_context_lens(L):
