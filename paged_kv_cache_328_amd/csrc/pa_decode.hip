@@ -135,6 +135,24 @@ __device__ __forceinline__ u32x2 stream8(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
 
+// V rows of a 64-token block are longer than one 32-token chunk: a chunk
+// reads half of each row (64 of 128 bytes for 16-bit values, 32 of 64 for
+// INT8 codes) and the sibling chunk, on another wave at about the same time,
+// reads the other half.  Those loads are kept ordinary so the line stays in
+// L2 for the sibling: measured on MI355X (LLaMA-13B-shaped step at block
+// size 64), non-temporal V loads fetched 1.23x the algorithmic bytes and
+// took 82.9 us, ordinary ones 74.4 us.  Other block sizes read whole lines.
+template <int BS>
+__device__ __forceinline__ u32x4 v_row16(const void* p) {
+  if constexpr (BS > kChunk) return load16(p);
+  else return stream16(p);
+}
+template <int BS>
+__device__ __forceinline__ u32x2 v_row8(const void* p) {
+  if constexpr (BS > kChunk) return load8(p);
+  else return stream8(p);
+}
+
 __device__ __forceinline__ uint32_t stream4(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
@@ -359,7 +377,7 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
         r.k[1][kk] = stream16(kc + ok1 + ((4 * kk + g4) * BS + rk1) * 8);
       }
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream16(vc + ov + (16 * mm + i) * BS + rv);
+      for (int mm = 0; mm < MM; ++mm) r.v[mm] = v_row16<BS>(vc + ov + (16 * mm + i) * BS + rv);
     } else {
       // K codes: one 16-byte x-vector 4*k2 + g4 (channels 16*(4*k2+g4)..+16)
       // of the token's row feeds products 2*k2 and 2*k2 + 1.
@@ -373,7 +391,7 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
         r.k[1][2 * k2 + 1] = u32x2{c[2], c[3]};
       }
 #pragma unroll
-      for (int mm = 0; mm < MM; ++mm) r.v[mm] = stream8(vc + ov + (16 * mm + i) * BS + rv);
+      for (int mm = 0; mm < MM; ++mm) r.v[mm] = v_row8<BS>(vc + ov + (16 * mm + i) * BS + rv);
       // Scales: one per lane (the chunk's 32 K scales, then its 32 V
       // scales); consume hands each lane the ones it needs by lane shuffles,
       // which keeps one register per chunk in flight instead of sixteen.
@@ -752,7 +770,7 @@ struct VaWaveDecoder : ChunkWalker<VaWaveDecoder<Ty, D, BS>, BS> {
     for (int bb = 0; bb < BPC; ++bb) {  // V rows: piece pc of channel ch0 + CPI*n
       const uint16_t* base = vc + (int64_t)b[bb] * blk_stride + head_off + r0 + 8 * pc;
 #pragma unroll
-      for (int n = 0; n < NCH; ++n) r.v[bb][n] = stream16(base + (ch0 + CPI * n) * BS);
+      for (int n = 0; n < NCH; ++n) r.v[bb][n] = v_row16<BS>(base + (ch0 + CPI * n) * BS);
     }
   }
 
