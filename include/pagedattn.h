@@ -447,6 +447,47 @@ PA_API int32_t pa_seq_num_blocks(const pa_allocator* a, int64_t seq);   /* -1 if
 PA_API pa_status pa_seq_block_table(const pa_allocator* a, int64_t seq, int32_t* out,
                                     int32_t cap, int32_t* n);
 
+/* ------------------------------------------------------------------------
+ * Prefix cache (wiblog.cn, section "Copy-on-Write、并行采样与 Prefix Caching
+ * 不是同一件事": sharing physical blocks is not yet a cross-request prefix
+ * cache, which also needs a cache key, exact matching of token sequences
+ * under one model configuration, a lifetime for cached blocks, and normal
+ * prefill of the unmatched suffix).  An index from the content of a FULL
+ * block to the physical block holding it:
+ *   - key of block i of a token sequence: a 128-bit hash chained from `salt`
+ *     (the caller's tag of everything that changes the KV of the same tokens:
+ *     model, tokenizer, chat template, positional configuration) over every
+ *     token from the sequence start to the block's end, so two blocks share a
+ *     key only when their whole prefixes are the same token ids under the
+ *     same salt (up to a 2^-128-scale hash collision);
+ *   - pa_prefix_register records the full blocks of a sequence whose KV is
+ *     written (tokens: the sequence's token ids, at least its full blocks);
+ *     a key already present, or a block already indexed, is left alone (the
+ *     first registration wins);
+ *   - pa_prefix_match gives how many leading tokens (whole blocks) of a new
+ *     token sequence the index holds, leaving at least one token unmatched
+ *     (it must be prefilled to give the next token);
+ *   - pa_seq_add_cached creates a sequence that references those blocks
+ *     (refcount + 1 each; its length is the matched token count): the caller
+ *     prefills the rest through pa_seq_append_slot as usual;
+ *   - an entry lives while its block is referenced: it is dropped when the
+ *     block returns to the free pool (no retention of unreferenced blocks).
+ * Full blocks are never written again (appends take a new block; copy-on-
+ * write only copies partly filled tails), so an indexed block's content is
+ * stable while it is indexed.
+ * ------------------------------------------------------------------------ */
+/* *n_registered: blocks newly indexed. */
+PA_API pa_status pa_prefix_register(pa_allocator* a, int64_t seq, const int32_t* tokens,
+                                    int32_t n_tokens, uint64_t salt, int32_t* n_registered);
+/* Tokens (a multiple of block_size, < n_tokens) a new sequence could adopt;
+ * -1 on bad arguments. */
+PA_API int32_t pa_prefix_match(const pa_allocator* a, const int32_t* tokens, int32_t n_tokens,
+                               uint64_t salt);
+/* New sequence `seq` over the matched blocks; *n_cached = its length. */
+PA_API pa_status pa_seq_add_cached(pa_allocator* a, int64_t seq, const int32_t* tokens,
+                                   int32_t n_tokens, uint64_t salt, int32_t* n_cached);
+PA_API int32_t pa_prefix_num_entries(const pa_allocator* a); /* -1 if a is NULL */
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,6 +37,22 @@ Readings where the pages are silent:
     on top (handed out first); a freed block is pushed on top.  free() walks
     a table in logical order.
   * Out of blocks: the call fails and leaves the state unchanged.
+Prefix cache (wiblog.cn, section "Copy-on-Write、并行采样与 Prefix Caching 不是
+同一件事": a cache key, exact token-sequence matching under one model
+configuration, a lifetime for cached blocks, and the unmatched suffix still
+prefilled).  Readings where the page is silent:
+  * Only full blocks are cached.  The key of block i of a sequence is
+    (salt, the token ids 0 .. (i+1) * block_size - 1): the whole prefix up to
+    the block's end, under the caller's configuration tag.
+  * register(seq, tokens, salt) indexes the sequence's full blocks (those
+    covered by both its length and `tokens`); a key already indexed, or a
+    block already indexed under a key, is left alone (first one wins).
+  * match(tokens, salt): the longest run of leading full blocks whose keys
+    are indexed, leaving at least one token unmatched; returns tokens.
+  * add_cached(seq, tokens, salt): a new sequence referencing the matched
+    blocks (refcount + 1), of length match(tokens, salt).
+  * An entry lives while its block is referenced: it is dropped when the
+    block returns to the free pool.
 """
 
 
@@ -56,6 +72,8 @@ class BlockManagerModel:
         self._stack = list(reversed(order))  # top of the stack = end of the list
         self._ref = [0] * num_blocks
         self._seqs = {}  # seq id -> {"blocks": [...], "len": int}
+        self._cache = {}   # (salt, token prefix tuple) -> block
+        self._key_of = {}  # block -> its key in _cache
 
     # ---- queries ----
     def num_free(self):
@@ -128,6 +146,50 @@ class BlockManagerModel:
             self._ref[b] -= 1
             if self._ref[b] == 0:
                 self._stack.append(b)
+                if b in self._key_of:
+                    del self._cache[self._key_of.pop(b)]
+
+    # ---- prefix cache ----
+    def register(self, seq, tokens, salt=0):
+        if seq not in self._seqs:
+            raise KeyError(f"sequence {seq} unknown")
+        st, bs = self._seqs[seq], self.block_size
+        tokens = [int(t) for t in tokens]
+        added = 0
+        for i in range(min(len(tokens), st["len"]) // bs):
+            key = (salt, tuple(tokens[:(i + 1) * bs]))
+            b = st["blocks"][i]
+            if key in self._cache or b in self._key_of:
+                continue
+            self._cache[key] = b
+            self._key_of[b] = key
+            added += 1
+        return added
+
+    def _matched_blocks(self, tokens, salt):
+        tokens = [int(t) for t in tokens]
+        bs, out = self.block_size, []
+        while (len(out) + 1) * bs <= len(tokens) - 1:  # at least one token left to prefill
+            key = (salt, tuple(tokens[:(len(out) + 1) * bs]))
+            if key not in self._cache:
+                break
+            out.append(self._cache[key])
+        return out
+
+    def match(self, tokens, salt=0):
+        return len(self._matched_blocks(tokens, salt)) * self.block_size
+
+    def add_cached(self, seq, tokens, salt=0):
+        if seq in self._seqs:
+            raise KeyError(f"sequence {seq} exists")
+        blocks = self._matched_blocks(tokens, salt)
+        for b in blocks:
+            self._ref[b] += 1
+        self._seqs[seq] = {"blocks": blocks, "len": len(blocks) * self.block_size}
+        return len(blocks) * self.block_size
+
+    def num_cache_entries(self):
+        return len(self._cache)
 
     # ---- invariants ----
     def check_invariants(self):
@@ -142,3 +204,7 @@ class BlockManagerModel:
         assert len(free) == len(self._stack), "a block is on the free pool twice"
         for b in range(self.num_blocks):
             assert (b in free) == (self._ref[b] == 0), "free pool / refcount mismatch"
+        assert len(self._cache) == len(self._key_of), "prefix cache maps differ"
+        for key, b in self._cache.items():
+            assert self._key_of[b] == key and self._ref[b] > 0, "cached block not referenced"
+            assert len(key[1]) % bs == 0 and key[1], "cache key not a whole number of blocks"

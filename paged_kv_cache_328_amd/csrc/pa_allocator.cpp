@@ -10,7 +10,11 @@
 // reference counts and copy a block only when they must write into a shared
 // one (kongchang.com, "PagedAttention原理详解", section "PagedAttention的三大
 // 核心优势", second advantage; wiblog.cn, section "Copy-on-Write、并行采样与
-// Prefix Caching 不是同一件事").
+// Prefix Caching 不是同一件事").  A prefix cache on top of the block sharing
+// lets a new request adopt full blocks whose exact token prefix another
+// sequence already holds (the same wiblog.cn section: a cache key, exact
+// token-sequence matching under one model configuration, a lifetime for the
+// cached blocks, and the unmatched suffix still prefilled).
 // The exact rules are stated with the declarations in pagedattn.h.
 #include <new>
 #include <unordered_map>
@@ -26,6 +30,39 @@ struct Sequence {
   int32_t len = 0;              // tokens stored
 };
 
+// Prefix-cache key of a full block: a 128-bit hash of the cache
+// configuration (the caller's salt: tokenizer, template, model) and of every
+// token from the sequence start to the block's end, chained block by block.
+// Two lanes of 64 bits with independent mixing; keys are compared whole.
+struct Key {
+  uint64_t a, b;
+  bool operator==(const Key& o) const { return a == o.a && b == o.b; }
+};
+struct KeyHash {
+  size_t operator()(const Key& k) const { return (size_t)(k.a ^ (k.b * 0x9E3779B97F4A7C15ull)); }
+};
+
+// splitmix64 finalizer (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", 2014).
+uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+Key root_key(uint64_t salt) { return Key{mix64(salt ^ 0x6A09E667F3BCC908ull), mix64(salt + 0xBB67AE8584CAA73Bull)}; }
+
+// Key of the block after `parent` holding tokens t[0 .. n).
+Key next_key(Key parent, const int32_t* t, int32_t n) {
+  uint64_t a = parent.a, b = parent.b;
+  for (int32_t i = 0; i < n; ++i) {
+    const uint64_t v = (uint32_t)t[i];
+    a = mix64(a ^ (v + 0x3C6EF372FE94F82Bull));
+    b = mix64(b + v * 0xA54FF53A5F1D36F1ull + 0x510E527FADE682D1ull);
+  }
+  return Key{mix64(a ^ (uint64_t)n), mix64(b + (uint64_t)n)};
+}
+
 }  // namespace
 
 struct pa_allocator {
@@ -34,6 +71,37 @@ struct pa_allocator {
   std::vector<int32_t> stack;   // free pool; back() is handed out next
   std::vector<int32_t> ref;     // reference count per physical block
   std::unordered_map<int64_t, Sequence> seqs;
+  // prefix cache: key of a full block's content -> the block holding it, and
+  // back (a block is indexed under at most one key while it is referenced)
+  std::unordered_map<Key, int32_t, KeyHash> prefix;
+  std::unordered_map<int32_t, Key> key_of;
+
+  // Length in blocks of the longest chain of indexed blocks that starts
+  // tokens[0 .. n) (at most max_blocks), and their ids.
+  int32_t match(const int32_t* tokens, int32_t n, uint64_t salt, int32_t max_blocks,
+                std::vector<int32_t>* ids) const {
+    Key k = root_key(salt);
+    int32_t m = 0;
+    while (m < max_blocks && (int64_t)(m + 1) * block_size <= n) {
+      k = next_key(k, tokens + (int64_t)m * block_size, block_size);
+      auto it = prefix.find(k);
+      if (it == prefix.end()) break;
+      if (ids) ids->push_back(it->second);
+      ++m;
+    }
+    return m;
+  }
+
+  // Returns block b (refcount 0) to the free pool and removes it from the
+  // prefix cache.
+  void release(int32_t b) {
+    stack.push_back(b);
+    auto it = key_of.find(b);
+    if (it != key_of.end()) {
+      prefix.erase(it->second);
+      key_of.erase(it);
+    }
+  }
 
   int32_t take() {
     int32_t b = stack.back();
@@ -211,10 +279,65 @@ PA_API pa_status pa_seq_free(pa_allocator* a, int64_t seq) {
   if (it == a->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
   for (int32_t b : it->second.blocks) {
     a->ref[b] -= 1;
-    if (a->ref[b] == 0) a->stack.push_back(b);
+    if (a->ref[b] == 0) a->release(b);
   }
   a->seqs.erase(it);
   return PA_OK;
+}
+
+PA_API pa_status pa_prefix_register(pa_allocator* a, int64_t seq, const int32_t* tokens,
+                                    int32_t n_tokens, uint64_t salt, int32_t* n_registered) {
+  if (!a || n_tokens < 0 || (n_tokens > 0 && !tokens) || !n_registered) return PA_ERR_INVALID;
+  *n_registered = 0;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+  const Sequence& s = it->second;
+  const int32_t full = (n_tokens < s.len ? n_tokens : s.len) / a->block_size;
+  try {
+    Key k = root_key(salt);
+    for (int32_t i = 0; i < full; ++i) {
+      k = next_key(k, tokens + (int64_t)i * a->block_size, a->block_size);
+      const int32_t b = s.blocks[i];
+      if (a->prefix.count(k) || a->key_of.count(b)) continue;  // first registration wins
+      a->prefix.emplace(k, b);
+      a->key_of.emplace(b, k);
+      ++*n_registered;
+    }
+  } catch (...) {
+    return PA_ERR_INVALID;
+  }
+  return PA_OK;
+}
+
+PA_API int32_t pa_prefix_match(const pa_allocator* a, const int32_t* tokens, int32_t n_tokens,
+                               uint64_t salt) {
+  if (!a || n_tokens < 0 || (n_tokens > 0 && !tokens)) return -1;
+  // at least one token stays out of the match: it must be prefilled
+  const int32_t max_blocks = n_tokens > 0 ? (n_tokens - 1) / a->block_size : 0;
+  return a->match(tokens, n_tokens, salt, max_blocks, nullptr) * a->block_size;
+}
+
+PA_API pa_status pa_seq_add_cached(pa_allocator* a, int64_t seq, const int32_t* tokens,
+                                   int32_t n_tokens, uint64_t salt, int32_t* n_cached) {
+  if (!a || n_tokens < 0 || (n_tokens > 0 && !tokens) || !n_cached) return PA_ERR_INVALID;
+  *n_cached = 0;
+  if (a->seqs.count(seq)) return PA_ERR_EXISTS;
+  try {
+    Sequence s;
+    const int32_t max_blocks = n_tokens > 0 ? (n_tokens - 1) / a->block_size : 0;
+    a->match(tokens, n_tokens, salt, max_blocks, &s.blocks);
+    s.len = (int32_t)s.blocks.size() * a->block_size;
+    a->seqs.emplace(seq, s);
+    for (int32_t b : s.blocks) a->ref[b] += 1;
+    *n_cached = s.len;
+  } catch (...) {
+    return PA_ERR_INVALID;
+  }
+  return PA_OK;
+}
+
+PA_API int32_t pa_prefix_num_entries(const pa_allocator* a) {
+  return a ? (int32_t)a->prefix.size() : -1;
 }
 
 PA_API int32_t pa_seq_len(const pa_allocator* a, int64_t seq) {

@@ -102,6 +102,10 @@ def lib():
                                         _I32, _I32, _I32, _P]),
         "pa_probe_read": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P, _I64, _I32, _I32, _I32, _P, _P]),
         "pa_alloc_create": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(_P)]),
+        "pa_prefix_register": (ctypes.c_int, [_P, _I64, _P, _I32, ctypes.c_uint64, ctypes.POINTER(_I32)]),
+        "pa_prefix_match": (_I32, [_P, _P, _I32, ctypes.c_uint64]),
+        "pa_seq_add_cached": (ctypes.c_int, [_P, _I64, _P, _I32, ctypes.c_uint64, ctypes.POINTER(_I32)]),
+        "pa_prefix_num_entries": (_I32, [_P]),
         "pa_alloc_destroy": (None, [_P]),
         "pa_alloc_num_free": (_I32, [_P]),
         "pa_alloc_num_seqs": (_I32, [_P]),
@@ -605,6 +609,33 @@ class Allocator:
 
     def pa_seq_free(self, seq):
         _check(lib().pa_seq_free(self._h, seq), "pa_seq_free")
+
+    @staticmethod
+    def _tokens(tokens):
+        t = [int(x) for x in tokens]
+        return (_I32 * max(len(t), 1))(*t), len(t)
+
+    def pa_prefix_register(self, seq, tokens, salt=0):
+        """Indexes the sequence's full blocks under their token prefixes;
+        returns how many blocks were newly indexed."""
+        arr, n = self._tokens(tokens)
+        out = _I32()
+        _check(lib().pa_prefix_register(self._h, seq, arr, n, salt, ctypes.byref(out)), "pa_prefix_register")
+        return out.value
+
+    def pa_prefix_match(self, tokens, salt=0):
+        arr, n = self._tokens(tokens)
+        return lib().pa_prefix_match(self._h, arr, n, salt)
+
+    def pa_seq_add_cached(self, seq, tokens, salt=0):
+        """New sequence over the cached prefix blocks; returns its length."""
+        arr, n = self._tokens(tokens)
+        out = _I32()
+        _check(lib().pa_seq_add_cached(self._h, seq, arr, n, salt, ctypes.byref(out)), "pa_seq_add_cached")
+        return out.value
+
+    def pa_prefix_num_entries(self):
+        return lib().pa_prefix_num_entries(self._h)
 
     def pa_seq_len(self, seq):
         return lib().pa_seq_len(self._h, seq)

@@ -155,3 +155,75 @@ def test_random_operation_sequences_keep_invariants(seed):
         for s in live:
             n = m.seq_len(s)
             assert len(m.block_table(s)) * BS - n < BS or n == 0
+
+
+# ---------------------------------------------------------------------------- prefix cache
+# Hand-worked scenarios with block size 4 and the identity free order (blocks
+# are handed out 0, 1, 2, ...), following the readings in allocator_model.py.
+
+def _prefill(m, seq, tokens):
+    for _ in tokens:
+        m.append_slot(seq)
+
+
+def test_prefix_cache_hand_worked_sharing():
+    m = BlockManagerModel(16, 4)
+    a = [7, 7, 1, 2, 9, 9, 3, 4, 5, 6]          # 2 full blocks + 2 tokens
+    m.add(1)
+    _prefill(m, 1, a)                           # blocks 0, 1, 2
+    assert m.block_table(1) == [0, 1, 2]
+    assert m.register(1, a) == 2                # the two full blocks only
+    assert m.num_cache_entries() == 2
+    # same 8-token prefix, different tail: both blocks are adopted
+    b = a[:8] + [11, 12, 13]
+    assert m.match(b) == 8
+    assert m.add_cached(2, b) == 8
+    assert m.block_table(2) == [0, 1] and m.refcount(0) == 2 and m.refcount(1) == 2
+    _prefill(m, 2, b[8:])                       # the suffix takes a new block (3)
+    assert m.block_table(2) == [0, 1, 3] and m.seq_len(2) == 11
+    m.check_invariants()
+
+
+def test_prefix_cache_needs_one_token_left_and_exact_prefixes():
+    m = BlockManagerModel(16, 4)
+    a = list(range(12))                         # exactly 3 full blocks
+    m.add(1)
+    _prefill(m, 1, a)
+    assert m.register(1, a) == 3
+    assert m.match(a) == 8                      # the last token must be prefilled: 2 blocks
+    assert m.match(a + [99]) == 12
+    assert m.match(a[:4] + [0] + a[5:]) == 4    # differs in block 1: stops after block 0
+    assert m.match([1] + a[1:]) == 0            # differs in block 0
+    assert m.match(a, salt=5) == 0              # another configuration tag
+    assert m.match(a[:3]) == 0                  # no full block
+    m.check_invariants()
+
+
+def test_prefix_cache_entries_live_while_blocks_are_referenced():
+    m = BlockManagerModel(16, 4)
+    a = list(range(9))
+    m.add(1)
+    _prefill(m, 1, a)
+    m.register(1, a)
+    m.fork(1, 2)                                # the sibling keeps the blocks alive
+    m.free(1)
+    assert m.num_cache_entries() == 2 and m.match(a) == 8
+    m.free(2)                                   # last holder: blocks back to the pool
+    assert m.num_cache_entries() == 0 and m.match(a) == 0
+    m.check_invariants()
+
+
+def test_prefix_cache_first_registration_wins():
+    m = BlockManagerModel(16, 4)
+    a = list(range(8)) + [50]
+    m.add(1)
+    _prefill(m, 1, a)                           # blocks 0, 1, 2
+    m.add(2)
+    _prefill(m, 2, a)                           # the same tokens computed again: 3, 4, 5
+    assert m.register(1, a) == 2
+    assert m.register(2, a) == 0                # keys already held by sequence 1's blocks
+    m.add_cached(3, a)
+    assert m.block_table(3) == [0, 1]
+    m.free(1)                                   # block 2 returns; 0 and 1 stay with sequence 3
+    assert m.match(a) == 8
+    m.check_invariants()

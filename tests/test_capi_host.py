@@ -279,6 +279,79 @@ def test_allocator_matches_model_on_random_operations(seed):
     m.check_invariants()
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_prefix_cache_matches_model_on_random_operations(seed):
+    """The native prefix cache (128-bit chained hashes) against the model
+    (whole token prefixes as keys), with a 3-token vocabulary so prefixes
+    repeat often, mixed with appends, forks and frees."""
+    rng = np.random.default_rng(300 + seed)
+    NB, BS = 64, 4
+    order = rng.permutation(NB).tolist()
+    a, m = pa.Allocator(NB, BS, order), BlockManagerModel(NB, BS, order)
+    toks, live, nid = {}, [], 0
+    prompts = [rng.integers(0, 3, size=int(rng.integers(1, 20))).tolist() for _ in range(6)]
+    for step in range(400):
+        op = int(rng.integers(0, 8))
+        if op <= 1 or not live:  # a new request: adopt cached blocks, prefill the rest
+            pr = prompts[int(rng.integers(len(prompts)))]
+            pr = pr + rng.integers(0, 3, size=int(rng.integers(0, 6))).tolist()
+            salt = int(rng.integers(0, 2))
+            assert a.pa_prefix_match(pr, salt) == m.match(pr, salt)
+            n = m.match(pr, salt)
+            if m.num_free() < -(-(len(pr) - n) // BS):
+                continue
+            assert a.pa_seq_add_cached(nid, pr, salt) == m.add_cached(nid, pr, salt) == n
+            for _ in pr[n:]:
+                assert a.pa_seq_append_slot(nid) == m.append_slot(nid)
+            toks[nid] = (list(pr), salt)
+            live.append(nid)
+            nid += 1
+        elif op == 2:  # register a live sequence's full blocks
+            s = live[int(rng.integers(len(live)))]
+            t, salt = toks[s]
+            assert a.pa_prefix_register(s, t, salt) == m.register(s, t, salt)
+        elif op == 3:
+            s = live.pop(int(rng.integers(len(live))))
+            a.pa_seq_free(s)
+            m.free(s)
+        elif op == 4:
+            p = live[int(rng.integers(len(live)))]
+            a.pa_seq_fork(p, nid)
+            m.fork(p, nid)
+            toks[nid] = (list(toks[p][0]), toks[p][1])
+            live.append(nid)
+            nid += 1
+        else:  # decode: one more token on a sequence
+            s = live[int(rng.integers(len(live)))]
+            try:
+                want = m.append_slot(s)
+            except NoBlocks:
+                continue
+            assert a.pa_seq_append_slot(s) == want
+            toks[s][0].append(int(rng.integers(0, 3)))
+        assert a.pa_prefix_num_entries() == m.num_cache_entries()
+        if step % 20 == 0:
+            _same_state(a, m, live)
+            m.check_invariants()
+    _same_state(a, m, live)
+    m.check_invariants()
+
+
+def test_prefix_cache_rejects_bad_arguments():
+    a = pa.Allocator(8, 4)
+    a.pa_seq_add(0)
+    with pytest.raises(pa.PaError) as e:
+        a.pa_prefix_register(5, [1, 2, 3, 4])
+    assert e.value.status == pa.PA_ERR_UNKNOWN_SEQ
+    with pytest.raises(pa.PaError) as e:
+        a.pa_seq_add_cached(0, [1, 2, 3, 4, 5])
+    assert e.value.status == pa.PA_ERR_EXISTS
+    L = pa.lib()
+    assert L.pa_prefix_match(None, None, 0, 0) == -1
+    assert L.pa_prefix_num_entries(None) == -1
+    a.close()
+
+
 def test_batch_append_with_all_sharers_copies_all_but_the_last_holder():
     BS = 4
     a, m = pa.Allocator(16, BS, list(range(16))), BlockManagerModel(16, BS, list(range(16)))
