@@ -55,6 +55,7 @@
 // products, the K scale multiplies the logit and the V scale the weight.
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -106,6 +107,16 @@ __device__ __forceinline__ bool flat_unit(const int32_t* __restrict__ lens, int 
   }
   return false;
 }
+
+// The flat work list in an order the host chose from its copy of the context
+// lengths: entry j (packed s | p << 16) is the (sequence, partition) unit of
+// grid row j.  Passed by value as a kernel argument; n = 0 means no list (the
+// kernel finds its unit with flat_unit, in sequence order).
+constexpr int kMaxUnits = 512;
+struct UnitList {
+  int32_t n;
+  uint32_t e[kMaxUnits];
+};
 
 // Running state of a log-sum-exp merge: max m, sum l, unnormalised output o
 // (4 channels).  Adding partition (m', l', o') with M = max(m, m'):
@@ -1067,7 +1078,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
     int max_blocks, int max_ctx, float scale_log2, int P, int max_parts,
     float* __restrict__ ws_acc, float* __restrict__ ws_ml, int num_seqs, int pre_parts, int pre_P,
     const int32_t* __restrict__ grp_start, const int32_t* __restrict__ grp_len, int n_grp,
-    int xcd_order) {
+    int xcd_order, UnitList ul) {
   extern __shared__ float lds[];
   // Workgroups are dealt to the XCDs round-robin (linear id L goes to XCD
   // L % kXcds).  With xcd_order the grid is renumbered so that each XCD
@@ -1096,6 +1107,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
     bx = (int)(lam % X);
     by = (int)((lam / X) % Y);
     bz = (int)(lam / (X * Y));
+  }
+  if (ul.n > 0) {  // the host's unit order: row by is unit (s, p) of its list
+    const uint32_t e = ul.e[by];
+    bz = (int)(e & 0xFFFFu);
+    by = (int)(e >> 16);
+    num_seqs = 0;  // the body then takes p = by, s = bz
   }
   decode_mfma_body<Ty, D, BS, NW, KV8, VALU>(bx, by, bz, lds, out, q, kcv, vcv, tables, lens, k_new,
                                        v_new, Hq, Hkv, G, n_groups, NB, max_blocks, max_ctx,
@@ -1889,6 +1906,9 @@ struct Plan {
   // (sequence, partition) units of the flat work list, from the host copy of
   // the context lengths (0 = unknown: the grid covers num_seqs * max_parts)
   int64_t units = 0;
+  // the flat list's units longest first (n = 0: sequence order, in-kernel)
+  UnitList order;
+  Plan() { order.n = 0; }
   // both products on the vector ALU (decode_mfma_kernel with VaWaveDecoder)
   bool valu = false;
 };
@@ -1970,6 +1990,24 @@ Plan make_plan(const pa_decode_args* a) {
     // the kernel's own count: every sequence has max(ceil(c / P), 1) units
     for (int s = 0; s < a->num_seqs; ++s)
       pl.units += max((a->context_lens_host[s] + pl.P - 1) / pl.P, 1);
+    // Longest unit first (ties in sequence order): the last units to start
+    // are the short tails of the sequences, so the workgroups still running
+    // when the grid drains are short ones.
+    if (pl.units <= kMaxUnits) {
+      int n = 0;
+      for (int s = 0; s < a->num_seqs; ++s) {
+        const int c = a->context_lens_host[s];
+        const int parts = max((c + pl.P - 1) / pl.P, 1);
+        for (int p = 0; p < parts; ++p) pl.order.e[n++] = (uint32_t)s | ((uint32_t)p << 16);
+      }
+      auto tokens = [&](uint32_t e) {
+        const int c = a->context_lens_host[e & 0xFFFFu];
+        return min(pl.P, c - (int)(e >> 16) * pl.P);
+      };
+      std::stable_sort(pl.order.e, pl.order.e + n,
+                       [&](uint32_t x, uint32_t y) { return tokens(x) > tokens(y); });
+      pl.order.n = n;
+    }
   }
   if (pl.max_parts > 1)
     pl.ws_bytes = (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * (a->head_dim + 2) * 4;
@@ -2000,7 +2038,7 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
       a->context_lens, (const uint16_t*)a->k_new, (const uint16_t*)a->v_new, a->num_q_heads,
       a->num_kv_heads, G, pl.groups, a->num_blocks, a->max_blocks_per_seq, a->max_context_len,
       a->scale * kLog2e, pl.P, max(pl.max_parts, 1), ws_acc, ws_ml, flat ? a->num_seqs : 0,
-      pl.pre_parts, pl.pre_P, pl.grp_start, pl.grp_len, pl.n_grp, (int)!flat);
+      pl.pre_parts, pl.pre_P, pl.grp_start, pl.grp_len, pl.n_grp, (int)!flat, pl.order);
 }
 
 // pa_decode_prefix: prefix_suffix_kernel, one launch of the shared-prefix

@@ -142,3 +142,34 @@ def test_static_entry_at_the_library_split():
     want = oracle.decode(np.ascontiguousarray(case.q[0]), case.k_cache, case.v_cache, tables,
                          case.context_lens, case.scale, dtype, num_threads=16, bound=True)
     check_attention(outs[1], want, dtype, "split static")
+
+
+@pytest.mark.parametrize("S", [128, 129])
+def test_unit_list_capacity(S):
+    """With the host lengths the library deals the flat list's units longest
+    first from a list it passes by value, which holds up to 512 units; past
+    that the kernel walks them in sequence order itself.  128 sequences of 4
+    partitions (97..128 tokens at 32-token partitions, tails of 1..32
+    tokens) fill the list exactly; 129 overflow it.  Either way the output
+    matches the oracle and does not depend on the host lengths, bit for bit
+    (the order changes when units run, not what they compute)."""
+    import torch
+    rng = np.random.default_rng(950 + S)
+    lens = rng.integers(97, 128, size=S, endpoint=True).tolist()
+    case = wl.random_case(950 + S, S, 8, 2, 64, 16, "bf16", lens, partition_size=32)
+    dtype = case.dtype
+    tables = np.ascontiguousarray(case.block_tables[0])
+    kd, vd = to_dev(case.k_cache, dtype), to_dev(case.v_cache, dtype)
+    qd, td, ld = to_dev(case.q[0], dtype), ints_to_dev(tables), ints_to_dev(case.context_lens)
+    outs = []
+    for host in (case.context_lens, None):
+        announce(f"unit list S={S}: pa_decode P=32 host lens={host is not None}")
+        out = torch.empty_like(qd)
+        pa.pa_decode(out, qd, kd, vd, td, ld, case.scale, case.max_context, partition_size=32,
+                     context_lens_host=host)
+        _sync()
+        outs.append(to_host(out, dtype))
+    assert same_bits(outs[0], outs[1]), f"S={S}: host lengths changed the output"
+    want = oracle.decode(np.ascontiguousarray(case.q[0]), case.k_cache, case.v_cache, tables,
+                         case.context_lens, case.scale, dtype, num_threads=16, bound=True)
+    check_attention(outs[0], want, dtype, f"unit list S={S}")
