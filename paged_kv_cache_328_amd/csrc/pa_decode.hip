@@ -303,6 +303,37 @@ struct ChunkWalker {
       }
     }
   }
+
+  // The same walk with one register set and the loads of chunk k + 1 split
+  // around chunk k's products: its K loads go out as soon as chunk k's QK
+  // product has read the K registers, its V loads once the PV product has
+  // read the V registers.  Loads are then in flight while the wave computes,
+  // without the second register set of walk<true> (Derived supplies
+  // issue_k / issue_v and consume_k / consume_v).
+  template <typename T0, typename Ids>
+  __device__ __forceinline__ void walk_skew(int n, T0 t0_of, Ids ids, int cc, int skip) {
+    Derived& d = static_cast<Derived&>(*this);
+    using RawT = typename Derived::RawT;
+    if (n <= 0) return;
+    int nb[BPC] = {};
+    ids(0, nb);
+    RawT r;
+    d.issue_k(nb, t0_of(0), r);
+    d.issue_v(nb, t0_of(0), r);
+    for (int k = 0; k < n; ++k) {
+      const bool more = k + 1 < n;
+      if (more) ids(k + 1, nb);
+      float x[8], sv[8];
+      __builtin_amdgcn_sched_barrier(0);
+      d.consume_k(t0_of(k), r, cc, skip, x, sv);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) d.issue_k(nb, t0_of(k + 1), r);
+      __builtin_amdgcn_sched_barrier(0);
+      d.consume_v(t0_of(k), r, cc, x, sv);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) d.issue_v(nb, t0_of(k + 1), r);
+    }
+  }
 };
 
 // One wave's share of the decode pass: q held as the B operand of both
@@ -369,26 +400,26 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
     }
   }
 
-  __device__ __forceinline__ void issue(const int (&b)[BPC], int t0, RawT& r) const {
-    const int r0 = BS > kChunk ? t0 % BS : 0;
-    auto at = [&](int tau, int64_t& off, int& row) {  // tile offset and row of token tau
-      const int id = pick_block<BPC>(b, tau / BS);
-      off = (int64_t)id * blk_stride + head_off;
-      row = BS >= kChunk ? r0 + tau : tau % BS;
-    };
-    int64_t ok0, ok1, ov;
-    int rk0, rk1, rv;
-    at(i, ok0, rk0);               // K operand of tile 0: token i
-    at(16 + i, ok1, rk1);          // tile 1: token 16 + i
-    at(8 * g4, ov, rv);            // V^T operand: tokens 8*g4..+8 (one block row)
+  // Tile offset and row of token tau (0..31) of the chunk at token t0.
+  __device__ __forceinline__ void token_at(const int (&b)[BPC], int t0, int tau, int64_t& off,
+                                           int& row) const {
+    const int id = pick_block<BPC>(b, tau / BS);
+    off = (int64_t)id * blk_stride + head_off;
+    row = BS >= kChunk ? (BS > kChunk ? t0 % BS : 0) + tau : tau % BS;
+  }
+
+  // The chunk's K loads (INT8: and its K and V scales).
+  __device__ __forceinline__ void issue_k(const int (&b)[BPC], int t0, RawT& r) const {
+    int64_t ok0, ok1;
+    int rk0, rk1;
+    token_at(b, t0, i, ok0, rk0);       // K operand of tile 0: token i
+    token_at(b, t0, 16 + i, ok1, rk1);  // tile 1: token 16 + i
     if constexpr (!KV8) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         r.k[0][kk] = stream16(kc + ok0 + ((4 * kk + g4) * BS + rk0) * 8);
         r.k[1][kk] = stream16(kc + ok1 + ((4 * kk + g4) * BS + rk1) * 8);
       }
-#pragma unroll
-      for (int mm = 0; mm < MM; ++mm) r.v[mm] = v_row16<BS>(vc + ov + (16 * mm + i) * BS + rv);
     } else {
       // K codes: one 16-byte x-vector 4*k2 + g4 (channels 16*(4*k2+g4)..+16)
       // of the token's row feeds products 2*k2 and 2*k2 + 1.
@@ -401,22 +432,50 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
         r.k[1][2 * k2] = u32x2{c[0], c[1]};
         r.k[1][2 * k2 + 1] = u32x2{c[2], c[3]};
       }
-#pragma unroll
-      for (int mm = 0; mm < MM; ++mm) r.v[mm] = v_row8<BS>(vc + ov + (16 * mm + i) * BS + rv);
       // Scales: one per lane (the chunk's 32 K scales, then its 32 V
       // scales); consume hands each lane the ones it needs by lane shuffles,
       // which keeps one register per chunk in flight instead of sixteen.
       constexpr int SC = I8Tile<D, BS>::kScales;
       int64_t osc;
       int rsc;
-      at(lane & 31, osc, rsc);
+      token_at(b, t0, lane & 31, osc, rsc);
       r.sc = stream_f1((lane < 32 ? kc : vc) + osc + SC + 4 * rsc);
     }
   }
 
+  // The chunk's V loads: the V^T operand, tokens 8*g4..+8 (one block row).
+  __device__ __forceinline__ void issue_v(const int (&b)[BPC], int t0, RawT& r) const {
+    int64_t ov;
+    int rv;
+    token_at(b, t0, 8 * g4, ov, rv);
+#pragma unroll
+    for (int mm = 0; mm < MM; ++mm) {
+      if constexpr (!KV8) r.v[mm] = v_row16<BS>(vc + ov + (16 * mm + i) * BS + rv);
+      else r.v[mm] = v_row8<BS>(vc + ov + (16 * mm + i) * BS + rv);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const int (&b)[BPC], int t0, RawT& r) const {
+    issue_k(b, t0, r);
+    issue_v(b, t0, r);
+  }
+
   // Both products and the online-softmax update for the chunk at token t0;
-  // tokens outside [skip, cc) are dropped.
+  // tokens outside [skip, cc) are dropped.  In two halves: consume_k (the QK
+  // product, which reads r.k and r.sc) and consume_v (softmax update and PV
+  // product, which reads r.v), so that a walk may reload r.k between them.
   __device__ __forceinline__ void consume(int t0, RawT& r, int cc, int skip) {
+    float x[8], sv[8];
+    consume_k(t0, r, cc, skip, x, sv);
+    consume_v(t0, r, cc, x, sv);
+  }
+
+  // x[e]: base-2 logit for head i of token t0 + 4*g4 + e (e < 4) or
+  // t0 + 16 + 4*g4 + e - 4 (e >= 4), the reduction index 8*g4 + e of the PV
+  // product; -inf for a dropped token.  INT8: sv[e] is that token's V scale
+  // (0 for a dropped token).
+  __device__ __forceinline__ void consume_k(int t0, const RawT& r, int cc, int skip, float (&x)[8],
+                                            float (&sv)[8]) const {
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
@@ -429,7 +488,6 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
       }
     }
     // INT8: V scales of this lane's tokens 4*g4 + (e & 3) + 16 * (e >> 2)
-    float sv[8];
     if constexpr (KV8) {  // logits of INT8 keys: code dot q times the token's scale
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -439,9 +497,6 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
 #pragma unroll
       for (int e = 0; e < 8; ++e) sv[e] = __shfl(r.sc, 32 + 16 * (e >> 2) + 4 * g4 + (e & 3));
     }
-    // x[e]: base-2 logit for head i of token t0 + 4*g4 + e (e < 4) or
-    // t0 + 16 + 4*g4 + e - 4 (e >= 4): reduction index 8*g4 + e of the PV product.
-    float x[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       x[j] = s0[j] * scale_log2;
@@ -453,8 +508,21 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
         const int tok = t0 + 4 * g4 + (e & 3) + 16 * (e >> 2);
         if (tok >= cc || tok < skip) x[e] = -INFINITY;
       }
-      if constexpr (!KV8) {  // zero the V bits of dropped tokens (they may hold NaN)
-        uint32_t keep[4];  // V word wd holds tokens t0 + 8*g4 + 2*wd, +1
+      if constexpr (KV8) {  // and their V scales (codes are finite; a scale may be NaN)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (x[e] == -INFINITY) sv[e] = 0.f;
+      }
+    }
+  }
+
+  // The online-softmax update with the logits x (and INT8 V scales sv) of
+  // consume_k, and the PV product over r.v.
+  __device__ __forceinline__ void consume_v(int t0, RawT& r, int cc, const float (&x)[8],
+                                            const float (&sv)[8]) {
+    if constexpr (!KV8) {
+      if (t0 + kChunk > cc) {  // zero the V bits of tokens past cc (they may hold NaN)
+        uint32_t keep[4];      // V word wd holds tokens t0 + 8*g4 + 2*wd, +1
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd)
           keep[wd] = (t0 + 8 * g4 + 2 * wd < cc ? 0x0000FFFFu : 0u) |
@@ -463,10 +531,6 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
         for (int mm = 0; mm < MM; ++mm)
 #pragma unroll
           for (int wd = 0; wd < 4; ++wd) r.v[mm][wd] &= keep[wd];
-      } else {  // and their V scales (codes are finite; a scale may be NaN)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (x[e] == -INFINITY) sv[e] = 0.f;
       }
     }
 
@@ -903,6 +967,19 @@ struct VaWaveDecoder : ChunkWalker<VaWaveDecoder<Ty, D, BS>, BS> {
   }
 };
 
+// Chunk walk of the matrix-core decoders.  INT8 caches take walk_skew (one
+// register set, the next chunk's loads split around the products); 16-bit
+// caches take walk<true>.  Measured on MI355X, 300 steps each against the
+// one-chunk walk<false> for INT8 and walk<true> for 16-bit:
+//   INT8: LLaMA-13B-shaped 43.2 -> 42.4 us, mixed lengths 43.4 -> 43.0, long
+//         context (P = 512) 112.4 -> 111.8 (168 VGPRs, still 3 waves per SIMD);
+//   16-bit: LLaMA-13B-shaped 64.1 -> 64.7 us, mixed lengths 60.8 -> 60.9, long
+//         context 183.8 -> 181.8; at block size 32 the 3-wave budget spilled
+//         (65.3 -> 77.9 us).
+// INT8 at block size 64 keeps walk<false>: walk_skew spilled there (f16).
+template <bool KV8, bool VALU, int BS>
+constexpr bool kSkewWalk = KV8 && !VALU && BS <= 32;
+
 // Body of the decode pass for the workgroup at grid position (bx, by, bz);
 // `lds` holds merge_lds_bytes(NW, G, D) bytes.  With prefix groups
 // (pa_decode_prefix, through prefix_suffix_kernel) it takes each member's
@@ -1015,8 +1092,9 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
   // look-ahead made the step slower; without it the kernel needs fewer
   // registers and more waves fit).
   const int n_mine = w < n_chunks ? (n_chunks - w + NW - 1) / NW : 0;
-  wd.template walk<!KV8>(n_mine, [&](int k) { return t_begin + chunk_of(k) * kChunk; }, block_ids,
-                         cc, skip);
+  auto t0_of = [&](int k) { return t_begin + chunk_of(k) * kChunk; };
+  if constexpr (kSkewWalk<KV8, VALU, BS>) wd.walk_skew(n_mine, t0_of, block_ids, cc, skip);
+  else wd.template walk<!KV8>(n_mine, t0_of, block_ids, cc, skip);
 
   // Fused append: that wave adds token c - 1 to its running state; the
   // group-0 workgroup also stores the token into the cache slot of position
