@@ -1315,7 +1315,26 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
   int hk, s, c, q0, nq, p = 0, t_begin = 0;
   if constexpr (!PFX) {
     hk = ya;
+    // Longest work first: the grid position za is a rank, and the sequence
+    // of rank za is the za-th longest context (ties in sequence order); the
+    // slot tiles of a (sequence, KV head) run last row first, since later
+    // rows see more keys.  The workgroups that start last are then the
+    // short ones, so fewer CUs idle while the grid drains.  Ranks need every
+    // length in one wave (at most 64 sequences); larger batches keep their
+    // order.
     s = za;
+    if (gz <= kWave) {
+      const int cmax = min(max_ctx, max_blocks * BS);
+      const int lane_c = lane < gz ? clampi(lens[lane], 0, cmax) : -1;
+      int rank = 0;  // sequences ahead of this lane's
+      for (int m = 0; m < gz; ++m) {
+        const int cm = __builtin_amdgcn_readlane(lane_c, m);
+        rank += (cm > lane_c || (cm == lane_c && m < lane)) ? 1 : 0;
+      }
+      const uint64_t hit = __ballot(lane < gz && rank == za);
+      s = uniform(__ffsll((unsigned long long)hit) - 1);
+    }
+    tile = gx - 1 - tile;
     c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
     q0 = clampi(qstart[s], 0, num_rows);
     nq = clampi(qstart[s + 1] - q0, 0, min(min(max_q, c), num_rows - q0));
