@@ -1200,11 +1200,36 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
 
 // LDS of the prefill pass: two chunk buffers, each a 32-token chunk's K and
 // V (16-bit), or its K codes, V codes and 64 scales (INT8).
-template <int D, bool KV8>
+// With DMA (16-bit caches, prefill proper) the chunks go from global memory
+// straight to LDS, into four buffers.
+template <int D, bool KV8, bool DMA = false>
 struct PrefillLds {
   static constexpr int kBuf = KV8 ? kChunk * (D / 16) * 16 + D * 4 * 8 + 64 * 4 : 2 * kChunk * (D / 8) * 16;
-  static constexpr int kBytes = 2 * kBuf;
+  static constexpr int kBufs = DMA ? 4 : 2;
+  static constexpr int kBytes = kBufs * kBuf;
 };
+
+// Direct global-to-LDS loads for the prefill pass of 16-bit caches (not the
+// shared-prefix pass, which shares its launch with decode workgroups).
+template <bool KV8, bool PFX>
+constexpr bool kPrefillDma = !KV8 && !PFX;
+
+// s_waitcnt immediate that waits until at most n vector memory operations
+// of this wave are outstanding (n <= 15), leaving the other counters free.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 15, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+// 16 bytes from global address g to LDS: lane l of the wave writes
+// lds_wave + 16 l (lds_wave must be the same in every lane).
+__device__ __forceinline__ void load_to_lds16(const void* g, void* lds_wave) {
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(g), (lds_void_ptr)(lds_wave), 16, 0, 0);
+}
 
 // A thread's share of one prefill chunk on its way to LDS.
 template <int PER>
@@ -1279,7 +1304,9 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
   constexpr int CPB = 64 / BPC;                         // chunks per batch of table entries
   // one LDS buffer: K then V (16-bit), or K codes, V codes and 64 scales (INT8)
   constexpr int BUF = KV8 ? CK8 * 16 + CV8 * 8 + 64 * 4 : 2 * CV * 16;
-  static_assert(2 * BUF == PrefillLds<D, KV8>::kBytes, "LDS size of the prefill pass");
+  constexpr bool DMA = kPrefillDma<KV8, PFX>;
+  static_assert(PrefillLds<D, KV8, DMA>::kBufs * BUF == PrefillLds<D, KV8, DMA>::kBytes,
+                "LDS size of the prefill pass");
   auto lk = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF); };
   auto lv = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF + CV * 16); };
   auto lk8 = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF); };
@@ -1518,7 +1545,7 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const int tau = 16 * t + i, j = 4 * kk + g4;
-          kop[t][kk] = lk(buf)[tau * XV + (j ^ (tau % XV))];
+          kop[t][kk] = DMA ? lk(buf)[j * kChunk + tau] : lk(buf)[tau * XV + (j ^ (tau % XV))];
         }
 #pragma unroll
       for (int mm = 0; mm < MM; ++mm) {
@@ -1671,6 +1698,65 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
     }
   };
 
+  if constexpr (DMA) {
+    // Chunk k goes from global memory straight into LDS buffer k % 4, each
+    // lane's 16-byte vector to its own place: instruction r of wave w fills
+    // vectors 64 (NW r + w) .. +63 of the buffer's K part and of its V part.
+    // K is stored x-vector major (vector (token tau, x-vector j) at j * 32 +
+    // tau): 16 lanes of an operand read take 16 consecutive vectors, and the
+    // lanes of a load instruction read 32 consecutive tokens of an x-vector
+    // (256 contiguous bytes per block).  V keeps the swizzled order of the
+    // register-staged path.
+    auto dma = [&](int k, int buf) {
+      __builtin_amdgcn_s_setprio(2);
+      if (k > 0 && k % CPB == 0) load_batch(k);
+      const int e = (k % CPB) * BPC;
+      int b[BPC];
+#pragma unroll
+      for (int j = 0; j < BPC; ++j) b[j] = __builtin_amdgcn_readlane(tbl, e + j);
+      const int r0 = BS > kChunk ? (t_begin + k * kChunk) % BS : 0;
+      auto at = [&](int tau, int64_t& off, int& row) {
+        const int id = pick_block<BPC>(b, tau / BS);
+        off = (int64_t)id * blk_stride + head_off;
+        row = BS >= kChunk ? r0 + tau : tau % BS;
+      };
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int base = 64 * (NW * r + w);  // first vector of the instruction
+        const int u = base + lane;
+        int64_t off;
+        int row;
+        at(u % kChunk, off, row);            // K: x-vector u / 32, token u % 32
+        load_to_lds16(kc + off + ((u / kChunk) * BS + row) * 8, lk(buf) + base);
+        const int d = u >> 2, qd = (u & 3) ^ ((d >> 1) & 3);
+        at(8 * qd, off, row);                // V: channel d, tokens 8 qd .. +8
+        load_to_lds16(vc + off + d * BS + row, lv(buf) + base);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    };
+    // Three chunks in flight while one is computed.  At step k the wave
+    // waits for its own loads of chunk k (in-order completion: the loads of
+    // chunks k + 1 and k + 2, 2 PER each, may stay outstanding), the barrier
+    // then covers every wave's loads of chunk k and every wave's reads of
+    // buffer (k - 1) % 4 in step k - 1, which chunk k + 3 then overwrites.
+    // Every wave takes every barrier (n_chunks is the workgroup's).
+    // The first three chunks are issued unconditionally (a chunk past
+    // n_chunks reads block 0 into a buffer no step reads), so that the
+    // compiler knows how many loads follow q's and does not wait for them
+    // all before the first step.
+    constexpr int PC = 2 * PER;  // load instructions per chunk and thread
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dma(j, j);
+    for (int k = 0; k < n_chunks; ++k) {
+      if (k + 2 < n_chunks) wait_vmcnt<2 * PC>();
+      else if (k + 1 < n_chunks) wait_vmcnt<PC>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (k + 3 < n_chunks) dma(k + 3, (k + 3) & 3);
+      if (k < n_mine) compute(k, k & 3);
+    }
+    wait_vmcnt<0>();  // no load may still write this workgroup's LDS when it ends
+  } else {
   // Chunk k is computed from buffer k % 2 while chunks k + 1 (in registers)
   // and k + 2 (being loaded) are in flight; the barrier after each step makes
   // the next chunk visible and frees the buffer just read.  Every wave takes
@@ -1690,6 +1776,7 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
     if (k + 1 < n_mine) compute(k + 1, 1);
     if (k + 2 < n_chunks) swrite(0, st_a);
     __syncthreads();
+  }
   }
 
 #pragma unroll
@@ -1726,7 +1813,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
     int NB, int max_blocks, int max_ctx, int max_q, int num_rows, float scale_log2,
     float* __restrict__ ws_acc, float* __restrict__ ws_ml, int P, int max_parts,
     const int32_t* __restrict__ grp_len) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[PrefillLds<D, KV8>::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[PrefillLds<D, KV8, kPrefillDma<KV8, PFX>>::kBytes];
   prefill_lds_body<Ty, D, BS, NW, NC, KV8, PFX>(blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x,
                                                 gridDim.y, gridDim.z, lds_raw, out, q, kcv, vcv, tables, lens, qstart, Hq, Hkv, G, NB, max_blocks, max_ctx, max_q,
       num_rows, scale_log2, ws_acc, ws_ml, P, max_parts, grp_len);
