@@ -1720,17 +1720,22 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
         off = (int64_t)id * blk_stride + head_off;
         row = BS >= kChunk ? r0 + tau : tau % BS;
       };
+      // Vector u = 64 (NW r + w) + lane of instruction r: K x-vector u / 32 of
+      // token u % 32 = lane % 32; V channel d = u / 4 and token group qd =
+      // (u % 4) ^ ((d / 2) % 4), which is (lane % 4) ^ ((lane / 8) % 4) for
+      // every r.  So a lane's K token and V token group, and their blocks,
+      // are the same in all its instructions of a chunk.
+      int64_t ok, ov;
+      int rk, rv;
+      at(lane & (kChunk - 1), ok, rk);
+      at(8 * ((lane & 3) ^ ((lane >> 3) & 3)), ov, rv);
+      const Elem* ksrc = kc + ok + rk * 8 + (lane >> 5) * BS * 8;
+      const Elem* vsrc = vc + ov + rv + (lane >> 2) * BS;
 #pragma unroll
       for (int r = 0; r < PER; ++r) {
         const int base = 64 * (NW * r + w);  // first vector of the instruction
-        const int u = base + lane;
-        int64_t off;
-        int row;
-        at(u % kChunk, off, row);            // K: x-vector u / 32, token u % 32
-        load_to_lds16(kc + off + ((u / kChunk) * BS + row) * 8, lk(buf) + base);
-        const int d = u >> 2, qd = (u & 3) ^ ((d >> 1) & 3);
-        at(8 * qd, off, row);                // V: channel d, tokens 8 qd .. +8
-        load_to_lds16(vc + off + d * BS + row, lv(buf) + base);
+        load_to_lds16(ksrc + (int64_t)(2 * (NW * r + w)) * BS * 8, lk(buf) + base);
+        load_to_lds16(vsrc + (int64_t)(16 * (NW * r + w)) * BS, lv(buf) + base);
       }
       __builtin_amdgcn_s_setprio(0);
     };
