@@ -1209,10 +1209,10 @@ struct PrefillLds {
   static constexpr int kBytes = kBufs * kBuf;
 };
 
-// Direct global-to-LDS loads for the prefill pass of 16-bit caches (not the
-// shared-prefix pass, which shares its launch with decode workgroups).
+// Direct global-to-LDS loads for the prefill pass (not the shared-prefix
+// pass, which shares its launch with decode workgroups).
 template <bool KV8, bool PFX>
-constexpr bool kPrefillDma = !KV8 && !PFX;
+constexpr bool kPrefillDma = !PFX;
 
 // s_waitcnt immediate that waits until at most n vector memory operations
 // of this wave are outstanding (n <= 15), leaving the other counters free.
@@ -1229,6 +1229,33 @@ typedef __attribute__((address_space(1))) void* global_void_ptr;
 // lds_wave + 16 l (lds_wave must be the same in every lane).
 __device__ __forceinline__ void load_to_lds16(const void* g, void* lds_wave) {
   __builtin_amdgcn_global_load_lds((global_void_ptr)(g), (lds_void_ptr)(lds_wave), 16, 0, 0);
+}
+
+// 4 bytes from global address g to LDS: lane l writes lds_wave + 4 l.
+__device__ __forceinline__ void load_to_lds4(const void* g, void* lds_wave) {
+  __builtin_amdgcn_global_load_lds((global_void_ptr)(g), (lds_void_ptr)(lds_wave), 4, 0, 0);
+}
+
+// wait_vmcnt for a wave-uniform count n (0 <= n <= 15).
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<15>(); break;
+  }
 }
 
 // A thread's share of one prefill chunk on its way to LDS.
@@ -1296,6 +1323,8 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
   constexpr int CV8 = D * 4;           // INT8: 8-byte V runs of a chunk
   static_assert(!KV8 || (CK8 <= 64 * NW && CV8 % (64 * NW) == 0), "INT8 chunk split over the threads");
   constexpr int PV8 = CV8 / (64 * NW);  // INT8: V runs each thread moves per chunk
+  constexpr int RV8 = 2 * CV8 / (64 * NW);  // INT8: 4-byte V loads per thread and chunk (straight to LDS)
+  static_assert(!KV8 || (CK8 % 64 == 0 && 2 * CV8 == RV8 * 64 * NW), "INT8 LDS loads");
   constexpr int TILE = KV8 ? I8Tile<D, BS>::kBytes : D * BS;  // elements (16-bit) or bytes (INT8)
   using Elem = typename std::conditional<KV8, uint8_t, uint16_t>::type;
   const Elem* kc = reinterpret_cast<const Elem*>(kcv);
@@ -1569,7 +1598,7 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
 #pragma unroll
         for (int k2 = 0; k2 < KK / 2; ++k2) {
           const int tau = 16 * t + i, j = 4 * k2 + g4;
-          kv8[t][k2] = lk8(buf)[tau * XV8 + (j ^ (tau % XV8))];
+          kv8[t][k2] = DMA ? lk8(buf)[j * kChunk + tau] : lk8(buf)[tau * XV8 + (j ^ (tau % XV8))];
         }
 #pragma unroll
       for (int mm = 0; mm < MM; ++mm) {
@@ -1720,22 +1749,52 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
         off = (int64_t)id * blk_stride + head_off;
         row = BS >= kChunk ? r0 + tau : tau % BS;
       };
-      // Vector u = 64 (NW r + w) + lane of instruction r: K x-vector u / 32 of
-      // token u % 32 = lane % 32; V channel d = u / 4 and token group qd =
-      // (u % 4) ^ ((d / 2) % 4), which is (lane % 4) ^ ((lane / 8) % 4) for
-      // every r.  So a lane's K token and V token group, and their blocks,
-      // are the same in all its instructions of a chunk.
-      int64_t ok, ov;
-      int rk, rv;
-      at(lane & (kChunk - 1), ok, rk);
-      at(8 * ((lane & 3) ^ ((lane >> 3) & 3)), ov, rv);
-      const Elem* ksrc = kc + ok + rk * 8 + (lane >> 5) * BS * 8;
-      const Elem* vsrc = vc + ov + rv + (lane >> 2) * BS;
+      if constexpr (!KV8) {
+        // Vector u = 64 (NW r + w) + lane of instruction r: K x-vector u / 32
+        // of token u % 32 = lane % 32; V channel d = u / 4 and token group qd
+        // = (u % 4) ^ ((d / 2) % 4), which is (lane % 4) ^ ((lane / 8) % 4)
+        // for every r.  So a lane's K token and V token group, and their
+        // blocks, are the same in all its instructions of a chunk.
+        int64_t ok, ov;
+        int rk, rv;
+        at(lane & (kChunk - 1), ok, rk);
+        at(8 * ((lane & 3) ^ ((lane >> 3) & 3)), ov, rv);
+        const Elem* ksrc = kc + ok + rk * 8 + (lane >> 5) * BS * 8;
+        const Elem* vsrc = vc + ov + rv + (lane >> 2) * BS;
 #pragma unroll
-      for (int r = 0; r < PER; ++r) {
-        const int base = 64 * (NW * r + w);  // first vector of the instruction
-        load_to_lds16(ksrc + (int64_t)(2 * (NW * r + w)) * BS * 8, lk(buf) + base);
-        load_to_lds16(vsrc + (int64_t)(16 * (NW * r + w)) * BS, lv(buf) + base);
+        for (int r = 0; r < PER; ++r) {
+          const int base = 64 * (NW * r + w);  // first vector of the instruction
+          load_to_lds16(ksrc + (int64_t)(2 * (NW * r + w)) * BS * 8, lk(buf) + base);
+          load_to_lds16(vsrc + (int64_t)(16 * (NW * r + w)) * BS, lv(buf) + base);
+        }
+      } else {
+        // K codes: vector u = 64 w + lane (waves w < CK8 / 64), x-vector u / 32
+        // of token lane % 32, stored x-vector major like the 16-bit K.
+        int64_t off;
+        int row;
+        if (w < CK8 / 64) {
+          at(lane & (kChunk - 1), off, row);
+          load_to_lds16(kc + off + (((64 * w + lane) >> 5) * BS + row) * 16, lk8(buf) + 64 * w);
+        }
+        // V codes in 4-byte halves of the 8-byte runs: dword v = 64 X + lane
+        // (X = NW r + w) of the buffer's V part is half v % 2 of run v / 2,
+        // which is channel d = run / 4, token group (run % 4) ^ ((d / 4) % 4)
+        // (the swizzled order the operand reads expect).
+#pragma unroll
+        for (int r = 0; r < RV8; ++r) {
+          const int X = NW * r + w;
+          const int run = 32 * X + (lane >> 1);
+          const int d = run >> 2, qd = (run & 3) ^ ((d >> 2) & 3);
+          at(8 * qd, off, row);
+          load_to_lds4(vc + off + d * BS + row + 4 * (lane & 1),
+                       reinterpret_cast<uint8_t*>(lv8(buf)) + 256 * X);
+        }
+        // scales (wave 0): lane l < 32 the K scale of token l, else the V
+        // scale of token l - 32
+        if (w == 0) {
+          at(lane & (kChunk - 1), off, row);
+          load_to_lds4((lane < 32 ? kc : vc) + off + I8Tile<D, BS>::kScales + 4 * row, lsc(buf));
+        }
       }
       __builtin_amdgcn_s_setprio(0);
     };
@@ -1749,12 +1808,13 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
     // n_chunks reads block 0 into a buffer no step reads), so that the
     // compiler knows how many loads follow q's and does not wait for them
     // all before the first step.
-    constexpr int PC = 2 * PER;  // load instructions per chunk and thread
+    // load instructions per chunk of this wave
+    const int pc = KV8 ? (w < CK8 / 64 ? 1 : 0) + RV8 + (w == 0 ? 1 : 0) : 2 * PER;
 #pragma unroll
     for (int j = 0; j < 3; ++j) dma(j, j);
     for (int k = 0; k < n_chunks; ++k) {
-      if (k + 2 < n_chunks) wait_vmcnt<2 * PC>();
-      else if (k + 1 < n_chunks) wait_vmcnt<PC>();
+      if (k + 2 < n_chunks) wait_vmcnt_upto(2 * pc);
+      else if (k + 1 < n_chunks) wait_vmcnt_upto(pc);
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
       if (k + 3 < n_chunks) dma(k + 3, (k + 3) & 3);
@@ -1827,8 +1887,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
 // Waves per workgroup of the 16-bit kernel (measured best on MI355X among 1,
 // 2, 4 and 8 for the workloads of the tests and the benchmark).
 constexpr int kWaves = 4;
-// Column groups of 16 slots per wave of prefill_lds_kernel over 16-bit caches
-// (INT8 caches take one, so that the widened operands fit 3 waves per SIMD).
+// Column groups of 16 slots per wave of prefill_lds_kernel (the shared-prefix
+// pass over INT8 caches, which stages its chunks through registers, takes one,
+// so that the widened operands fit 3 waves per SIMD).
 constexpr int kLdsGroups = 2;
 
 // ----------------------------------------------------------------------------
@@ -2290,9 +2351,11 @@ void launch_fused_dims(const pa_decode_args* a, const Plan& pl, float* wa, float
 template <typename Ty, int D, int BS, int NW, bool KV8>
 void launch_prefill(const pa_prefill_args* a, hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
-  // K/V (or INT8 codes and scales) staged through LDS, 16 * NC slots per wave
-  // (INT8: one column group, so that the widened operands fit 2 waves per SIMD)
-  constexpr int NC = KV8 ? 1 : kLdsGroups;
+  // K/V (or INT8 codes and scales) loaded straight into LDS, 16 * NC slots
+  // per wave.  INT8 takes two column groups too: without the register
+  // staging they fit in 238 VGPRs with no spill (measured on MI355X, chunked
+  // prefill at LLaMA-13B shape: 299 -> 262 us against one column group).
+  constexpr int NC = kLdsGroups;
   const int64_t tiles = ((int64_t)a->max_query_len * G + 16 * NC * NW - 1) / (16 * NC * NW);
   dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
   prefill_lds_kernel<Ty, D, BS, NW, NC, KV8, false><<<grid, 64 * NW, 0, st>>>(
