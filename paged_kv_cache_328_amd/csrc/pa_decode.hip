@@ -1887,10 +1887,17 @@ __global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
 // Waves per workgroup of the 16-bit kernel (measured best on MI355X among 1,
 // 2, 4 and 8 for the workloads of the tests and the benchmark).
 constexpr int kWaves = 4;
-// Column groups of 16 slots per wave of prefill_lds_kernel (the shared-prefix
-// pass over INT8 caches, which stages its chunks through registers, takes one,
-// so that the widened operands fit 3 waves per SIMD).
+// Column groups of 16 slots per wave in the shared-prefix pass, which stages
+// its chunks through registers (INT8 caches take one, so that the widened
+// operands fit 3 waves per SIMD).
 constexpr int kLdsGroups = 2;
+// Column groups per wave of the prefill pass proper, whose chunks go straight
+// to LDS.  Measured on MI355X (chunked prefill at LLaMA-13B shape): 16-bit
+// caches 176.9 -> 171.6 us with three groups (256 VGPRs, still 2 waves per
+// SIMD, although 512-row chunks then fill 3 tiles of 192 slots); INT8 caches
+// 264 -> 359 us with three (314 registers, 1 wave per SIMD), so they keep two.
+template <bool KV8>
+constexpr int kPrefillGroups = KV8 ? 2 : 3;
 
 // ----------------------------------------------------------------------------
 // pa_decode_prefix in one launch.  The shared-prefix pass and the members'
@@ -2352,10 +2359,10 @@ template <typename Ty, int D, int BS, int NW, bool KV8>
 void launch_prefill(const pa_prefill_args* a, hipStream_t st) {
   const int G = a->num_q_heads / a->num_kv_heads;
   // K/V (or INT8 codes and scales) loaded straight into LDS, 16 * NC slots
-  // per wave.  INT8 takes two column groups too: without the register
-  // staging they fit in 238 VGPRs with no spill (measured on MI355X, chunked
-  // prefill at LLaMA-13B shape: 299 -> 262 us against one column group).
-  constexpr int NC = kLdsGroups;
+  // per wave.  INT8 takes two column groups: without the register staging
+  // they fit in 238 VGPRs with no spill (measured on MI355X, chunked prefill
+  // at LLaMA-13B shape: 299 -> 262 us against one column group).
+  constexpr int NC = kPrefillGroups<KV8>;
   const int64_t tiles = ((int64_t)a->max_query_len * G + 16 * NC * NW - 1) / (16 * NC * NW);
   dim3 grid((unsigned)tiles, (unsigned)a->num_kv_heads, (unsigned)a->num_seqs);
   prefill_lds_kernel<Ty, D, BS, NW, NC, KV8, false><<<grid, 64 * NW, 0, st>>>(
