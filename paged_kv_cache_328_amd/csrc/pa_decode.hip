@@ -46,7 +46,7 @@
 // 动态负载均衡"); each wave keeps its own running (max, sum, output) and the
 // waves are merged through LDS at the end.
 //
-// Prefill: one workgroup per (tile of 64 or 128 (row, head) slots, KV head,
+// Prefill: one workgroup per (tile of 64 NC (row, head) slots, KV head,
 // sequence) walks the keys in 32-token chunks staged through LDS; every wave
 // computes its own slots' columns against each staged chunk.
 //
@@ -1087,10 +1087,11 @@ __device__ __forceinline__ void decode_mfma_body(int bx, int by, int bz, float* 
   };
 
   // Chunk loop over the wave's chunks w, w + NW, ... of the partition.
-  // 16-bit caches keep the next chunk in flight; INT8 caches load one chunk
-  // at a time (measured on MI355X: with half the bytes per chunk, the
-  // look-ahead made the step slower; without it the kernel needs fewer
-  // registers and more waves fit).
+  // 16-bit caches keep the next chunk in flight in a second register set;
+  // INT8 caches (block sizes up to 32) keep one register set and load the
+  // next chunk's K and V halves as the products free them (measured on
+  // MI355X: with half the bytes per chunk, a second register set made the
+  // INT8 step slower; with one the kernel fits 3 waves per SIMD).
   const int n_mine = w < n_chunks ? (n_chunks - w + NW - 1) / NW : 0;
   auto t0_of = [&](int k) { return t_begin + chunk_of(k) * kChunk; };
   if constexpr (kSkewWalk<KV8, VALU, BS>) wd.walk_skew(n_mine, t0_of, block_ids, cc, skip);
@@ -1274,18 +1275,24 @@ struct StageI8 {
 // Paged prefill with K/V staged through LDS.  A workgroup of
 // NW waves takes 16 * NC * NW (row, head) slots of one sequence and KV head;
 // wave w owns slots sb .. sb + 16*NC - 1 (NC column groups of 16).  The
-// workgroup walks the keys in 32-token chunks: all threads load a chunk's K
-// and V (16-byte vectors in the pool's order, coalesced) into registers,
-// store them into one of two LDS buffers, and every wave reads its matrix-core
-// operands from there, so each K/V byte crosses L1 once per workgroup rather
-// than once per wave.  Two chunks are in flight while one is computed.
-// The LDS order is swizzled so that the operand reads (16 bytes per lane,
-// 16 lanes on 16 tokens or channels) hit distinct banks:
-//   K vector (token tau, x-vector j) at tau * XV + (j ^ (tau % XV)),
+// workgroup walks the keys in 32-token chunks, stages each chunk's K and V
+// in LDS, and every wave reads its matrix-core operands from there, so each
+// K/V byte crosses L1 once per workgroup rather than once per wave.  Staging:
+//   - the prefill pass proper (DMA): the chunk goes from global memory
+//     straight into one of four LDS buffers (global_load_lds), three chunks
+//     in flight while one is computed;
+//   - the shared-prefix pass: all threads load a chunk (16-byte vectors in
+//     the pool's order, coalesced) into registers and store it into one of
+//     two LDS buffers; two chunks in flight while one is computed.
+// The LDS order makes the operand reads (16 bytes per lane, 16 lanes on 16
+// tokens or channels) hit distinct banks:
+//   K vector (token tau, x-vector j) at j * 32 + tau (DMA) or
+//     tau * XV + (j ^ (tau % XV)) (register staging),
 //   V vector (channel d, tokens 8*qd..+8) at d * 4 + (qd ^ ((d / 2) % 4)).
 // INT8 caches (KV8): a chunk is its K codes (16-byte x-vectors, 4 KiB at
 // D = 128), its V codes (8-byte runs of 8 tokens, 4 KiB) and its 64 scales;
-//   K vector (token tau, x-vector j) at tau * XV8 + (j ^ (tau % XV8)),
+//   K vector (token tau, x-vector j) at j * 32 + tau (DMA) or
+//     tau * XV8 + (j ^ (tau % XV8)) (register staging),
 //   V run (channel d, tokens 8*qd..+8) at d * 4 + (qd ^ ((d / 4) % 4)),
 // and the codes are widened to the query type as the operands are read.
 // Arithmetic per column as in decode_mfma_kernel: base-2 online softmax with
@@ -1293,7 +1300,7 @@ struct StageI8 {
 // element type for the PV product.
 // ----------------------------------------------------------------------------
 // Body of the prefill pass for the workgroup at grid position (bx, by, bz) of
-// a (gx, gy, gz) grid; `lds_raw` holds PrefillLds<D, KV8>::kBytes bytes.
+// a (gx, gy, gz) grid; `lds_raw` holds PrefillLds<D, KV8, DMA>::kBytes bytes.
 // PFX: the shared-prefix pass of pa_decode_prefix instead (run by
 // prefix_suffix_kernel).  Grid x = slot tiles of a group's (member, head)
 // slots, y = partition of the prefix (P tokens), z = group * Hkv + KV head;

@@ -137,3 +137,19 @@ def test_one_row_chunks_match_decode():
     a = wl.storage_to_f32(pre, "bf16")
     b = wl.storage_to_f32(to_host(out, "bf16"), "bf16")
     assert float(np.max(np.abs(a - b))) <= 2e-2
+
+
+@pytest.mark.parametrize("kv", [None, "i8"])
+@pytest.mark.parametrize("S", [64, 65])
+def test_prefill_rank_order_batches(kv, S):
+    """The prefill grid takes sequences longest context first, ranked in one
+    wave from the lengths: 64 sequences is the most it ranks (with ties,
+    which keep sequence order), 65 keep the grid's order.  Either way every
+    row matches the oracle."""
+    rng = np.random.default_rng(3600 + S)
+    priors = rng.integers(0, 60, size=S).tolist()
+    chunks = rng.integers(1, 40, size=S).tolist()
+    for s in range(0, S, 7):  # equal contexts: ties in the ranking
+        priors[s], chunks[s] = 20, 12
+    case = wl.prefill_case(3600 + S, priors, chunks, 8, 2, 64, 16, "bf16", kv_dtype=kv)
+    run_prefill(case, f"rank order S={S} kv={kv}")
