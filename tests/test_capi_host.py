@@ -469,3 +469,23 @@ def test_prefill_and_prefix_validation(L):
     f = _args(dtype=pa.PA_F32)
     g.num_groups, g.max_group_size = 1, 1
     assert L.pa_decode_prefix(f, ctypes.byref(g), None) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_probe_read_rejects_bad_arguments(L):
+    """pa_probe_read validates before any launch: range sizes that are not a
+    positive multiple of 16 up to 16384, a ranges-in-flight other than 1, 2
+    or 4, a negative grid cap or range count, and (with ranges to read)
+    null or misaligned pointers; zero ranges is a no-op."""
+    ok = dict(a=None, b=None, buf=1 << 20, offs=None, n=0, rb=4096, rif=2, wg=0, sink=None)
+
+    def call(**over):
+        a = dict(ok, **over)
+        return L.pa_probe_read(a["a"], a["b"], a["buf"], a["offs"], a["n"], a["rb"], a["rif"], a["wg"],
+                               a["sink"], None)
+
+    assert call() == pa.PA_OK
+    for over in (dict(rb=0), dict(rb=24), dict(rb=16400), dict(rif=3), dict(wg=-1), dict(n=-1)):
+        assert call(**over) == pa.PA_ERR_INVALID, over
+    assert call(n=1) == pa.PA_ERR_INVALID           # null buffers, offsets and sink
+    assert call(n=1, a=8, b=32, offs=64, sink=128) == pa.PA_ERR_INVALID  # a not 16-byte aligned
+    assert call(n=1, a=16, b=40, offs=64, sink=128) == pa.PA_ERR_INVALID  # b not 16-byte aligned
