@@ -99,7 +99,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
-              "(the kernels shard by sequence / KV head with no exchange; see the design notes)",
+              "(one process drives one GPU; sharding sequences or KV heads over several GPUs "
+              "is not built)",
               file=sys.stderr)
         sys.exit(2)
     import torch

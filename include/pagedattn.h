@@ -173,9 +173,11 @@ typedef struct pa_decode_args {
    * caches are 16-bit: PA_PRODUCTS_MATRIX (the gfx950 matrix cores, the
    * query heads of a KV head as the columns of the tile), PA_PRODUCTS_VALU
    * (packed dot products on the vector ALU), or PA_PRODUCTS_AUTO (the
-   * library's choice, measured: see the design notes).  With more query heads per KV
-   * head the matrix cores always take the products; PA_PRODUCTS_VALU there,
-   * or with INT8 or fp32 caches, returns PA_ERR_UNSUPPORTED.  The results
+   * library's choice: the matrix cores, which measured on MI355X as fast as
+   * the vector ALU or up to 2% faster at every block size).  With more query
+   * heads per KV head the matrix cores always take the products;
+   * PA_PRODUCTS_VALU there, or with INT8 or fp32 caches, returns
+   * PA_ERR_UNSUPPORTED.  The results
    * agree within the same error bound (same rounding of the weights). */
   int32_t products;
 } pa_decode_args;

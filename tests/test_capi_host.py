@@ -489,3 +489,17 @@ def test_probe_read_rejects_bad_arguments(L):
     assert call(n=1) == pa.PA_ERR_INVALID           # null buffers, offsets and sink
     assert call(n=1, a=8, b=32, offs=64, sink=128) == pa.PA_ERR_INVALID  # a not 16-byte aligned
     assert call(n=1, a=16, b=40, offs=64, sink=128) == pa.PA_ERR_INVALID  # b not 16-byte aligned
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py drives one GPU: any other --gpus exits with status 2 and says
+    why, before it touches torch or the library."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
