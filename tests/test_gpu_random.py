@@ -113,3 +113,39 @@ def test_random_configuration(seed):
     else:
         want = oracle.decode(q, kc, vc, tables, lens_np, case.scale, dtype, num_threads=16, bound=True)
     check_attention(got, want, dtype, label, kv_scale_min=i8_scale_min(vc, D, BS) if i8 else None)
+
+
+def draw_prefill(seed):
+    rng = np.random.default_rng([2025, seed])
+    S = int(rng.integers(1, 71))
+    Hkv = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    D = int(rng.choice([64, 128]))
+    BS = int(rng.choice([8, 16, 32, 64]))
+    dtype = str(rng.choice(["f16", "bf16"]))
+    kv = "i8" if rng.random() < 0.35 else None
+    priors = rng.integers(0, 400, size=S)
+    chunks = rng.integers(0, 200, size=S)
+    priors[rng.random(S) < 0.2] = 0
+    tot = int((priors + chunks).sum()) * Hkv
+    if tot > 120_000:  # keep a case's pools and oracle run small
+        f = 120_000 / tot
+        priors, chunks = (priors * f).astype(int), (chunks * f).astype(int)
+    if chunks.sum() == 0:
+        chunks[0] = 1
+    return dict(S=S, Hkv=Hkv, G=G, D=D, BS=BS, dtype=dtype, kv=kv,
+                priors=[int(x) for x in priors], chunks=[int(x) for x in chunks])
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_prefill_configuration(seed):
+    """pa_prefill over drawn batches (1..70 sequences, so both the ranked and
+    the unranked grid order), chunks of 0..199 rows on 0..399 earlier tokens,
+    1..4 KV heads with 1..16 query heads each, both head_dims, every block
+    size, f16/bf16, 16-bit or INT8 caches."""
+    from tests.test_gpu_prefill import run_prefill
+    c = draw_prefill(seed)
+    case = wl.prefill_case(8000 + seed, c["priors"], c["chunks"], c["G"] * c["Hkv"], c["Hkv"], c["D"],
+                           c["BS"], c["dtype"], kv_dtype=c["kv"])
+    run_prefill(case, f"random prefill seed {seed}: S={c['S']} Hkv={c['Hkv']} G={c['G']} D={c['D']} "
+                      f"BS={c['BS']} {c['dtype']} kv={c['kv']}")
