@@ -1201,13 +1201,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(KV8 ? 3
 
 // LDS of the prefill pass: two chunk buffers, each a 32-token chunk's K and
 // V (16-bit), or its K codes, V codes and 64 scales (INT8).
-// With DMA (16-bit caches, prefill proper) the chunks go from global memory
-// straight to LDS, into four buffers.
+// With DMA (the prefill pass proper) the chunks go from global memory
+// straight to LDS, into four buffers; INT8 chunks are then widened into two
+// more buffers of 16-bit K and V.
 template <int D, bool KV8, bool DMA = false>
 struct PrefillLds {
   static constexpr int kBuf = KV8 ? kChunk * (D / 16) * 16 + D * 4 * 8 + 64 * 4 : 2 * kChunk * (D / 8) * 16;
   static constexpr int kBufs = DMA ? 4 : 2;
-  static constexpr int kBytes = kBufs * kBuf;
+  // INT8 chunks loaded straight to LDS are widened once per workgroup into
+  // one of two buffers of 16-bit K and V
+  static constexpr int kConvBuf = KV8 && DMA ? 2 * kChunk * (D / 8) * 16 : 0;
+  static constexpr int kBytes = kBufs * kBuf + 2 * kConvBuf;
 };
 
 // Direct global-to-LDS loads for the prefill pass (not the shared-prefix
@@ -1341,8 +1345,19 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
   // one LDS buffer: K then V (16-bit), or K codes, V codes and 64 scales (INT8)
   constexpr int BUF = KV8 ? CK8 * 16 + CV8 * 8 + 64 * 4 : 2 * CV * 16;
   constexpr bool DMA = kPrefillDma<KV8, PFX>;
-  static_assert(PrefillLds<D, KV8, DMA>::kBufs * BUF == PrefillLds<D, KV8, DMA>::kBytes,
+  // INT8 chunks loaded straight to LDS: widened once per workgroup (each
+  // thread a share of the chunk) into conversion buffer k % 2, in the 16-bit
+  // LDS order, from which every wave reads 16-bit operands
+  constexpr bool CONV = KV8 && DMA;
+  constexpr int CBUF = PrefillLds<D, KV8, DMA>::kConvBuf;
+  static_assert(PrefillLds<D, KV8, DMA>::kBufs * BUF + 2 * CBUF == PrefillLds<D, KV8, DMA>::kBytes,
                 "LDS size of the prefill pass");
+  auto lck = [&](int c) {
+    return reinterpret_cast<u32x4*>(lds_raw + PrefillLds<D, KV8, DMA>::kBufs * BUF + c * CBUF);
+  };
+  auto lcv = [&](int c) {
+    return reinterpret_cast<u32x4*>(lds_raw + PrefillLds<D, KV8, DMA>::kBufs * BUF + c * CBUF + CV * 16);
+  };
   auto lk = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF); };
   auto lv = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF + CV * 16); };
   auto lk8 = [&](int buf) { return reinterpret_cast<u32x4*>(lds_raw + buf * BUF); };
@@ -1443,7 +1458,7 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
   // Q^T operand: lane feeds column i, channels 8*m..+8 with m = 4*kk + g4
   // (INT8: 8*(kk/2) + 2*g4 + kk%2, so that one 16-byte code vector feeds two
   // products)
-  auto qchunk = [&](int kk) { return KV8 ? 8 * (kk >> 1) + 2 * g4 + (kk & 1) : 4 * kk + g4; };
+  auto qchunk = [&](int kk) { return KV8 && !CONV ? 8 * (kk >> 1) + 2 * g4 + (kk & 1) : 4 * kk + g4; };
   // The softmax step takes its maximum over the raw products and scales it
   // once, which needs a scale >= 0: a negative scale is moved onto q by
   // flipping its sign bits (exact; every product and sum is negated exactly).
@@ -1575,7 +1590,22 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
     u32x4 kv8[2][KK / 2 > 0 ? KK / 2 : 1];
     u32x2 vv8[MM];
     f32x4 sk[2], sv[2];
-    if constexpr (!KV8) {
+    if constexpr (CONV) {  // widened INT8 codes (finite), scales of the chunk
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kop[t][kk] = lck(buf & 1)[(4 * kk + g4) * kChunk + 16 * t + i];
+#pragma unroll
+      for (int mm = 0; mm < MM; ++mm) {
+        const int d = 16 * mm + i;
+        vop[mm] = lcv(buf & 1)[d * 4 + (g4 ^ ((d >> 1) & 3))];
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sk[t] = *reinterpret_cast<const f32x4*>(lsc(buf) + 16 * t + 4 * g4);
+        sv[t] = *reinterpret_cast<const f32x4*>(lsc(buf) + 32 + 16 * t + 4 * g4);
+      }
+    } else if constexpr (!KV8) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1624,7 +1654,7 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        if constexpr (!KV8) {
+        if constexpr (!KV8 || CONV) {
           s0 = Ty::mma(__builtin_bit_cast(V8, kop[0][kk]), qop[nc][kk], s0);
           s1 = Ty::mma(__builtin_bit_cast(V8, kop[1][kk]), qop[nc][kk], s1);
         } else {  // product kk takes half kk % 2 of code vector kk / 2
@@ -1726,7 +1756,7 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
       const V8 pop = __builtin_bit_cast(V8, pwords);
 #pragma unroll
       for (int mm = 0; mm < MM; ++mm) {
-        if constexpr (!KV8)
+        if constexpr (!KV8 || CONV)
           acc[nc][mm] = Ty::mma(__builtin_bit_cast(V8, vop[mm]), pop, acc[nc][mm]);
         else
           acc[nc][mm] = Ty::mma(__builtin_bit_cast(V8, codes_to_operand<Ty>(vv8[mm])), pop, acc[nc][mm]);
@@ -1819,13 +1849,55 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
     const int pc = KV8 ? (w < CK8 / 64 ? 1 : 0) + RV8 + (w == 0 ? 1 : 0) : 2 * PER;
 #pragma unroll
     for (int j = 0; j < 3; ++j) dma(j, j);
-    for (int k = 0; k < n_chunks; ++k) {
-      if (k + 2 < n_chunks) wait_vmcnt_upto(2 * pc);
-      else if (k + 1 < n_chunks) wait_vmcnt_upto(pc);
+    if constexpr (!CONV) {
+      for (int k = 0; k < n_chunks; ++k) {
+        if (k + 2 < n_chunks) wait_vmcnt_upto(2 * pc);
+        else if (k + 1 < n_chunks) wait_vmcnt_upto(pc);
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (k + 3 < n_chunks) dma(k + 3, (k + 3) & 3);
+        if (k < n_mine) compute(k, k & 3);
+      }
+    } else {
+      // Chunk j's codes (buffer j % 4) widened to 16-bit operands in
+      // conversion buffer j % 2, each thread a share: K code vector g (token
+      // g % 32, channels 16 (g / 32) ..) becomes 16-bit x-vectors 2 (g / 32)
+      // and 2 (g / 32) + 1, V code run g (channel g / 4, token group g % 4)
+      // one 16-bit vector.  The exact small integers feed the matrix cores
+      // as in the per-wave widening; the scales stay in the code buffer.
+      auto convert = [&](int j) {
+        const int cb = j & 3, ob = j & 1;
+        for (int g = tid; g < CK8; g += 64 * NW) {
+          const int tau = g & (kChunk - 1), j8 = g / kChunk;
+          const u32x4 c = lk8(cb)[j8 * kChunk + tau];
+          lck(ob)[2 * j8 * kChunk + tau] = codes_to_operand<Ty>(u32x2{c[0], c[1]});
+          lck(ob)[(2 * j8 + 1) * kChunk + tau] = codes_to_operand<Ty>(u32x2{c[2], c[3]});
+        }
+        for (int g = tid; g < CV8; g += 64 * NW) {
+          const int d = g >> 2, qd = g & 3;
+          lcv(ob)[d * 4 + (qd ^ ((d >> 1) & 3))] = codes_to_operand<Ty>(lv8(cb)[d * 4 + (qd ^ ((d >> 2) & 3))]);
+        }
+      };
+      // Step k: the wave's own loads of chunk k + 1 are done (chunk k + 2's
+      // may stay outstanding) and so are its LDS writes of conversion k;
+      // after the barrier chunk k + 1's codes and chunk k's 16-bit operands
+      // are in LDS for every wave, and nobody reads code buffer (k - 1) % 4
+      // (converted in step k - 2, its scales read in step k - 1) or
+      // conversion buffer (k + 1) % 2 (read in step k - 1) any more.  Every
+      // wave takes every barrier.
+      if (1 < n_chunks) wait_vmcnt_upto(2 * pc);
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      if (k + 3 < n_chunks) dma(k + 3, (k + 3) & 3);
-      if (k < n_mine) compute(k, k & 3);
+      convert(0);
+      for (int k = 0; k < n_chunks; ++k) {
+        if (k + 2 < n_chunks) wait_vmcnt_upto(pc);
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));  // lgkmcnt(0): the conversion's LDS writes
+        __builtin_amdgcn_s_barrier();
+        if (k + 3 < n_chunks) dma(k + 3, (k + 3) & 3);
+        if (k + 1 < n_chunks) convert(k + 1);
+        if (k < n_mine) compute(k, k & 3);
+      }
     }
     wait_vmcnt<0>();  // no load may still write this workgroup's LDS when it ends
   } else {
@@ -1877,8 +1949,11 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
   }
 }
 
+// Two waves per SIMD at least (at most 256 registers): the INT8 kernels at
+// block size 32 would otherwise take 260 and run one wave per SIMD (measured
+// on MI355X: 367 us against 250 us with 12 bytes of spill).
 template <typename Ty, int D, int BS, int NW, int NC, bool KV8, bool PFX>
-__global__ __launch_bounds__(64 * NW) void prefill_lds_kernel(
+__global__ __launch_bounds__(64 * NW, 2) void prefill_lds_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const void* __restrict__ kcv,
     const void* __restrict__ vcv, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, const int32_t* __restrict__ qstart, int Hq, int Hkv, int G,
