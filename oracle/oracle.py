@@ -72,6 +72,20 @@ def lib():
         L.oracle_decode_i8.restype = _I
         L.oracle_decode_i8.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                        ctypes.c_float, _I, _P, _P, _P, _P]
+        L.oracle_fp8_value.restype = ctypes.c_double
+        L.oracle_fp8_value.argtypes = [_I]
+        L.oracle_fp8_encode.restype = _I
+        L.oracle_fp8_encode.argtypes = [ctypes.c_float]
+        L.oracle_quantize_row_fp8.restype = None
+        L.oracle_quantize_row_fp8.argtypes = [_P, _I, _P, _P]
+        L.oracle_write_kv_q8.restype = _I
+        L.oracle_write_kv_q8.argtypes = [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I]
+        L.oracle_decode_q8.restype = _I
+        L.oracle_decode_q8.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                       ctypes.c_float, _I, _P, _P, _P, _P, _I]
+        L.oracle_prefill_q8.restype = _I
+        L.oracle_prefill_q8.argtypes = [_P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                        ctypes.c_float, _I, _P, _P, _P, _P, _I]
         _lib = L
     return _lib
 
@@ -255,6 +269,30 @@ def i8_offsets(b, h, o, d, Hkv, D, BS):
             L.oracle_i8_scale_offset(b, h, o, Hkv, D, BS))
 
 
+# 8-bit code formats of a quantised pool: INT8, or FP8 (E4M3; see the FP8
+# section of pa_oracle.c).  Both share the tile layout and the scales.
+Q8_FORMAT = {"i8": 0, "fp8": 1}
+
+
+def fp8_value(code):
+    """Value of an E4M3 code (NaN for S.1111.111)."""
+    return float(lib().oracle_fp8_value(int(code)))
+
+
+def fp8_encode(r):
+    """E4M3 code of the fp32 value r (nearest, ties to even, saturating)."""
+    return int(lib().oracle_fp8_encode(ctypes.c_float(r)))
+
+
+def quantize_row_fp8(x):
+    """fp32 row -> (E4M3 codes as uint8, fp32 scale)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes = np.empty(x.shape[0], np.uint8)
+    sc = np.empty(1, np.float32)
+    lib().oracle_quantize_row_fp8(_ptr(x), x.shape[0], _ptr(codes), _ptr(sc))
+    return codes, sc[0]
+
+
 def quantize_row(x):
     """fp32 row -> (int8 codes, fp32 scale)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
@@ -264,8 +302,9 @@ def quantize_row(x):
     return codes, sc[0]
 
 
-def write_kv_i8(k_new, v_new, src_dtype, k_pool, v_pool, slot_mapping, D, BS):
-    """Quantising cache write of k_new / v_new [T, Hkv, D] (src_dtype storage)."""
+def write_kv_i8(k_new, v_new, src_dtype, k_pool, v_pool, slot_mapping, D, BS, fmt="i8"):
+    """Quantising cache write of k_new / v_new [T, Hkv, D] (src_dtype storage)
+    into 8-bit pools of code format fmt ("i8" or "fp8")."""
     NB, Hkv = i8_geometry(k_pool, v_pool, D, BS)
     _check(k_new, NP_STORAGE[src_dtype], "k_new")
     _check(v_new, NP_STORAGE[src_dtype], "v_new")
@@ -273,10 +312,10 @@ def write_kv_i8(k_new, v_new, src_dtype, k_pool, v_pool, slot_mapping, D, BS):
     T = slot_mapping.shape[0]
     if k_new.shape != (T, Hkv, D) or v_new.shape != (T, Hkv, D):
         raise ValueError("k_new / v_new must be [T, Hkv, D]")
-    rc = lib().oracle_write_kv_i8(_ptr(k_new), _ptr(v_new), DTYPE_CODE[src_dtype], _ptr(k_pool),
-                                  _ptr(v_pool), _ptr(slot_mapping), T, Hkv, D, BS, NB)
+    rc = lib().oracle_write_kv_q8(_ptr(k_new), _ptr(v_new), DTYPE_CODE[src_dtype], _ptr(k_pool),
+                                  _ptr(v_pool), _ptr(slot_mapping), T, Hkv, D, BS, NB, Q8_FORMAT[fmt])
     if rc != 0:
-        raise ValueError("oracle_write_kv_i8 rejected its arguments")
+        raise ValueError("oracle_write_kv_q8 rejected its arguments")
 
 
 def copy_blocks_i8(k_pool, v_pool, pairs, D, BS):
@@ -289,9 +328,9 @@ def copy_blocks_i8(k_pool, v_pool, pairs, D, BS):
 
 
 def decode_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, scale, D, BS, num_threads=1,
-              bound=False):
-    """Paged decode attention over INT8 pools, fp64 output [S, Hq, D]; with
-    bound=True an Attention."""
+              bound=False, fmt="i8"):
+    """Paged decode attention over 8-bit pools (code format fmt: "i8" or
+    "fp8"), fp64 output [S, Hq, D]; with bound=True an Attention."""
     NB, Hkv = i8_geometry(k_pool, v_pool, D, BS)
     _check(q, NP_STORAGE[q_dtype], "q")
     _check(block_tables, np.int32, "block_tables")
@@ -301,19 +340,19 @@ def decode_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, scale, D, 
         raise ValueError("q head_dim does not match")
     out = np.empty((S, Hq, D), np.float64)
     spread, devmax, lam = _bound_buffers(S, Hq, D, bound)
-    rc = lib().oracle_decode_i8(_ptr(q), DTYPE_CODE[q_dtype], _ptr(k_pool), _ptr(v_pool),
+    rc = lib().oracle_decode_q8(_ptr(q), DTYPE_CODE[q_dtype], _ptr(k_pool), _ptr(v_pool),
                                 _ptr(block_tables), _ptr(context_lens), S, Hq, Hkv, D, BS,
                                 block_tables.shape[1], ctypes.c_float(scale), int(num_threads),
-                                _ptr(out), _opt(spread), _opt(devmax), _opt(lam))
+                                _ptr(out), _opt(spread), _opt(devmax), _opt(lam), Q8_FORMAT[fmt])
     if rc != 0:
-        raise ValueError("oracle_decode_i8 rejected its arguments")
+        raise ValueError("oracle_decode_q8 rejected its arguments")
     return Attention(out, spread, devmax, lam, np.maximum(context_lens, 0)) if bound else out
 
 
 def prefill_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, query_start, scale, D, BS,
-               num_threads=1, bound=False):
-    """Paged (chunked) prefill over INT8 pools, fp64 output [T, Hq, D]; with
-    bound=True an Attention."""
+               num_threads=1, bound=False, fmt="i8"):
+    """Paged (chunked) prefill over 8-bit pools (code format fmt: "i8" or
+    "fp8"), fp64 output [T, Hq, D]; with bound=True an Attention."""
     NB, Hkv = i8_geometry(k_pool, v_pool, D, BS)
     _check(q, NP_STORAGE[q_dtype], "q")
     _check(block_tables, np.int32, "block_tables")
@@ -325,12 +364,13 @@ def prefill_i8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, query_sta
         raise ValueError("q must be [T, Hq, D] with T = query_start[S]")
     out = np.empty((T, Hq, D), np.float64)
     spread, devmax, lam = _bound_buffers(T, Hq, D, bound)
-    rc = lib().oracle_prefill_i8(_ptr(q), DTYPE_CODE[q_dtype], _ptr(k_pool), _ptr(v_pool),
+    rc = lib().oracle_prefill_q8(_ptr(q), DTYPE_CODE[q_dtype], _ptr(k_pool), _ptr(v_pool),
                                  _ptr(block_tables), _ptr(context_lens), _ptr(query_start), S, Hq,
                                  Hkv, D, BS, block_tables.shape[1], ctypes.c_float(scale),
-                                 int(num_threads), _ptr(out), _opt(spread), _opt(devmax), _opt(lam))
+                                 int(num_threads), _ptr(out), _opt(spread), _opt(devmax), _opt(lam),
+                                 Q8_FORMAT[fmt])
     if rc != 0:
-        raise ValueError("oracle_prefill_i8 rejected its arguments")
+        raise ValueError("oracle_prefill_q8 rejected its arguments")
     return Attention(out, spread, devmax, lam, _row_keys(context_lens, query_start)) if bound else out
 
 

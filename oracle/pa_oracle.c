@@ -47,6 +47,8 @@
 #include <string.h>
 
 enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+/* Code formats of 8-bit caches: INT8 and FP8 (E4M3). */
+enum { OR_Q_I8 = 0, OR_Q_FP8 = 1 };
 
 static int elem_bytes(int dtype) { return dtype == OR_F32 ? 4 : 2; }
 
@@ -431,14 +433,65 @@ void oracle_quantize_row(const float* x, int D, int8_t* codes, float* scale) {
   }
 }
 
+/* FP8 caches (the other 8-bit KV format the quantised-block design allows;
+ * kongchang.com, section "量化技术：与PagedAttention正交的显存优化路径", names
+ * lower-precision KV caches as orthogonal to paging).  Reading: the OCP
+ * "E4M3" 8-bit float -- 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits; exponent field 0 holds the subnormals m * 2^-9; no infinities; the
+ * codes S.1111.111 are NaN, so the largest finite magnitude is 1.75 * 2^8 =
+ * 448.  Same tile layout and per-(token, KV head) fp32 scales as INT8:
+ * scale = max|x| / 448 in fp32, code = the E4M3 value nearest to x / scale
+ * (fp32 quotient), ties to an even mantissa, magnitudes of 448 and more
+ * (and NaN) saturated to 448.  parity pins: tests/test_oracle_fp8.py. */
+
+/* Value of an E4M3 code (NaN for S.1111.111). */
+double oracle_fp8_value(int code) {
+  const int sgn = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(1.0 + m / 8.0, e - 7);
+  return sgn ? -v : v;
+}
+
+/* E4M3 code of r: round to nearest, ties to even mantissa, saturating. */
+int oracle_fp8_encode(float r) {
+  const int sgn = signbit(r) ? 0x80 : 0;
+  const double a = fabs((double)r);
+  if (!(a < 448.0)) return sgn | 0x7E;
+  if (a < ldexp(1.0, -6)) /* subnormal grid, step 2^-9; 8 steps is the smallest normal */
+    return sgn | (int)rint(a * 512.0);
+  int e2;
+  frexp(a, &e2); /* a = f * 2^e2, f in [0.5, 1): a in [2^(e2-1), 2^e2) */
+  int E = e2 - 1;
+  double q = rint(ldexp(a, 3 - E)); /* a / 2^(E-3), in [8, 16] */
+  if (q == 16.0) {
+    q = 8.0;
+    E += 1;
+  }
+  return sgn | ((E + 7) << 3) | ((int)q - 8);
+}
+
+/* Quantises x[0..D) (fp32) into E4M3 codes[0..D) and *scale, as stated above. */
+void oracle_quantize_row_fp8(const float* x, int D, uint8_t* codes, float* scale) {
+  float amax = 0.0f;
+  for (int d = 0; d < D; ++d) {
+    float a = fabsf(x[d]);
+    if (a > amax) amax = a;
+  }
+  float s = amax / 448.0f;
+  *scale = s;
+  for (int d = 0; d < D; ++d) codes[d] = s == 0.0f ? 0 : (uint8_t)oracle_fp8_encode(x[d] / s);
+}
+
 /* Quantising cache write: token t's K and V rows of every KV head (k_new,
  * v_new [T, Hkv, D] of src_dtype) go to slot slot_mapping[t] as codes plus
  * scale; negative slots are skipped; a slot past the pool is an error. */
-int oracle_write_kv_i8(const void* k_new, const void* v_new, int src_dtype, uint8_t* k_pool,
+int oracle_write_kv_q8(const void* k_new, const void* v_new, int src_dtype, uint8_t* k_pool,
                        uint8_t* v_pool, const int64_t* slot_mapping, int T, int Hkv, int D,
-                       int BS, int num_blocks) {
+                       int BS, int num_blocks, int fmt) {
   if (src_dtype < OR_F32 || src_dtype > OR_BF16 || T < 0 || Hkv <= 0 || D <= 0 || D % 16 ||
-      BS <= 0)
+      BS <= 0 || (fmt != OR_Q_I8 && fmt != OR_Q_FP8))
     return -1;
   for (int t = 0; t < T; ++t)
     if (slot_mapping[t] >= (int64_t)num_blocks * BS) return -1;
@@ -460,7 +513,8 @@ int oracle_write_kv_i8(const void* k_new, const void* v_new, int src_dtype, uint
         uint8_t* pool = kv == 0 ? k_pool : v_pool;
         for (int d = 0; d < D; ++d) row[d] = load_f32(src, ((int64_t)t * Hkv + h) * D + d, src_dtype);
         float s;
-        oracle_quantize_row(row, D, codes, &s);
+        if (fmt == OR_Q_FP8) oracle_quantize_row_fp8(row, D, (uint8_t*)codes, &s);
+        else oracle_quantize_row(row, D, codes, &s);
         for (int d = 0; d < D; ++d) {
           int64_t off = kv == 0 ? oracle_i8_k_offset(b, h, o, d, Hkv, D, BS)
                                 : oracle_i8_v_offset(b, h, o, d, Hkv, D, BS);
@@ -475,7 +529,14 @@ int oracle_write_kv_i8(const void* k_new, const void* v_new, int src_dtype, uint
   return 0;
 }
 
-/* Block copy of INT8 pools: whole tiles (codes and scales) of every KV head. */
+int oracle_write_kv_i8(const void* k_new, const void* v_new, int src_dtype, uint8_t* k_pool,
+                       uint8_t* v_pool, const int64_t* slot_mapping, int T, int Hkv, int D,
+                       int BS, int num_blocks) {
+  return oracle_write_kv_q8(k_new, v_new, src_dtype, k_pool, v_pool, slot_mapping, T, Hkv, D, BS,
+                            num_blocks, OR_Q_I8);
+}
+
+/* Block copy of INT8 (or FP8) pools: whole tiles (codes and scales) of every KV head. */
 int oracle_copy_blocks_i8(uint8_t* k_pool, uint8_t* v_pool, const int32_t* pairs, int num_pairs,
                           int Hkv, int D, int BS, int num_blocks) {
   if (num_pairs < 0 || Hkv <= 0 || D <= 0 || D % 16 || BS <= 0) return -1;
@@ -492,22 +553,23 @@ int oracle_copy_blocks_i8(uint8_t* k_pool, uint8_t* v_pool, const int32_t* pairs
   return 0;
 }
 
-static double i8_value(const uint8_t* pool, int64_t code_off, int64_t scale_off) {
+static double i8_value(const uint8_t* pool, int64_t code_off, int64_t scale_off, int fmt) {
   float s;
   memcpy(&s, pool + scale_off, sizeof s);
-  return (double)(int8_t)pool[code_off] * (double)s;
+  const double v = fmt == OR_Q_FP8 ? oracle_fp8_value(pool[code_off]) : (double)(int8_t)pool[code_off];
+  return v * (double)s;
 }
 
 /* Decode attention over INT8 pools: the same textbook single-query softmax
  * attention as oracle_decode, on the exact values code * scale (fp64).
  * q is [S, Hq, D] of q_dtype; out is [S, Hq, D] fp64; spread, devmax and lam
  * are oracle_decode's optional bound ingredients, over the same values. */
-int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
+int oracle_decode_q8(const void* q, int q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
                      const int32_t* block_tables, const int32_t* context_lens, int S, int Hq,
                      int Hkv, int D, int BS, int max_blocks, float scale, int num_threads,
-                     double* out, double* spread, double* devmax, double* lam) {
+                     double* out, double* spread, double* devmax, double* lam, int fmt) {
   if (q_dtype < OR_F32 || q_dtype > OR_BF16 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
-      D <= 0 || D % 16 || BS <= 0)
+      D <= 0 || D % 16 || BS <= 0 || (fmt != OR_Q_I8 && fmt != OR_Q_FP8))
     return -1;
   for (int s = 0; s < S; ++s)
     if (context_lens[s] > max_blocks * BS) return -1;
@@ -538,7 +600,7 @@ int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const ui
       double dot = 0.0, mag = 0.0;
       for (int d = 0; d < D; ++d) {
         double qk = load_elem(q, sh * D + d, q_dtype) *
-                    i8_value(k_pool, oracle_i8_k_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+                    i8_value(k_pool, oracle_i8_k_offset(b, g, t % BS, d, Hkv, D, BS), soff, fmt);
         dot += qk;
         mag += fabs(qk);
       }
@@ -557,7 +619,7 @@ int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const ui
       int64_t b = block_of(block_tables, max_blocks, s, t, BS);
       int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
       for (int d = 0; d < D; ++d)
-        o[d] += x[t] * i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+        o[d] += x[t] * i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff, fmt);
     }
     for (int d = 0; d < D; ++d) o[d] /= z;
     if (spread)
@@ -565,7 +627,7 @@ int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const ui
         int64_t b = block_of(block_tables, max_blocks, s, t, BS);
         int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
         for (int d = 0; d < D; ++d) {
-          double dv = fabs(i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff) - o[d]);
+          double dv = fabs(i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff, fmt) - o[d]);
           spread[sh * D + d] += x[t] / z * dv;
           if (dv > devmax[sh * D + d]) devmax[sh * D + d] = dv;
         }
@@ -578,13 +640,13 @@ int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const ui
 /* Paged prefill over INT8 pools: oracle_prefill's causal rows on the exact
  * values code * scale (fp64).  q is [T, Hq, D] of q_dtype; spread, devmax
  * and lam as for oracle_prefill. */
-int oracle_prefill_i8(const void* q, int q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
+int oracle_prefill_q8(const void* q, int q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
                       const int32_t* block_tables, const int32_t* context_lens,
                       const int32_t* query_start, int S, int Hq, int Hkv, int D, int BS,
                       int max_blocks, float scale, int num_threads, double* out,
-                      double* spread, double* devmax, double* lam) {
+                      double* spread, double* devmax, double* lam, int fmt) {
   if (q_dtype < OR_F32 || q_dtype > OR_BF16 || S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv ||
-      D <= 0 || D % 16 || BS <= 0 || query_start[0] != 0)
+      D <= 0 || D % 16 || BS <= 0 || query_start[0] != 0 || (fmt != OR_Q_I8 && fmt != OR_Q_FP8))
     return -1;
   for (int s = 0; s < S; ++s) {
     const int n = query_start[s + 1] - query_start[s];
@@ -623,7 +685,7 @@ int oracle_prefill_i8(const void* q, int q_dtype, const uint8_t* k_pool, const u
       double dot = 0.0, mag = 0.0;
       for (int d = 0; d < D; ++d) {
         double qk = load_elem(q, rh * D + d, q_dtype) *
-                    i8_value(k_pool, oracle_i8_k_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+                    i8_value(k_pool, oracle_i8_k_offset(b, g, t % BS, d, Hkv, D, BS), soff, fmt);
         dot += qk;
         mag += fabs(qk);
       }
@@ -642,7 +704,7 @@ int oracle_prefill_i8(const void* q, int q_dtype, const uint8_t* k_pool, const u
       int64_t b = block_of(block_tables, max_blocks, s, t, BS);
       int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
       for (int d = 0; d < D; ++d)
-        o[d] += x[t] * i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff);
+        o[d] += x[t] * i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff, fmt);
     }
     for (int d = 0; d < D; ++d) o[d] /= z;
     if (spread)
@@ -650,7 +712,7 @@ int oracle_prefill_i8(const void* q, int q_dtype, const uint8_t* k_pool, const u
         int64_t b = block_of(block_tables, max_blocks, s, t, BS);
         int64_t soff = oracle_i8_scale_offset(b, g, t % BS, Hkv, D, BS);
         for (int d = 0; d < D; ++d) {
-          double dv = fabs(i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff) - o[d]);
+          double dv = fabs(i8_value(v_pool, oracle_i8_v_offset(b, g, t % BS, d, Hkv, D, BS), soff, fmt) - o[d]);
           spread[rh * D + d] += x[t] / z * dv;
           if (dv > devmax[rh * D + d]) devmax[rh * D + d] = dv;
         }
@@ -659,4 +721,22 @@ int oracle_prefill_i8(const void* q, int q_dtype, const uint8_t* k_pool, const u
   }
   free(seq_of);
   return bad ? -1 : 0;
+}
+
+/* The INT8 entry points of the formats above. */
+int oracle_decode_i8(const void* q, int q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
+                     const int32_t* block_tables, const int32_t* context_lens, int S, int Hq,
+                     int Hkv, int D, int BS, int max_blocks, float scale, int num_threads,
+                     double* out, double* spread, double* devmax, double* lam) {
+  return oracle_decode_q8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, S, Hq, Hkv, D, BS,
+                          max_blocks, scale, num_threads, out, spread, devmax, lam, OR_Q_I8);
+}
+int oracle_prefill_i8(const void* q, int q_dtype, const uint8_t* k_pool, const uint8_t* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      const int32_t* query_start, int S, int Hq, int Hkv, int D, int BS,
+                      int max_blocks, float scale, int num_threads, double* out,
+                      double* spread, double* devmax, double* lam) {
+  return oracle_prefill_q8(q, q_dtype, k_pool, v_pool, block_tables, context_lens, query_start, S, Hq,
+                           Hkv, D, BS, max_blocks, scale, num_threads, out, spread, devmax, lam,
+                           OR_Q_I8);
 }

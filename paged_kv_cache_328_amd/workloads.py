@@ -96,7 +96,7 @@ class DecodeCase:
     slot_mapping: np.ndarray = None   # [R, S] int64: slot of each new token
     referenced: np.ndarray = None     # [NB] bool: block referenced by some table
     trap_block: int = 0               # unreferenced block used to pad table rows
-    kv_dtype: str = None              # cache type: same as dtype, or "i8" (INT8 pools)
+    kv_dtype: str = None              # cache type: same as dtype, "i8" or "fp8" (8-bit pools)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -112,10 +112,10 @@ class DecodeCase:
         return int(self.context_lens.max()) if self.S else 0
 
     def kv_bytes(self):
-        """K + V bytes over every context (one replica); for INT8 pools the
+        """K + V bytes over every context (one replica); for 8-bit pools the
         codes plus each token's two fp32 scales."""
         tokens = int(self.context_lens.astype(np.int64).sum()) * self.Hkv
-        if self.kv_dtype == "i8":
+        if is_q8(self.kv_dtype):
             return 2 * tokens * (self.D + 4)
         return 2 * tokens * self.D * ELEM_BYTES[self.dtype]
 
@@ -144,17 +144,32 @@ def _fill_pool(rng_k, rng_v, NB, Hkv, D, BS, dtype, referenced, chunk_blocks=204
     return k, v
 
 
+def is_q8(kv_dtype):
+    """Whether a cache type is an 8-bit code format (INT8 or FP8 E4M3)."""
+    return kv_dtype in ("i8", "fp8")
+
+
 def i8_tile_bytes(D, BS):
     """Bytes of one (block, KV head) tile of an INT8 pool: D*BS codes, then
     BS fp32 scales."""
     return D * BS + 4 * BS
 
 
-def _fill_pool_i8(rng_k, rng_v, NB, Hkv, D, BS, referenced, chunk_blocks=2048):
-    """INT8 pools [NB, Hkv, tile] (uint8).  Referenced blocks get random codes
-    (a rounded normal of spread 40, clipped to [-127, 127]) and random scales
-    uniform in [0.01, 0.04]; other blocks get code 0x7F and NaN scales.  Only
-    random numbers are drawn here: no quantisation is performed."""
+def _fp8_codes(rng, shape):
+    """Random finite E4M3 codes: random sign, exponent field 4..13 (magnitudes
+    2^-3 .. 2^6 * 1.875), random mantissa -- drawn as bits, no conversion."""
+    e = rng.integers(4, 14, size=shape)
+    m = rng.integers(0, 8, size=shape)
+    sgn = rng.integers(0, 2, size=shape)
+    return ((sgn << 7) | (e << 3) | m).astype(np.uint8)
+
+
+def _fill_pool_i8(rng_k, rng_v, NB, Hkv, D, BS, referenced, chunk_blocks=2048, fmt="i8"):
+    """8-bit pools [NB, Hkv, tile] (uint8).  Referenced blocks get random codes
+    (INT8: a rounded normal of spread 40, clipped to [-127, 127]; FP8: see
+    _fp8_codes) and random scales uniform in [0.01, 0.04]; other blocks get
+    code 0x7F (an FP8 NaN) and NaN scales.  Only random numbers are drawn
+    here: no quantisation is performed."""
     tile = i8_tile_bytes(D, BS)
     out = []
     for rng in (rng_k, rng_v):
@@ -163,9 +178,13 @@ def _fill_pool_i8(rng_k, rng_v, NB, Hkv, D, BS, referenced, chunk_blocks=2048):
         ids = np.flatnonzero(referenced)
         for i in range(0, ids.size, chunk_blocks):
             sel = ids[i:i + chunk_blocks]
-            codes = np.clip(np.rint(40.0 * rng.standard_normal((sel.size, Hkv, D * BS))), -127, 127)
+            if fmt == "fp8":
+                codes = _fp8_codes(rng, (sel.size, Hkv, D * BS))
+            else:
+                codes = np.clip(np.rint(40.0 * rng.standard_normal((sel.size, Hkv, D * BS))), -127,
+                                127).astype(np.int8).view(np.uint8)
             scales = rng.uniform(0.01, 0.04, size=(sel.size, Hkv, BS)).astype(np.float32)
-            pool[sel, :, :D * BS] = codes.astype(np.int8).view(np.uint8)
+            pool[sel, :, :D * BS] = codes
             pool[sel, :, D * BS:] = scales.view(np.uint8).reshape(sel.size, Hkv, 4 * BS)
         out.append(pool)
     return out[0], out[1]
@@ -189,8 +208,9 @@ def _finish(name, dtype, S, Hq, Hkv, D, BS, NB, partition_size, lens, table_list
                       context_lens=np.asarray(lens, np.int32), block_tables=tables, q=q,
                       referenced=referenced, trap_block=trap)
     case.kv_dtype = kv_dtype or dtype
-    if fill and case.kv_dtype == "i8":
-        case.k_cache, case.v_cache = _fill_pool_i8(rngs["k"], rngs["v"], NB, Hkv, D, BS, referenced)
+    if fill and is_q8(case.kv_dtype):
+        case.k_cache, case.v_cache = _fill_pool_i8(rngs["k"], rngs["v"], NB, Hkv, D, BS, referenced,
+                                                   fmt=case.kv_dtype)
     elif fill:
         case.k_cache, case.v_cache = _fill_pool(rngs["k"], rngs["v"], NB, Hkv, D, BS, dtype, referenced)
     if with_new_token:
