@@ -73,8 +73,14 @@ typedef enum pa_status {
  * scales, one per token: tile = head_dim * block_size + 4 * block_size bytes.
  * A cached value is code * scale.  Codes are made symmetric per (token, KV
  * head) in fp32: scale = max|x| / 127, code = rint(x / scale) clamped to
- * [-127, 127] (a zero row has scale 0). */
-typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_I8 = 3 } pa_dtype;
+ * [-127, 127] (a zero row has scale 0).
+ * PA_FP8 is the other 8-bit cache type: the same pools, tiles and scales
+ * with codes in the OCP E4M3 8-bit float (sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9; largest
+ * finite magnitude 448; S.1111.111 is NaN): scale = max|x| / 448, code = the
+ * E4M3 value nearest to x / scale, ties to an even mantissa, magnitudes of
+ * 448 and more saturated to 448 (the writes never make a NaN code). */
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_I8 = 3, PA_FP8 = 4 } pa_dtype;
 
 /* Static, never-NULL text for a status code. */
 PA_API const char* pa_status_string(pa_status s);
@@ -109,8 +115,8 @@ PA_API const char* pa_status_string(pa_status s);
  * read.  All pointers 16-byte aligned.
  * Supported: dtype f16 / bf16 / f32, head_dim 64 or 128, block_size 8, 16,
  * 32 or 64, any G = num_q_heads / num_kv_heads >= 1.  The caches hold dtype, or
- * (kv_dtype PA_I8, f16 / bf16 only) INT8 codes whose values code * scale
- * stand for K_t and V_t: each code is widened exactly to dtype for the
+ * (kv_dtype PA_I8 or PA_FP8, f16 / bf16 only) 8-bit codes whose values
+ * value(code) * scale stand for K_t and V_t: each code is widened exactly to dtype for the
  * matrix cores, K's scale multiplies the token's logit and V's scale the
  * token's softmax weight before that weight is rounded to dtype.
  * The workspace (caller-allocated device memory, any contents) holds the
@@ -151,9 +157,10 @@ typedef struct pa_decode_args {
    * sequence (copy-on-write it first with pa_copy_blocks). */
   const void* k_new;
   const void* v_new;
-  /* pa_dtype of k_cache / v_cache: equal to dtype, or PA_I8 (INT8 pools, see
-   * pa_dtype) with f16 / bf16 queries.  With PA_I8 a fused append quantises
-   * the new token as pa_write_kv_i8 does; k_new / v_new stay of dtype. */
+  /* pa_dtype of k_cache / v_cache: equal to dtype, or PA_I8 / PA_FP8 (8-bit
+   * pools, see pa_dtype) with f16 / bf16 queries.  With an 8-bit pool a fused
+   * append quantises the new token as pa_write_kv_i8 / pa_write_kv_fp8 does;
+   * k_new / v_new stay of dtype. */
   int32_t kv_dtype;
   /* Optional host copy of context_lens ([num_seqs] int32 in host memory,
    * NULL = none), read during the call.  From the device lengths the library
@@ -281,7 +288,7 @@ PA_API pa_status pa_decode_prefix(const pa_decode_args* args, const pa_prefix_gr
  * query_start [num_seqs + 1] int32 with query_start[0] = 0,
  * non-decreasing, query_start[num_seqs] = num_tokens and 0 <= n_s <=
  * min(c, max_query_len); the caches, tables and lengths as for pa_decode
- * (kv_dtype PA_I8 for INT8 pools).  No workspace.  Device contents are
+ * (kv_dtype PA_I8 / PA_FP8 for 8-bit pools).  No workspace.  Device contents are
  * preconditions; out-of-range lengths are clamped, never read past.  Sizes
  * beyond the launch limits (num_seqs or num_kv_heads above 65535, or more
  * than 2^31 - 1 workgroups of 64 (row, head) slots per sequence and KV head)
@@ -307,7 +314,7 @@ typedef struct pa_prefill_args {
   int32_t max_context_len;     /* host-known upper bound of context_lens */
   float scale;
   int32_t dtype;               /* pa_dtype of q and out */
-  int32_t kv_dtype;            /* dtype, or PA_I8 */
+  int32_t kv_dtype;            /* dtype, PA_I8 or PA_FP8 */
 } pa_prefill_args;
 
 PA_API pa_status pa_prefill(const pa_prefill_args* args, void* stream);
@@ -349,14 +356,25 @@ PA_API pa_status pa_write_kv_i8(const void* k_new, const void* v_new, int32_t sr
                                 int32_t block_size, int32_t num_blocks, void* stream);
 
 /* ------------------------------------------------------------------------
+ * pa_write_kv_fp8 -- pa_write_kv_i8 for FP8 pools (same passages): the rows
+ * are quantised to E4M3 codes as pa_dtype states for PA_FP8; arguments,
+ * layouts and errors as for pa_write_kv_i8.
+ * ------------------------------------------------------------------------ */
+PA_API pa_status pa_write_kv_fp8(const void* k_new, const void* v_new, int32_t src_dtype,
+                                 void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, void* stream);
+
+/* ------------------------------------------------------------------------
  * pa_copy_blocks -- copy-on-write block copies (bmjup.com, section
  * "PagedAttention 的核心工作机制与创新", item 2 "写入时拷贝（Copy-on-Write）";
  * wiblog.cn, section "Copy-on-Write、并行采样与 Prefix Caching 不是同一件
  * 事").  block_mapping is [num_pairs][2] int32 = {src, dst}: every element of
  * physical block dst (all KV heads, K and V) becomes a bit copy of block src.  A dst must not appear twice nor
  * as any pair's src (the pairs pa_seq_append_slot reports satisfy this).
- * Pairs with an id outside [0, num_blocks) are skipped.  dtype PA_I8 copies
- * whole INT8 tiles, codes and scales (block_size must be a multiple of 4).
+ * Pairs with an id outside [0, num_blocks) are skipped.  dtype PA_I8 or
+ * PA_FP8 copies whole 8-bit tiles, codes and scales (block_size must be a
+ * multiple of 4).
  * ------------------------------------------------------------------------ */
 PA_API pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
                                 int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
@@ -370,7 +388,7 @@ PA_API pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* blo
  * Rows t >= context_lens[s] are left untouched.  This is the "concatenate
  * the blocks, then run ordinary attention" route that wiblog.cn (section
  * "非连续 KV 为什么需要专门的 Attention Kernel") warns costs extra copies; it
- * exists only to check addressing.  PA_I8 pools are not supported.
+ * exists only to check addressing.  PA_I8 and PA_FP8 pools are not supported.
  * ------------------------------------------------------------------------ */
 PA_API pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
                               const int32_t* block_tables, const int32_t* context_lens,

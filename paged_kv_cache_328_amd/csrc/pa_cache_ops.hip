@@ -101,10 +101,11 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
   store16(v_out + dst * ESIZE, v);
 }
 
-// Quantising cache write into INT8 pools: one wave per (token, KV head); the
+// Quantising cache write into 8-bit pools: one wave per (token, KV head); the
 // wave quantises the K row, then the V row.  A row x (widened exactly to
-// fp32) gets scale = max|x| / 127 and codes rint(x / scale) clamped to
-// [-127, 127], all in fp32 with correctly rounded division; a zero row gets
+// fp32) gets scale = max|x| / Code::kMax and codes Code::encode(x / scale)
+// (INT8: rint clamped to [-127, 127]; FP8: nearest E4M3, ties to even,
+// saturating), all in fp32 with correctly rounded division; a zero row gets
 // scale 0 and zero codes.  Per (block, KV head) tile: K codes
 // [D/16][BS][16], or V codes [D][BS], then BS fp32 scales.
 template <typename Src>
@@ -113,8 +114,8 @@ __device__ inline float load_src(const void* p, int64_t i) {
   else return Src::to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
 }
 
-template <typename Src>
-__global__ __launch_bounds__(256) void write_kv_i8_kernel(const void* __restrict__ k_new,
+template <typename Src, typename Code>
+__global__ __launch_bounds__(256) void write_kv_q8_kernel(const void* __restrict__ k_new,
                                                           const void* __restrict__ v_new,
                                                           uint8_t* __restrict__ k_cache,
                                                           uint8_t* __restrict__ v_cache,
@@ -144,12 +145,11 @@ __global__ __launch_bounds__(256) void write_kv_i8_kernel(const void* __restrict
       const float other = __shfl_xor(am, off);
       am = other > am ? other : am;
     }
-    const float sc = am / 127.0f;
+    const float sc = am / Code::kMax;
     for (int d = lane; d < D; d += 64) {
-      float r = 0.f;
-      if (sc != 0.f) r = fminf(fmaxf(rintf(load_src<Src>(x, src + d) / sc), -127.f), 127.f);
+      const uint32_t code = sc != 0.f ? Code::encode(load_src<Src>(x, src + d) / sc) : 0u;
       const int64_t off = kv == 0 ? ((int64_t)(d / 16) * BS + o) * 16 + d % 16 : (int64_t)d * BS + o;
-      dst[off] = (uint8_t)(int8_t)(int)r;
+      dst[off] = (uint8_t)code;
     }
     if (lane == 0) *reinterpret_cast<float*>(dst + (int64_t)D * BS + 4 * o) = sc;
   }
@@ -163,6 +163,46 @@ inline bool fits1d(int64_t n) { return (n + 255) / 256 <= 0x7FFFFFFF; }
 }  // namespace pa
 
 using namespace pa;
+
+// The quantising write for 8-bit pools of code format Code.
+template <typename Code>
+pa_status write_kv_q8(const void* k_new, const void* v_new, int32_t src_dtype, void* k_cache,
+                      void* v_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t num_blocks, void* stream) {
+  if (!elem_bytes(src_dtype)) return PA_ERR_INVALID;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return PA_ERR_INVALID;
+  if (head_dim % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !slot_mapping)
+    return PA_ERR_INVALID;
+  const int64_t waves = (int64_t)num_tokens * num_kv_heads;
+  if ((waves + 3) / 4 > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* kc = (uint8_t*)k_cache;
+  uint8_t* vc = (uint8_t*)v_cache;
+  switch (src_dtype) {
+    case PA_F16:
+      write_kv_q8_kernel<F16, Code><<<grid, 256, 0, st>>>(k_new, v_new, kc, vc, slot_mapping,
+                                                          num_tokens, num_kv_heads, head_dim,
+                                                          block_size, num_blocks);
+      break;
+    case PA_BF16:
+      write_kv_q8_kernel<BF16, Code><<<grid, 256, 0, st>>>(k_new, v_new, kc, vc, slot_mapping,
+                                                           num_tokens, num_kv_heads, head_dim,
+                                                           block_size, num_blocks);
+      break;
+    default:
+      write_kv_q8_kernel<float, Code><<<grid, 256, 0, st>>>(k_new, v_new, kc, vc, slot_mapping,
+                                                            num_tokens, num_kv_heads, head_dim,
+                                                            block_size, num_blocks);
+      break;
+  }
+  return launch_status();
+}
 
 extern "C" {
 
@@ -197,42 +237,23 @@ PA_API pa_status pa_write_kv_i8(const void* k_new, const void* v_new, int32_t sr
                                 void* k_cache, void* v_cache, const int64_t* slot_mapping,
                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t block_size, int32_t num_blocks, void* stream) {
-  if (!elem_bytes(src_dtype)) return PA_ERR_INVALID;
-  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
-    return PA_ERR_INVALID;
-  if (head_dim % 16 != 0) return PA_ERR_UNSUPPORTED;
-  if (num_tokens == 0) return PA_OK;
-  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !slot_mapping)
-    return PA_ERR_INVALID;
-  const int64_t waves = (int64_t)num_tokens * num_kv_heads;
-  if ((waves + 3) / 4 > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
-  const unsigned grid = (unsigned)((waves + 3) / 4);
-  hipStream_t st = (hipStream_t)stream;
-  uint8_t* kc = (uint8_t*)k_cache;
-  uint8_t* vc = (uint8_t*)v_cache;
-  switch (src_dtype) {
-    case PA_F16:
-      write_kv_i8_kernel<F16><<<grid, 256, 0, st>>>(k_new, v_new, kc, vc, slot_mapping, num_tokens,
-                                                    num_kv_heads, head_dim, block_size, num_blocks);
-      break;
-    case PA_BF16:
-      write_kv_i8_kernel<BF16><<<grid, 256, 0, st>>>(k_new, v_new, kc, vc, slot_mapping, num_tokens,
-                                                     num_kv_heads, head_dim, block_size, num_blocks);
-      break;
-    default:
-      write_kv_i8_kernel<float><<<grid, 256, 0, st>>>(k_new, v_new, kc, vc, slot_mapping, num_tokens,
-                                                      num_kv_heads, head_dim, block_size, num_blocks);
-      break;
-  }
-  return launch_status();
+  return write_kv_q8<I8Code>(k_new, v_new, src_dtype, k_cache, v_cache, slot_mapping, num_tokens,
+                             num_kv_heads, head_dim, block_size, num_blocks, stream);
+}
+
+PA_API pa_status pa_write_kv_fp8(const void* k_new, const void* v_new, int32_t src_dtype,
+                                 void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, void* stream) {
+  return write_kv_q8<Fp8Code>(k_new, v_new, src_dtype, k_cache, v_cache, slot_mapping, num_tokens,
+                              num_kv_heads, head_dim, block_size, num_blocks, stream);
 }
 
 PA_API pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_mapping,
                                 int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t block_size, int32_t num_blocks, int32_t dtype,
                                 void* stream) {
-  const bool i8 = dtype == PA_I8;
+  const bool i8 = dtype == PA_I8 || dtype == PA_FP8;  // 8-bit tiles: codes, then scales
   const int es = elem_bytes(dtype);
   if (!es && !i8) return PA_ERR_INVALID;
   if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
@@ -258,7 +279,7 @@ PA_API pa_status pa_gather_kv(const void* k_cache, const void* v_cache,
                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
                               int32_t max_blocks_per_seq, int32_t max_context_len, int32_t dtype,
                               void* stream) {
-  if (dtype == PA_I8) return PA_ERR_UNSUPPORTED;
+  if (dtype == PA_I8 || dtype == PA_FP8) return PA_ERR_UNSUPPORTED;
   const int es = elem_bytes(dtype);
   if (!es) return PA_ERR_INVALID;
   if (num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||

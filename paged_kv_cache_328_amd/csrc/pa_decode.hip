@@ -171,8 +171,8 @@ __device__ __forceinline__ float stream_f1(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const float*>(p));
 }
 
-// INT8 codes -> 16-bit operand values (8 codes, exact: Ty::codes4).
-__device__ __forceinline__ int sbyte(uint32_t w, int k) { return (int)(int8_t)(w >> (8 * k)); }
+// 8-bit codes (INT8, or FP8 with an Fp8Elem type) -> 16-bit operand values
+// (8 codes, exact: Ty::codes4).
 template <typename Ty>
 __device__ __forceinline__ u32x4 codes_to_operand(u32x2 c) {
   const u32x2 a = Ty::codes4(c[0]), b = Ty::codes4(c[1]);
@@ -698,10 +698,11 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
         }
       }
     } else {
-      // INT8 caches: quantise the token's K and V rows in fp32 (scale =
-      // max|x| / 127, code = rint(x / scale) clamped to +-127), then add the
-      // token with the values code * scale, as a cache write followed by a
-      // read would.  Each half of the lanes finds its row maximum.
+      // 8-bit caches: quantise the token's K and V rows in fp32 (scale =
+      // max|x| / Code::kMax, codes Code::encode(x / scale): INT8 or FP8),
+      // then add the token with the values value(code) * scale, as a cache
+      // write followed by a read would.  Each half of the lanes finds its
+      // row maximum.
       float xv[4];
       float am = 0.f;
 #pragma unroll
@@ -711,13 +712,11 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
       }
 #pragma unroll
       for (int off = D / 8; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-      const float qsc = am / 127.0f;
+      using Code = typename Ty::Code;
+      const float qsc = am / Code::kMax;
       uint32_t cw = 0;  // this lane's 4 codes
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float rr = qsc > 0.f ? fminf(fmaxf(rintf(xv[j] / qsc), -127.f), 127.f) : 0.f;
-        cw |= (uint32_t)(uint8_t)(int8_t)(int)rr << (8 * j);
-      }
+      for (int j = 0; j < 4; ++j) cw |= (qsc > 0.f ? Code::encode(xv[j] / qsc) : 0u) << (8 * j);
       const float sk_new = __shfl(qsc, 0);
       const float sv_new = __shfl(qsc, D / 4);
       float dot = 0.f;
@@ -729,7 +728,7 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           dot = fmaf(Ty::to_f32((uint16_t)(qw[e / 2] >> (16 * (e & 1)))),
-                     (float)sbyte(kq[e / 4], e % 4), dot);
+                     Code::value((kq[e / 4] >> (8 * (e % 4))) & 0xFFu), dot);
       }
       dot += __shfl_xor(dot, 16);
       dot += __shfl_xor(dot, 32);
@@ -744,7 +743,8 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
       for (int mm = 0; mm < MM; ++mm) {  // V codes of channels 16*mm + 4*g4..+3
         const uint32_t vq = (uint32_t)__shfl((int)cw, D / 4 + 4 * mm + g4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[mm][j] = fmaf(pv, (float)sbyte(vq, j), acc[mm][j] * alpha);
+        for (int j = 0; j < 4; ++j)
+          acc[mm][j] = fmaf(pv, Code::value((vq >> (8 * j)) & 0xFFu), acc[mm][j] * alpha);
       }
       if (store && lane < D / 2) {
         constexpr int SC = I8Tile<D, BS>::kScales;
@@ -2254,9 +2254,9 @@ struct Plan {
 
 pa_status validate(const pa_decode_args* a) {
   if (!a) return PA_ERR_INVALID;
-  if (!elem_bytes(a->dtype) || a->dtype == PA_I8) return PA_ERR_INVALID;
-  // the caches hold q's type, or INT8 codes with scales under 16-bit queries
-  if (a->kv_dtype != a->dtype && !(a->kv_dtype == PA_I8 && a->dtype != PA_F32))
+  if (!elem_bytes(a->dtype)) return PA_ERR_INVALID;
+  // the caches hold q's type, or 8-bit codes with scales under 16-bit queries
+  if (a->kv_dtype != a->dtype && !(is_q8(a->kv_dtype) && a->dtype != PA_F32))
     return PA_ERR_INVALID;
   if (a->num_seqs < 0 || a->num_q_heads <= 0 || a->num_kv_heads <= 0 || a->head_dim <= 0 ||
       a->block_size <= 0 || a->num_blocks <= 0 || a->max_blocks_per_seq <= 0 ||
@@ -2275,7 +2275,7 @@ pa_status validate(const pa_decode_args* a) {
   if (a->dtype == PA_F32 && a->partition_size > kMaxF32Part) return PA_ERR_UNSUPPORTED;
   if (a->products < PA_PRODUCTS_AUTO || a->products > PA_PRODUCTS_VALU) return PA_ERR_INVALID;
   if (a->products == PA_PRODUCTS_VALU &&
-      (a->num_q_heads != a->num_kv_heads || a->kv_dtype == PA_I8 || a->dtype == PA_F32))
+      (a->num_q_heads != a->num_kv_heads || is_q8(a->kv_dtype) || a->dtype == PA_F32))
     return PA_ERR_UNSUPPORTED;
   if (a->context_lens_host)
     for (int s = 0; s < a->num_seqs; ++s)
@@ -2350,7 +2350,7 @@ Plan make_plan(const pa_decode_args* a) {
   }
   if (pl.max_parts > 1)
     pl.ws_bytes = (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * (a->head_dim + 2) * 4;
-  pl.valu = G == 1 && a->kv_dtype != PA_I8 && a->dtype != PA_F32 &&
+  pl.valu = G == 1 && !is_q8(a->kv_dtype) && a->dtype != PA_F32 &&
             (a->products == PA_PRODUCTS_VALU || (a->products == PA_PRODUCTS_AUTO && kValuForMha));
   return pl;
 }
@@ -2387,7 +2387,7 @@ void launch_mfma(const pa_decode_args* a, const Plan& pl, float* ws_acc, float* 
 // (KV head * head group x partitions x sequences).
 int64_t fused_prefix_wgs(const pa_decode_args* a, const Plan& pl, int* px, int* py, int* pz) {
   const int G = a->num_q_heads / a->num_kv_heads;
-  const int NC = a->kv_dtype == PA_I8 ? 1 : kLdsGroups;
+  const int NC = is_q8(a->kv_dtype) ? 1 : kLdsGroups;
   const int64_t tiles = ((int64_t)pl.max_group * G + 16 * NC * kWaves - 1) / (16 * NC * kWaves);
   *px = (int)tiles;
   *py = pl.pre_parts;
@@ -2593,22 +2593,28 @@ pa_status run_plan(const pa_decode_args* a, const Plan& pl, hipStream_t hs) {
     ws_acc = (float*)a->workspace;
     ws_ml = ws_acc + (size_t)a->num_seqs * a->num_q_heads * pl.max_parts * a->head_dim;
   }
-  const bool kv8 = a->kv_dtype == PA_I8;
+  // 8-bit caches: the element type carries the code format (F16 / BF16:
+  // INT8 codes; Fp8Elem: FP8)
+  const bool kv8 = is_q8(a->kv_dtype), fp8 = a->kv_dtype == PA_FP8;
   if (pl.n_grp > 0) {  // shared prefixes and own tokens in one launch (16-bit queries only)
     if (a->dtype == PA_F16) {
-      if (kv8) launch_fused_dims<F16, true>(a, pl, ws_acc, ws_ml, hs);
+      if (fp8) launch_fused_dims<Fp8Elem<F16>, true>(a, pl, ws_acc, ws_ml, hs);
+      else if (kv8) launch_fused_dims<F16, true>(a, pl, ws_acc, ws_ml, hs);
       else launch_fused_dims<F16, false>(a, pl, ws_acc, ws_ml, hs);
     } else {
-      if (kv8) launch_fused_dims<BF16, true>(a, pl, ws_acc, ws_ml, hs);
+      if (fp8) launch_fused_dims<Fp8Elem<BF16>, true>(a, pl, ws_acc, ws_ml, hs);
+      else if (kv8) launch_fused_dims<BF16, true>(a, pl, ws_acc, ws_ml, hs);
       else launch_fused_dims<BF16, false>(a, pl, ws_acc, ws_ml, hs);
     }
   } else switch (a->dtype) {
     case PA_F16:
-      if (kv8) launch_mfma_dims<F16, true>(a, pl, ws_acc, ws_ml, hs);
+      if (fp8) launch_mfma_dims<Fp8Elem<F16>, true>(a, pl, ws_acc, ws_ml, hs);
+      else if (kv8) launch_mfma_dims<F16, true>(a, pl, ws_acc, ws_ml, hs);
       else launch_mfma_dims<F16, false>(a, pl, ws_acc, ws_ml, hs);
       break;
     case PA_BF16:
-      if (kv8) launch_mfma_dims<BF16, true>(a, pl, ws_acc, ws_ml, hs);
+      if (fp8) launch_mfma_dims<Fp8Elem<BF16>, true>(a, pl, ws_acc, ws_ml, hs);
+      else if (kv8) launch_mfma_dims<BF16, true>(a, pl, ws_acc, ws_ml, hs);
       else launch_mfma_dims<BF16, false>(a, pl, ws_acc, ws_ml, hs);
       break;
     default:
@@ -2740,7 +2746,7 @@ PA_API pa_status pa_prefill(const pa_prefill_args* a, void* stream) {
   if (a->dtype != PA_F16 && a->dtype != PA_BF16) {
     return a->dtype == PA_F32 ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID;
   }
-  if (a->kv_dtype != a->dtype && a->kv_dtype != PA_I8) return PA_ERR_INVALID;
+  if (a->kv_dtype != a->dtype && !is_q8(a->kv_dtype)) return PA_ERR_INVALID;
   if (a->num_seqs < 0 || a->num_tokens < 0 || a->num_q_heads <= 0 || a->num_kv_heads <= 0 ||
       a->head_dim <= 0 || a->block_size <= 0 || a->num_blocks <= 0 ||
       a->max_blocks_per_seq <= 0 || a->max_query_len < 0 || a->max_context_len < 0)
@@ -2765,12 +2771,14 @@ PA_API pa_status pa_prefill(const pa_prefill_args* a, void* stream) {
       tiles * a->num_kv_heads * a->num_seqs > 0x7FFFFFFF)
     return PA_ERR_UNSUPPORTED;
   hipStream_t hs = (hipStream_t)stream;
-  const bool kv8 = a->kv_dtype == PA_I8;
+  const bool kv8 = is_q8(a->kv_dtype), fp8 = a->kv_dtype == PA_FP8;
   if (a->dtype == PA_F16) {
-    if (kv8) launch_prefill_dims<F16, true>(a, hs);
+    if (fp8) launch_prefill_dims<Fp8Elem<F16>, true>(a, hs);
+    else if (kv8) launch_prefill_dims<F16, true>(a, hs);
     else launch_prefill_dims<F16, false>(a, hs);
   } else {
-    if (kv8) launch_prefill_dims<BF16, true>(a, hs);
+    if (fp8) launch_prefill_dims<Fp8Elem<BF16>, true>(a, hs);
+    else if (kv8) launch_prefill_dims<BF16, true>(a, hs);
     else launch_prefill_dims<BF16, false>(a, hs);
   }
   return launch_status();

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pagedattn.h"
 
 namespace pa {
@@ -19,9 +21,53 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
-// 16-bit element types: storage is the raw 16-bit pattern.
+// 8-bit codes of quantised caches (one fp32 scale per token and KV head; a
+// cached value is value(code) * scale; a row x is stored with scale =
+// max|x| / kMax and codes encode(x / scale), all in fp32).
+// INT8: symmetric integers, encode = round to nearest even, clamped to
+// [-127, 127].
+struct I8Code {
+  static constexpr float kMax = 127.f;
+  static __device__ __forceinline__ uint32_t encode(float r) {
+    return (uint32_t)(uint8_t)(int8_t)(int)fminf(fmaxf(rintf(r), -127.f), 127.f);
+  }
+  static __device__ __forceinline__ float value(uint32_t b) { return (float)(int8_t)(uint8_t)b; }
+};
+
+// FP8: the OCP E4M3 8-bit float (sign, 4 exponent bits with bias 7, 3
+// mantissa bits; exponent field 0 holds the subnormals m * 2^-9; the largest
+// finite magnitude is 448, and S.1111.111 is NaN).  encode rounds to the
+// nearest E4M3 value, ties to an even mantissa, and saturates magnitudes of
+// 448 and more (and NaN) to 448, so it never makes a NaN code.  value reads
+// S.1111.111 as 480 (the exponent rule continued): a NaN code, found only in
+// slots no token was written to, then meets a zero weight as a finite value.
+struct Fp8Code {
+  static constexpr float kMax = 448.f;
+  static __device__ __forceinline__ uint32_t encode(float r) {
+    const uint32_t u = __float_as_uint(r);
+    const uint32_t sgn = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;  // |r|
+    if (!(__uint_as_float(a) < 448.f)) return sgn | 0x7Eu;
+    if (a < 0x3C800000u)  // |r| < 2^-6: the subnormal grid, steps of 2^-9 (8 steps = 2^-6)
+      return sgn | (uint32_t)rintf(__uint_as_float(a) * 512.f);
+    // normal: 3 of the 23 mantissa bits, the 20 dropped ones rounded to
+    // nearest even (a carry moves into the exponent); rebias 127 -> 7
+    const uint32_t rounded = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return sgn | ((rounded >> 20) - (120u << 3));
+  }
+  // exact: the code's bits under an fp32 exponent bias of 127 read the value
+  // times 2^-120 (subnormals included)
+  static __device__ __forceinline__ float value(uint32_t b) {
+    return __uint_as_float(((b & 0x80u) << 24) | ((b & 0x7Fu) << 20)) * 0x1p120f;
+  }
+};
+
+// 16-bit element types: storage is the raw 16-bit pattern.  Code is the
+// format of 8-bit caches read with queries of this type (INT8; Fp8Elem below
+// for FP8), codes4 widens four of its codes to this type, exactly.
 struct F16 {
   using vec8 = f16x8;
+  using Code = I8Code;
   static __device__ __forceinline__ float to_f32(uint16_t u) {
     return (float)__builtin_bit_cast(_Float16, u);
   }
@@ -62,6 +108,7 @@ struct F16 {
 
 struct BF16 {
   using vec8 = bf16x8;
+  using Code = I8Code;
   static __device__ __forceinline__ float to_f32(uint16_t u) {
     return __uint_as_float((uint32_t)u << 16);
   }
@@ -88,6 +135,28 @@ struct BF16 {
   }
   static __device__ __forceinline__ f32x4 mma(vec8 a, vec8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// The element type Base with FP8 (E4M3) cache codes.
+template <typename Base>
+struct Fp8Elem : Base {
+  using Code = Fp8Code;
+  static __device__ __forceinline__ u32x2 codes4(uint32_t c) {
+    if constexpr (std::is_same<Base, F16>::value) {
+      // code b under byte 1 of a 16-bit lane (b << 8), its magnitude moved
+      // down one bit: sign | exponent field << 10 | mantissa << 7 reads as
+      // f16 the value times 2^-8 (subnormals included); times 256 is exact
+      auto w = [](uint32_t t) {
+        const uint32_t h = (t & 0x80008000u) | ((t >> 1) & 0x3F803F80u);
+        return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, h) *
+                                                f16x2{(_Float16)256.f, (_Float16)256.f});
+      };
+      return u32x2{w(__builtin_amdgcn_perm(0u, c, 0x010C000Cu)), w(__builtin_amdgcn_perm(0u, c, 0x030C020Cu))};
+    } else {
+      return u32x2{Base::pack2(Fp8Code::value(c & 0xFFu), Fp8Code::value((c >> 8) & 0xFFu)),
+                   Base::pack2(Fp8Code::value((c >> 16) & 0xFFu), Fp8Code::value(c >> 24))};
+    }
   }
 };
 

@@ -18,6 +18,9 @@ inline int elem_bytes(int32_t dtype) {
   }
 }
 
+// Whether a cache pa_dtype holds 8-bit codes with scales (INT8 or FP8).
+inline bool is_q8(int32_t dtype) { return dtype == PA_I8 || dtype == PA_FP8; }
+
 inline bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
 
 // Status of the launches just made (clears HIP's sticky launch error).

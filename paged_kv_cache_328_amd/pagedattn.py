@@ -28,10 +28,10 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pagedattn.h")
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS = 0, 1, 2, 3
 PA_ERR_HIP, PA_ERR_WORKSPACE, PA_ERR_UNKNOWN_SEQ, PA_ERR_EXISTS = 4, 5, 6, 7
-PA_F32, PA_F16, PA_BF16, PA_I8 = 0, 1, 2, 3
+PA_F32, PA_F16, PA_BF16, PA_I8, PA_FP8 = 0, 1, 2, 3, 4
 PA_PRODUCTS_AUTO, PA_PRODUCTS_MATRIX, PA_PRODUCTS_VALU = 0, 1, 2
 PRODUCTS = {"auto": PA_PRODUCTS_AUTO, "matrix": PA_PRODUCTS_MATRIX, "valu": PA_PRODUCTS_VALU}
-DTYPE_NAMES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "i8": PA_I8}
+DTYPE_NAMES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "i8": PA_I8, "fp8": PA_FP8}
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -97,6 +97,8 @@ def lib():
         "pa_write_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
         "pa_write_kv_i8": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                           _P]),
+        "pa_write_kv_fp8": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                           _P]),
         "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
         "pa_gather_kv": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                         _I32, _I32, _I32, _P]),
@@ -182,26 +184,37 @@ def _workspace(need, device, stream):
 
 
 def is_i8(k_cache):
+    """An INT8 pool: a uint8 tensor [NB, Hkv, tile bytes]."""
     return k_cache.dtype == _torch().uint8
 
 
+def is_fp8(k_cache):
+    """An FP8 (E4M3) pool: a float8_e4m3fn tensor [NB, Hkv, tile bytes] (the
+    scales sit in its bytes like the codes)."""
+    return k_cache.dtype == _torch().float8_e4m3fn
+
+
+def is_q8(k_cache):
+    return is_i8(k_cache) or is_fp8(k_cache)
+
+
 def i8_tile_bytes(head_dim, block_size):
-    """Bytes of one (block, KV head) tile of an INT8 pool."""
+    """Bytes of one (block, KV head) tile of an 8-bit (INT8 or FP8) pool."""
     return head_dim * block_size + 4 * block_size
 
 
 def cache_geometry(k_cache, v_cache, head_dim=None):
     """(NB, Hkv, D, BS) of the two pools; checks they agree with the layout.
-    INT8 pools need head_dim."""
-    if is_i8(k_cache):
+    8-bit pools need head_dim."""
+    if is_q8(k_cache):
         if head_dim is None:
-            raise ValueError("INT8 pools need head_dim")
+            raise ValueError("8-bit pools need head_dim")
         if k_cache.dim() != 3 or tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype:
-            raise ValueError("INT8 pools must both be [NB, Hkv, D*BS + 4*BS] uint8")
+            raise ValueError("8-bit pools must both be [NB, Hkv, D*BS + 4*BS] of one 1-byte dtype")
         NB, Hkv, tile = k_cache.shape
         D = int(head_dim)
         if D <= 0 or tile % (D + 4):
-            raise ValueError(f"INT8 tile of {tile} bytes does not fit head_dim {D}")
+            raise ValueError(f"8-bit tile of {tile} bytes does not fit head_dim {D}")
         return NB, Hkv, D, tile // (D + 4)
     if k_cache.dim() != 5 or v_cache.dim() != 4 or k_cache.dtype != v_cache.dtype:
         raise ValueError("k_cache must be [NB, Hkv, D/x, BS, x] and v_cache [NB, Hkv, D, BS]")
@@ -225,9 +238,9 @@ def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale
     exists.  The struct keeps the int32 copy it points to alive."""
     S, Hq, Dq = q.shape
     NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, Dq)
-    i8 = is_i8(k_cache)
+    q8 = is_q8(k_cache)
     if (Dq != D or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or
-            (q.dtype != k_cache.dtype and not i8)):
+            (q.dtype != k_cache.dtype and not q8)):
         raise ValueError("q / out must be [S, Hq, D] of the cache's dtype")
     torch = _torch()
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
@@ -242,7 +255,7 @@ def make_decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale
     a.max_context_len = int(max_context_len)
     a.scale = float(scale)
     a.dtype = _dtype_code(q)
-    a.kv_dtype = PA_I8 if i8 else _dtype_code(k_cache)
+    a.kv_dtype = _pool_code(k_cache)
     a.partition_size = int(partition_size)
     a.products = PRODUCTS[products]
     if workspace is not None:
@@ -320,9 +333,9 @@ def make_prefill_args(out, q, k_cache, v_cache, block_tables, context_lens, quer
     """Fill a pa_prefill_args from tensors (no call into the library)."""
     T, Hq, Dq = q.shape
     NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, Dq)
-    i8 = is_i8(k_cache)
+    q8 = is_q8(k_cache)
     if (Dq != D or tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or
-            (q.dtype != k_cache.dtype and not i8)):
+            (q.dtype != k_cache.dtype and not q8)):
         raise ValueError("q / out must be [T, Hq, D] of the cache's dtype")
     torch = _torch()
     S = context_lens.shape[0]
@@ -340,7 +353,7 @@ def make_prefill_args(out, q, k_cache, v_cache, block_tables, context_lens, quer
     a.max_query_len, a.max_context_len = int(max_query_len), int(max_context_len)
     a.scale = float(scale)
     a.dtype = _dtype_code(q)
-    a.kv_dtype = PA_I8 if i8 else _dtype_code(k_cache)
+    a.kv_dtype = _pool_code(k_cache)
     return a
 
 
@@ -469,15 +482,28 @@ def _write_i8_args(k_new, v_new, k_cache, v_cache, slot_mapping, stream):
 def pa_write_kv_i8(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
     """Quantising cache write of k_new / v_new [T, Hkv, D] (float32 / float16
     / bfloat16) into INT8 pools."""
+    if not is_i8(k_cache):
+        raise TypeError("pa_write_kv_i8 writes uint8 (INT8) pools")
     _check(lib().pa_write_kv_i8(*_write_i8_args(k_new, v_new, k_cache, v_cache, slot_mapping, stream)),
            "pa_write_kv_i8")
 
 
+def pa_write_kv_fp8(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
+    """Quantising cache write of k_new / v_new [T, Hkv, D] (float32 / float16
+    / bfloat16) into FP8 (E4M3) pools."""
+    if not is_fp8(k_cache):
+        raise TypeError("pa_write_kv_fp8 writes float8_e4m3fn (FP8) pools")
+    _check(lib().pa_write_kv_fp8(*_write_i8_args(k_new, v_new, k_cache, v_cache, slot_mapping, stream)),
+           "pa_write_kv_fp8")
+
+
 def prepare_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
-    """pa_write_kv (pa_write_kv_i8 for INT8 pools) with its arguments marshalled once."""
-    if is_i8(k_cache):
+    """pa_write_kv (pa_write_kv_i8 / pa_write_kv_fp8 for 8-bit pools) with its
+    arguments marshalled once."""
+    if is_q8(k_cache):
+        name = "pa_write_kv_fp8" if is_fp8(k_cache) else "pa_write_kv_i8"
         args = _write_i8_args(k_new, v_new, k_cache, v_cache, slot_mapping, stream)
-        return PreparedCall("pa_write_kv_i8", lib().pa_write_kv_i8, args,
+        return PreparedCall(name, getattr(lib(), name), args,
                             (k_new, v_new, k_cache, v_cache, slot_mapping))
     NB, Hkv, D, BS = cache_geometry(k_cache, v_cache)
     T = slot_mapping.shape[0]
@@ -492,7 +518,7 @@ def prepare_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
 
 
 def _pool_code(k_cache):
-    return PA_I8 if is_i8(k_cache) else _dtype_code(k_cache)
+    return PA_I8 if is_i8(k_cache) else PA_FP8 if is_fp8(k_cache) else _dtype_code(k_cache)
 
 
 def prepare_copy_blocks(k_cache, v_cache, block_mapping, stream=None, head_dim=None):
@@ -518,7 +544,7 @@ def pa_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None):
 
 
 def pa_copy_blocks(k_cache, v_cache, block_mapping, stream=None, head_dim=None):
-    """Copy-on-write block copies (INT8 pools: whole tiles; pass head_dim)."""
+    """Copy-on-write block copies (8-bit pools: whole tiles; pass head_dim)."""
     NB, Hkv, D, BS = cache_geometry(k_cache, v_cache, head_dim)
     if block_mapping.dtype != _torch().int32 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [P, 2] int32")

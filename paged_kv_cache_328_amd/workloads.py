@@ -157,8 +157,9 @@ def i8_tile_bytes(D, BS):
 
 def _fp8_codes(rng, shape):
     """Random finite E4M3 codes: random sign, exponent field 4..13 (magnitudes
-    2^-3 .. 2^6 * 1.875), random mantissa -- drawn as bits, no conversion."""
-    e = rng.integers(4, 14, size=shape)
+    2^-3 .. 2^6 * 1.875), or 0 (zeros and subnormals) for about 3% of them,
+    random mantissa -- drawn as bits, no conversion."""
+    e = np.where(rng.random(shape) < 0.03, 0, rng.integers(4, 14, size=shape))
     m = rng.integers(0, 8, size=shape)
     sgn = rng.integers(0, 2, size=shape)
     return ((sgn << 7) | (e << 3) | m).astype(np.uint8)

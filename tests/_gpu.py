@@ -17,9 +17,13 @@ def announce(msg):
 
 
 def to_dev(a, dtype):
+    """Host array -> device tensor: "bf16" from uint16 bits, "fp8" (an FP8
+    pool) from uint8 bytes as float8_e4m3fn, else as is."""
     import torch
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEVICE, copy=True)
+    if dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(DEVICE, copy=True).view(torch.float8_e4m3fn)
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEVICE, copy=True)
 
 
@@ -28,7 +32,14 @@ def to_host(t, dtype):
     t = t.detach().cpu().contiguous()
     if dtype == "bf16":
         return t.view(torch.int16).numpy().view(np.uint16)
+    if dtype == "fp8" or t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()
+
+
+def pool_dtype(kv_dtype):
+    """Device pool type of a cache type ("i8" -> uint8 bytes, "fp8" -> FP8 bytes)."""
+    return {"i8": "u8", "fp8": "fp8"}.get(kv_dtype, kv_dtype)
 
 
 def same_bits(a, b):

@@ -54,10 +54,15 @@ def _args(**over):
     ({"dtype": pa.PA_I8}, pa.PA_ERR_INVALID),           # INT8 is a cache type only
     ({"dtype": pa.PA_F32, "kv_dtype": pa.PA_I8}, pa.PA_ERR_INVALID),
     ({"kv_dtype": pa.PA_I8, "head_dim": 96}, pa.PA_ERR_UNSUPPORTED),
+    ({"dtype": pa.PA_FP8}, pa.PA_ERR_INVALID),          # FP8 is a cache type only
+    ({"dtype": pa.PA_F32, "kv_dtype": pa.PA_FP8}, pa.PA_ERR_INVALID),
+    ({"kv_dtype": pa.PA_FP8, "head_dim": 96}, pa.PA_ERR_UNSUPPORTED),
+    ({"kv_dtype": 5}, pa.PA_ERR_INVALID),
     ({"products": 3}, pa.PA_ERR_INVALID),
     ({"products": -1}, pa.PA_ERR_INVALID),
     ({"products": pa.PA_PRODUCTS_VALU}, pa.PA_ERR_UNSUPPORTED),          # 8 q heads on 2 KV heads
     ({"products": pa.PA_PRODUCTS_VALU, "num_q_heads": 2, "kv_dtype": pa.PA_I8}, pa.PA_ERR_UNSUPPORTED),
+    ({"products": pa.PA_PRODUCTS_VALU, "num_q_heads": 2, "kv_dtype": pa.PA_FP8}, pa.PA_ERR_UNSUPPORTED),
     ({"products": pa.PA_PRODUCTS_VALU, "num_q_heads": 2, "dtype": pa.PA_F32}, pa.PA_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects_bad_arguments_before_launch(L, over, status):
@@ -75,6 +80,7 @@ def test_products_choice(L):
     assert L.pa_decode_products(_args(products=pa.PA_PRODUCTS_MATRIX, **mha)) == pa.PA_PRODUCTS_MATRIX
     assert L.pa_decode_products(_args(**mha)) in (pa.PA_PRODUCTS_MATRIX, pa.PA_PRODUCTS_VALU)
     assert L.pa_decode_products(_args(kv_dtype=pa.PA_I8, **mha)) == pa.PA_PRODUCTS_MATRIX
+    assert L.pa_decode_products(_args(kv_dtype=pa.PA_FP8, **mha)) == pa.PA_PRODUCTS_MATRIX
     assert L.pa_decode_products(_args(products=7)) == -1
 
 
@@ -180,6 +186,17 @@ def test_cache_ops_reject_bad_arguments(L):
     assert L.pa_copy_blocks(None, None, None, 0, 2, 128, 16, 10, pa.PA_I8, None) == pa.PA_OK
     assert L.pa_gather_kv(None, None, None, None, None, None, 1, 2, 128, 16, 10, 4, 64,
                           pa.PA_I8, None) == pa.PA_ERR_UNSUPPORTED
+    # FP8 pools (the same tiles)
+    assert L.pa_write_kv_fp8(None, None, 9, None, None, None, 1, 2, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert L.pa_write_kv_fp8(None, None, pa.PA_FP8, None, None, None, 1, 2, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert L.pa_write_kv_fp8(None, None, pa.PA_BF16, None, None, None, 1, 2, 72, 16, 10, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_write_kv_fp8(None, None, pa.PA_BF16, None, None, None, 0, 2, 128, 16, 10, None) == pa.PA_OK
+    assert L.pa_write_kv_fp8(None, None, pa.PA_F16, None, None, None, 1, 2, 128, 16, 10, None) == pa.PA_ERR_INVALID
+    assert L.pa_write_kv(None, None, None, None, None, 1, 2, 128, 16, 10, pa.PA_FP8, None) == pa.PA_ERR_INVALID
+    assert L.pa_copy_blocks(None, None, None, 1, 2, 128, 6, 10, pa.PA_FP8, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_copy_blocks(None, None, None, 0, 2, 128, 16, 10, pa.PA_FP8, None) == pa.PA_OK
+    assert L.pa_gather_kv(None, None, None, None, None, None, 1, 2, 128, 16, 10, 4, 64,
+                          pa.PA_FP8, None) == pa.PA_ERR_UNSUPPORTED
 
 
 def test_int8_workspace_matches_16_bit(L):

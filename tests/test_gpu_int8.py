@@ -17,8 +17,8 @@ from oracle import oracle
 from paged_kv_cache_328_amd import pagedattn as pa
 from paged_kv_cache_328_amd import workloads as wl
 import tests._gpu as _g
-from tests._gpu import (TOL, announce, check_attention, i8_scale_min, ints_to_dev, same_bits,
-                        tail_slots, to_dev, to_host)
+from tests._gpu import (TOL, announce, check_attention, i8_scale_min, ints_to_dev, pool_dtype,
+                        same_bits, tail_slots, to_dev, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,13 +43,16 @@ def poison_scales(kp, vp, slots, Hkv, D, BS):
 
 
 def run_i8_decode(case, label, partition_size=None, fused=False, r=0):
-    """Decode over INT8 pools.  Separate: pa_write_kv_i8 of the step's tokens,
-    pools compared with the oracle's write, then pa_decode.  Fused: the slot of
-    position c - 1 is poisoned first and pa_decode appends the token itself;
-    the touched blocks must equal the oracle's write."""
+    """Decode over 8-bit pools (case.kv_dtype "i8" or "fp8").  Separate:
+    pa_write_kv_i8 / pa_write_kv_fp8 of the step's tokens, pools compared with
+    the oracle's write, then pa_decode.  Fused: the slot of position c - 1 is
+    poisoned first and pa_decode appends the token itself; the touched blocks
+    must equal the oracle's write."""
     import torch
-    dtype = case.dtype
-    assert case.kv_dtype == "i8"
+    dtype, fmt = case.dtype, case.kv_dtype
+    assert fmt in ("i8", "fp8")
+    pt = pool_dtype(fmt)
+    write = pa.pa_write_kv_fp8 if fmt == "fp8" else pa.pa_write_kv_i8
     tables = np.ascontiguousarray(case.block_tables[r])
     lens = case.context_lens
     kp, vp = case.k_cache, case.v_cache
@@ -59,23 +62,23 @@ def run_i8_decode(case, label, partition_size=None, fused=False, r=0):
     live = slots >= 0
     if fused:
         poison_scales(kp, vp, slots[live], Hkv, D, BS)
-    announce(f"{label}: upload INT8 pools NB={case.NB} S={case.S} Hq={case.Hq} Hkv={Hkv} "
+    announce(f"{label}: upload {fmt} pools NB={case.NB} S={case.S} Hq={case.Hq} Hkv={Hkv} "
              f"D={D} BS={BS} q={dtype} max_ctx={case.max_context}")
-    kd, vd = to_dev(kp, "u8"), to_dev(vp, "u8")
+    kd, vd = to_dev(kp, pt), to_dev(vp, pt)
     k_new, v_new = np.ascontiguousarray(case.new_k[r]), np.ascontiguousarray(case.new_v[r])
     kn, vn = to_dev(k_new, dtype), to_dev(v_new, dtype)
-    oracle.write_kv_i8(k_new, v_new, dtype, kp, vp, slots, D, BS)
+    oracle.write_kv_i8(k_new, v_new, dtype, kp, vp, slots, D, BS, fmt=fmt)
     if not fused:
-        announce(f"{label}: pa_write_kv_i8 T={case.S}")
-        pa.pa_write_kv_i8(kn, vn, kd, vd, ints_to_dev(slots))
+        announce(f"{label}: {fmt} write T={case.S}")
+        write(kn, vn, kd, vd, ints_to_dev(slots))
         _sync()
-        assert same_bits(to_host(kd, "u8"), kp), f"{label}: K pool after the INT8 write"
-        assert same_bits(to_host(vd, "u8"), vp), f"{label}: V pool after the INT8 write"
+        assert same_bits(to_host(kd, pt), kp), f"{label}: K pool after the {fmt} write"
+        assert same_bits(to_host(vd, pt), vp), f"{label}: V pool after the {fmt} write"
     q = np.ascontiguousarray(case.q[r])
     qd = to_dev(q, dtype)
     out = torch.empty_like(qd)
     P = case.partition_size if partition_size is None else partition_size
-    announce(f"{label}: pa_decode INT8 P={P} fused={fused}")
+    announce(f"{label}: pa_decode {fmt} P={P} fused={fused}")
     extra = dict(k_new=kn, v_new=vn) if fused else {}
     pa.pa_decode(out, qd, kd, vd, ints_to_dev(tables), ints_to_dev(lens), case.scale,
                  case.max_context, partition_size=P, **extra)
@@ -83,9 +86,12 @@ def run_i8_decode(case, label, partition_size=None, fused=False, r=0):
     if fused:
         touched = np.unique(slots[live] // BS)
         idx = torch.from_numpy(touched.astype(np.int64)).to(_g.DEVICE)
-        assert same_bits(to_host(kd.index_select(0, idx), "u8"), kp[touched]), f"{label}: K blocks"
-        assert same_bits(to_host(vd.index_select(0, idx), "u8"), vp[touched]), f"{label}: V blocks"
-    want = oracle.decode_i8(q, dtype, kp, vp, tables, lens, case.scale, D, BS, num_threads=16, bound=True)
+        assert same_bits(to_host(kd.view(torch.uint8).index_select(0, idx), "u8"), kp[touched]), \
+            f"{label}: K blocks"
+        assert same_bits(to_host(vd.view(torch.uint8).index_select(0, idx), "u8"), vp[touched]), \
+            f"{label}: V blocks"
+    want = oracle.decode_i8(q, dtype, kp, vp, tables, lens, case.scale, D, BS, num_threads=16, bound=True,
+                            fmt=fmt)
     return (check_attention(to_host(out, dtype), want, dtype, label, kv_scale_min=i8_scale_min(vp, D, BS)),
             to_host(out, dtype))
 

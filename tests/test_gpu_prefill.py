@@ -12,7 +12,7 @@ from oracle import oracle
 from paged_kv_cache_328_amd import pagedattn as pa
 from paged_kv_cache_328_amd import workloads as wl
 from tests._gpu import (announce, check_attention, i8_scale_min, ints_to_dev, poison_tails,
-                        same_bits, tail_slots, to_dev, to_host)
+                        pool_dtype, same_bits, tail_slots, to_dev, to_host)
 from tests.test_gpu_int8 import poison_scales
 
 pytestmark = pytest.mark.gpu
@@ -26,7 +26,7 @@ def _sync():
 def run_prefill(case, label, q=None, query_start=None, context_lens=None):
     """pa_prefill on the case (optionally other rows / chunk split of it) vs the oracle."""
     import torch
-    dtype, i8 = case.dtype, case.kv_dtype == "i8"
+    dtype, i8 = case.dtype, wl.is_q8(case.kv_dtype)  # i8: an 8-bit pool (INT8 or FP8)
     q = case.q if q is None else q
     qs = case.query_start if query_start is None else query_start
     lens = case.context_lens if context_lens is None else context_lens
@@ -38,7 +38,7 @@ def run_prefill(case, label, q=None, query_start=None, context_lens=None):
         poison_tails(oracle, case.k_cache, case.v_cache, tables, case.context_lens, dtype)
     announce(f"{label}: upload NB={case.NB} S={case.S} T={q.shape[0]} Hq={case.Hq} Hkv={case.Hkv} "
              f"D={case.D} BS={case.BS} q={dtype} kv={case.kv_dtype}")
-    pool_t = "u8" if i8 else dtype
+    pool_t = pool_dtype(case.kv_dtype) if i8 else dtype
     kd, vd = to_dev(case.k_cache, pool_t), to_dev(case.v_cache, pool_t)
     qd = to_dev(q, dtype)
     out = torch.empty_like(qd)
@@ -49,7 +49,7 @@ def run_prefill(case, label, q=None, query_start=None, context_lens=None):
     _sync()
     if i8:
         want = oracle.prefill_i8(q, dtype, case.k_cache, case.v_cache, tables, lens, qs, case.scale,
-                                 case.D, case.BS, num_threads=16, bound=True)
+                                 case.D, case.BS, num_threads=16, bound=True, fmt=case.kv_dtype)
     else:
         want = oracle.prefill(q, case.k_cache, case.v_cache, tables, lens, qs, case.scale, dtype,
                               num_threads=16, bound=True)

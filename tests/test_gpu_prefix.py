@@ -15,7 +15,7 @@ from paged_kv_cache_328_amd import pagedattn as pa
 from paged_kv_cache_328_amd import workloads as wl
 import tests._gpu as _g
 from tests._gpu import (announce, check_attention, i8_scale_min, ints_to_dev, poison_tails,
-                        same_bits, tail_slots, to_dev, to_host)
+                        pool_dtype, same_bits, tail_slots, to_dev, to_host)
 from tests.test_gpu_int8 import poison_scales
 
 pytestmark = pytest.mark.gpu
@@ -29,7 +29,7 @@ def _sync():
 def run_prefix_case(case, group_start, prefix_len, label, fused=False, partition_size=0,
                     min_prefix=False):
     import torch
-    dtype, i8 = case.dtype, case.kv_dtype == "i8"
+    dtype, i8 = case.dtype, wl.is_q8(case.kv_dtype)  # i8: an 8-bit pool (INT8 or FP8)
     tables = np.ascontiguousarray(case.block_tables[0])
     lens = case.context_lens
     kc, vc = case.k_cache, case.v_cache
@@ -38,7 +38,7 @@ def run_prefix_case(case, group_start, prefix_len, label, fused=False, partition
     else:
         poison_tails(oracle, kc, vc, tables, lens, dtype)
     slots = np.ascontiguousarray(case.slot_mapping[0])
-    pool_t = "u8" if i8 else dtype
+    pool_t = pool_dtype(case.kv_dtype) if i8 else dtype
     announce(f"{label}: upload NB={case.NB} S={case.S} groups={len(prefix_len)} Hq={case.Hq} "
              f"Hkv={case.Hkv} D={case.D} BS={case.BS} q={dtype} kv={case.kv_dtype} fused={fused}")
     kd, vd = to_dev(kc, pool_t), to_dev(vc, pool_t)
@@ -47,7 +47,7 @@ def run_prefix_case(case, group_start, prefix_len, label, fused=False, partition
     if fused:
         extra = dict(k_new=to_dev(k_new, dtype), v_new=to_dev(v_new, dtype))
         if i8:
-            oracle.write_kv_i8(k_new, v_new, dtype, kc, vc, slots, case.D, case.BS)
+            oracle.write_kv_i8(k_new, v_new, dtype, kc, vc, slots, case.D, case.BS, fmt=case.kv_dtype)
         else:
             oracle.write_kv(k_new, v_new, kc, vc, slots, dtype)
     q = np.ascontiguousarray(case.q[0])
@@ -64,11 +64,12 @@ def run_prefix_case(case, group_start, prefix_len, label, fused=False, partition
         live = slots >= 0
         touched = np.unique(slots[live] // case.BS)
         idx = torch.from_numpy(touched.astype(np.int64)).to(_g.DEVICE)
-        assert same_bits(to_host(kd.index_select(0, idx), pool_t), kc[touched]), f"{label}: K blocks"
-        assert same_bits(to_host(vd.index_select(0, idx), pool_t), vc[touched]), f"{label}: V blocks"
+        kb, vb = (kd.view(torch.uint8), vd.view(torch.uint8)) if i8 else (kd, vd)
+        assert same_bits(to_host(kb.index_select(0, idx), pool_t), kc[touched]), f"{label}: K blocks"
+        assert same_bits(to_host(vb.index_select(0, idx), pool_t), vc[touched]), f"{label}: V blocks"
     if i8:
         want = oracle.decode_i8(q, dtype, kc, vc, tables, lens, case.scale, case.D, case.BS,
-                                num_threads=16, bound=True)
+                                num_threads=16, bound=True, fmt=case.kv_dtype)
     else:
         want = oracle.decode(q, kc, vc, tables, lens, case.scale, dtype, num_threads=16, bound=True)
     return (check_attention(to_host(out, dtype), want, dtype, label,
@@ -90,12 +91,12 @@ def test_prefix_groups_edge_shapes(dtype, D, BS, Hq, Hkv, fused):
     run_prefix_case(case, gs, shared, f"prefix {dtype} D{D} BS{BS} {Hq}/{Hkv} fused={fused}", fused=fused)
 
 
-@pytest.mark.parametrize("kv", ["i8"])
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("min_prefix", [False, True])
 def test_prefix_groups_int8(kv, fused, min_prefix):
     case, gs, shared = wl.shared_prefix_case(4200, GROUPS, 32, 8, 128, 16, "bf16", kv_dtype=kv)
-    run_prefix_case(case, gs, shared, f"prefix int8 fused={fused} min_prefix={min_prefix}",
+    run_prefix_case(case, gs, shared, f"prefix {kv} fused={fused} min_prefix={min_prefix}",
                     fused=fused, min_prefix=min_prefix)
 
 

@@ -20,8 +20,8 @@ from oracle import oracle
 from paged_kv_cache_328_amd import pagedattn as pa
 from paged_kv_cache_328_amd import workloads as wl
 from tests import _gpu as _g
-from tests._gpu import (announce, check_attention, i8_scale_min, ints_to_dev, poison_tails, same_bits,
-                        tail_slots, to_dev, to_host)
+from tests._gpu import (announce, check_attention, i8_scale_min, ints_to_dev, poison_tails,
+                        pool_dtype, same_bits, tail_slots, to_dev, to_host)
 from tests.test_gpu_int8 import poison_scales
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +35,8 @@ def draw(seed):
     D = int(rng.choice([64, 128]))
     BS = int(rng.choice([8, 16, 32, 64]))
     dtype = str(rng.choice(["f16", "bf16"]))
-    kv = "i8" if rng.random() < 0.3 else None
+    u = rng.random()
+    kv = "i8" if u < 0.3 else "fp8" if u < 0.45 else None
     kind = rng.random()
     if kind < 0.2:
         lens = rng.integers(0, 40, size=S)
@@ -65,7 +66,7 @@ def test_random_configuration(seed):
     lens = c["lens"]
     fused = c["fused"] and max(lens) > 0
     case = wl.random_case(7000 + seed, S, G * Hkv, Hkv, D, BS, dtype, lens, kv_dtype=kv)
-    i8 = kv == "i8"
+    i8 = wl.is_q8(kv)  # an 8-bit pool (INT8 or FP8)
     tables = np.ascontiguousarray(case.block_tables[0])
     lens_np = case.context_lens
     kc, vc = case.k_cache, case.v_cache
@@ -82,7 +83,7 @@ def test_random_configuration(seed):
             oracle.write_kv(nan, nan.copy(), kc, vc, slots[live], dtype)
     label = (f"random seed {seed}: S={S} Hkv={Hkv} G={G} D={D} BS={BS} {dtype} kv={kv} "
              f"max_ctx={case.max_context} P={c['P']} host={c['host']} fused={fused} products={c['products']}")
-    pool_t = "u8" if i8 else dtype
+    pool_t = pool_dtype(kv) if i8 else dtype
     announce(label + ": upload")
     kd, vd = to_dev(kc, pool_t), to_dev(vc, pool_t)
     q = np.ascontiguousarray(case.q[0])
@@ -102,14 +103,15 @@ def test_random_configuration(seed):
         touched = np.unique(slots[live] // BS)
         idx = torch.from_numpy(touched.astype(np.int64)).to(_g.DEVICE)
         if i8:
-            oracle.write_kv_i8(k_new, v_new, dtype, kc, vc, slots, D, BS)
+            oracle.write_kv_i8(k_new, v_new, dtype, kc, vc, slots, D, BS, fmt=kv)
         else:
             oracle.write_kv(k_new, v_new, kc, vc, slots, dtype)
-        assert same_bits(to_host(kd.index_select(0, idx), pool_t), kc[touched]), label + ": K blocks"
-        assert same_bits(to_host(vd.index_select(0, idx), pool_t), vc[touched]), label + ": V blocks"
+        kb, vb = (kd.view(torch.uint8), vd.view(torch.uint8)) if i8 else (kd, vd)
+        assert same_bits(to_host(kb.index_select(0, idx), pool_t), kc[touched]), label + ": K blocks"
+        assert same_bits(to_host(vb.index_select(0, idx), pool_t), vc[touched]), label + ": V blocks"
     if i8:
         want = oracle.decode_i8(q, dtype, kc, vc, tables, lens_np, case.scale, D, BS, num_threads=16,
-                                bound=True)
+                                bound=True, fmt=kv)
     else:
         want = oracle.decode(q, kc, vc, tables, lens_np, case.scale, dtype, num_threads=16, bound=True)
     check_attention(got, want, dtype, label, kv_scale_min=i8_scale_min(vc, D, BS) if i8 else None)
@@ -123,7 +125,8 @@ def draw_prefill(seed):
     D = int(rng.choice([64, 128]))
     BS = int(rng.choice([8, 16, 32, 64]))
     dtype = str(rng.choice(["f16", "bf16"]))
-    kv = "i8" if rng.random() < 0.35 else None
+    u = rng.random()
+    kv = "i8" if u < 0.35 else "fp8" if u < 0.5 else None
     priors = rng.integers(0, 400, size=S)
     chunks = rng.integers(0, 200, size=S)
     priors[rng.random(S) < 0.2] = 0
