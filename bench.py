@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--separate-write", action="store_true",
                     help="write the new tokens with pa_write_kv, then pa_decode (default: "
                          "pa_decode appends them itself)")
-    ap.add_argument("--kv", default="same", choices=["same", "i8"],
+    ap.add_argument("--kv", default="same", choices=["same", "i8", "fp8"],
                     help="KV-cache type: the workload's own element type, or INT8 codes with "
                          "per-token scales (queries keep the workload's type)")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64],
@@ -80,6 +80,30 @@ def parse():
                     help="first run one plain device-to-device copy of this many bytes (a "
                          "known-size reference for hardware byte counters)")
     return ap.parse_args()
+
+
+def random_q8_pools(case, kv, g, dev):
+    """Two 8-bit pools [NB, Hkv, tile] on the device: random codes (INT8 in
+    [-127, 127]; FP8: random sign, exponent field 4..13, mantissa, as bits),
+    then per-token scales uniform in [0.01, 0.04].  FP8 pools are
+    float8_e4m3fn tensors, INT8 ones uint8."""
+    import torch
+    from paged_kv_cache_328_amd import workloads as wl
+    tile, cb = wl.i8_tile_bytes(case.D, case.BS), case.D * case.BS
+    shape = (case.NB, case.Hkv, tile)
+    pools = []
+    for _ in range(2):
+        if kv == "fp8":
+            e = torch.randint(4, 14, shape, dtype=torch.int32, device=dev, generator=g)
+            m = torch.randint(0, 8, shape, dtype=torch.int32, device=dev, generator=g)
+            sgn = torch.randint(0, 2, shape, dtype=torch.int32, device=dev, generator=g)
+            p = ((sgn << 7) | (e << 3) | m).to(torch.uint8)
+        else:
+            p = torch.randint(-127, 128, shape, dtype=torch.int8, device=dev, generator=g).view(torch.uint8)
+        sc = torch.rand((case.NB, case.Hkv, case.BS), device=dev, generator=g) * 0.03 + 0.01
+        p[:, :, cb:] = sc.view(torch.uint8)
+        pools.append(p.view(torch.float8_e4m3fn) if kv == "fp8" else p)
+    return pools
 
 
 def build_case(name, replicas, kv_dtype=None, block_size=16):
@@ -184,8 +208,8 @@ def run_decode(args, dev, name):
     from paged_kv_cache_328_amd import pagedattn as pa
     from paged_kv_cache_328_amd import workloads as wl
 
-    i8 = args.kv == "i8"
-    case = build_case(name, args.replicas, "i8" if i8 else None, args.block_size)
+    i8 = args.kv in ("i8", "fp8")  # 8-bit pools (INT8 or FP8 codes)
+    case = build_case(name, args.replicas, args.kv if i8 else None, args.block_size)
     R, S, dtype = case.replicas, case.S, case.dtype
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
     P = case.partition_size if args.partition_size < 0 else args.partition_size
@@ -194,17 +218,8 @@ def run_decode(args, dev, name):
     g = torch.Generator(device=dev)
     g.manual_seed(wl.base_seed(case.name))
     if i8:
-        # INT8 tiles: codes in [-127, 127], then per-token scales in [0.01, 0.04]
-        tile, cb = wl.i8_tile_bytes(case.D, case.BS), case.D * case.BS
-        pools = []
-        for _ in range(2):
-            p = torch.randint(-127, 128, (case.NB, case.Hkv, tile), dtype=torch.int8, device=dev,
-                              generator=g).view(torch.uint8)
-            sc = torch.rand((case.NB, case.Hkv, case.BS), device=dev, generator=g) * 0.03 + 0.01
-            p[:, :, cb:] = sc.view(torch.uint8)
-            pools.append(p)
-        kd, vd = pools
-        tile_bytes = tile
+        kd, vd = random_q8_pools(case, args.kv, g, dev)
+        tile_bytes = wl.i8_tile_bytes(case.D, case.BS)
     else:
         ks, vs = wl.pool_shapes(case.NB, case.Hkv, case.D, case.BS, dtype)
         kd = torch.randn(ks, dtype=tdt, device=dev, generator=g)
@@ -325,13 +340,13 @@ def run_decode(args, dev, name):
                    "kv_bytes_per_step": kv_bytes,
                    "step": ("pa_copy_blocks(0 pairs) + pa_decode(fused append of the new token)"
                             if fused else "pa_copy_blocks(0 pairs) + %s + pa_decode"
-                            % ("pa_write_kv_i8" if i8 else "pa_write_kv"))},
+                            % ({"i8": "pa_write_kv_i8", "fp8": "pa_write_kv_fp8"}.get(args.kv, "pa_write_kv")))},
         "roofline": {"kernel": "decode_mfma_kernel" + (" (vector-ALU products)" if valu else "")
                      + (" (fused append)" if fused else "")
                      + (" + merge_kernel (split-K)" if split else ""),
                      "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(case.name + (":i8" if i8 else "")
+                     "traffic": measured_traffic(case.name + (":" + args.kv if i8 else "")
                                                  + (f":bs{case.BS}" if case.BS != 16 else ""), P_eff, fused,
                                                  host_lens is not None),
                      "avg_launch_ms": round(decode_ms, 5),
@@ -393,23 +408,15 @@ def bench_prefill(args, dev):
     import torch
     from paged_kv_cache_328_amd import pagedattn as pa
     from paged_kv_cache_328_amd import workloads as wl
-    i8 = args.kv == "i8"
-    case = wl.prefill_llama13b_f16(fill=False, kv_dtype="i8" if i8 else None,
+    i8 = args.kv in ("i8", "fp8")
+    case = wl.prefill_llama13b_f16(fill=False, kv_dtype=args.kv if i8 else None,
                                    block_size=args.block_size)
     dtype = case.dtype
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
     g = torch.Generator(device=dev)
     g.manual_seed(wl.base_seed(case.name))
     if i8:
-        tile, cb = wl.i8_tile_bytes(case.D, case.BS), case.D * case.BS
-        pools = []
-        for _ in range(2):
-            p = torch.randint(-127, 128, (case.NB, case.Hkv, tile), dtype=torch.int8, device=dev,
-                              generator=g).view(torch.uint8)
-            sc = torch.rand((case.NB, case.Hkv, case.BS), device=dev, generator=g) * 0.03 + 0.01
-            p[:, :, cb:] = sc.view(torch.uint8)
-            pools.append(p)
-        kd, vd = pools
+        kd, vd = random_q8_pools(case, args.kv, g, dev)
     else:
         ks, vs = wl.pool_shapes(case.NB, case.Hkv, case.D, case.BS, dtype)
         kd = torch.randn(ks, dtype=tdt, device=dev, generator=g)
@@ -677,6 +684,7 @@ def cpu_baseline_prefill(case, kd, vd, budget_s):
     (all heads), repeated until ~budget_s of CPU work."""
     import torch
     from oracle import oracle
+    from paged_kv_cache_328_amd import workloads as wl
     cores = len(os.sched_getaffinity(0))
     n = int(min(64, case.query_start[1]))
     c = int(case.context_lens[0]) - int(case.query_start[1]) + n  # rows keep their positions
@@ -687,15 +695,15 @@ def cpu_baseline_prefill(case, kd, vd, budget_s):
     lens = np.array([c], np.int32)
     qs = np.array([0, n], np.int32)
     q = np.ascontiguousarray(case.q[:n])
-    kc = kd.index_select(0, idx).cpu().contiguous()
-    vc = vd.index_select(0, idx).cpu().contiguous()
-    i8 = case.kv_dtype == "i8"
-    kc, vc = kc.numpy(), vc.numpy()
+    i8 = wl.is_q8(case.kv_dtype)
+    as_bytes = (lambda x: x.view(torch.uint8)) if i8 else (lambda x: x)  # 8-bit pools as bytes
+    kc = as_bytes(kd).index_select(0, idx).cpu().contiguous().numpy()
+    vc = as_bytes(vd).index_select(0, idx).cpu().contiguous().numpy()
     reps, t0 = 0, time.perf_counter()
     while True:
         if i8:
             oracle.prefill_i8(q, case.dtype, kc, vc, tables, lens, qs, case.scale, case.D, case.BS,
-                              num_threads=cores)
+                              num_threads=cores, fmt=case.kv_dtype)
         else:
             oracle.prefill(q, kc, vc, tables, lens, qs, case.scale, case.dtype, num_threads=cores)
         reps += 1
@@ -793,13 +801,15 @@ def cpu_baseline(case, kd, vd, budget_s):
     idx = torch.from_numpy(used.astype(np.int64)).to(kd.device)
 
     def host(x):
+        if x.dtype == torch.float8_e4m3fn:  # FP8 pools as bytes
+            x = x.view(torch.uint8)
         x = x.index_select(0, idx).cpu().contiguous()
         return (x.view(torch.int16).numpy().view(np.uint16)
                 if x.dtype == torch.bfloat16 else x.numpy())
 
     kc, vc = host(kd), host(vd)
     q = np.ascontiguousarray(case.q[0][:n])
-    i8 = case.kv_dtype == "i8"
+    i8 = wl.is_q8(case.kv_dtype)
     per_tok = (case.D + 4) if i8 else case.D * wl.ELEM_BYTES[dtype]
 
     def timed(rows, threads, budget):
@@ -807,7 +817,7 @@ def cpu_baseline(case, kd, vd, budget_s):
         while True:
             if i8:
                 oracle.decode_i8(q[rows], dtype, kc, vc, tables[rows], lens[rows], case.scale, case.D,
-                                 case.BS, num_threads=threads)
+                                 case.BS, num_threads=threads, fmt=case.kv_dtype)
             else:
                 oracle.decode(q[rows], kc, vc, tables[rows], lens[rows], case.scale, dtype,
                               num_threads=threads)

@@ -532,6 +532,15 @@ struct WaveDecoder : ChunkWalker<WaveDecoder<Ty, D, BS, KV8>, BS> {
 #pragma unroll
           for (int wd = 0; wd < 4; ++wd) r.v[mm][wd] &= keep[wd];
       }
+    } else if constexpr (kFp8Codes<Ty>) {
+      if (t0 + kChunk > cc) {  // zero the codes of tokens past cc (an unwritten slot may hold NaN)
+        const uint32_t keep0 = bytes_before(t0 + 8 * g4, cc), keep1 = bytes_before(t0 + 8 * g4 + 4, cc);
+#pragma unroll
+        for (int mm = 0; mm < MM; ++mm) {
+          r.v[mm][0] &= keep0;
+          r.v[mm][1] &= keep1;
+        }
+      }
     }
 
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
@@ -1642,6 +1651,16 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
         const int d = 16 * mm + i;
         vv8[mm] = lv8(buf)[d * 4 + (g4 ^ ((d >> 2) & 3))];
       }
+      if constexpr (kFp8Codes<Ty>) {
+        if (edge) {  // zero the codes of tokens past the wave's keys (an unwritten slot may hold NaN)
+          const uint32_t keep0 = bytes_before(t0 + 8 * g4, cc), keep1 = bytes_before(t0 + 8 * g4 + 4, cc);
+#pragma unroll
+          for (int mm = 0; mm < MM; ++mm) {
+            vv8[mm][0] &= keep0;
+            vv8[mm][1] &= keep1;
+          }
+        }
+      }
       // scales of tokens 16*t + 4*g4 .. +3 (K, then V)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -1865,17 +1884,24 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
       // and 2 (g / 32) + 1, V code run g (channel g / 4, token group g % 4)
       // one 16-bit vector.  The exact small integers feed the matrix cores
       // as in the per-wave widening; the scales stay in the code buffer.
+      // FP8 codes of tokens past the workgroup's keys are zeroed first (an
+      // unwritten slot may hold a NaN code, which would meet a zero weight).
       auto convert = [&](int j) {
         const int cb = j & 3, ob = j & 1;
+        const int t0 = t_begin + j * kChunk;
+        const bool tail = kFp8Codes<Ty> && t0 + kChunk > c_load;
         for (int g = tid; g < CK8; g += 64 * NW) {
           const int tau = g & (kChunk - 1), j8 = g / kChunk;
-          const u32x4 c = lk8(cb)[j8 * kChunk + tau];
+          u32x4 c = lk8(cb)[j8 * kChunk + tau];
+          if (tail && t0 + tau >= c_load) c = u32x4{0u, 0u, 0u, 0u};
           lck(ob)[2 * j8 * kChunk + tau] = codes_to_operand<Ty>(u32x2{c[0], c[1]});
           lck(ob)[(2 * j8 + 1) * kChunk + tau] = codes_to_operand<Ty>(u32x2{c[2], c[3]});
         }
         for (int g = tid; g < CV8; g += 64 * NW) {
           const int d = g >> 2, qd = g & 3;
-          lcv(ob)[d * 4 + (qd ^ ((d >> 1) & 3))] = codes_to_operand<Ty>(lv8(cb)[d * 4 + (qd ^ ((d >> 2) & 3))]);
+          u32x2 c = lv8(cb)[d * 4 + (qd ^ ((d >> 2) & 3))];
+          if (tail) c = u32x2{c[0] & bytes_before(t0 + 8 * qd, c_load), c[1] & bytes_before(t0 + 8 * qd + 4, c_load)};
+          lcv(ob)[d * 4 + (qd ^ ((d >> 1) & 3))] = codes_to_operand<Ty>(c);
         }
       };
       // Step k: the wave's own loads of chunk k + 1 are done (chunk k + 2's

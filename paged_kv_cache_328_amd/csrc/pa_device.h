@@ -38,9 +38,8 @@ struct I8Code {
 // mantissa bits; exponent field 0 holds the subnormals m * 2^-9; the largest
 // finite magnitude is 448, and S.1111.111 is NaN).  encode rounds to the
 // nearest E4M3 value, ties to an even mantissa, and saturates magnitudes of
-// 448 and more (and NaN) to 448, so it never makes a NaN code.  value reads
-// S.1111.111 as 480 (the exponent rule continued): a NaN code, found only in
-// slots no token was written to, then meets a zero weight as a finite value.
+// 448 and more (and NaN) to 448, so it never makes a NaN code.  value (of a
+// code a write made) is exact.
 struct Fp8Code {
   static constexpr float kMax = 448.f;
   static __device__ __forceinline__ uint32_t encode(float r) {
@@ -138,27 +137,36 @@ struct BF16 {
   }
 };
 
-// The element type Base with FP8 (E4M3) cache codes.
+// The element type Base with FP8 (E4M3) cache codes.  codes4 is the gfx950
+// conversion of two packed E4M3 codes (OCP format, scale 1: exact for every
+// finite code; a NaN code gives NaN, so the kernels zero the codes of slots
+// past a context, which no write has filled, before widening them).
 template <typename Base>
 struct Fp8Elem : Base {
   using Code = Fp8Code;
   static __device__ __forceinline__ u32x2 codes4(uint32_t c) {
-    if constexpr (std::is_same<Base, F16>::value) {
-      // code b under byte 1 of a 16-bit lane (b << 8), its magnitude moved
-      // down one bit: sign | exponent field << 10 | mantissa << 7 reads as
-      // f16 the value times 2^-8 (subnormals included); times 256 is exact
-      auto w = [](uint32_t t) {
-        const uint32_t h = (t & 0x80008000u) | ((t >> 1) & 0x3F803F80u);
-        return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, h) *
-                                                f16x2{(_Float16)256.f, (_Float16)256.f});
-      };
-      return u32x2{w(__builtin_amdgcn_perm(0u, c, 0x010C000Cu)), w(__builtin_amdgcn_perm(0u, c, 0x030C020Cu))};
-    } else {
-      return u32x2{Base::pack2(Fp8Code::value(c & 0xFFu), Fp8Code::value((c >> 8) & 0xFFu)),
-                   Base::pack2(Fp8Code::value((c >> 16) & 0xFFu), Fp8Code::value(c >> 24))};
-    }
+    if constexpr (std::is_same<Base, F16>::value)
+      return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c, 1.f, true))};
+    else
+      return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.f, true))};
   }
 };
+
+// Whether the 8-bit codes of element type Ty are FP8 (whose unwritten slots
+// may hold NaN codes).
+template <typename Ty>
+constexpr bool kFp8Codes = std::is_same<typename Ty::Code, Fp8Code>::value;
+
+// Byte mask of the codes of tokens first .. first + 3 (byte j: token first + j)
+// that lie before end.
+__device__ __forceinline__ uint32_t bytes_before(int first, int end) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m |= first + j < end ? 0xFFu << (8 * j) : 0u;
+  return m;
+}
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
