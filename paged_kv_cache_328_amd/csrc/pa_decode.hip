@@ -2310,7 +2310,7 @@ pa_status validate(const pa_decode_args* a) {
   return PA_OK;
 }
 
-// Partition size when the caller leaves it to the library (16-bit kernel).
+// Partition size when the caller leaves it to the library.
 // Measured on MI355X (non-temporal loads, 4 waves per workgroup): a
 // workgroup streams best when it walks a long run of tokens, but splits must
 // leave enough workgroups to keep every CU's loads in flight, and with mixed
@@ -2321,14 +2321,19 @@ pa_status validate(const pa_decode_args* a) {
 //     [256, 4096] tokens, halved (down to one 32-token chunk) while fewer
 //     than 1024 workgroups would exist even if every context were maximal.
 // Measured on MI355X (4 sequences of 16k..128k tokens, 8 KV heads): P = 512
-// 185 us, 1024 171 us, 2048 162 us, 4096 156 us.
+// 185 us, 1024 171 us, 2048 162 us, 4096 156 us.  8-bit caches move half the
+// bytes per token, so a split pays for its merge at twice the tokens: P starts
+// from max_context / 8 (measured, mixed-length batch of 64 sequences up to
+// 7.6k tokens: INT8 P = 512 43.0 us, 768 40.6, 1024 40.8, 2048 40.5; FP8
+// 41.8, 39.9, 39.9, 39.9).
 int choose_partition(const pa_decode_args* a, int wg_per_part) {
   if (a->dtype == PA_F32) return 512;
   const int64_t base = (int64_t)a->num_seqs * wg_per_part;
   const int64_t max_ctx = a->max_context_len;
   if (max_ctx <= 2048 && base >= 512) return 2048;
+  const int per = is_q8(a->kv_dtype) ? 8 : 16;
   int P = 256;
-  while (P < 4096 && (int64_t)P * 16 < max_ctx) P *= 2;
+  while (P < 4096 && (int64_t)P * per < max_ctx) P *= 2;
   while (P > kChunk && base * ((max_ctx + P - 1) / P) < 1024) P /= 2;
   return max(P, a->block_size);  // a power of two >= 32: a multiple of the block size
 }

@@ -104,18 +104,21 @@ def test_decode_checks_the_host_copy_of_context_lens(L):
     assert L.pa_decode_partition_size(a) == -1
 
 
-@pytest.mark.parametrize("S,Hq,Hkv,max_ctx,want", [
-    (16, 40, 40, 1280, 2048),     # LLaMA-13B-shaped: 640 workgroups, not split
-    (64, 32, 8, 8192, 512),       # mixed lengths up to 8k over 8 KV heads
-    (4, 64, 8, 131072, 4096),     # 16k..128k contexts: 1024 workgroups at 4096
-    (1, 8, 1, 131072, 128),       # one sequence, one KV head: halved to 1024 units
+@pytest.mark.parametrize("S,Hq,Hkv,max_ctx,want,want8", [
+    (16, 40, 40, 1280, 2048, 2048),   # LLaMA-13B-shaped: 640 workgroups, not split
+    (64, 32, 8, 8192, 512, 1024),     # mixed lengths up to 8k over 8 KV heads
+    (4, 64, 8, 131072, 4096, 4096),   # 16k..128k contexts: 1024 workgroups at 4096
+    (1, 8, 1, 131072, 128, 128),      # one sequence, one KV head: halved to 1024 units
 ])
-def test_library_partition_choice(L, S, Hq, Hkv, max_ctx, want):
+def test_library_partition_choice(L, S, Hq, Hkv, max_ctx, want, want8):
     """The heuristic behind partition_size = 0 at the benchmark shapes (a
-    host-side computation; no device memory is touched)."""
-    a = _args(num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv, max_context_len=max_ctx,
-              max_blocks_per_seq=max_ctx // 16, num_blocks=max_ctx // 16)
-    assert L.pa_decode_partition_size(a) == want
+    host-side computation; no device memory is touched); 8-bit caches start
+    from twice the tokens per partition."""
+    shape = dict(num_seqs=S, num_q_heads=Hq, num_kv_heads=Hkv, max_context_len=max_ctx,
+                 max_blocks_per_seq=max_ctx // 16, num_blocks=max_ctx // 16)
+    assert L.pa_decode_partition_size(_args(**shape)) == want
+    for kv in (pa.PA_I8, pa.PA_FP8):
+        assert L.pa_decode_partition_size(_args(kv_dtype=kv, **shape)) == want8
 
 
 def test_decode_rejects_null_pointers_and_missing_workspace(L):
@@ -203,7 +206,6 @@ def test_int8_workspace_matches_16_bit(L):
     a16 = _args(partition_size=32)
     a8 = _args(partition_size=32, kv_dtype=pa.PA_I8)
     assert L.pa_decode_workspace_bytes(a8) == L.pa_decode_workspace_bytes(a16) > 0
-    assert L.pa_decode_partition_size(_args(kv_dtype=pa.PA_I8)) == L.pa_decode_partition_size(_args())
 
 
 # ---------------------------------------------------------------------------- block manager
