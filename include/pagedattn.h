@@ -348,7 +348,9 @@ PA_API pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache
  * num_kv_heads, head_dim] of src_dtype (PA_F32, PA_F16 or PA_BF16); the
  * pools are [num_blocks, num_kv_heads, head_dim * block_size + 4 *
  * block_size] bytes.  head_dim must be a multiple of 16.  Two tokens with
- * the same slot race.
+ * the same slot race.  The rows must hold finite values: a row with an
+ * infinity or a NaN gets unspecified codes and scale (no access leaves the
+ * buffers either way).
  * ------------------------------------------------------------------------ */
 PA_API pa_status pa_write_kv_i8(const void* k_new, const void* v_new, int32_t src_dtype,
                                 void* k_cache, void* v_cache, const int64_t* slot_mapping,
