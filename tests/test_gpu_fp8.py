@@ -64,6 +64,39 @@ def test_write_kv_fp8_bit_exact(src, D, BS):
     assert same_bits(to_host(vd, "fp8"), vp)
 
 
+@pytest.mark.parametrize("src", ["f32", "f16", "bf16"])
+def test_write_kv_fp8_ties(src):
+    """Rounding ties on the device: a row whose maximum is 448 has scale 1
+    exactly, so every quotient is the value itself.  Hand-worked E4M3 codes
+    (ties to the even mantissa): 1.0625 -> 1.0 (56), -1.1875 -> -1.25 (186),
+    1.5 * 2^-9 and 2.5 * 2^-9 -> 2 * 2^-9 (2), 0.5 * 2^-9 -> 0, 7.5 * 2^-9
+    -> 2^-6 (8, into the next exponent), 248 -> 256 (120), -248 -> 248; and
+    the oracle's codes bit for bit."""
+    D, BS, NB, Hkv = 64, 16, 4, 1
+    vals = [448.0, 1.0625, -1.1875, 1.5 * 2.0 ** -9, 2.5 * 2.0 ** -9, 0.5 * 2.0 ** -9, 7.5 * 2.0 ** -9,
+            248.0, -248.0]
+    want = [126, 56, 186, 2, 2, 0, 8, 120, 248]
+    row = np.zeros((1, Hkv, D), np.float32)
+    row[0, 0, :len(vals)] = vals
+    kn = wl.round_to_storage(row, src)
+    assert np.array_equal(wl.storage_to_f32(kn, src) if src != "f32" else kn, row), "values exact in the source type"
+    tile = wl.i8_tile_bytes(D, BS)
+    kp = np.zeros((NB, Hkv, tile), np.uint8)
+    vp = np.zeros((NB, Hkv, tile), np.uint8)
+    slots = np.array([BS + 5], np.int64)
+    kd, vd = to_dev(kp, "fp8"), to_dev(vp, "fp8")
+    announce(f"pa_write_kv_fp8 ties src={src}")
+    pa.pa_write_kv_fp8(to_dev(kn, src), to_dev(kn.copy(), src), kd, vd, ints_to_dev(slots))
+    _sync()
+    oracle.write_kv_i8(kn, kn.copy(), src, kp, vp, slots, D, BS, fmt="fp8")
+    assert same_bits(to_host(kd, "fp8"), kp)
+    assert same_bits(to_host(vd, "fp8"), vp)
+    got = to_host(vd, "fp8")[1, 0, :D * BS].reshape(D, BS)[:len(vals), 5]  # V codes [D][BS], row 5
+    assert [int(x) for x in got] == want
+    scale = to_host(vd, "fp8")[1, 0, D * BS + 4 * 5:D * BS + 4 * 6].view(np.float32)[0]
+    assert scale == 1.0
+
+
 def test_copy_blocks_fp8_bit_exact():
     rng = np.random.default_rng(5200)
     NB, Hkv, D, BS = 40, 4, 128, 16
