@@ -64,3 +64,47 @@ def test_static_scratch_two_calls_second_smaller():
     _static_vs_plain(big, 256, False, "static scratch call 1")
     small = wl.random_case(711, 5, 16, 4, 128, 16, "f16", [700, 33, 1, 1500, 257])
     _static_vs_plain(small, 128, True, "static scratch call 2 (smaller, fused)")
+
+
+@pytest.mark.parametrize("kv", ["i8", "fp8"])
+def test_static_scratch_8bit_pools(kv):
+    """The allocation-free entry point over INT8 and FP8 pools (fused append,
+    split into 256-token partitions): bit for bit pa_decode's result, and the
+    oracle's within the parity bound.  Unused tail slots hold NaN scales."""
+    import torch
+    from tests._gpu import i8_scale_min, pool_dtype, tail_slots
+    from tests.test_gpu_int8 import poison_scales
+    case = wl.random_case(712, 9, 16, 4, 128, 16, "bf16", [1, 40, 300, 1200, 2100, 7, 513, 0, 900],
+                          kv_dtype=kv)
+    D, BS, Hkv, dtype = case.D, case.BS, case.Hkv, case.dtype
+    tables = np.ascontiguousarray(case.block_tables[0])
+    lens = case.context_lens
+    kc, vc = case.k_cache, case.v_cache
+    poison_scales(kc, vc, tail_slots(tables, lens, BS), Hkv, D, BS)
+    pool_t = pool_dtype(kv)
+    q = np.ascontiguousarray(case.q[0])
+    k_new, v_new = np.ascontiguousarray(case.new_k[0]), np.ascontiguousarray(case.new_v[0])
+    qd, td, ld = to_dev(q, dtype), ints_to_dev(tables), ints_to_dev(lens)
+    outs = []
+    for static in (True, False):
+        kd, vd = to_dev(kc, pool_t), to_dev(vc, pool_t)
+        extra = dict(k_new=to_dev(k_new, dtype), v_new=to_dev(v_new, dtype))
+        o = torch.empty_like(qd)
+        announce(f"{kv} pools: {'pa_decode_static' if static else 'pa_decode'} P=256 fused")
+        if static:
+            pa.pa_decode_static(o, qd, kd, vd, td, ld, case.scale, case.max_context, partition_size=256,
+                                **extra)
+        else:
+            a = pa.make_decode_args(o, qd, kd, vd, td, ld, case.scale, case.max_context, 256)
+            ws = torch.full((pa.pa_decode_workspace_bytes(a),), 0x7F, dtype=torch.uint8, device=qd.device)
+            pa.pa_decode(o, qd, kd, vd, td, ld, case.scale, case.max_context, partition_size=256,
+                         workspace=ws, **extra)
+        _sync()
+        outs.append(to_host(o, dtype))
+    assert same_bits(outs[0], outs[1]), f"{kv}: pa_decode_static differs from pa_decode"
+    oracle.write_kv_i8(k_new, v_new, dtype, kc, vc, np.ascontiguousarray(case.slot_mapping[0]), D, BS,
+                       fmt=kv)
+    want = oracle.decode_i8(q, dtype, kc, vc, tables, lens, case.scale, D, BS, num_threads=16, bound=True,
+                            fmt=kv)
+    check_attention(outs[0], want, dtype, f"static scratch {kv} pools",
+                    kv_scale_min=i8_scale_min(vc, D, BS))
