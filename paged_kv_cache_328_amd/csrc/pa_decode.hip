@@ -1383,7 +1383,9 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
   // L2.  The linear id is remapped so that the consecutive workgroups of one
   // XCD are the slot tiles of one (sequence, KV head) -- they read the same
   // K/V lines at about the same time, through one L2 -- while the (sequence,
-  // KV head) pairs are dealt to the XCDs round-robin (balanced work).
+  // KV head) pairs are dealt to the XCDs round-robin (balanced work).  (The
+  // prefill pass over at most 64 (sequence, slot tile) pairs orders its
+  // workgroups by work instead, below.)
   int tile, ya, za;  // grid position after the reordering
   {
     const int X = gx, Y = gy;
@@ -1402,26 +1404,62 @@ __device__ __forceinline__ void prefill_lds_body(int bx, int by, int bz, int gx,
   int hk, s, c, q0, nq, p = 0, t_begin = 0;
   if constexpr (!PFX) {
     hk = ya;
-    // Longest work first: the grid position za is a rank, and the sequence
-    // of rank za is the za-th longest context (ties in sequence order); the
-    // slot tiles of a (sequence, KV head) run last row first, since later
-    // rows see more keys.  The workgroups that start last are then the
-    // short ones, so fewer CUs idle while the grid drains.  Ranks need every
-    // length in one wave (at most 64 sequences); larger batches keep their
-    // order.
+    // Longest work first, so that the workgroups that start last are short
+    // ones and fewer CUs idle while the grid drains.  With at most 64
+    // (sequence, slot tile) pairs the whole grid is ordered by each pair's
+    // work (measured on MI355X, chunked prefill at LLaMA-13B shape: f16
+    // 174.9 / 172.0 -> 171.1 / 169.0 us, INT8 251 / 248 -> 234 / 229 us, FP8
+    // 248 -> 229 us, against the order below; a makespan model of the 960
+    // workgroups on 512 slots gave 93 -> 87 chunk-times, bound 79).  Larger
+    // grids: the grid position za is a rank, and the sequence of rank za is
+    // the za-th longest context (ties in sequence order), its slot tiles
+    // last row first, since later rows see more keys (ranks need every
+    // length in one wave: at most 64 sequences; larger batches keep their
+    // order).
     s = za;
-    if (gz <= kWave) {
-      const int cmax = min(max_ctx, max_blocks * BS);
-      const int lane_c = lane < gz ? clampi(lens[lane], 0, cmax) : -1;
-      int rank = 0;  // sequences ahead of this lane's
-      for (int m = 0; m < gz; ++m) {
-        const int cm = __builtin_amdgcn_readlane(lane_c, m);
-        rank += (cm > lane_c || (cm == lane_c && m < lane)) ? 1 : 0;
+    const int cmax = min(max_ctx, max_blocks * BS);
+    if (gz * gx <= kWave) {
+      // At most 64 (sequence, slot tile) pairs: the grid runs them longest
+      // first across the whole batch, each pair's KV heads together (and
+      // thus spread over the XCDs).  Lane m weighs pair m (sequence m / gx,
+      // tile m % gx) by the keys its last slot sees; the workgroup takes the
+      // pair of rank L / gy (ties in pair order) and KV head L % gy.
+      constexpr int TS = NW * NC * 16;  // slots per tile
+      const int L = bx + gx * (by + gy * bz);
+      const int r = L / gy;
+      hk = L - r * gy;
+      const int npair = gz * gx;
+      int wl = -1;
+      if (lane < npair) {
+        const int sm = lane / gx, jm = lane - sm * gx;
+        const int cm = clampi(lens[sm], 0, cmax);
+        const int q0m = clampi(qstart[sm], 0, num_rows);
+        const int nqm = clampi(qstart[sm + 1] - q0m, 0, min(min(max_q, cm), num_rows - q0m));
+        const int first = jm * TS;
+        wl = first < nqm * G ? cm - nqm + (min(first + TS, nqm * G) - 1) / G + 1 : 0;
       }
-      const uint64_t hit = __ballot(lane < gz && rank == za);
-      s = uniform(__ffsll((unsigned long long)hit) - 1);
+      int rank = 0;  // pairs ahead of this lane's
+      for (int m = 0; m < npair; ++m) {
+        const int wm = __builtin_amdgcn_readlane(wl, m);
+        rank += (wm > wl || (wm == wl && m < lane)) ? 1 : 0;
+      }
+      const uint64_t hit = __ballot(lane < npair && rank == r);
+      const int pick = uniform(__ffsll((unsigned long long)hit) - 1);
+      s = pick / gx;
+      tile = pick - s * gx;
+    } else {
+      if (gz <= kWave) {
+        const int lane_c = lane < gz ? clampi(lens[lane], 0, cmax) : -1;
+        int rank = 0;  // sequences ahead of this lane's
+        for (int m = 0; m < gz; ++m) {
+          const int cm = __builtin_amdgcn_readlane(lane_c, m);
+          rank += (cm > lane_c || (cm == lane_c && m < lane)) ? 1 : 0;
+        }
+        const uint64_t hit = __ballot(lane < gz && rank == za);
+        s = uniform(__ffsll((unsigned long long)hit) - 1);
+      }
+      tile = gx - 1 - tile;
     }
-    tile = gx - 1 - tile;
     c = clampi(lens[s], 0, min(max_ctx, max_blocks * BS));
     q0 = clampi(qstart[s], 0, num_rows);
     nq = clampi(qstart[s + 1] - q0, 0, min(min(max_q, c), num_rows - q0));
