@@ -153,3 +153,40 @@ def test_prefill_rank_order_batches(kv, S):
         priors[s], chunks[s] = 20, 12
     case = wl.prefill_case(3600 + S, priors, chunks, 8, 2, 64, 16, "bf16", kv_dtype=kv)
     run_prefill(case, f"rank order S={S} kv={kv}")
+
+
+@pytest.mark.parametrize("kv", [None, "i8"])
+@pytest.mark.parametrize("S", [6, 30])
+def test_prefill_batch_order_leaves_rows_bit_identical(kv, S):
+    """The grid order depends on the whole batch (at most 64 (sequence, slot
+    tile) pairs: every pair longest first; more: sequences longest first),
+    so the workgroup that computes a row changes with the batch.  The same
+    sequences in reversed order give every row bit for bit; 6 sequences (18
+    or 24 pairs) take the first order, 30 (90 or 120) the second."""
+    import torch
+    rng = np.random.default_rng(3700 + S)
+    priors = rng.integers(0, 300, size=S).tolist()
+    chunks = rng.integers(1, 100, size=S).tolist()
+    G, Hkv = 4, 2
+    case = wl.prefill_case(3700 + S, priors, chunks, G * Hkv, Hkv, 64, 16, "bf16", kv_dtype=kv)
+    pool_t = pool_dtype(kv) if kv else "bf16"
+    kd, vd = to_dev(case.k_cache, pool_t), to_dev(case.v_cache, pool_t)
+    qs, lens, tables = case.query_start, case.context_lens, case.block_tables
+    outs = []
+    for order in (list(range(S)), list(range(S))[::-1]):
+        rows = [np.arange(qs[s], qs[s + 1]) for s in order]
+        q = np.ascontiguousarray(case.q[np.concatenate(rows)])
+        qs2 = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+        qd = to_dev(q, "bf16")
+        out = torch.empty_like(qd)
+        announce(f"batch order S={S} kv={kv} reversed={order[0] != 0}")
+        pa.pa_prefill(out, qd, kd, vd, ints_to_dev(np.ascontiguousarray(tables[order])),
+                      ints_to_dev(np.ascontiguousarray(lens[order])), ints_to_dev(qs2), case.scale,
+                      int(np.max(np.diff(qs2))), int(lens.max()))
+        _sync()
+        got = to_host(out, "bf16")
+        back = np.empty_like(got)
+        for k, s in enumerate(order):
+            back[qs[s]:qs[s + 1]] = got[qs2[k]:qs2[k + 1]]
+        outs.append(back)
+    assert same_bits(outs[0], outs[1]), "the batch order changed a row"
